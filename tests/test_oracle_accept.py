@@ -1,0 +1,172 @@
+"""Pins for the oracle's acceptance step (O7): greedy brute force, the pages' worked
+walk-through, planted paths, tie rules, and the chi-square losslessness check."""
+import json
+import os
+
+import numpy as np
+import pytest
+from scipy import stats
+
+from oracle import eagle3_oracle as O
+from speculative_decoding_round_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "accept_walk.json")
+
+
+def brute_force_greedy(parents, tokens, logits):
+    """Enumerate every root-to-node path from the root downwards (depth-first) and keep
+    the longest whose every edge token is the argmax of its parent's row; ties go to the
+    lowest end-node index.  Returns (length, end node)."""
+    n = len(parents)
+    children = {i: [j for j in range(n) if parents[j] == i] for i in range(n)}
+    am = [int(max(range(logits.shape[1]), key=lambda t: (logits[i, t], -t))) for i in range(n)]
+    best = (0, 0)
+    stack = [(0, 0)]
+    while stack:
+        node, L = stack.pop()
+        if L > best[0] or (L == best[0] and node < best[1]):
+            best = (L, node)
+        for c in children[node]:
+            if tokens[c] == am[node]:
+                stack.append((c, L + 1))
+    return best, am
+
+
+def test_worked_walkthrough():
+    with open(GOLD) as f:
+        g = json.load(f)
+    par, tok = g["parents"], g["tokens"]
+    n, V = len(par), g["vocab"]
+    logits = np.zeros((n, V), dtype=np.float32)
+    for i in range(n):
+        logits[i, (i * 7 + 3) % V] = 1.0        # an argmax no child token equals
+    for i, t in g["target_argmax"].items():
+        logits[int(i)] = 0.0
+        logits[int(i), t] = 2.0
+    acc, path, outt, bonus = O.accept([0, n], tok, par, logits, 0.0, 0, 0, 2)
+    e = g["expect"]
+    assert acc[0] == e["accept_len"]
+    assert list(path[0]) == e["path"]
+    assert list(outt[0]) == e["out_tokens"]
+    assert bonus[0] == e["bonus"]
+    assert g["parents"][path[0][-1]] == 1     # x_1a is a child of x_1
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_greedy_equals_bruteforce_with_planted_paths(seed):
+    V = 40
+    rng = np.random.default_rng(seed)
+    trees = [synth.random_tree(int(n), 6, seed * 31 + k) for k, n in enumerate(rng.integers(1, 30, 4))]
+    par = [p for t in trees for p in t]
+    cu = [0]
+    for t in trees:
+        cu.append(cu[-1] + len(t))
+    import torch
+    tokens = torch.tensor(rng.integers(0, V, cu[-1]), dtype=torch.int32)
+    logits = torch.tensor(rng.standard_normal((cu[-1], V)), dtype=torch.float32)
+    planted = []
+    for b, t in enumerate(trees):
+        end = int(rng.integers(0, len(t)))
+        synth.plant_path(logits, tokens, t, cu[b], end)
+        planted.append(end)
+    acc, path, outt, bonus = O.accept(cu, tokens.tolist(), par, logits, 0.0, 0, 0, 6)
+    for b, t in enumerate(trees):
+        lg = logits[cu[b]:cu[b + 1]].numpy()
+        (L, end), am = brute_force_greedy(t, tokens[cu[b]:cu[b + 1]].tolist(), lg)
+        assert acc[b] == L
+        assert path[b][L] == end and all(x == -1 for x in path[b][L + 1:])
+        assert bonus[b] == am[end]
+        d_planted = 0
+        j = planted[b]
+        while t[j] >= 0:
+            d_planted += 1
+            j = t[j]
+        assert acc[b] >= d_planted
+        assert outt[b][L] == bonus[b]
+
+
+def test_no_match_and_root_only():
+    logits = np.zeros((3, 8), dtype=np.float32)
+    logits[:, 5] = 1.0
+    acc, path, outt, bonus = O.accept([0, 3], [0, 1, 2], [-1, 0, 1], logits, 0.0, 0, 0, 2)
+    assert acc[0] == 0 and bonus[0] == 5 and list(path[0]) == [0, -1, -1]
+    assert list(outt[0]) == [5, -1, -1]
+    acc, path, outt, bonus = O.accept([0, 1], [3], [-1], logits[:1], 0.0, 0, 0, 0)
+    assert acc[0] == 0 and bonus[0] == 5
+
+
+def test_duplicate_siblings_and_ties():
+    # two siblings carry the same (matching) token; both are length-1 paths -> the lower
+    # index wins; a deeper match under the higher-index sibling wins by length
+    par = [-1, 0, 0, 2]
+    tok = [9, 4, 4, 6]
+    logits = np.zeros((4, 10), dtype=np.float32)
+    logits[0, 4] = 1
+    logits[1, 1] = 1
+    logits[2, 7] = 1
+    logits[3, 2] = 1
+    acc, path, _, bonus = O.accept([0, 4], tok, par, logits, 0.0, 0, 0, 2)
+    assert acc[0] == 1 and path[0][1] == 1 and bonus[0] == 1
+    logits[2, 7] = 0
+    logits[2, 6] = 1
+    acc, path, _, bonus = O.accept([0, 4], tok, par, logits, 0.0, 0, 0, 2)
+    assert acc[0] == 2 and list(path[0]) == [0, 2, 3] and bonus[0] == 2
+    # greedy ties inside a row go to the lowest token id
+    logits = np.zeros((1, 6), dtype=np.float32)
+    logits[0, [2, 4]] = 3.0
+    assert O.node_draw(logits[0], 0.0, 0, 0, 0, 0) == 2
+
+
+def test_low_temperature_matches_greedy():
+    rng = np.random.default_rng(3)
+    z = (np.arange(64) * 0.1 + 0.05).astype(np.float32)[rng.permutation(64)]
+    g = O.node_draw(z, 0.0, 1, 0, 0, 0)
+    for r in range(20):
+        assert O.node_draw(z, 1e-3, 11, r, 0, 2) == g
+
+
+def test_sampler_consistent_with_vectorised_draws():
+    rng = np.random.default_rng(4)
+    z = rng.standard_normal(16).astype(np.float32)
+    rounds = np.arange(300)
+    v = O.draws_over_rounds(z, 0.7, 77, rounds, 2, 5)
+    for r in range(0, 300, 13):
+        assert v[r] == O.node_draw(z, 0.7, 77, r, 2, 5)
+
+
+@pytest.mark.slow
+def test_chi_square_lossless():
+    """Speculative sampling must reproduce the target distribution: on the K=3 two-level
+    tree with V=16 and T=1, the first emitted token follows softmax(z_root), and the
+    second token, conditioned on accepting child c, follows softmax(z_c); 1e6 draws,
+    chi-square p > 0.01."""
+    V, T = 16, 1.0
+    rng = np.random.default_rng(5)
+    par = synth.full_tree(3, 2)
+    n = len(par)
+    tok = [0] + [int(x) for x in rng.choice(V, 3, replace=False)] + \
+        [int(x) for x in rng.integers(0, V, 9)]
+    z = (rng.standard_normal((n, V)) * 1.2).astype(np.float32)
+    rounds = np.arange(1_000_000, dtype=np.uint64)
+    seed = 20260601
+    y_root = O.draws_over_rounds(z[0], T, seed, rounds, 0, 0)
+
+    def probs(row):
+        p = np.exp(row.astype(np.float64) - row.max())
+        return p / p.sum()
+
+    obs = np.bincount(y_root, minlength=V)
+    p = probs(z[0] / T)
+    assert stats.chisquare(obs, p * obs.sum()).pvalue > 0.01
+    # second token given the accepted depth-1 child c
+    for c in (1, 2, 3):
+        sel = rounds[y_root == tok[c]]
+        y_c = O.draws_over_rounds(z[c], T, seed, sel, 0, c)
+        obs = np.bincount(y_c, minlength=V)
+        pc = probs(z[c] / T)
+        keep = pc * obs.sum() >= 5
+        assert stats.chisquare(obs[keep], pc[keep] / pc[keep].sum() * obs[keep].sum()).pvalue > 0.01
+    # the full acceptance rule on a sample of rounds emits exactly those draws
+    for r in range(0, 400):
+        acc, path, outt, bonus = O.accept([0, n], tok, par, z, T, seed, r, 2)
+        assert outt[0][0] == y_root[r]

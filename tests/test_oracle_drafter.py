@@ -1,0 +1,199 @@
+"""Pins for the oracle's drafter (O1, O2), top-K/LSE (A7) and tree expansion (O3)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as Fnn
+
+from oracle import eagle3_oracle as O
+from speculative_decoding_round_amd import synth
+
+SMALL = synth.scaled(synth.TINY, d=32, Hq=4, Hkv=2, Dh=8, F=48, V=50)
+
+
+def small_drafter(seed=0, shape=SMALL):
+    w = synth.drafter_weights(shape, seed=seed)
+    return w, O.Drafter(w, shape.Hq, shape.Hkv, shape.Dh)
+
+
+def test_fusion_identity_block():
+    d = 16
+    rng = np.random.default_rng(0)
+    h = [rng.standard_normal((3, d)) for _ in range(3)]
+    wf = np.concatenate([np.eye(d), np.zeros((d, d)), np.zeros((d, d))], axis=1)
+    np.testing.assert_array_equal(O.fuse_features(*h, wf), h[0])
+    wf = np.concatenate([np.zeros((d, d)), 2 * np.eye(d), -np.eye(d)], axis=1)
+    np.testing.assert_allclose(O.fuse_features(*h, wf), 2 * h[1] - h[2])
+
+
+def test_rope_properties():
+    rng = np.random.default_rng(1)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    np.testing.assert_array_equal(O.rope(q, 0, 5e5), q)
+    for p in (1, 17, 4097, 65543):
+        assert abs(np.linalg.norm(O.rope(q, p, 5e5)) - np.linalg.norm(q)) < 1e-12
+    # scores depend only on the position difference
+    a = O.rope(q, 100, 5e5) @ O.rope(k, 37, 5e5)
+    b = O.rope(q, 1100, 5e5) @ O.rope(k, 1037, 5e5)
+    assert abs(a - b) < 1e-9
+    # complex-number form: (x_i + i x_{i+half}) * e^{i pos theta^(-2i/Dh)}
+    half = 32
+    zc = (q[:half] + 1j * q[half:]) * np.exp(1j * 77 * 5e5 ** (-2 * np.arange(half) / 64))
+    np.testing.assert_allclose(O.rope(q, 77, 5e5), np.concatenate([zc.real, zc.imag]), rtol=1e-12)
+
+
+def test_rmsnorm_closed_forms():
+    g = np.full(8, 2.0)
+    x = np.full(8, 3.0)
+    np.testing.assert_allclose(O.rmsnorm(x, g, 1e-5), 2 * 3 / math.sqrt(9 + 1e-5))
+    rng = np.random.default_rng(2)
+    y = rng.standard_normal(8)
+    r = O.rmsnorm(y, np.ones(8), 0.0)
+    assert abs(np.mean(r * r) - 1.0) < 1e-12
+
+
+def test_topk_and_lse():
+    z = np.array([1.0, 3.0, 3.0, -1.0, 2.0, 3.0, 0.0])
+    ids, vals = O.topk_desc(z, 4)
+    ref = sorted(range(len(z)), key=lambda t: (-z[t], t))[:4]
+    assert list(ids) == ref == [1, 2, 5, 4]
+    assert list(vals) == [3.0, 3.0, 3.0, 2.0]
+    rng = np.random.default_rng(3)
+    row = rng.standard_normal(1000) * 4
+    assert abs(np.sum(np.exp(row - O.log_sum_exp(row))) - 1.0) < 1e-12
+    assert abs(O.log_sum_exp(np.zeros(16)) - math.log(16)) < 1e-14
+
+
+def textbook_layer(w, shape, tokens, feats_fn, P, kpre, vpre):
+    """A Llama-style decoder layer written with torch ops (F.rms_norm, F.linear, complex
+    RoPE, grouped scaled_dot_product_attention, F.silu), run along a chain of nodes where
+    node t's feature is node t-1's output (the drafter recursion).  Returns per node
+    (a, z, lse)."""
+    d, Hq, Hkv, Dh, F = shape.d, shape.Hq, shape.Hkv, shape.Dh, shape.F
+    W = {k: v.double() for k, v in w.items()}
+    eps = 1e-5
+
+    def rot(x, pos):
+        half = Dh // 2
+        fr = torch.tensor(500000.0, dtype=torch.float64) ** (-2 * torch.arange(half, dtype=torch.float64) / Dh)
+        c = torch.polar(torch.ones(half, dtype=torch.float64), pos * fr)
+        z = torch.complex(x[..., :half], x[..., half:]) * c
+        return torch.cat([z.real, z.imag], dim=-1)
+
+    keys = [kpre.double()]
+    vals = [vpre.double()]
+    outs = []
+    f = None
+    for t, tok in enumerate(tokens):
+        f = feats_fn(t, f)
+        e = W["embed"][tok]
+        u = torch.cat([Fnn.rms_norm(e, (d,), W["g_embed"], eps), Fnn.rms_norm(f, (d,), W["g_feat"], eps)])
+        y = Fnn.linear(u, W["w_qkv"])
+        q = rot(y[:Hq * Dh].view(Hq, Dh), P + t)
+        k = rot(y[Hq * Dh:(Hq + Hkv) * Dh].view(Hkv, Dh), P + t)
+        v = y[(Hq + Hkv) * Dh:].view(Hkv, Dh)
+        keys.append(k[None])
+        vals.append(v[None])
+        K = torch.cat(keys).permute(1, 0, 2)[None]
+        Vv = torch.cat(vals).permute(1, 0, 2)[None]
+        att = Fnn.scaled_dot_product_attention(q[None, :, None, :], K, Vv, enable_gqa=True,
+                                               scale=float(np.float32(1 / math.sqrt(Dh))))
+        h1 = f + Fnn.linear(att.reshape(Hq * Dh), W["w_o"])
+        gu = Fnn.linear(Fnn.rms_norm(h1, (d,), W["g_mlp"], eps), W["w_gate_up"])
+        a = h1 + Fnn.linear(Fnn.silu(gu[:F]) * gu[F:], W["w_down"])
+        z = Fnn.linear(Fnn.rms_norm(a, (d,), W["g_final"], eps), W["w_lm"])
+        outs.append((a.numpy(), z.numpy(), float(torch.logsumexp(z, 0))))
+        f = a
+    return outs
+
+
+def test_drafter_chain_matches_textbook_layer():
+    """With K = W = 1 the draft tree is a chain; every node must equal a textbook decoder
+    layer applied recursively (feature of step t = output a of step t-1)."""
+    w, dr = small_drafter(5)
+    di = synth.draft_inputs(SMALL, seed=6, prefix=[9])
+    g = O.fuse_features(O.f64(di["h_low"]), O.f64(di["h_mid"]), O.f64(di["h_high"]), dr.w_fuse)[0]
+    res = O.draft_round(dr, 4, 1, 1, 4, di["h_low"], di["h_mid"], di["h_high"], di["root_tok"],
+                        di["kpre"], di["vpre"], [9])[0]
+    assert res["parents"] == [-1, 0, 1, 2, 3]
+    toks = res["tokens"][:4]
+    ref = textbook_layer(w, SMALL, toks,
+                         lambda t, f: torch.tensor(g) if t == 0 else f, 9, di["kpre"], di["vpre"])
+    for t in range(4):
+        st = res["store"][t]
+        np.testing.assert_allclose(st["a"], ref[t][0], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(st["z"], ref[t][1], rtol=1e-10, atol=1e-12)
+        assert abs(st["lse"] - ref[t][2]) < 1e-10
+        # chain: each child token is its parent's argmax
+        if t + 1 < 5:
+            assert res["tokens"][t + 1] == int(np.argmax(st["z"]))
+
+
+def test_single_key_attention_returns_value():
+    """Root with an empty prefix attends to itself only: attention output = its own v."""
+    w, dr = small_drafter(7)
+    rng = np.random.default_rng(0)
+    f = rng.standard_normal((1, SMALL.d))
+    r = dr.forward_nodes([3], f, [0], np.zeros((0, 2, 8)), np.zeros((0, 2, 8)),
+                         [np.zeros((0, 2, 8))], [np.zeros((0, 2, 8))])
+    G = SMALL.Hq // SMALL.Hkv
+    for h in range(SMALL.Hq):
+        np.testing.assert_allclose(r["attn"][0, h * 8:(h + 1) * 8], r["v"][0, h // G], rtol=1e-12)
+
+
+def test_full_binary_tree_for_tiny_budget():
+    shape = synth.scaled(synth.TINY, d=32, Hq=4, Hkv=4, Dh=8, F=48, V=64)
+    w, dr = small_drafter(8, shape)
+    di = synth.draft_inputs(shape, seed=9, prefix=[5])
+    res = O.draft_round(dr, 3, 2, 4, 14, di["h_low"], di["h_mid"], di["h_high"], di["root_tok"],
+                        di["kpre"], di["vpre"], [5])[0]
+    assert len(res["tokens"]) == 15
+    assert [res["depth"].count(t) for t in range(4)] == [1, 2, 4, 8]
+    for i in range(1, 15):
+        p = res["parents"][i]
+        assert 0 <= p < i and res["depth"][i] == res["depth"][p] + 1
+    assert len(res["slots"]) == 1 + 2 + 4
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_selection_invariants(seed):
+    D, K, W, N = 4, 3, 2, 9
+    w, dr = small_drafter(20 + seed)
+    di = synth.draft_inputs(SMALL, seed=30 + seed, prefix=[4])
+    res = O.draft_round(dr, D, K, W, N, di["h_low"], di["h_mid"], di["h_high"], di["root_tok"],
+                        di["kpre"], di["vpre"], [4])[0]
+    cands = res["cands"]
+    assert len(cands) == K + (D - 1) * W * K
+    # brute force: every kept candidate beats every dropped one by (score desc, creation asc)
+    kept_keys = set()
+    sc = res["score"]
+    for i in range(1, N + 1):
+        kept_keys.add((res["tokens"][i], res["depth"][i], float(sc[i])))
+    kept = [c for c in cands if (c["token"], c["depth"], float(c["score"])) in kept_keys]
+    dropped = [c for c in cands if c not in kept]
+    assert len(kept) == N
+    for a in kept:
+        for b in dropped:
+            assert (a["score"] > b["score"]) or (a["score"] == b["score"] and a["creation"] < b["creation"])
+    # level order, parents earlier, scores non-increasing along every path
+    assert res["depth"] == sorted(res["depth"])
+    for i in range(1, N + 1):
+        p = res["parents"][i]
+        assert 0 <= p < i and sc[i] <= sc[p]
+    # each depth's frontier is the top-W of that depth's candidates
+    for t in range(1, D):
+        at = [c for c in cands if c["depth"] == t]
+        ev = sorted([c for c in at if c["slot"] >= 0], key=lambda c: c["slot"])
+        best = sorted(at, key=lambda c: (-float(c["score"]), c["creation"]))[:W]
+        assert [c["creation"] for c in ev] == [c["creation"] for c in best]
+
+
+def test_child_score_never_exceeds_parent():
+    rng = np.random.default_rng(4)
+    for _ in range(2000):
+        z = rng.standard_normal(30).astype(np.float32) * rng.uniform(0.01, 40)
+        lse = np.float32(O.log_sum_exp(z.astype(np.float64)))
+        sp = np.float32(rng.uniform(-30, 0))
+        for v in z[:3]:
+            assert O.child_score(sp, v, max(lse, z.max())) <= sp
