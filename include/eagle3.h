@@ -1,0 +1,260 @@
+/*
+ * eagle3.h -- C-ABI of libeagle3.so: one EAGLE-3 draft-tree round and one
+ * tree-verification round on an MI355X (gfx950) GPU.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The library never
+ *    allocates or frees device memory; scratch space comes from a caller-provided device
+ *    workspace whose size the matching *_workspace_size() function returns.
+ *  - Every call is asynchronous on the caller's HIP stream, passed as `void* stream`
+ *    (NULL = the default stream).  No call synchronises the host.
+ *  - Tensors are dense, row-major, in the layouts stated per argument.  Float tensors are
+ *    EAGLE3_F32 (IEEE fp32) or EAGLE3_BF16 (bfloat16) as the `dtype` argument says; ids and
+ *    indices are int32; tree masks are uint64; log-sum-exp values and attention partials
+ *    are always fp32 and use the natural logarithm.
+ *  - Return value: EAGLE3_OK, or a negative status found on the host before any launch
+ *    (nothing is enqueued then), or EAGLE3_EHIP if a launch failed.
+ *  - Malformed DEVICE data (a parent index out of range, a token >= vocab) cannot be seen on
+ *    the host: kernels clamp such indices so that no access leaves its buffer, and OR a
+ *    flag into the optional caller-owned device word `dev_status` where one is taken.
+ *  - The same inputs (and for sampling the same seed and round) give bit-identical outputs:
+ *    every reduction runs in a fixed order and no floating-point atomics are used.
+ *
+ * Sources.  The pages that define each operation are cited per function:
+ *  [P1] "EAGLE-3: Training-time Test 的投机推理加速" (paper deep-dive page).
+ *  [P2] The EAGLE series evolution page (EAGLE-1 -> EAGLE-2 -> EAGLE-3, DFlash).
+ *  [P3] "SpecForge：把 EAGLE3 从训练样本交付到 SGLang".
+ *  [P4] "EAGLE-3 投机解码与 USP 长序列训练优化".
+ *  [P5] The speculative-decoding thinking-budget page (tree verification steps).
+ */
+#ifndef EAGLE3_H
+#define EAGLE3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EAGLE3_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define EAGLE3_API __attribute__((visibility("default")))
+#else
+#define EAGLE3_API
+#endif
+
+/* status codes */
+#define EAGLE3_OK 0
+#define EAGLE3_EINVAL (-1)       /* null pointer, bad dtype, bad shape or size          */
+#define EAGLE3_EUNSUPPORTED (-2) /* valid but outside what the kernels implement        */
+#define EAGLE3_EWORKSPACE (-3)   /* workspace NULL or smaller than *_workspace_size()   */
+#define EAGLE3_EHIP (-4)         /* a HIP launch or runtime call failed                 */
+
+/* element types */
+#define EAGLE3_F32 0
+#define EAGLE3_BF16 1
+
+/* bits OR-ed into the optional device status word */
+#define EAGLE3_DEV_BAD_PARENT 1  /* parent[i] not in [0, i) (or root parent != -1)      */
+#define EAGLE3_DEV_TOO_DEEP 2    /* a request has more nodes than the mask can hold     */
+#define EAGLE3_DEV_BAD_TOKEN 4   /* a token id outside [0, vocab)                       */
+
+EAGLE3_API int eagle3_abi_version(void);
+EAGLE3_API const char* eagle3_status_string(int status);
+
+/* ====================================================================================
+ * Drafter description.
+ * A single Llama-style decoder layer ([P1] 训练细节: "A single Transformer decoder
+ * layer"; [P3] 多层特征融合到底融合了什么: a_{t+1} = D(e(x_t), g_t)) plus the feature-fusion
+ * projection and the LM head.  Every projection is stored [out_features, in_features]
+ * row-major; all tensors have element type `dtype`.
+ * ==================================================================================== */
+typedef struct eagle3_drafter {
+  int32_t d;          /* hidden size of target features and drafter                      */
+  int32_t n_heads_q;  /* Hq                                                              */
+  int32_t n_heads_kv; /* Hkv (Hq % Hkv == 0; query head h uses KV head h / (Hq/Hkv))     */
+  int32_t head_dim;   /* Dh: 64 or 128                                                   */
+  int32_t ffn;        /* F: width of the SiLU-gated MLP                                  */
+  int32_t vocab;      /* V                                                               */
+  int32_t dtype;      /* EAGLE3_F32 or EAGLE3_BF16                                       */
+  float eps;          /* RMSNorm epsilon (1e-5 for the Llama family)                     */
+  float rope_theta;   /* RoPE base (500000 for the Llama-3.1 family)                     */
+  const void* embed;     /* [V, d]           token embedding                             */
+  const void* w_fuse;    /* [d, 3d]          W_f: g = W_f [h_low; h_mid; h_high]          */
+  const void* g_embed;   /* [d]              RMSNorm gain on the token embedding          */
+  const void* g_feat;    /* [d]              RMSNorm gain on the feature                  */
+  const void* g_mlp;     /* [d]              RMSNorm gain before the MLP                  */
+  const void* g_final;   /* [d]              RMSNorm gain before the LM head              */
+  const void* w_qkv;     /* [(Hq+2Hkv)*Dh, 2d] rows: q heads, then k heads, then v heads */
+  const void* w_o;       /* [d, Hq*Dh]                                                    */
+  const void* w_gate_up; /* [2F, d]          rows 0..F-1 gate, F..2F-1 up                 */
+  const void* w_down;    /* [d, F]                                                        */
+  const void* w_lm;      /* [V, d]           LM head                                      */
+} eagle3_drafter;
+
+/* Draft-tree budget ([P1] Draft tree 配置: total draft tokens, depth, nodes selected per
+ * expansion; [P2] 二、EAGLE-2动态草稿树: top-K children per expanded node).
+ * depth D >= 1 evaluation steps, topk K >= 1 children per evaluated node, width W >= 1
+ * nodes evaluated per depth, n_nodes N >= 1 draft nodes kept (the root is extra).
+ * Limits: K <= 16, 1 + (D-1)*W <= 64, N <= 255. */
+typedef struct eagle3_tree_cfg {
+  int32_t depth;
+  int32_t topk;
+  int32_t width;
+  int32_t n_nodes;
+} eagle3_tree_cfg;
+
+/* Optional per-evaluation-slot outputs of eagle3_draft_expand, for checking it.  Slot 0 is
+ * the root; the j-th node evaluated at depth t >= 1 is slot 1 + (t-1)*W + j, so a request
+ * has S = 1 + (D-1)*W slots.  Every pointer may be NULL (then that output is skipped). */
+typedef struct eagle3_draft_debug {
+  float* g;              /* [B, d]     fused feature g (fp32)                             */
+  int32_t* slot_token;   /* [B, S]     token evaluated in the slot                        */
+  int32_t* slot_parent;  /* [B, S]     parent slot; -1 for the root, -2 for an unused slot */
+  float* slot_a;         /* [B, S, d]  drafter output a (fp32)                            */
+  int32_t* slot_topk_id; /* [B, S, K]  top-K token ids (value desc, id asc)               */
+  float* slot_topk_val;  /* [B, S, K]  their logits (fp32)                                */
+  float* slot_lse;       /* [B, S]     ln sum_t e^{z_t} of the slot's logits              */
+  float* slot_logits;    /* [B, S, V]  full logits (fp32), or NULL                        */
+} eagle3_draft_debug;
+
+/* ------------------------------------------------------------------------------------
+ * eagle3_draft_expand -- one draft-tree round for B independent requests.
+ * [P3] 多层特征融合到底融合了什么 and [P1] 推理流程: g = W_f [h_low; h_mid; h_high];
+ * [P3] 第二步为什么没有“正确隐藏状态”可用: the root step uses (root token, g), every later
+ * node uses (its token, the drafter output a of its parent); [P2] 二、EAGLE-2动态草稿树 and
+ * [P1] Draft tree 配置: per-depth top-K expansion with a node budget.
+ *
+ * Per request: evaluate the root at position P_b; every evaluated node v creates its top-K
+ * children (value desc, id asc) with score s = s_v + (z_v[t] - lse_v) in fp32; at each depth
+ * t = 1..D-1 the W best depth-t candidates by (score desc, creation asc) are evaluated at
+ * position P_b + t, attending to the drafter prefix KV and their evaluated ancestors; after
+ * D steps the N best candidates overall are kept and relabelled by (depth asc, creation
+ * asc), root = node 0.  Output is in level order with parent[i] < i.
+ *
+ *  h_low, h_mid, h_high : [B, d] dtype    target features of each request's root token
+ *  root_tok             : [B] int32       root token ids
+ *  kpre, vpre           : [sum P_b, Hkv, Dh] dtype  the drafter's own prefix KV, requests
+ *                         concatenated; RoPE already applied to kpre
+ *  cu_prefix            : [B+1] int32     prefix offsets (device); max_prefix >= every P_b
+ *  tokens, parents, depth : [B, N+1] int32  the tree (padding -1)
+ *  score                : [B, N+1] fp32   cumulative log-probability (root 0, padding -inf)
+ *  n_nodes              : [B] int32       nodes written per request (root included)
+ *  dbg                  : optional, see eagle3_draft_debug
+ * ------------------------------------------------------------------------------------ */
+EAGLE3_API size_t eagle3_draft_expand_workspace_size(const eagle3_drafter* w, const eagle3_tree_cfg* t,
+                                          int B, int max_prefix);
+EAGLE3_API int eagle3_draft_expand(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B,
+                        const void* h_low, const void* h_mid, const void* h_high,
+                        const int32_t* root_tok, const void* kpre, const void* vpre,
+                        const int32_t* cu_prefix, int max_prefix, int32_t* tokens,
+                        int32_t* parents, int32_t* depth, float* score, int32_t* n_nodes,
+                        const eagle3_draft_debug* dbg, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * eagle3_build_tree_mask -- pack flattened trees: ancestor bitmask, depth and position.
+ * [P2] 二、EAGLE-2动态草稿树 (flatten the tree, add positions, build the 0/1 tree attention
+ * mask so a node sees only itself and its ancestors); [P5] 一棵候选树怎样被验证 (assign each
+ * node a position; mask so nodes see only their ancestors).
+ *
+ *  cu_nodes : [B+1] int32  node offsets per request (device); T = cu_nodes[B] (host copy)
+ *  parents  : [T] int32    request-local parent index; root (node 0 of a request) = -1;
+ *                          parent[i] < i is required (topological order)
+ *  cu_prefix: [B+1] int32  prefix offsets; pos = P_b + depth
+ *  mask     : [T, W64] uint64  bit j of word j/64 set iff node j is i or an ancestor of i
+ *  depth    : [T] int32 (may be NULL)   pos : [T] int32 (may be NULL)
+ *  dev_status: optional device int32; EAGLE3_DEV_BAD_PARENT / _TOO_DEEP are OR-ed in
+ *  max_nodes: host upper bound on nodes per request, <= 64*W64
+ * ------------------------------------------------------------------------------------ */
+EAGLE3_API int eagle3_build_tree_mask(int B, int T, const int32_t* cu_nodes, const int32_t* parents,
+                           const int32_t* cu_prefix, int max_nodes, uint64_t* mask, int W64,
+                           int32_t* depth, int32_t* pos, int32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * eagle3_tree_attention -- tree-masked attention of every tree node over the prefix KV
+ * plus the tree KV.  [P3] 从序列到动态草稿树 (tree attention: each node attends only to its
+ * ancestor path); [P5] 一棵候选树怎样被验证 steps 2-3; [P4] USP 核心设计 (attention results
+ * carried as (Out, LSE) pairs).
+ *
+ * For node i of request b and query head h (KV head c = h / (Hq/Hkv)): softmax over the
+ * prefix keys 0..P_b-1 (all visible) and the tree keys j with mask bit j set, scores
+ * scale * q.k.  The prefix is cut into S splits, the tree keys form one more partial:
+ *  o_part [S+1, T, Hq, Dh] fp32 and lse_part [S+1, T, Hq] fp32 receive the partials
+ *  (partial s < S covers prefix keys [s*ceil(P_b/S), (s+1)*ceil(P_b/S)); partial S covers
+ *  the tree keys); an empty partial has O = 0, LSE = -inf.  If `o` is not NULL the partials
+ *  are also merged (as eagle3_lse_merge) into o [T, Hq, Dh] (dtype) and lse [T, Hq] fp32;
+ *  then o_part/lse_part may be NULL and the workspace holds them.
+ *
+ *  q [T, Hq, Dh], k_tree, v_tree [T, Hkv, Dh], kpre, vpre [sum P_b, Hkv, Dh]: dtype
+ *  cu_nodes [B+1], cu_prefix [B+1]: int32 device; mask [T, W64] as built above
+ *  max_nodes, max_prefix: host upper bounds per request; n_splits: S (0 = automatic;
+ *  eagle3_tree_attention_num_splits returns the S used).  Dh must be 64 or 128.
+ * ------------------------------------------------------------------------------------ */
+EAGLE3_API int eagle3_tree_attention_num_splits(int max_prefix, int n_splits);
+EAGLE3_API size_t eagle3_tree_attention_workspace_size(int T, int Hq, int Dh, int max_prefix, int n_splits);
+EAGLE3_API int eagle3_tree_attention(int B, int T, int Hq, int Hkv, int Dh, int dtype, const void* q,
+                          const void* k_tree, const void* v_tree, const int32_t* cu_nodes,
+                          int max_nodes, const uint64_t* mask, int W64, const void* kpre,
+                          const void* vpre, const int32_t* cu_prefix, int max_prefix,
+                          float scale, int n_splits, float* o_part, float* lse_part, void* o,
+                          float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * eagle3_lse_merge -- merge S attention partials by log-sum-exp.  [P4] USP 核心设计：三步走,
+ * Step 3: fold Out_branch/LSE_branch into Out_main/LSE_main by streaming softmax with one
+ * consistent normalisation.
+ *
+ * Per row r: m = max_s LSE_s; w_s = e^{LSE_s - m}; O = sum_s w_s O_s / sum_s w_s;
+ * LSE = m + ln sum_s w_s.  Partials with LSE = -inf weigh 0; a row whose partials are all
+ * -inf gives O = 0 and LSE = -inf.
+ *  o_part [S, rows, Dh] fp32, lse_part [S, rows] fp32 -> o [rows, Dh] (out_dtype),
+ *  lse [rows] fp32 (may be NULL).  S >= 1; Dh % 4 == 0.
+ * ------------------------------------------------------------------------------------ */
+EAGLE3_API int eagle3_lse_merge(int S, int rows, int Dh, const float* o_part, const float* lse_part,
+                     int out_dtype, void* o, float* lse, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * eagle3_accept -- accept the longest draft path.  [P1] 论文位置 (accept the longest
+ * correct prefix; the standard speculative-sampling rule keeps the target distribution);
+ * [P2] 二、EAGLE-2动态草稿树 (accept the longest coherent path, roll back to its last node);
+ * [P3] 先看 checkpoint 最终要参与什么计算 (accept the continuous prefix, correct at the
+ * rejection); [P5] 一棵候选树怎样被验证 step 4.
+ *
+ * At every node i the target draw is y_i = argmax_t z_i[t] (temperature == 0) or
+ * y_i = argmax_t (z_i[t] * invT + G_t), invT = 1/temperature in fp32, G_t Gumbel noise from
+ * Philox4x32-10 with counter (t>>2, i, b, round mod 2^32), key (seed lo, seed hi), word
+ * t & 3, u = ((x>>9)+0.5)*2^-23, G = -ln(-ln u) with a fixed float32 ln; ties go to the
+ * lowest token id.  The accepted end node is the deepest node whose every non-root
+ * ancestor-or-self j has tokens[j] == y_parent(j) (ties: lowest node index).
+ *
+ *  cu_nodes [B+1], tokens [T], parents [T] (request-local), mask [T, W64] (from
+ *  eagle3_build_tree_mask), logits [T, V] dtype (target logits at every node).
+ *  accept_len [B]; path [B, max_depth+1] accepted node indices, root first;
+ *  out_tokens [B, max_depth+1] accepted draft tokens then the bonus token; bonus [B];
+ *  padding -1.  max_depth >= the deepest node of any request.
+ * ------------------------------------------------------------------------------------ */
+EAGLE3_API size_t eagle3_accept_workspace_size(int T, int V);
+EAGLE3_API int eagle3_accept(int B, int T, const int32_t* cu_nodes, const int32_t* tokens,
+                  const int32_t* parents, const uint64_t* mask, int W64, const void* logits,
+                  int V, int dtype, float temperature, uint64_t seed, uint64_t round,
+                  int max_depth, int32_t* accept_len, int32_t* path, int32_t* out_tokens,
+                  int32_t* bonus, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Launch timing.  While enabled, the library records a HIP event pair on the launch stream
+ * around every kernel it enqueues, tagged with the kernel's name.  eagle3_profile_read
+ * waits for the recorded events and reports the summed device time and launch count of
+ * one kernel name (e.g. "gemm_lm_head").  eagle3_profile_reset drops all records.
+ * ------------------------------------------------------------------------------------ */
+EAGLE3_API int eagle3_profile_enable(int on);
+EAGLE3_API int eagle3_profile_reset(void);
+EAGLE3_API int eagle3_profile_read(const char* kernel, double* total_ms, int* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EAGLE3_H */

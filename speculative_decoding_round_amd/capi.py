@@ -1,0 +1,365 @@
+"""ctypes binding over libeagle3.so's C-ABI (include/eagle3.h).
+
+Argument marshalling only: every function checks tensor dtype, device and contiguity,
+allocates outputs and the device workspace with torch when the caller does not pass them,
+and hands raw device pointers plus the current HIP stream to the library.  No compute step
+runs here.  If the library is missing this module raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libeagle3.so")
+
+EAGLE3_OK, EAGLE3_EINVAL, EAGLE3_EUNSUPPORTED, EAGLE3_EWORKSPACE, EAGLE3_EHIP = 0, -1, -2, -3, -4
+EAGLE3_F32, EAGLE3_BF16 = 0, 1
+
+c_int, c_float, c_size_t, c_void_p, c_uint64, c_double = (
+    ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_double)
+c_char_p = ctypes.c_char_p
+
+
+class Eagle3Drafter(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("n_heads_q", ctypes.c_int32), ("n_heads_kv", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("eps", c_float), ("rope_theta", c_float),
+                ("embed", c_void_p), ("w_fuse", c_void_p), ("g_embed", c_void_p),
+                ("g_feat", c_void_p), ("g_mlp", c_void_p), ("g_final", c_void_p),
+                ("w_qkv", c_void_p), ("w_o", c_void_p), ("w_gate_up", c_void_p),
+                ("w_down", c_void_p), ("w_lm", c_void_p)]
+
+
+class Eagle3TreeCfg(ctypes.Structure):
+    _fields_ = [("depth", ctypes.c_int32), ("topk", ctypes.c_int32), ("width", ctypes.c_int32),
+                ("n_nodes", ctypes.c_int32)]
+
+
+class Eagle3DraftDebug(ctypes.Structure):
+    _fields_ = [("g", c_void_p), ("slot_token", c_void_p), ("slot_parent", c_void_p),
+                ("slot_a", c_void_p), ("slot_topk_id", c_void_p), ("slot_topk_val", c_void_p),
+                ("slot_lse", c_void_p), ("slot_logits", c_void_p)]
+
+
+EXPORTS = {
+    "eagle3_abi_version": (c_int, []),
+    "eagle3_status_string": (c_char_p, [c_int]),
+    "eagle3_draft_expand_workspace_size": (c_size_t, [c_void_p, c_void_p, c_int, c_int]),
+    "eagle3_draft_expand": (c_int, [c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p,
+                                    c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
+                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                    c_size_t, c_void_p]),
+    "eagle3_build_tree_mask": (c_int, [c_int, c_int, c_void_p, c_void_p, c_void_p, c_int,
+                                       c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "eagle3_tree_attention_num_splits": (c_int, [c_int, c_int]),
+    "eagle3_tree_attention_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
+    "eagle3_tree_attention": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p,
+                                      c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_int,
+                                      c_void_p, c_void_p, c_void_p, c_int, c_float, c_int,
+                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_size_t, c_void_p]),
+    "eagle3_lse_merge": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_int, c_void_p,
+                                 c_void_p, c_void_p]),
+    "eagle3_accept_workspace_size": (c_size_t, [c_int, c_int]),
+    "eagle3_accept": (c_int, [c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                              c_void_p, c_int, c_int, c_float, c_uint64, c_uint64, c_int,
+                              c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                              c_void_p]),
+    "eagle3_profile_enable": (c_int, [c_int]),
+    "eagle3_profile_reset": (c_int, []),
+    "eagle3_profile_read": (c_int, [c_char_p, ctypes.POINTER(c_double), ctypes.POINTER(c_int)]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libeagle3.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m speculative_decoding_round_amd.build_lib`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+class Eagle3Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = lib().eagle3_status_string(status).decode()
+        super().__init__(f"{fn} returned {status}: {msg}")
+        self.status = status
+
+
+def _check(fn: str, status: int) -> None:
+    if status != EAGLE3_OK:
+        raise Eagle3Error(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return EAGLE3_F32
+    if dt == torch.bfloat16:
+        return EAGLE3_BF16
+    raise ValueError(f"unsupported element type {dt}")
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def abi_version() -> int:
+    return lib().eagle3_abi_version()
+
+
+# ---------------------------------------------------------------------------------------
+# Drafter
+# ---------------------------------------------------------------------------------------
+
+WEIGHT_KEYS = ("embed", "w_fuse", "g_embed", "g_feat", "g_mlp", "g_final", "w_qkv", "w_o",
+               "w_gate_up", "w_down", "w_lm")
+
+
+def make_drafter(weights: dict, n_heads_q: int, n_heads_kv: int, head_dim: int,
+                 eps: float = 1e-5, rope_theta: float = 500000.0) -> Eagle3Drafter:
+    """Describe device-resident drafter weights (layouts as in include/eagle3.h).  The
+    returned struct holds raw pointers: keep `weights` alive while it is used."""
+    dt = weights["embed"].dtype
+    for k in WEIGHT_KEYS:
+        _dev(weights[k], k, dt)
+    V, d = weights["embed"].shape
+    F = weights["w_down"].shape[1]
+    s = Eagle3Drafter(d=d, n_heads_q=n_heads_q, n_heads_kv=n_heads_kv, head_dim=head_dim, ffn=F,
+                      vocab=V, dtype=dtype_code(dt), eps=eps, rope_theta=rope_theta)
+    for k in WEIGHT_KEYS:
+        setattr(s, k, weights[k].data_ptr())
+    return s
+
+
+def eagle3_draft_expand_workspace_size(drafter: Eagle3Drafter, tree: Eagle3TreeCfg, B: int,
+                                       max_prefix: int) -> int:
+    return lib().eagle3_draft_expand_workspace_size(ctypes.byref(drafter), ctypes.byref(tree), B,
+                                                    max_prefix)
+
+
+def eagle3_draft_expand(drafter: Eagle3Drafter, tree: Eagle3TreeCfg, h_low, h_mid, h_high,
+                        root_tok, kpre, vpre, cu_prefix, max_prefix: int, debug: bool = False,
+                        debug_logits: bool = False, workspace: Optional[torch.Tensor] = None,
+                        out: Optional[dict] = None, stream=None) -> dict:
+    """One draft-tree round.  Returns dict(tokens, parents, depth, score, n_nodes[, debug])."""
+    B = h_low.shape[0]
+    dev = h_low.device
+    dt = h_low.dtype
+    for n, t in (("h_low", h_low), ("h_mid", h_mid), ("h_high", h_high), ("kpre", kpre),
+                 ("vpre", vpre)):
+        _dev(t, n, dt)
+    _dev(root_tok, "root_tok", torch.int32)
+    _dev(cu_prefix, "cu_prefix", torch.int32)
+    N1 = tree.n_nodes + 1
+    if out is None:
+        out = {
+            "tokens": torch.empty((B, N1), dtype=torch.int32, device=dev),
+            "parents": torch.empty((B, N1), dtype=torch.int32, device=dev),
+            "depth": torch.empty((B, N1), dtype=torch.int32, device=dev),
+            "score": torch.empty((B, N1), dtype=torch.float32, device=dev),
+            "n_nodes": torch.empty((B,), dtype=torch.int32, device=dev),
+        }
+    dbg_struct = None
+    if debug:
+        S = 1 + (tree.depth - 1) * tree.width
+        K, d, V = tree.topk, drafter.d, drafter.vocab
+        dbg = {
+            "g": torch.empty((B, d), dtype=torch.float32, device=dev),
+            "slot_token": torch.empty((B, S), dtype=torch.int32, device=dev),
+            "slot_parent": torch.empty((B, S), dtype=torch.int32, device=dev),
+            "slot_a": torch.zeros((B, S, d), dtype=torch.float32, device=dev),
+            "slot_topk_id": torch.full((B, S, K), -1, dtype=torch.int32, device=dev),
+            "slot_topk_val": torch.zeros((B, S, K), dtype=torch.float32, device=dev),
+            "slot_lse": torch.zeros((B, S), dtype=torch.float32, device=dev),
+        }
+        if debug_logits:
+            dbg["slot_logits"] = torch.zeros((B, S, V), dtype=torch.float32, device=dev)
+        dbg_struct = Eagle3DraftDebug(**{k: v.data_ptr() for k, v in dbg.items()})
+        out["debug"] = dbg
+    if workspace is None:
+        workspace = _workspace(eagle3_draft_expand_workspace_size(drafter, tree, B, max_prefix), dev)
+    st = lib().eagle3_draft_expand(
+        ctypes.byref(drafter), ctypes.byref(tree), B, h_low.data_ptr(), h_mid.data_ptr(),
+        h_high.data_ptr(), root_tok.data_ptr(), kpre.data_ptr(), vpre.data_ptr(),
+        cu_prefix.data_ptr(), int(max_prefix), out["tokens"].data_ptr(), out["parents"].data_ptr(),
+        out["depth"].data_ptr(), out["score"].data_ptr(), out["n_nodes"].data_ptr(),
+        ctypes.byref(dbg_struct) if dbg_struct is not None else None,
+        workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _check("eagle3_draft_expand", st)
+    return out
+
+
+# ---------------------------------------------------------------------------------------
+# Verify side
+# ---------------------------------------------------------------------------------------
+
+
+def eagle3_build_tree_mask(cu_nodes, parents, cu_prefix, max_nodes: int, W64: int = 1,
+                           T: Optional[int] = None, dev_status: Optional[torch.Tensor] = None,
+                           out: Optional[dict] = None, stream=None) -> dict:
+    _dev(cu_nodes, "cu_nodes", torch.int32)
+    _dev(parents, "parents", torch.int32)
+    if cu_prefix is not None:
+        _dev(cu_prefix, "cu_prefix", torch.int32)
+    B = cu_nodes.numel() - 1
+    T = parents.numel() if T is None else T
+    dev = parents.device
+    if out is None:
+        out = {"mask": torch.empty((T, W64), dtype=torch.uint64, device=dev),
+               "depth": torch.empty((T,), dtype=torch.int32, device=dev),
+               "pos": torch.empty((T,), dtype=torch.int32, device=dev)}
+    st = lib().eagle3_build_tree_mask(B, T, cu_nodes.data_ptr(), parents.data_ptr(),
+                                      _ptr(cu_prefix), int(max_nodes), out["mask"].data_ptr(), W64,
+                                      _ptr(out.get("depth")), _ptr(out.get("pos")), _ptr(dev_status),
+                                      _stream(stream))
+    _check("eagle3_build_tree_mask", st)
+    return out
+
+
+def eagle3_tree_attention_num_splits(max_prefix: int, n_splits: int = 0) -> int:
+    return lib().eagle3_tree_attention_num_splits(max_prefix, n_splits)
+
+
+def eagle3_tree_attention(q, k_tree, v_tree, cu_nodes, max_nodes: int, mask, kpre, vpre,
+                          cu_prefix, max_prefix: int, scale: float, n_splits: int = 0,
+                          partials: bool = False, merged: bool = True,
+                          workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None,
+                          stream=None) -> dict:
+    """Tree attention.  partials=True returns o_part/lse_part; merged=True returns o/lse."""
+    T, Hq, Dh = q.shape
+    Hkv = k_tree.shape[1]
+    dt = q.dtype
+    for n, t in (("q", q), ("k_tree", k_tree), ("v_tree", v_tree)):
+        _dev(t, n, dt)
+    _dev(cu_nodes, "cu_nodes", torch.int32)
+    _dev(mask, "mask", torch.uint64)
+    if max_prefix > 0:
+        _dev(kpre, "kpre", dt)
+        _dev(vpre, "vpre", dt)
+        _dev(cu_prefix, "cu_prefix", torch.int32)
+    B = cu_nodes.numel() - 1
+    W64 = mask.shape[1] if mask.dim() == 2 else 1
+    S = eagle3_tree_attention_num_splits(max_prefix, n_splits)
+    dev = q.device
+    if out is None:
+        out = {}
+        if partials:
+            out["o_part"] = torch.empty((S + 1, T, Hq, Dh), dtype=torch.float32, device=dev)
+            out["lse_part"] = torch.empty((S + 1, T, Hq), dtype=torch.float32, device=dev)
+        if merged:
+            out["o"] = torch.empty((T, Hq, Dh), dtype=dt, device=dev)
+            out["lse"] = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    if workspace is None and "o_part" not in out:
+        workspace = _workspace(lib().eagle3_tree_attention_workspace_size(T, Hq, Dh, max_prefix,
+                                                                          n_splits), dev)
+    st = lib().eagle3_tree_attention(
+        B, T, Hq, Hkv, Dh, dtype_code(dt), q.data_ptr(), k_tree.data_ptr(), v_tree.data_ptr(),
+        cu_nodes.data_ptr(), int(max_nodes), mask.data_ptr(), W64, _ptr(kpre), _ptr(vpre),
+        _ptr(cu_prefix), int(max_prefix), float(scale), int(n_splits), _ptr(out.get("o_part")),
+        _ptr(out.get("lse_part")), _ptr(out.get("o")), _ptr(out.get("lse")), _ptr(workspace),
+        0 if workspace is None else workspace.numel(), _stream(stream))
+    _check("eagle3_tree_attention", st)
+    out["splits"] = S
+    return out
+
+
+def eagle3_lse_merge(o_part, lse_part, out_dtype=torch.float32, out: Optional[dict] = None,
+                     stream=None) -> dict:
+    """o_part [S, rows, Dh] fp32, lse_part [S, rows] fp32 -> dict(o [rows, Dh], lse [rows])."""
+    _dev(o_part, "o_part", torch.float32)
+    _dev(lse_part, "lse_part", torch.float32)
+    S, rows, Dh = o_part.shape
+    if out is None:
+        out = {"o": torch.empty((rows, Dh), dtype=out_dtype, device=o_part.device),
+               "lse": torch.empty((rows,), dtype=torch.float32, device=o_part.device)}
+    st = lib().eagle3_lse_merge(S, rows, Dh, o_part.data_ptr(), lse_part.data_ptr(),
+                                dtype_code(out["o"].dtype), out["o"].data_ptr(), _ptr(out.get("lse")),
+                                _stream(stream))
+    _check("eagle3_lse_merge", st)
+    return out
+
+
+def eagle3_accept(cu_nodes, tokens, parents, mask, logits, temperature: float, seed: int,
+                  round: int, max_depth: int, workspace: Optional[torch.Tensor] = None,
+                  out: Optional[dict] = None, stream=None) -> dict:
+    _dev(cu_nodes, "cu_nodes", torch.int32)
+    _dev(tokens, "tokens", torch.int32)
+    _dev(parents, "parents", torch.int32)
+    _dev(mask, "mask", torch.uint64)
+    _dev(logits, "logits")
+    B = cu_nodes.numel() - 1
+    T, V = logits.shape
+    W64 = mask.shape[1] if mask.dim() == 2 else 1
+    dev = logits.device
+    if out is None:
+        out = {"accept_len": torch.empty((B,), dtype=torch.int32, device=dev),
+               "path": torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev),
+               "out_tokens": torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev),
+               "bonus": torch.empty((B,), dtype=torch.int32, device=dev)}
+    if workspace is None:
+        workspace = _workspace(lib().eagle3_accept_workspace_size(T, V), dev)
+    st = lib().eagle3_accept(B, T, cu_nodes.data_ptr(), tokens.data_ptr(), parents.data_ptr(),
+                             mask.data_ptr(), W64, logits.data_ptr(), V, dtype_code(logits.dtype),
+                             float(temperature), int(seed) & (2**64 - 1), int(round) & (2**64 - 1),
+                             int(max_depth), out["accept_len"].data_ptr(), out["path"].data_ptr(),
+                             out["out_tokens"].data_ptr(), out["bonus"].data_ptr(),
+                             workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _check("eagle3_accept", st)
+    return out
+
+
+# ---------------------------------------------------------------------------------------
+# Launch timing
+# ---------------------------------------------------------------------------------------
+
+
+def eagle3_profile_enable(on: bool = True) -> None:
+    _check("eagle3_profile_enable", lib().eagle3_profile_enable(1 if on else 0))
+
+
+def eagle3_profile_reset() -> None:
+    _check("eagle3_profile_reset", lib().eagle3_profile_reset())
+
+
+def eagle3_profile_read(kernel: str):
+    """(total milliseconds, launches) recorded for one kernel name."""
+    ms = c_double(0.0)
+    n = c_int(0)
+    _check("eagle3_profile_read", lib().eagle3_profile_read(kernel.encode(), ctypes.byref(ms),
+                                                            ctypes.byref(n)))
+    return ms.value, n.value

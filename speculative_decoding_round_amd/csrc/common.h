@@ -1,0 +1,213 @@
+// Shared device/host helpers for libeagle3 (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "eagle3.h"
+
+namespace e3 {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// ---------------------------------------------------------------------------------------
+// Scalar conversions
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+
+// 16-byte vector load/store (addresses must be 16-byte aligned).
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Elements of T in one 16-byte chunk.
+template <typename T>
+struct Vec {
+  static constexpr int N = 16 / sizeof(T);
+};
+
+// Unpack element e of a 16-byte chunk of T into fp32.
+template <typename T>
+__device__ __forceinline__ float chunk_elem(u32x4 v, int e);
+template <>
+__device__ __forceinline__ float chunk_elem<float>(u32x4 v, int e) {
+  return __uint_as_float(v[e]);
+}
+template <>
+__device__ __forceinline__ float chunk_elem<bf16>(u32x4 v, int e) {
+  uint32_t w = v[e >> 1];
+  uint32_t bits = (e & 1) ? (w & 0xffff0000u) : (w << 16);
+  return __uint_as_float(bits);
+}
+
+// ---------------------------------------------------------------------------------------
+// MFMA on one 16-byte operand chunk per lane (16x16 output tile, fp32 accumulate).
+//
+// Operand layout (16x16 MFMA family): lane l supplies row (A) / column (B) l % 16 and the
+// k-group l / 16.  One 16-byte chunk per lane covers 4 * Vec<T>::N values of k across the
+// four lane groups: group g holds k in [g*N, (g+1)*N) of the chunk.  A and B use the same
+// k placement, so the product is the plain sum over k.  Output: lane l holds column l % 16,
+// rows 4*(l/16) + i, i = 0..3.
+// ---------------------------------------------------------------------------------------
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<bf16> {
+  static constexpr int KPC = 32;  // k per chunk (8 per lane group)
+  __device__ __forceinline__ static floatx4 run(u32x4 a, u32x4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mfma<float> {
+  static constexpr int KPC = 16;  // k per chunk (4 per lane group, one per MFMA)
+  __device__ __forceinline__ static floatx4 run(u32x4 a, u32x4 b, floatx4 c) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j]), __uint_as_float(b[j]), c,
+                                               0, 0, 0);
+    return c;
+  }
+};
+
+// ---------------------------------------------------------------------------------------
+// Wave / block reductions (wave64)
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Block-wide sum with a fixed reduction tree (deterministic for a given block size).
+// `scratch` needs blockDim.x/64 floats.  All threads receive the result.
+__device__ __forceinline__ float block_sum(float v, float* scratch) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += scratch[i];
+  return t;
+}
+
+// Block-wide max; scratch needs blockDim.x/64 floats.  All threads receive the result.
+__device__ __forceinline__ float block_max(float v, float* scratch) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_max(v);
+  __syncthreads();
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  float t = scratch[0];
+  for (int i = 1; i < nw; ++i) t = fmaxf(t, scratch[i]);
+  return t;
+}
+
+// (value desc, index asc) ordering used by every argmax / top-K in the library.
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float ov = __shfl_xor(v, o, 64);
+    int oi = __shfl_xor(i, o, 64);
+    if (better(ov, oi, v, i)) {
+      v = ov;
+      i = oi;
+    }
+  }
+}
+
+// Block argmax; scratch needs 2 * blockDim.x/64 words.  All threads receive the result.
+__device__ __forceinline__ void block_argmax(float& v, int& i, float* sv, int* si) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  wave_argmax(v, i);
+  __syncthreads();
+  if (lane == 0) {
+    sv[w] = v;
+    si[w] = i;
+  }
+  __syncthreads();
+  v = sv[0];
+  i = si[0];
+  for (int k = 1; k < nw; ++k)
+    if (better(sv[k], si[k], v, i)) {
+      v = sv[k];
+      i = si[k];
+    }
+}
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+}  // namespace e3
+
+// ---------------------------------------------------------------------------------------
+// Host side: launch timing registry and workspace carving
+// ---------------------------------------------------------------------------------------
+namespace e3h {
+
+// RAII: records an event pair around the launches in its scope when timing is enabled.
+struct ProfScope {
+  ProfScope(const char* name, hipStream_t s);
+  ~ProfScope();
+  int slot;
+  hipStream_t stream;
+};
+
+// Bump allocator over a workspace; with base == nullptr it only measures.
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t n) {
+    off = (off + 255) & ~size_t(255);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += n * sizeof(T);
+    return p;
+  }
+  size_t size() const { return (off + 255) & ~size_t(255); }
+};
+
+inline int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? EAGLE3_OK : EAGLE3_EHIP;
+}
+
+inline int elem_size(int dtype) { return dtype == EAGLE3_BF16 ? 2 : 4; }
+inline bool dtype_ok(int dtype) { return dtype == EAGLE3_F32 || dtype == EAGLE3_BF16; }
+
+}  // namespace e3h
+
+#define E3_RETURN_IF(cond, code) \
+  do {                           \
+    if (cond) return (code);     \
+  } while (0)

@@ -1,0 +1,760 @@
+// One draft-tree round: feature fusion, D evaluation steps of the single-layer drafter
+// over the growing tree, and on-device tree selection.  All shapes are static, so the
+// host enqueues a fixed sequence of launches and never waits on the device.
+//
+// Row layout: at step 0 row b is request b's root; at step t >= 1 row b*W + j is the j-th
+// node evaluated at depth t (evaluation slot 1 + (t-1)*W + j).  Slots that receive no node
+// (fewer candidates than W) are computed as padding and ignored.
+#include "common.h"
+#include "internal.h"
+
+using namespace e3;
+
+namespace {
+
+constexpr int KMAX = 16;     // largest top-K
+constexpr int SMAX = 64;     // largest slot count (one mask word)
+
+struct SlotState {
+  int32_t* tok;      // [B*S]
+  int32_t* parent;   // [B*S]  -1 root, -2 unused
+  int32_t* valid;    // [B*S]
+  float* score;      // [B*S]
+  uint64_t* mask;    // [B*S]  ancestors-or-self over slots
+  int32_t* cand;     // [B*S]  candidate index of the slot's node (-1 root)
+};
+struct CandState {
+  int32_t* tok;      // [B*PMAX]
+  int32_t* pslot;    // [B*PMAX]
+  int32_t* depth;    // [B*PMAX]
+  float* score;      // [B*PMAX]
+  int32_t* count;    // [B]
+};
+
+// ---------------------------------------------------------------------------------------
+// init: slot 0 = root, every other slot unused; concatenated fusion input.
+// ---------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_init(int B, int S, int d, int V, const int32_t* __restrict__ root_tok,
+                                              SlotState st, CandState cs, const T* __restrict__ hl,
+                                              const T* __restrict__ hm, const T* __restrict__ hh,
+                                              T* __restrict__ xf, int32_t* dbg_tok, int32_t* dbg_par) {
+  const int b = blockIdx.x;
+  for (int s = threadIdx.x; s < S; s += blockDim.x) {
+    const int i = b * S + s;
+    const int rt = clampi(root_tok[b], 0, V - 1);
+    st.tok[i] = s == 0 ? rt : -1;
+    st.parent[i] = s == 0 ? -1 : -2;
+    st.valid[i] = s == 0;
+    st.score[i] = 0.f;
+    st.mask[i] = s == 0 ? 1ull : 0ull;
+    st.cand[i] = -1;
+    if (dbg_tok) dbg_tok[i] = st.tok[i];
+    if (dbg_par) dbg_par[i] = st.parent[i];
+  }
+  if (threadIdx.x == 0) cs.count[b] = 0;
+  for (int k = threadIdx.x; k < d; k += blockDim.x) {
+    xf[(size_t)b * 3 * d + k] = hl[(size_t)b * d + k];
+    xf[(size_t)b * 3 * d + d + k] = hm[(size_t)b * d + k];
+    xf[(size_t)b * 3 * d + 2 * d + k] = hh[(size_t)b * d + k];
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// prep: u = [rms(E[x]) * g_e ; rms(f) * g_f], f = g (root) or a of the parent slot.
+// ---------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_prep(int R, int sb, int S, int d, int V, float eps, int step,
+                                              SlotState st, const T* __restrict__ embed,
+                                              const T* __restrict__ g_e, const T* __restrict__ g_f,
+                                              const float* __restrict__ gfeat,
+                                              const float* __restrict__ slot_a,
+                                              float* __restrict__ f_rows, T* __restrict__ u,
+                                              uint64_t* __restrict__ row_mask) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  const int b = r / R, j = r % R;
+  const int si = b * S + sb + j;
+  const bool valid = st.valid[si] != 0;
+  const int tok = valid ? clampi(st.tok[si], 0, V - 1) : 0;
+  const float* f = nullptr;
+  if (valid) {
+    if (step == 0) {
+      f = gfeat + (size_t)b * d;
+    } else {
+      const int ps = clampi(st.parent[si], 0, S - 1);
+      f = slot_a + ((size_t)b * S + ps) * d;
+    }
+  }
+  const T* e = embed + (size_t)tok * d;
+  float se = 0.f, sf = 0.f;
+  for (int k = threadIdx.x; k < d; k += blockDim.x) {
+    const float ev = to_f32(e[k]);
+    se += ev * ev;
+    if (f) sf += f[k] * f[k];
+  }
+  se = block_sum(se, red);
+  sf = block_sum(sf, red);
+  const float ie = 1.f / sqrtf(se / d + eps);
+  const float inf_ = 1.f / sqrtf(sf / d + eps);
+  T* ur = u + (size_t)r * 2 * d;
+  for (int k = threadIdx.x; k < d; k += blockDim.x) {
+    const float fv = f ? f[k] : 0.f;
+    ur[k] = from_f32<T>(to_f32(e[k]) * ie * to_f32(g_e[k]));
+    ur[d + k] = from_f32<T>(fv * inf_ * to_f32(g_f[k]));
+    f_rows[(size_t)r * d + k] = fv;
+  }
+  if (threadIdx.x == 0) row_mask[r] = valid ? st.mask[si] : 0ull;
+}
+
+// ---------------------------------------------------------------------------------------
+// rmsnorm of fp32 rows into dtype rows; optionally keep the fp32 input per slot (the
+// drafter output a that later nodes take as their feature).
+// ---------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ in, int d, float eps,
+                                                 const T* __restrict__ gamma, T* __restrict__ out,
+                                                 int R, int sb, int S, SlotState st,
+                                                 float* __restrict__ keep, float* __restrict__ keep_dbg) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  const float* x = in + (size_t)r * d;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < d; k += blockDim.x) ss += x[k] * x[k];
+  ss = block_sum(ss, red);
+  const float inv = 1.f / sqrtf(ss / d + eps);
+  for (int k = threadIdx.x; k < d; k += blockDim.x)
+    out[(size_t)r * d + k] = from_f32<T>(x[k] * inv * to_f32(gamma[k]));
+  if (keep) {
+    const int b = r / R, j = r % R;
+    const int si = b * S + sb + j;
+    if (st.valid[si]) {
+      for (int k = threadIdx.x; k < d; k += blockDim.x) {
+        keep[(size_t)si * d + k] = x[k];
+        if (keep_dbg) keep_dbg[(size_t)si * d + k] = x[k];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// QKV epilogue: sum partials, RoPE on q and k (half-split pairs, angle pos*theta^(-2i/Dh)
+// evaluated in fp64), scatter q to rows and k/v to the request's slot KV.
+// ---------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_epi_qkv(const float* __restrict__ part, int splits, int M, int Hq,
+                                                 int Hkv, int Dh, int R, int sb, int S, int step,
+                                                 float theta, const int32_t* __restrict__ cu_prefix,
+                                                 SlotState st, T* __restrict__ q_rows,
+                                                 T* __restrict__ kslot, T* __restrict__ vslot) {
+  const int half = Dh / 2;
+  const int H = Hq + 2 * Hkv;
+  const int N = H * Dh;
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long)M * H * half) return;
+  const int i = (int)(idx % half);
+  const int h = (int)((idx / half) % H);
+  const int m = (int)(idx / ((long)half * H));
+  float y1 = 0.f, y2 = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float* p = part + ((size_t)s * M + m) * N + h * Dh;
+    y1 += p[i];
+    y2 += p[i + half];
+  }
+  const int b = m / R, j = m % R;
+  const int si = b * S + sb + j;
+  if (h < Hq + Hkv) {
+    const int P = cu_prefix ? cu_prefix[b + 1] - cu_prefix[b] : 0;
+    const double pos = (double)(P + step);
+    const double ang = pos * pow((double)theta, -2.0 * i / Dh);
+    double sn, cn;
+    sincos(ang, &sn, &cn);
+    const float c = (float)cn, s = (float)sn;
+    const float o1 = y1 * c - y2 * s;
+    const float o2 = y1 * s + y2 * c;
+    y1 = o1;
+    y2 = o2;
+  }
+  T* dst;
+  if (h < Hq) {
+    dst = q_rows + ((size_t)m * Hq + h) * Dh;
+  } else {
+    if (!st.valid[si]) return;
+    const int c = h < Hq + Hkv ? h - Hq : h - Hq - Hkv;
+    T* base = h < Hq + Hkv ? kslot : vslot;
+    dst = base + ((size_t)si * Hkv + c) * Dh;
+  }
+  dst[i] = from_f32<T>(y1);
+  dst[i + half] = from_f32<T>(y2);
+}
+
+// ---------------------------------------------------------------------------------------
+// LM head top-K / log-sum-exp, pass 1: per (row, vocab chunk) the chunk's top-K
+// (value desc, id asc) and its (max, sum e^{z-max}).
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_topk_chunk(const float* __restrict__ part, int splits, int M,
+                                                    int V, int K, int chunk, int n_chunks,
+                                                    float* __restrict__ cv, int* __restrict__ ci,
+                                                    float* __restrict__ cmax, float* __restrict__ csum,
+                                                    float* __restrict__ dbg_logits, int R, int sb, int S,
+                                                    SlotState st) {
+  __shared__ float sv[8];
+  __shared__ int si[8];
+  __shared__ float red[4];
+  const int m = blockIdx.y, c = blockIdx.x;
+  const int t0 = c * chunk, t1 = min(V, t0 + chunk);
+  float* dl = nullptr;
+  if (dbg_logits) {
+    const int b = m / R, j = m % R;
+    const int sidx = b * S + sb + j;
+    if (st.valid[sidx]) dl = dbg_logits + (size_t)sidx * V;
+  }
+  float vals[KMAX];
+  int ids[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    vals[k] = kNegInf;
+    ids[k] = 0x7fffffff;
+  }
+  float lm = kNegInf, ls = 0.f;
+  for (int t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
+    float z = 0.f;
+    for (int s = 0; s < splits; ++s) z += part[((size_t)s * M + m) * V + t];
+    if (dl) dl[t] = z;
+    if (z > lm) {
+      ls = ls * expf(lm - z) + 1.f;
+      lm = z;
+    } else {
+      ls += expf(z - lm);
+    }
+    if (better(z, t, vals[K - 1], ids[K - 1])) {
+      float cvv = z;
+      int cii = t;
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) {
+        if (k < K && better(cvv, cii, vals[k], ids[k])) {
+          const float tv = vals[k];
+          const int ti = ids[k];
+          vals[k] = cvv;
+          ids[k] = cii;
+          cvv = tv;
+          cii = ti;
+        }
+      }
+    }
+  }
+  // chunk (max, sum) with a fixed reduction order
+  const float bm = block_max(lm, red);
+  const float scaled = lm == kNegInf ? 0.f : ls * expf(lm - bm);
+  const float tot = block_sum(scaled, red);
+  // chunk top-K: K rounds of block argmax over each thread's sorted head
+  for (int k = 0; k < K; ++k) {
+    float v = vals[0];
+    int id = ids[0];
+    block_argmax(v, id, sv, si);
+    if (ids[0] == id && vals[0] == v && id != 0x7fffffff) {
+#pragma unroll
+      for (int q = 0; q < KMAX - 1; ++q) {
+        vals[q] = vals[q + 1];
+        ids[q] = ids[q + 1];
+      }
+      vals[KMAX - 1] = kNegInf;
+      ids[KMAX - 1] = 0x7fffffff;
+    }
+    if (threadIdx.x == 0) {
+      cv[((size_t)m * n_chunks + c) * K + k] = v;
+      ci[((size_t)m * n_chunks + c) * K + k] = id;
+    }
+  }
+  if (threadIdx.x == 0) {
+    cmax[(size_t)m * n_chunks + c] = bm;
+    csum[(size_t)m * n_chunks + c] = tot;
+  }
+}
+
+// pass 2: per row, merge the chunks' top-K and (max, sum) in chunk order.
+__global__ __launch_bounds__(256) void k_topk_merge(const float* __restrict__ cv, const int* __restrict__ ci,
+                                                    const float* __restrict__ cmax,
+                                                    const float* __restrict__ csum, int n_chunks, int K,
+                                                    int* __restrict__ top_id, float* __restrict__ top_val,
+                                                    float* __restrict__ lse, int R, int sb, int S,
+                                                    SlotState st, int32_t* dbg_id, float* dbg_val,
+                                                    float* dbg_lse) {
+  __shared__ float sv[8];
+  __shared__ int si[8];
+  __shared__ float s_lse;
+  const int m = blockIdx.x;
+  const int n = n_chunks * K;
+  if (threadIdx.x == 0) {
+    float mx = kNegInf;
+    for (int c = 0; c < n_chunks; ++c) mx = fmaxf(mx, cmax[(size_t)m * n_chunks + c]);
+    float tot = 0.f;
+    for (int c = 0; c < n_chunks; ++c) {
+      const float cm = cmax[(size_t)m * n_chunks + c];
+      if (cm != kNegInf) tot += csum[(size_t)m * n_chunks + c] * expf(cm - mx);
+    }
+    s_lse = mx + logf(tot);
+  }
+  // each thread owns candidates threadIdx.x + 256*q (q < 4 covers n <= 1024)
+  float v_own[4];
+  int i_own[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = threadIdx.x + 256 * q;
+    v_own[q] = e < n ? cv[(size_t)m * n + e] : kNegInf;
+    i_own[q] = e < n ? ci[(size_t)m * n + e] : 0x7fffffff;
+  }
+  const int b = m / R, j = m % R;
+  const int sidx = b * S + sb + j;
+  const bool dbg = st.valid[sidx] != 0;
+  for (int k = 0; k < K; ++k) {
+    float v = kNegInf;
+    int id = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (better(v_own[q], i_own[q], v, id)) {
+        v = v_own[q];
+        id = i_own[q];
+      }
+    block_argmax(v, id, sv, si);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (i_own[q] == id) {
+        v_own[q] = kNegInf;
+        i_own[q] = 0x7fffffff;
+      }
+    if (threadIdx.x == 0) {
+      top_id[(size_t)m * K + k] = id;
+      top_val[(size_t)m * K + k] = v;
+      if (dbg && dbg_id) dbg_id[(size_t)sidx * K + k] = id;
+      if (dbg && dbg_val) dbg_val[(size_t)sidx * K + k] = v;
+    }
+  }
+  if (threadIdx.x == 0) {
+    lse[m] = s_lse;
+    if (dbg && dbg_lse) dbg_lse[sidx] = s_lse;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Tree selection for one request per workgroup.  Children of the nodes evaluated at this
+// step get s = s_parent + (z - lse) in fp32; then either the next depth's W best by
+// (s desc, creation asc) become evaluation slots, or (last step) the N best candidates of
+// the pool are kept and relabelled by (depth asc, creation asc).
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ bool cand_better(float sa, int ia, float sb_, int ib) {
+  return sa > sb_ || (sa == sb_ && ia < ib);
+}
+
+__global__ __launch_bounds__(256) void k_select(int step, int D, int K, int W, int N, int S, int PMAX,
+                                                int R, const int* __restrict__ top_id,
+                                                const float* __restrict__ top_val,
+                                                const float* __restrict__ lse, SlotState st,
+                                                CandState cs, int32_t* __restrict__ out_tok,
+                                                int32_t* __restrict__ out_par,
+                                                int32_t* __restrict__ out_dep, float* __restrict__ out_score,
+                                                int32_t* __restrict__ out_n, int32_t* dbg_tok,
+                                                int32_t* dbg_par) {
+#pragma clang fp contract(off)
+  __shared__ float ssc[1024];
+  __shared__ int sdep[1024];
+  __shared__ int skeep[1024];
+  __shared__ int slab[1024];
+  __shared__ int n_eval_s;
+  const int b = blockIdx.x;
+  const int sb = step == 0 ? 0 : 1 + (step - 1) * W;
+  const int n_before = cs.count[b];
+  if (threadIdx.x == 0) {
+    int ne = 0;
+    for (int j = 0; j < R; ++j) ne += st.valid[b * S + sb + j] ? 1 : 0;
+    n_eval_s = ne;
+  }
+  __syncthreads();
+  const int nE = n_eval_s;  // valid slots form a prefix of the step's slots
+  const int n_new = nE * K;
+  const int n_total = n_before + n_new;
+  int32_t* ctok = cs.tok + (size_t)b * PMAX;
+  int32_t* cps = cs.pslot + (size_t)b * PMAX;
+  int32_t* cdep = cs.depth + (size_t)b * PMAX;
+  float* csc = cs.score + (size_t)b * PMAX;
+  for (int e = threadIdx.x; e < n_new; e += blockDim.x) {
+    const int j = e / K, rk = e % K;
+    const int slot = sb + j;
+    const int row = b * R + j;
+    const int ci_ = n_before + e;
+    const float val = top_val[(size_t)row * K + rk];
+    const float lp = val - lse[row];
+    ctok[ci_] = top_id[(size_t)row * K + rk];
+    cps[ci_] = slot;
+    cdep[ci_] = step + 1;
+    csc[ci_] = st.score[b * S + slot] + lp;
+    ssc[ci_] = csc[ci_];
+  }
+  // earlier candidates' scores into LDS for the final ranking
+  if (step + 1 == D) {
+    for (int e = threadIdx.x; e < n_before; e += blockDim.x) {
+      ssc[e] = csc[e];
+      sdep[e] = cdep[e];
+    }
+    for (int e = threadIdx.x; e < n_new; e += blockDim.x) sdep[n_before + e] = step + 1;
+  }
+  __syncthreads();
+  if (step + 1 < D) {
+    // rank the new candidates; the W best take the next step's slots
+    const int nsb = 1 + step * W;
+    for (int e = threadIdx.x; e < n_new; e += blockDim.x) {
+      const int ia = n_before + e;
+      const float sa = ssc[ia];
+      int rank = 0;
+      for (int f = 0; f < n_new; ++f) rank += cand_better(ssc[n_before + f], n_before + f, sa, ia) ? 1 : 0;
+      if (rank < W) {
+        const int slot = nsb + rank;
+        const int i = b * S + slot;
+        const int ps = cps[ia];
+        st.tok[i] = ctok[ia];
+        st.parent[i] = ps;
+        st.valid[i] = 1;
+        st.score[i] = sa;
+        st.cand[i] = ia;
+        st.mask[i] = st.mask[b * S + ps] | (1ull << slot);
+        if (dbg_tok) dbg_tok[i] = ctok[ia];
+        if (dbg_par) dbg_par[i] = ps;
+      }
+    }
+    if (threadIdx.x == 0) cs.count[b] = n_total;
+    return;
+  }
+  // final prune: keep the N best of the whole pool, relabel in level order
+  for (int e = threadIdx.x; e < n_total; e += blockDim.x) {
+    const float sa = ssc[e];
+    int rank = 0;
+    for (int f = 0; f < n_total; ++f) rank += cand_better(ssc[f], f, sa, e) ? 1 : 0;
+    skeep[e] = rank < N ? 1 : 0;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < n_total; e += blockDim.x) {
+    int lab = -1;
+    if (skeep[e]) {
+      lab = 1;
+      const int de = sdep[e];
+      for (int f = 0; f < n_total; ++f)
+        if (skeep[f] && (sdep[f] < de || (sdep[f] == de && f < e))) ++lab;
+    }
+    slab[e] = lab;
+  }
+  __syncthreads();
+  const int n_keep = min(N, n_total);
+  const size_t ob = (size_t)b * (N + 1);
+  for (int e = threadIdx.x; e < n_total; e += blockDim.x) {
+    if (!skeep[e]) continue;
+    const int lab = slab[e];
+    const int ps = cps[e];
+    int plab = 0;
+    if (ps > 0) {
+      const int pc = st.cand[b * S + ps];
+      plab = (pc >= 0 && pc < n_total) ? slab[pc] : -1;
+    }
+    out_tok[ob + lab] = ctok[e];
+    out_par[ob + lab] = plab;
+    out_dep[ob + lab] = sdep[e];
+    out_score[ob + lab] = ssc[e];
+  }
+  for (int l = n_keep + 1 + threadIdx.x; l <= N; l += blockDim.x) {
+    out_tok[ob + l] = -1;
+    out_par[ob + l] = -1;
+    out_dep[ob + l] = -1;
+    out_score[ob + l] = kNegInf;
+  }
+  if (threadIdx.x == 0) {
+    out_tok[ob] = st.tok[b * S];
+    out_par[ob] = -1;
+    out_dep[ob] = 0;
+    out_score[ob] = 0.f;
+    out_n[b] = 1 + n_keep;
+    cs.count[b] = n_total;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Workspace plan
+// ---------------------------------------------------------------------------------------
+struct Plan {
+  int B, d, Hq, Hkv, Dh, F, V, D, K, W, N, S, PMAX, Mmax, att_splits, lm_chunk, lm_nchunk;
+  size_t gemm_part_elems;
+  // pointers (null when measuring)
+  SlotState st;
+  CandState cs;
+  float *g, *slot_a, *f_rows, *h1, *a_rows, *gpart, *att_o, *att_lse, *cv, *cmax, *csum, *top_val, *lse;
+  int *ci, *top_id;
+  uint64_t* row_mask;
+  void *xf, *u, *q_rows, *kslot, *vslot, *attn, *mn, *act, *xl;
+  size_t bytes;
+};
+
+Plan make_plan(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, int max_prefix, void* ws) {
+  Plan p;
+  p.B = B;
+  p.d = w->d;
+  p.Hq = w->n_heads_q;
+  p.Hkv = w->n_heads_kv;
+  p.Dh = w->head_dim;
+  p.F = w->ffn;
+  p.V = w->vocab;
+  p.D = t->depth;
+  p.K = t->topk;
+  p.W = t->width;
+  p.N = t->n_nodes;
+  p.S = 1 + (p.D - 1) * p.W;
+  p.PMAX = p.K + (p.D - 1) * p.W * p.K;
+  p.Mmax = B * (p.W > 1 ? p.W : 1);
+  p.att_splits = e3h::attention_splits(max_prefix, 0);
+  p.lm_chunk = p.V < 4096 ? p.V : 4096;
+  p.lm_nchunk = (p.V + p.lm_chunk - 1) / p.lm_chunk;
+  const int es = e3h::elem_size(w->dtype);
+  const int nqkv = (p.Hq + 2 * p.Hkv) * p.Dh;
+  size_t gp = 0;
+  auto upd = [&](int M, int N_, int K_) {
+    e3h::GemmPlan gpl = e3h::plan_gemm(M, N_, K_, w->dtype);
+    size_t e = (size_t)gpl.splits * M * N_;
+    if (e > gp) gp = e;
+  };
+  upd(B, p.d, 3 * p.d);
+  for (int M : {B, p.Mmax}) {
+    upd(M, nqkv, 2 * p.d);
+    upd(M, p.d, p.Hq * p.Dh);
+    upd(M, 2 * p.F, p.d);
+    upd(M, p.d, p.F);
+    upd(M, p.V, p.d);
+  }
+  p.gemm_part_elems = gp;
+  e3h::Carve c(ws);
+  const size_t BS = (size_t)B * p.S, BP = (size_t)B * p.PMAX;
+  p.st.tok = c.take<int32_t>(BS);
+  p.st.parent = c.take<int32_t>(BS);
+  p.st.valid = c.take<int32_t>(BS);
+  p.st.score = c.take<float>(BS);
+  p.st.mask = c.take<uint64_t>(BS);
+  p.st.cand = c.take<int32_t>(BS);
+  p.cs.tok = c.take<int32_t>(BP);
+  p.cs.pslot = c.take<int32_t>(BP);
+  p.cs.depth = c.take<int32_t>(BP);
+  p.cs.score = c.take<float>(BP);
+  p.cs.count = c.take<int32_t>(B);
+  p.g = c.take<float>((size_t)B * p.d);
+  p.xf = c.take<char>((size_t)B * 3 * p.d * es);
+  p.slot_a = c.take<float>(BS * p.d);
+  p.kslot = c.take<char>(BS * p.Hkv * p.Dh * es);
+  p.vslot = c.take<char>(BS * p.Hkv * p.Dh * es);
+  const size_t M = p.Mmax;
+  p.row_mask = c.take<uint64_t>(M);
+  p.f_rows = c.take<float>(M * p.d);
+  p.u = c.take<char>(M * 2 * p.d * es);
+  p.q_rows = c.take<char>(M * p.Hq * p.Dh * es);
+  p.attn = c.take<char>(M * p.Hq * p.Dh * es);
+  p.h1 = c.take<float>(M * p.d);
+  p.mn = c.take<char>(M * p.d * es);
+  p.act = c.take<char>(M * p.F * es);
+  p.a_rows = c.take<float>(M * p.d);
+  p.xl = c.take<char>(M * p.d * es);
+  p.gpart = c.take<float>(gp);
+  p.att_o = c.take<float>((size_t)(p.att_splits + 1) * M * p.Hq * p.Dh);
+  p.att_lse = c.take<float>((size_t)(p.att_splits + 1) * M * p.Hq);
+  p.cv = c.take<float>(M * p.lm_nchunk * p.K);
+  p.ci = c.take<int>(M * p.lm_nchunk * p.K);
+  p.cmax = c.take<float>(M * p.lm_nchunk);
+  p.csum = c.take<float>(M * p.lm_nchunk);
+  p.top_id = c.take<int>(M * p.K);
+  p.top_val = c.take<float>(M * p.K);
+  p.lse = c.take<float>(M);
+  p.bytes = c.size();
+  return p;
+}
+
+template <typename T>
+int run_draft(const eagle3_drafter* w, const Plan& p, const void* h_low, const void* h_mid,
+              const void* h_high, const int32_t* root_tok, const void* kpre, const void* vpre,
+              const int32_t* cu_prefix, int32_t* tokens, int32_t* parents, int32_t* depth,
+              float* score, int32_t* n_nodes, const eagle3_draft_debug* dbg, hipStream_t s) {
+  using namespace e3h;
+  const int B = p.B, d = p.d;
+  const int dt = w->dtype;
+  const int nqkv = (p.Hq + 2 * p.Hkv) * p.Dh;
+  int32_t* dbg_tok = dbg ? dbg->slot_token : nullptr;
+  int32_t* dbg_par = dbg ? dbg->slot_parent : nullptr;
+  int st;
+  {
+    ProfScope ps("draft_init", s);
+    hipLaunchKernelGGL(k_init<T>, dim3(B), dim3(256), 0, s, B, p.S, d, p.V, root_tok, p.st, p.cs,
+                       (const T*)h_low, (const T*)h_mid, (const T*)h_high, (T*)p.xf, dbg_tok, dbg_par);
+    if ((st = launch_status())) return st;
+  }
+  // feature fusion g = W_f [h_low; h_mid; h_high]
+  {
+    GemmPlan gp = plan_gemm(B, d, 3 * d, dt);
+    if ((st = launch_gemm(gp, dt, p.xf, 3 * d, w->w_fuse, p.gpart, s, "gemm_fuse"))) return st;
+    if ((st = launch_epi_sum(gp, p.gpart, p.g, nullptr, s, "epi_fuse"))) return st;
+    if (dbg && dbg->g)
+      if (hipMemcpyAsync(dbg->g, p.g, (size_t)B * d * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+        return EAGLE3_EHIP;
+  }
+  for (int step = 0; step < p.D; ++step) {
+    const int R = step == 0 ? 1 : p.W;
+    const int sb = step == 0 ? 0 : 1 + (step - 1) * p.W;
+    const int M = B * R;
+    {
+      ProfScope ps("draft_prep", s);
+      hipLaunchKernelGGL(k_prep<T>, dim3(M), dim3(256), 0, s, R, sb, p.S, d, p.V, w->eps, step, p.st,
+                         (const T*)w->embed, (const T*)w->g_embed, (const T*)w->g_feat, p.g, p.slot_a,
+                         p.f_rows, (T*)p.u, p.row_mask);
+      if ((st = launch_status())) return st;
+    }
+    // QKV + RoPE
+    {
+      GemmPlan gp = plan_gemm(M, nqkv, 2 * d, dt);
+      if ((st = launch_gemm(gp, dt, p.u, 2 * d, w->w_qkv, p.gpart, s, "gemm_qkv"))) return st;
+      ProfScope ps("epi_qkv", s);
+      const long n = (long)M * (p.Hq + 2 * p.Hkv) * (p.Dh / 2);
+      hipLaunchKernelGGL(k_epi_qkv<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p.gpart,
+                         gp.splits, M, p.Hq, p.Hkv, p.Dh, R, sb, p.S, step, w->rope_theta, cu_prefix,
+                         p.st, (T*)p.q_rows, (T*)p.kslot, (T*)p.vslot);
+      if ((st = launch_status())) return st;
+    }
+    // attention over the drafter prefix + evaluated ancestors-or-self
+    {
+      AttnArgs a;
+      a.B = B;
+      a.Hq = p.Hq;
+      a.Hkv = p.Hkv;
+      a.Dh = p.Dh;
+      a.dtype = dt;
+      a.q = p.q_rows;
+      a.q_cu = nullptr;
+      a.q_stride = R;
+      a.q_rows_total = M;
+      a.kt = p.kslot;
+      a.vt = p.vslot;
+      a.kt_cu = nullptr;
+      a.kt_stride = p.S;
+      a.kt_count = sb + R;
+      a.mask = p.row_mask;
+      a.W64 = 1;
+      a.kp = kpre;
+      a.vp = vpre;
+      a.p_cu = cu_prefix;
+      a.scale = (float)(1.0 / sqrt((double)p.Dh));
+      a.S = p.att_splits;
+      a.max_q_per_req = R;
+      a.o_part = p.att_o;
+      a.lse_part = p.att_lse;
+      if ((st = launch_tree_attention(a, s, "draft_attention"))) return st;
+      if ((st = launch_lse_merge(p.att_splits + 1, M * p.Hq, p.Dh, p.att_o, p.att_lse, dt, p.attn,
+                                 nullptr, s, "draft_lse_merge")))
+        return st;
+    }
+    // O projection + residual
+    {
+      GemmPlan gp = plan_gemm(M, d, p.Hq * p.Dh, dt);
+      if ((st = launch_gemm(gp, dt, p.attn, p.Hq * p.Dh, w->w_o, p.gpart, s, "gemm_o"))) return st;
+      if ((st = launch_epi_sum(gp, p.gpart, p.h1, p.f_rows, s, "epi_o"))) return st;
+      ProfScope ps("rmsnorm", s);
+      hipLaunchKernelGGL(k_rmsnorm<T>, dim3(M), dim3(256), 0, s, p.h1, d, w->eps, (const T*)w->g_mlp,
+                         (T*)p.mn, R, sb, p.S, p.st, (float*)nullptr, (float*)nullptr);
+      if ((st = launch_status())) return st;
+    }
+    // SiLU-gated MLP + residual
+    {
+      GemmPlan gp = plan_gemm(M, 2 * p.F, d, dt);
+      if ((st = launch_gemm(gp, dt, p.mn, d, w->w_gate_up, p.gpart, s, "gemm_gate_up"))) return st;
+      if ((st = launch_epi_silu_mul(gp, p.gpart, dt, p.act, s, "epi_silu_mul"))) return st;
+      GemmPlan gd = plan_gemm(M, d, p.F, dt);
+      if ((st = launch_gemm(gd, dt, p.act, p.F, w->w_down, p.gpart, s, "gemm_down"))) return st;
+      if ((st = launch_epi_sum(gd, p.gpart, p.a_rows, p.h1, s, "epi_down"))) return st;
+      ProfScope ps("rmsnorm", s);
+      hipLaunchKernelGGL(k_rmsnorm<T>, dim3(M), dim3(256), 0, s, p.a_rows, d, w->eps,
+                         (const T*)w->g_final, (T*)p.xl, R, sb, p.S, p.st, p.slot_a,
+                         dbg ? dbg->slot_a : (float*)nullptr);
+      if ((st = launch_status())) return st;
+    }
+    // LM head, top-K and log-sum-exp
+    {
+      GemmPlan gp = plan_gemm(M, p.V, d, dt);
+      if ((st = launch_gemm(gp, dt, p.xl, d, w->w_lm, p.gpart, s, "gemm_lm_head"))) return st;
+      {
+        ProfScope ps("topk_chunk", s);
+        hipLaunchKernelGGL(k_topk_chunk, dim3(p.lm_nchunk, M), dim3(256), 0, s, p.gpart, gp.splits, M,
+                           p.V, p.K, p.lm_chunk, p.lm_nchunk, p.cv, p.ci, p.cmax, p.csum,
+                           dbg ? dbg->slot_logits : (float*)nullptr, R, sb, p.S, p.st);
+        if ((st = launch_status())) return st;
+      }
+      ProfScope ps("topk_merge", s);
+      hipLaunchKernelGGL(k_topk_merge, dim3(M), dim3(256), 0, s, p.cv, p.ci, p.cmax, p.csum,
+                         p.lm_nchunk, p.K, p.top_id, p.top_val, p.lse, R, sb, p.S, p.st,
+                         dbg ? dbg->slot_topk_id : (int32_t*)nullptr,
+                         dbg ? dbg->slot_topk_val : (float*)nullptr, dbg ? dbg->slot_lse : (float*)nullptr);
+      if ((st = launch_status())) return st;
+    }
+    {
+      ProfScope ps("draft_select", s);
+      hipLaunchKernelGGL(k_select, dim3(B), dim3(256), 0, s, step, p.D, p.K, p.W, p.N, p.S, p.PMAX, R,
+                         p.top_id, p.top_val, p.lse, p.st, p.cs, tokens, parents, depth, score, n_nodes,
+                         dbg_tok, dbg_par);
+      if ((st = launch_status())) return st;
+    }
+  }
+  return EAGLE3_OK;
+}
+
+}  // namespace
+
+namespace e3h {
+
+int draft_check(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, int max_prefix) {
+  if (!w || !t || B <= 0 || max_prefix < 0) return EAGLE3_EINVAL;
+  if (!dtype_ok(w->dtype)) return EAGLE3_EINVAL;
+  if (w->d <= 0 || w->n_heads_q <= 0 || w->n_heads_kv <= 0 || w->ffn <= 0 || w->vocab <= 0)
+    return EAGLE3_EINVAL;
+  if (w->n_heads_q % w->n_heads_kv) return EAGLE3_EINVAL;
+  if (w->head_dim != 64 && w->head_dim != 128) return EAGLE3_EUNSUPPORTED;
+  if (w->d % 8 || w->ffn % 8 || w->vocab % 4) return EAGLE3_EUNSUPPORTED;
+  if (!(w->eps > 0.f) || !(w->rope_theta > 0.f)) return EAGLE3_EINVAL;
+  if (t->depth < 1 || t->topk < 1 || t->width < 1 || t->n_nodes < 1) return EAGLE3_EINVAL;
+  if (t->topk > KMAX || t->topk > w->vocab) return EAGLE3_EUNSUPPORTED;
+  if (1 + (long)(t->depth - 1) * t->width > SMAX) return EAGLE3_EUNSUPPORTED;
+  if ((long)t->topk + (long)(t->depth - 1) * t->width * t->topk > 1024) return EAGLE3_EUNSUPPORTED;
+  if (t->n_nodes > 255) return EAGLE3_EUNSUPPORTED;
+  if ((long)B * (t->width > 1 ? t->width : 1) > 160) return EAGLE3_EUNSUPPORTED;
+  const long nch = (w->vocab + 4095) / 4096;
+  if (nch * t->topk > 1024) return EAGLE3_EUNSUPPORTED;
+  if (!w->embed || !w->w_fuse || !w->g_embed || !w->g_feat || !w->g_mlp || !w->g_final ||
+      !w->w_qkv || !w->w_o || !w->w_gate_up || !w->w_down || !w->w_lm)
+    return EAGLE3_EINVAL;
+  return EAGLE3_OK;
+}
+
+size_t draft_workspace(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, int max_prefix) {
+  if (draft_check(w, t, B, max_prefix) != EAGLE3_OK) return 0;
+  return make_plan(w, t, B, max_prefix, nullptr).bytes;
+}
+
+int draft_expand(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, const void* h_low,
+                 const void* h_mid, const void* h_high, const int32_t* root_tok, const void* kpre,
+                 const void* vpre, const int32_t* cu_prefix, int max_prefix, int32_t* tokens,
+                 int32_t* parents, int32_t* depth, float* score, int32_t* n_nodes,
+                 const eagle3_draft_debug* dbg, void* ws, size_t ws_bytes, hipStream_t s) {
+  int st = draft_check(w, t, B, max_prefix);
+  if (st) return st;
+  if (!h_low || !h_mid || !h_high || !root_tok || !cu_prefix || !tokens || !parents || !depth ||
+      !score || !n_nodes)
+    return EAGLE3_EINVAL;
+  if (max_prefix > 0 && (!kpre || !vpre)) return EAGLE3_EINVAL;
+  Plan p = make_plan(w, t, B, max_prefix, nullptr);
+  if (!ws || ws_bytes < p.bytes) return EAGLE3_EWORKSPACE;
+  p = make_plan(w, t, B, max_prefix, ws);
+  if (w->dtype == EAGLE3_BF16)
+    return run_draft<bf16>(w, p, h_low, h_mid, h_high, root_tok, kpre, vpre, cu_prefix, tokens, parents,
+                           depth, score, n_nodes, dbg, s);
+  return run_draft<float>(w, p, h_low, h_mid, h_high, root_tok, kpre, vpre, cu_prefix, tokens, parents,
+                          depth, score, n_nodes, dbg, s);
+}
+
+}  // namespace e3h

@@ -1,0 +1,62 @@
+// Host-side launchers shared between the translation units of libeagle3.
+#pragma once
+
+#include "common.h"
+
+namespace e3h {
+
+// ---- attention -------------------------------------------------------------------------
+// Query rows and tree keys of request b are either given by offset arrays (cu_* != null)
+// or by a fixed per-request stride and count.
+struct AttnArgs {
+  int B, Hq, Hkv, Dh, dtype;
+  const void* q;
+  const int32_t* q_cu;
+  int q_stride, q_rows_total;  // q_stride: rows per request when q_cu == null
+  const void* kt;
+  const void* vt;
+  const int32_t* kt_cu;
+  int kt_stride, kt_count;     // used when kt_cu == null
+  const uint64_t* mask;        // [q_rows_total, W64], bits over the request's tree keys
+  int W64;
+  const void* kp;
+  const void* vp;
+  const int32_t* p_cu;         // [B+1] prefix offsets (may be null: no prefix)
+  float scale;
+  int S;                       // prefix splits; partial S is the tree
+  int max_q_per_req;           // host bound on query rows (nodes) per request
+  float* o_part;               // [S+1, q_rows_total, Hq, Dh]
+  float* lse_part;             // [S+1, q_rows_total, Hq]
+};
+int launch_tree_attention(const AttnArgs& a, hipStream_t s, const char* tag);
+int launch_lse_merge(int S, int rows, int Dh, const float* o_part, const float* lse_part,
+                     int out_dtype, void* o, float* lse, hipStream_t s, const char* tag);
+int attention_splits(int max_prefix, int n_splits);
+
+// ---- verify ----------------------------------------------------------------------------
+int launch_build_mask(int B, int T, const int32_t* cu_nodes, const int32_t* parents,
+                      const int32_t* cu_prefix, uint64_t* mask, int W64, int32_t* depth,
+                      int32_t* pos, int32_t* dev_status, hipStream_t s);
+int launch_accept(int B, int T, const int32_t* cu_nodes, const int32_t* tokens,
+                  const int32_t* parents, const uint64_t* mask, int W64, const void* logits,
+                  int V, int dtype, float temperature, uint64_t seed, uint64_t round,
+                  int max_depth, int32_t* accept_len, int32_t* path, int32_t* out_tokens,
+                  int32_t* bonus, float* part_v, int* part_i, hipStream_t s);
+size_t accept_workspace(int T, int V);
+
+// ---- GEMM ------------------------------------------------------------------------------
+// Y_part[split][m][n] = sum over the split's k of X[m][k] * W[n][k]  (fp32 partials).
+struct GemmPlan {
+  int M, N, K, MT, NT, n_blocks, splits, chunks_total, chunks_per_split, waves;
+};
+GemmPlan plan_gemm(int M, int N, int K, int dtype);
+int launch_gemm(const GemmPlan& p, int dtype, const void* X, int ldx, const void* W, float* Ypart,
+                hipStream_t s, const char* tag);
+
+// Epilogues over the split partials (all sums in split order).
+int launch_epi_sum(const GemmPlan& p, const float* part, float* out, const float* resid,
+                   hipStream_t s, const char* tag);
+int launch_epi_silu_mul(const GemmPlan& p, const float* part, int dtype, void* out,
+                        hipStream_t s, const char* tag);
+
+}  // namespace e3h
