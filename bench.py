@@ -1,0 +1,230 @@
+"""Benchmark: one EAGLE-3 draft-tree round + one tree-verification round per step.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b]
+
+A step runs the whole hot path on one stream through the C-ABI:
+  eagle3_draft_expand -> eagle3_build_tree_mask -> eagle3_tree_attention (partials)
+  -> eagle3_lse_merge -> eagle3_accept.
+Inputs are seeded synthetic tensors already resident in HBM (random-init drafter weights of
+the Llama-3.1-8B shape, Gaussian features and KV); the verify layer's Q/K/V and the target
+logits are given, untimed.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified tree tokens/sec per draft+verify round; % HBM/MFMA peak"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "batch16", "llama70b", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel", default="gemm_lm_head", help="kernel timed for the roofline")
+    return ap.parse_args()
+
+
+class Round:
+    """Preallocated buffers for one draft + verify round."""
+
+    def __init__(self, shape, dev, seed=1234):
+        import torch
+        from speculative_decoding_round_amd import capi, synth
+        self.shape = shape
+        self.capi = capi
+        self.B = shape.B
+        self.prefix = synth.prefix_lengths(shape, seed)
+        self.w = synth.drafter_weights(shape, seed=seed, device=dev)
+        self.di = synth.draft_inputs(shape, seed=seed + 1, device=dev, prefix=self.prefix)
+        self.drafter = capi.make_drafter(self.w, shape.Hq, shape.Hkv, shape.Dh)
+        self.tree = capi.Eagle3TreeCfg(depth=shape.depth, topk=shape.topk, width=shape.width,
+                                       n_nodes=shape.n_nodes)
+        self.max_prefix = max(self.prefix)
+        n1 = shape.n_nodes + 1
+        self.n1 = n1
+        self.T = self.B * n1
+        ws = capi.eagle3_draft_expand_workspace_size(self.drafter, self.tree, self.B, self.max_prefix)
+        self.ws_draft = torch.empty(ws, dtype=torch.uint8, device=dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.draft_out = {"tokens": torch.empty((self.B, n1), **i32),
+                          "parents": torch.empty((self.B, n1), **i32),
+                          "depth": torch.empty((self.B, n1), **i32),
+                          "score": torch.empty((self.B, n1), dtype=torch.float32, device=dev),
+                          "n_nodes": torch.empty((self.B,), **i32)}
+        # verify layer: queries and tree K/V for every node, its own prefix KV, target logits
+        trees = [[-1] + [0] * (n1 - 1)] * self.B        # shapes only; topology comes from the draft
+        self.vi = synth.verify_inputs(shape, trees, self.prefix, seed=seed + 2, device=dev)
+        self.cu_nodes = torch.arange(0, self.T + 1, n1, **i32)
+        self.mask_out = {"mask": torch.empty((self.T, 1), dtype=torch.uint64, device=dev),
+                         "depth": torch.empty((self.T,), **i32), "pos": torch.empty((self.T,), **i32)}
+        self.S = capi.eagle3_tree_attention_num_splits(self.max_prefix, 0)
+        Hq, Dh = shape.Hq, shape.Dh
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.att_out = {"o_part": torch.empty((self.S + 1, self.T, Hq, Dh), **f32),
+                        "lse_part": torch.empty((self.S + 1, self.T, Hq), **f32)}
+        self.merge_out = {"o": torch.empty((self.T * Hq, Dh), dtype=synth.torch_dtype(shape), device=dev),
+                          "lse": torch.empty((self.T * Hq,), **f32)}
+        self.ws_acc = torch.empty(capi.lib().eagle3_accept_workspace_size(self.T, shape.V),
+                                  dtype=torch.uint8, device=dev)
+        D = shape.depth
+        self.acc_out = {"accept_len": torch.empty((self.B,), **i32),
+                        "path": torch.empty((self.B, D + 1), **i32),
+                        "out_tokens": torch.empty((self.B, D + 1), **i32),
+                        "bonus": torch.empty((self.B,), **i32)}
+        self.scale = float(1.0 / math.sqrt(Dh))
+        self.round = 0
+
+    def step(self):
+        c, s, di, vi = self.capi, self.shape, self.di, self.vi
+        out = c.eagle3_draft_expand(self.drafter, self.tree, di["h_low"], di["h_mid"], di["h_high"],
+                                    di["root_tok"], di["kpre"], di["vpre"], di["cu_prefix"],
+                                    self.max_prefix, workspace=self.ws_draft, out=self.draft_out)
+        parents = out["parents"].view(-1)
+        tokens = out["tokens"].view(-1)
+        mk = c.eagle3_build_tree_mask(self.cu_nodes, parents, vi["cu_prefix"], self.n1,
+                                      out=self.mask_out)
+        att = c.eagle3_tree_attention(vi["q"], vi["k_tree"], vi["v_tree"], self.cu_nodes, self.n1,
+                                      mk["mask"], vi["kpre"], vi["vpre"], vi["cu_prefix"],
+                                      self.max_prefix, self.scale, out=self.att_out)
+        T, Hq, Dh = self.T, s.Hq, s.Dh
+        c.eagle3_lse_merge(att["o_part"].view(self.S + 1, T * Hq, Dh),
+                           att["lse_part"].view(self.S + 1, T * Hq), out=self.merge_out)
+        c.eagle3_accept(self.cu_nodes, tokens, parents, mk["mask"], vi["logits"], s.temperature,
+                        seed=20260101, round=self.round, max_depth=s.depth, workspace=self.ws_acc,
+                        out=self.acc_out)
+        self.round += 1
+
+
+def lm_head_bytes(shape, M):
+    """Algorithmic HBM bytes of one LM-head launch: weights once, the M input rows, the M
+    logit rows written in fp32."""
+    es = 4 if shape.dtype == "f32" else 2
+    return shape.V * shape.d * es + M * shape.d * es + M * shape.V * 4
+
+
+def cpu_baseline(rnd: Round):
+    """Time the oracle (as written, untuned) on a bounded sample: one full draft + verify
+    round of the same workload on the host cores."""
+    import numpy as np
+    import torch
+    from oracle import eagle3_oracle as O
+    from speculative_decoding_round_amd import synth
+    s = rnd.shape
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    w = {k: v.cpu() for k, v in rnd.w.items()}
+    di = {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in rnd.di.items()}
+    drafter = O.Drafter(w, s.Hq, s.Hkv, s.Dh)                 # fp64 upcast: not timed
+    vi = {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in rnd.vi.items()}
+    t0 = time.perf_counter()
+    res = O.draft_round(drafter, s.depth, s.topk, s.width, s.n_nodes, di["h_low"], di["h_mid"],
+                        di["h_high"], di["root_tok"], di["kpre"], di["vpre"], rnd.prefix)
+    parents, tokens, cu = [], [], [0]
+    for r in res:
+        n = len(r["parents"])
+        parents += r["parents"] + [0] * (rnd.n1 - n)
+        tokens += r["tokens"] + [0] * (rnd.n1 - n)
+        cu.append(cu[-1] + rnd.n1)
+    cup = vi["cu_prefix"].tolist()
+    mask, _, _, _ = O.build_tree_mask(parents, cu, cup)
+    S = rnd.S
+    o_parts, l_parts = [], []
+    for sp in range(S + 1):
+        def filt(b, P, sp=sp):
+            keep = np.zeros(P, dtype=bool)
+            if sp < S:
+                ch = -(-P // S)
+                keep[min(P, sp * ch):min(P, sp * ch + ch)] = True
+            return keep, np.full(rnd.n1, sp == S)
+        o, l = O.tree_attention(vi["q"], vi["k_tree"], vi["v_tree"], cu, mask, vi["kpre"],
+                                vi["vpre"], cup, rnd.scale, key_filter=filt)
+        o_parts.append(o.reshape(-1, s.Dh))
+        l_parts.append(l.reshape(-1))
+    O.lse_merge(np.stack(o_parts), np.stack(l_parts))
+    O.accept(cu, tokens, parents, vi["logits"], s.temperature, 20260101, 0, s.depth)
+    dt = time.perf_counter() - t0
+    verified = sum(len(r["tokens"]) - 1 for r in res)
+    return {"value": verified / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one full draft+verify round of the same workload ({verified} verified "
+                      f"tree tokens) in {dt:.2f} s, float64 numpy oracle"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from speculative_decoding_round_amd import capi, synth
+    dev = "cuda:0"
+    shape = {"llama8b": synth.LLAMA8B, "batch16": synth.BATCH16, "llama70b": synth.LLAMA70B,
+             "tiny": synth.TINY}[args.workload]
+    rnd = Round(shape, dev)
+    for _ in range(args.warmup):
+        rnd.step()
+    torch.cuda.synchronize()
+    n_verified = int(rnd.draft_out["n_nodes"].sum().item()) - rnd.B
+
+    stream = torch.cuda.current_stream()
+    capi.eagle3_profile_reset()
+    capi.eagle3_profile_enable(True, only_kernel=args.kernel)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        rnd.step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    capi.eagle3_profile_enable(False)
+    ms = ev0.elapsed_time(ev1) / args.steps
+    k_ms, k_n = capi.eagle3_profile_read(args.kernel)
+    capi.eagle3_profile_reset()
+
+    value = n_verified / (ms / 1e3)
+    # rows the LM head sees: B at the root step, B*W at every later step
+    rows = [shape.B] + [shape.B * shape.width] * (shape.depth - 1)
+    bytes_avg = sum(lm_head_bytes(shape, m) for m in rows) / len(rows)
+    k_avg_ms = k_ms / max(k_n, 1)
+    achieved = bytes_avg / (k_avg_ms / 1e3) / 1e9
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if shape.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": f"{shape.name}: draft tree D={shape.depth} K={shape.topk} "
+                               f"W={shape.width} N={shape.n_nodes}, verify over prefix {rnd.max_prefix}",
+                   "batch": shape.B, "d": shape.d, "heads": [shape.Hq, shape.Hkv, shape.Dh],
+                   "ffn": shape.F, "vocab": shape.V, "prefix": rnd.prefix if shape.B <= 4 else "ragged",
+                   "verified_nodes_per_round": n_verified, "temperature": shape.temperature},
+        "roofline": {"kernel": args.kernel, "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(k_avg_ms * 1e3, 2),
+                     "launches": k_n, "algorithmic_bytes_per_launch": int(bytes_avg)},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(rnd)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -246,11 +246,13 @@ EAGLE3_API int eagle3_accept(int B, int T, const int32_t* cu_nodes, const int32_
 
 /* ------------------------------------------------------------------------------------
  * Launch timing.  While enabled, the library records a HIP event pair on the launch stream
- * around every kernel it enqueues, tagged with the kernel's name.  eagle3_profile_read
- * waits for the recorded events and reports the summed device time and launch count of
- * one kernel name (e.g. "gemm_lm_head").  eagle3_profile_reset drops all records.
+ * around every kernel it enqueues whose name equals `only_kernel` (every kernel when
+ * `only_kernel` is NULL).  eagle3_profile_read waits for the recorded events and reports
+ * the summed device time and launch count of one kernel name (e.g. "gemm_lm_head").
+ * eagle3_profile_reset drops all records.  Host-side bookkeeping only; not thread-safe
+ * against concurrent launches from other threads beyond a global lock.
  * ------------------------------------------------------------------------------------ */
-EAGLE3_API int eagle3_profile_enable(int on);
+EAGLE3_API int eagle3_profile_enable(int on, const char* only_kernel);
 EAGLE3_API int eagle3_profile_reset(void);
 EAGLE3_API int eagle3_profile_read(const char* kernel, double* total_ms, int* launches);
 

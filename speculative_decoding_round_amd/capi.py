@@ -69,7 +69,7 @@ EXPORTS = {
                               c_void_p, c_int, c_int, c_float, c_uint64, c_uint64, c_int,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                               c_void_p]),
-    "eagle3_profile_enable": (c_int, [c_int]),
+    "eagle3_profile_enable": (c_int, [c_int, c_char_p]),
     "eagle3_profile_reset": (c_int, []),
     "eagle3_profile_read": (c_int, [c_char_p, ctypes.POINTER(c_double), ctypes.POINTER(c_int)]),
 }
@@ -348,8 +348,10 @@ def eagle3_accept(cu_nodes, tokens, parents, mask, logits, temperature: float, s
 # ---------------------------------------------------------------------------------------
 
 
-def eagle3_profile_enable(on: bool = True) -> None:
-    _check("eagle3_profile_enable", lib().eagle3_profile_enable(1 if on else 0))
+def eagle3_profile_enable(on: bool = True, only_kernel: Optional[str] = None) -> None:
+    """Time the library's launches (only those named `only_kernel` if given)."""
+    name = only_kernel.encode() if only_kernel else None
+    _check("eagle3_profile_enable", lib().eagle3_profile_enable(1 if on else 0, name))
 
 
 def eagle3_profile_reset() -> None:

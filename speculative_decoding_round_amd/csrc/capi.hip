@@ -27,6 +27,7 @@ struct Rec {
 };
 std::mutex g_mu;
 bool g_on = false;
+std::string g_only;             // empty: every kernel
 std::vector<Rec> g_recs;        // recorded pairs (events owned here)
 std::vector<hipEvent_t> g_pool; // spare events
 int g_open = -1;
@@ -46,6 +47,7 @@ hipEvent_t take_event() {
 ProfScope::ProfScope(const char* name, hipStream_t s) : slot(-1), stream(s) {
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_on || g_open >= 0) return;  // nested scopes are timed by the outermost one
+  if (!g_only.empty() && g_only != name) return;
   Rec r;
   r.name = name;
   r.e0 = take_event();
@@ -225,9 +227,10 @@ int eagle3_accept(int B, int T, const int32_t* cu_nodes, const int32_t* tokens,
 }
 
 // ---- timing ---------------------------------------------------------------------------
-int eagle3_profile_enable(int on) {
+int eagle3_profile_enable(int on, const char* only_kernel) {
   std::lock_guard<std::mutex> lk(e3h::g_mu);
   e3h::g_on = on != 0;
+  e3h::g_only = only_kernel ? only_kernel : "";
   return EAGLE3_OK;
 }
 

@@ -179,7 +179,8 @@ __global__ __launch_bounds__(256) void k_epi_qkv(const float* __restrict__ part,
   if (h < Hq) {
     dst = q_rows + ((size_t)m * Hq + h) * Dh;
   } else {
-    if (!st.valid[si]) return;
+    // padding rows (unused slots) are written too: their keys are masked out of every
+    // row, but P = 0 times a non-finite stale value would still poison P.V
     const int c = h < Hq + Hkv ? h - Hq : h - Hq - Hkv;
     T* base = h < Hq + Hkv ? kslot : vslot;
     dst = base + ((size_t)si * Hkv + c) * Dh;

@@ -184,3 +184,27 @@ def test_draft_llama8b_full_size_sampled():
                 s = by[s]["parent_slot"]
         return [by[s] for s in sorted(keep)]
     check_teacher_forced(shape, w, di, out, 1, prefix, slots_per_request=chains)
+
+
+def test_draft_ignores_stale_workspace_contents():
+    """Unused evaluation slots sit inside the drafter's tree-key range (masked out); the
+    round must not depend on what the workspace held before (here: all NaN bytes)."""
+    need_gpu()
+    shape = SMALL_BF16
+    prefix = [300, 0, 1000]
+    w = synth.drafter_weights(shape, seed=7, device=DEV)
+    di = synth.draft_inputs(shape, seed=8, device=DEV, prefix=prefix)
+    dr = capi.make_drafter(w, shape.Hq, shape.Hkv, shape.Dh)
+    tree = capi.Eagle3TreeCfg(depth=shape.depth, topk=shape.topk, width=shape.width,
+                              n_nodes=shape.n_nodes)
+    nbytes = capi.eagle3_draft_expand_workspace_size(dr, tree, shape.B, max(prefix))
+    outs = []
+    for fill in (0xFF, 0x00):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device=DEV)
+        outs.append(capi.eagle3_draft_expand(dr, tree, di["h_low"], di["h_mid"], di["h_high"],
+                                             di["root_tok"], di["kpre"], di["vpre"], di["cu_prefix"],
+                                             max(prefix), workspace=ws))
+    torch.cuda.synchronize()
+    for k in ("tokens", "parents", "depth", "score", "n_nodes"):
+        assert torch.equal(outs[0][k], outs[1][k]), k
+    assert torch.isfinite(outs[0]["score"][:, :shape.n_nodes + 1]).all()
