@@ -69,7 +69,7 @@ class Round:
         self.cu_nodes = torch.arange(0, self.T + 1, n1, **i32)
         self.mask_out = {"mask": torch.empty((self.T, 1), dtype=torch.uint64, device=dev),
                          "depth": torch.empty((self.T,), **i32), "pos": torch.empty((self.T,), **i32)}
-        self.S = capi.eagle3_tree_attention_num_splits(self.max_prefix, 0)
+        self.S = capi.eagle3_tree_attention_num_splits(self.B, shape.Hq, shape.Hkv, n1, self.max_prefix, 0)
         Hq, Dh = shape.Hq, shape.Dh
         f32 = dict(dtype=torch.float32, device=dev)
         self.att_out = {"o_part": torch.empty((self.S + 1, self.T, Hq, Dh), **f32),

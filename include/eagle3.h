@@ -191,11 +191,14 @@ EAGLE3_API int eagle3_build_tree_mask(int B, int T, const int32_t* cu_nodes, con
  *
  *  q [T, Hq, Dh], k_tree, v_tree [T, Hkv, Dh], kpre, vpre [sum P_b, Hkv, Dh]: dtype
  *  cu_nodes [B+1], cu_prefix [B+1]: int32 device; mask [T, W64] as built above
- *  max_nodes, max_prefix: host upper bounds per request; n_splits: S (0 = automatic;
- *  eagle3_tree_attention_num_splits returns the S used).  Dh must be 64 or 128.
+ *  max_nodes, max_prefix: host upper bounds per request; n_splits: S (0 = automatic: about
+ *  1024 workgroups, at least 128 keys per split and 64-row block; the same arguments give
+ *  the same S in eagle3_tree_attention_num_splits).  Dh must be 64 or 128.
  * ------------------------------------------------------------------------------------ */
-EAGLE3_API int eagle3_tree_attention_num_splits(int max_prefix, int n_splits);
-EAGLE3_API size_t eagle3_tree_attention_workspace_size(int T, int Hq, int Dh, int max_prefix, int n_splits);
+EAGLE3_API int eagle3_tree_attention_num_splits(int B, int Hq, int Hkv, int max_nodes,
+                                                int max_prefix, int n_splits);
+EAGLE3_API size_t eagle3_tree_attention_workspace_size(int B, int T, int Hq, int Hkv, int Dh,
+                                                      int max_nodes, int max_prefix, int n_splits);
 EAGLE3_API int eagle3_tree_attention(int B, int T, int Hq, int Hkv, int Dh, int dtype, const void* q,
                           const void* k_tree, const void* v_tree, const int32_t* cu_nodes,
                           int max_nodes, const uint64_t* mask, int W64, const void* kpre,

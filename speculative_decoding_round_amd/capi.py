@@ -55,8 +55,9 @@ EXPORTS = {
                                     c_size_t, c_void_p]),
     "eagle3_build_tree_mask": (c_int, [c_int, c_int, c_void_p, c_void_p, c_void_p, c_int,
                                        c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
-    "eagle3_tree_attention_num_splits": (c_int, [c_int, c_int]),
-    "eagle3_tree_attention_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
+    "eagle3_tree_attention_num_splits": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int]),
+    "eagle3_tree_attention_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int,
+                                                        c_int, c_int]),
     "eagle3_tree_attention": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p,
                                       c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_int,
                                       c_void_p, c_void_p, c_void_p, c_int, c_float, c_int,
@@ -251,8 +252,12 @@ def eagle3_build_tree_mask(cu_nodes, parents, cu_prefix, max_nodes: int, W64: in
     return out
 
 
-def eagle3_tree_attention_num_splits(max_prefix: int, n_splits: int = 0) -> int:
-    return lib().eagle3_tree_attention_num_splits(max_prefix, n_splits)
+def eagle3_tree_attention_num_splits(B: int, Hq: int, Hkv: int, max_nodes: int, max_prefix: int,
+                                     n_splits: int = 0) -> int:
+    s = lib().eagle3_tree_attention_num_splits(B, Hq, Hkv, max_nodes, max_prefix, n_splits)
+    if s < 1:
+        raise Eagle3Error("eagle3_tree_attention_num_splits", s)
+    return s
 
 
 def eagle3_tree_attention(q, k_tree, v_tree, cu_nodes, max_nodes: int, mask, kpre, vpre,
@@ -274,7 +279,7 @@ def eagle3_tree_attention(q, k_tree, v_tree, cu_nodes, max_nodes: int, mask, kpr
         _dev(cu_prefix, "cu_prefix", torch.int32)
     B = cu_nodes.numel() - 1
     W64 = mask.shape[1] if mask.dim() == 2 else 1
-    S = eagle3_tree_attention_num_splits(max_prefix, n_splits)
+    S = eagle3_tree_attention_num_splits(B, Hq, Hkv, max_nodes, max_prefix, n_splits)
     dev = q.device
     if out is None:
         out = {}
@@ -285,8 +290,8 @@ def eagle3_tree_attention(q, k_tree, v_tree, cu_nodes, max_nodes: int, mask, kpr
             out["o"] = torch.empty((T, Hq, Dh), dtype=dt, device=dev)
             out["lse"] = torch.empty((T, Hq), dtype=torch.float32, device=dev)
     if workspace is None and "o_part" not in out:
-        workspace = _workspace(lib().eagle3_tree_attention_workspace_size(T, Hq, Dh, max_prefix,
-                                                                          n_splits), dev)
+        workspace = _workspace(lib().eagle3_tree_attention_workspace_size(
+            B, T, Hq, Hkv, Dh, max_nodes, max_prefix, n_splits), dev)
     st = lib().eagle3_tree_attention(
         B, T, Hq, Hkv, Dh, dtype_code(dt), q.data_ptr(), k_tree.data_ptr(), v_tree.data_ptr(),
         cu_nodes.data_ptr(), int(max_nodes), mask.data_ptr(), W64, _ptr(kpre), _ptr(vpre),

@@ -308,11 +308,20 @@ int launch_attn_t(const e3h::AttnArgs& h, hipStream_t s) {
 
 namespace e3h {
 
-int attention_splits(int max_prefix, int n_splits) {
+// Prefix splits: aim at ~1024 workgroups in total, but give every split at least
+// 128 keys per 64-row block so that a split's fp32 partial (64 rows x Dh x 4 B per row
+// block) stays at or below half of the bf16 K+V bytes it streams.
+int attention_splits(int B, int Hkv, int rows_per_kv, int max_prefix, int n_splits) {
   if (n_splits > 0) return n_splits;
-  if (max_prefix <= 0) return 1;
-  int s = (max_prefix + 511) / 512;
-  return s < 1 ? 1 : (s > 256 ? 256 : s);
+  if (max_prefix <= 0 || B <= 0 || Hkv <= 0) return 1;
+  const int rb = rows_per_kv > 0 ? (rows_per_kv + ROWS - 1) / ROWS : 1;
+  const long base = (long)B * Hkv * rb;
+  long s = (1024 + base - 1) / base;
+  const long min_keys = 128L * rb;
+  const long max_s = (max_prefix + min_keys - 1) / min_keys;
+  if (s > max_s) s = max_s;
+  if (s > 256) s = 256;
+  return s < 1 ? 1 : (int)s;
 }
 
 int launch_tree_attention(const AttnArgs& a, hipStream_t s, const char* tag) {

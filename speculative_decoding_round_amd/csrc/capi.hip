@@ -116,14 +116,17 @@ int eagle3_build_tree_mask(int B, int T, const int32_t* cu_nodes, const int32_t*
 }
 
 // ---- attention ------------------------------------------------------------------------
-int eagle3_tree_attention_num_splits(int max_prefix, int n_splits) {
-  if (max_prefix < 0 || n_splits < 0) return EAGLE3_EINVAL;
-  return attention_splits(max_prefix, n_splits);
+int eagle3_tree_attention_num_splits(int B, int Hq, int Hkv, int max_nodes, int max_prefix,
+                                     int n_splits) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || max_nodes < 0 || max_prefix < 0 || n_splits < 0)
+    return EAGLE3_EINVAL;
+  return attention_splits(B, Hkv, max_nodes * (Hq / Hkv), max_prefix, n_splits);
 }
 
-size_t eagle3_tree_attention_workspace_size(int T, int Hq, int Dh, int max_prefix, int n_splits) {
-  if (T < 0 || Hq <= 0 || Dh <= 0 || max_prefix < 0 || n_splits < 0) return 0;
-  const int S = attention_splits(max_prefix, n_splits);
+size_t eagle3_tree_attention_workspace_size(int B, int T, int Hq, int Hkv, int Dh, int max_nodes,
+                                            int max_prefix, int n_splits) {
+  const int S = eagle3_tree_attention_num_splits(B, Hq, Hkv, max_nodes, max_prefix, n_splits);
+  if (S < 1 || T < 0 || Dh <= 0) return 0;
   Carve c(nullptr);
   c.take<float>((size_t)(S + 1) * T * Hq * Dh);
   c.take<float>((size_t)(S + 1) * T * Hq);
@@ -147,9 +150,10 @@ int eagle3_tree_attention(int B, int T, int Hq, int Hkv, int Dh, int dtype, cons
   if (!q || !k_tree || !v_tree || !cu_nodes || !mask) return EAGLE3_EINVAL;
   if (max_prefix > 0 && (!kpre || !vpre || !cu_prefix)) return EAGLE3_EINVAL;
   if (!o && (!o_part || !lse_part)) return EAGLE3_EINVAL;
-  const int S = attention_splits(max_prefix, n_splits);
+  const int S = attention_splits(B, Hkv, max_nodes * (Hq / Hkv), max_prefix, n_splits);
   if (!o_part || !lse_part) {
-    const size_t need = eagle3_tree_attention_workspace_size(T, Hq, Dh, max_prefix, n_splits);
+    const size_t need =
+        eagle3_tree_attention_workspace_size(B, T, Hq, Hkv, Dh, max_nodes, max_prefix, n_splits);
     if (!workspace || workspace_bytes < need) return EAGLE3_EWORKSPACE;
     Carve c(workspace);
     o_part = c.take<float>((size_t)(S + 1) * T * Hq * Dh);
@@ -217,8 +221,7 @@ int eagle3_accept(int B, int T, const int32_t* cu_nodes, const int32_t* tokens,
   const size_t need = accept_workspace(T, V);
   if (!workspace || workspace_bytes < need) return EAGLE3_EWORKSPACE;
   Carve c(workspace);
-  const int chunk = V < 4096 ? V : 4096;
-  const int n_chunks = (V + chunk - 1) / chunk;
+  const int n_chunks = accept_chunks(V);
   float* pv = c.take<float>((size_t)T * n_chunks);
   int* pi = c.take<int>((size_t)T * n_chunks);
   return launch_accept(B, T, cu_nodes, tokens, parents, mask, W64, logits, V, dtype, temperature,

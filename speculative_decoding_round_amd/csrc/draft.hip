@@ -61,78 +61,143 @@ __global__ __launch_bounds__(256) void k_init(int B, int S, int d, int V, const 
 }
 
 // ---------------------------------------------------------------------------------------
-// prep: u = [rms(E[x]) * g_e ; rms(f) * g_f], f = g (root) or a of the parent slot.
+// Row kernels.  One workgroup per row, one thread per 8-element chunk (d <= 8 * 1024), every
+// load issued before any arithmetic so a row costs one memory round trip.
 // ---------------------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void k_prep(int R, int sb, int S, int d, int V, float eps, int step,
-                                              SlotState st, const T* __restrict__ embed,
-                                              const T* __restrict__ g_e, const T* __restrict__ g_f,
-                                              const float* __restrict__ gfeat,
-                                              const float* __restrict__ slot_a,
-                                              float* __restrict__ f_rows, T* __restrict__ u,
-                                              uint64_t* __restrict__ row_mask) {
-  __shared__ float red[4];
+__device__ __forceinline__ void load8(const T* p, float* v);
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* v) {
+  const u32x4 a = ld16(p), b = ld16(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = __uint_as_float(a[i]);
+    v[4 + i] = __uint_as_float(b[i]);
+  }
+}
+template <>
+__device__ __forceinline__ void load8<bf16>(const bf16* p, float* v) {
+  const u32x4 a = ld16(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = chunk_elem<bf16>(a, i);
+}
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float* v);
+template <>
+__device__ __forceinline__ void store8<float>(float* p, const float* v) {
+  st16(p, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
+  st16(p + 4, u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])});
+}
+template <>
+__device__ __forceinline__ void store8<bf16>(bf16* p, const float* v) {
+  bf16x8 o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = static_cast<bf16>(v[i]);
+  st16(p, __builtin_bit_cast(u32x4, o));
+}
+
+// Sum of two values over the block (fixed order); scratch needs 2 * 16 floats.
+__device__ __forceinline__ void block_sum2(float& a, float& b, float* scratch) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  a = wave_sum(a);
+  b = wave_sum(b);
+  if (lane == 0) {
+    scratch[w] = a;
+    scratch[16 + w] = b;
+  }
+  __syncthreads();
+  a = 0.f;
+  b = 0.f;
+  for (int i = 0; i < nw; ++i) {
+    a += scratch[i];
+    b += scratch[16 + i];
+  }
+}
+
+// prep: u = [rms(E[x]) * g_e ; rms(f) * g_f], f = g (root) or a of the parent slot.
+template <typename T>
+__global__ __launch_bounds__(1024) void k_prep(int R, int sb, int S, int d, int V, float eps, int step,
+                                               SlotState st, const T* __restrict__ embed,
+                                               const T* __restrict__ g_e, const T* __restrict__ g_f,
+                                               const float* __restrict__ gfeat,
+                                               const float* __restrict__ slot_a,
+                                               float* __restrict__ f_rows, T* __restrict__ u,
+                                               uint64_t* __restrict__ row_mask) {
+  __shared__ float red[32];
   const int r = blockIdx.x;
   const int b = r / R, j = r % R;
   const int si = b * S + sb + j;
   const bool valid = st.valid[si] != 0;
   const int tok = valid ? clampi(st.tok[si], 0, V - 1) : 0;
   const float* f = nullptr;
-  if (valid) {
-    if (step == 0) {
-      f = gfeat + (size_t)b * d;
-    } else {
-      const int ps = clampi(st.parent[si], 0, S - 1);
-      f = slot_a + ((size_t)b * S + ps) * d;
+  if (valid) f = step == 0 ? gfeat + (size_t)b * d : slot_a + ((size_t)b * S + clampi(st.parent[si], 0, S - 1)) * d;
+  const int k0 = threadIdx.x * 8;
+  const bool act = k0 < d;
+  float e[8], fv[8], ge[8], gf[8];
+  float se = 0.f, sf = 0.f;
+  if (act) {
+    load8<T>(embed + (size_t)tok * d + k0, e);
+    if (f) load8<float>(f + k0, fv);
+    else
+#pragma unroll
+      for (int i = 0; i < 8; ++i) fv[i] = 0.f;
+    load8<T>(g_e + k0, ge);
+    load8<T>(g_f + k0, gf);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      se += e[i] * e[i];
+      sf += fv[i] * fv[i];
     }
   }
-  const T* e = embed + (size_t)tok * d;
-  float se = 0.f, sf = 0.f;
-  for (int k = threadIdx.x; k < d; k += blockDim.x) {
-    const float ev = to_f32(e[k]);
-    se += ev * ev;
-    if (f) sf += f[k] * f[k];
-  }
-  se = block_sum(se, red);
-  sf = block_sum(sf, red);
+  block_sum2(se, sf, red);
+  if (!act) return;
   const float ie = 1.f / sqrtf(se / d + eps);
-  const float inf_ = 1.f / sqrtf(sf / d + eps);
-  T* ur = u + (size_t)r * 2 * d;
-  for (int k = threadIdx.x; k < d; k += blockDim.x) {
-    const float fv = f ? f[k] : 0.f;
-    ur[k] = from_f32<T>(to_f32(e[k]) * ie * to_f32(g_e[k]));
-    ur[d + k] = from_f32<T>(fv * inf_ * to_f32(g_f[k]));
-    f_rows[(size_t)r * d + k] = fv;
+  const float iff = 1.f / sqrtf(sf / d + eps);
+  float o1[8], o2[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    o1[i] = e[i] * ie * ge[i];
+    o2[i] = fv[i] * iff * gf[i];
   }
+  T* ur = u + (size_t)r * 2 * d;
+  store8<T>(ur + k0, o1);
+  store8<T>(ur + d + k0, o2);
+  store8<float>(f_rows + (size_t)r * d + k0, fv);
   if (threadIdx.x == 0) row_mask[r] = valid ? st.mask[si] : 0ull;
 }
 
-// ---------------------------------------------------------------------------------------
 // rmsnorm of fp32 rows into dtype rows; optionally keep the fp32 input per slot (the
 // drafter output a that later nodes take as their feature).
-// ---------------------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ in, int d, float eps,
-                                                 const T* __restrict__ gamma, T* __restrict__ out,
-                                                 int R, int sb, int S, SlotState st,
-                                                 float* __restrict__ keep, float* __restrict__ keep_dbg) {
-  __shared__ float red[4];
+__global__ __launch_bounds__(1024) void k_rmsnorm(const float* __restrict__ in, int d, float eps,
+                                                  const T* __restrict__ gamma, T* __restrict__ out,
+                                                  int R, int sb, int S, SlotState st,
+                                                  float* __restrict__ keep, float* __restrict__ keep_dbg) {
+  __shared__ float red[32];
   const int r = blockIdx.x;
-  const float* x = in + (size_t)r * d;
-  float ss = 0.f;
-  for (int k = threadIdx.x; k < d; k += blockDim.x) ss += x[k] * x[k];
-  ss = block_sum(ss, red);
+  const int k0 = threadIdx.x * 8;
+  const bool act = k0 < d;
+  float x[8], gm[8];
+  float ss = 0.f, dummy = 0.f;
+  if (act) {
+    load8<float>(in + (size_t)r * d + k0, x);
+    load8<T>(gamma + k0, gm);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
+  }
+  block_sum2(ss, dummy, red);
+  if (!act) return;
   const float inv = 1.f / sqrtf(ss / d + eps);
-  for (int k = threadIdx.x; k < d; k += blockDim.x)
-    out[(size_t)r * d + k] = from_f32<T>(x[k] * inv * to_f32(gamma[k]));
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = x[i] * inv * gm[i];
+  store8<T>(out + (size_t)r * d + k0, o);
   if (keep) {
     const int b = r / R, j = r % R;
     const int si = b * S + sb + j;
     if (st.valid[si]) {
-      for (int k = threadIdx.x; k < d; k += blockDim.x) {
-        keep[(size_t)si * d + k] = x[k];
-        if (keep_dbg) keep_dbg[(size_t)si * d + k] = x[k];
-      }
+      store8<float>(keep + (size_t)si * d + k0, x);
+      if (keep_dbg) store8<float>(keep_dbg + (size_t)si * d + k0, x);
     }
   }
 }
@@ -190,150 +255,203 @@ __global__ __launch_bounds__(256) void k_epi_qkv(const float* __restrict__ part,
 }
 
 // ---------------------------------------------------------------------------------------
-// LM head top-K / log-sum-exp, pass 1: per (row, vocab chunk) the chunk's top-K
-// (value desc, id asc) and its (max, sum e^{z-max}).
+// LM head top-K / log-sum-exp, pass 1: per (row, chunk of 4096 logits) the chunk's top-K
+// (value desc, id asc) and its (max, sum e^{z-max}).  Each thread holds 16 logits (four
+// float4 loads issued together), sorts them with a fixed network, and the K winners are
+// drawn first per wave and then across the four waves, popping sorted heads.
 // ---------------------------------------------------------------------------------------
+constexpr int TK_CHUNK = 4096;
+
+__device__ __forceinline__ void cswap(float& va, int& ia, float& vb, int& ib) {
+  // afterwards (va, ia) is the better of the two
+  if (better(vb, ib, va, ia)) {
+    const float tv = va;
+    const int ti = ia;
+    va = vb;
+    ia = ib;
+    vb = tv;
+    ib = ti;
+  }
+}
+
+// Sort 16 (value, id) pairs best-first with a bitonic network (static indices only).
+__device__ __forceinline__ void sort16(float* v, int* id) {
+#pragma unroll
+  for (int k = 2; k <= 16; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int l = i ^ j;
+        if (l > i) {
+          if ((i & k) == 0)
+            cswap(v[i], id[i], v[l], id[l]);
+          else
+            cswap(v[l], id[l], v[i], id[i]);
+        }
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void pop16(float* v, int* id) {
+#pragma unroll
+  for (int q = 0; q < 15; ++q) {
+    v[q] = v[q + 1];
+    id[q] = id[q + 1];
+  }
+  v[15] = kNegInf;
+  id[15] = 0x7fffffff;
+}
+
 __global__ __launch_bounds__(256) void k_topk_chunk(const float* __restrict__ part, int splits, int M,
-                                                    int V, int K, int chunk, int n_chunks,
+                                                    int V, int K, int n_chunks,
                                                     float* __restrict__ cv, int* __restrict__ ci,
                                                     float* __restrict__ cmax, float* __restrict__ csum,
                                                     float* __restrict__ dbg_logits, int R, int sb, int S,
                                                     SlotState st) {
-  __shared__ float sv[8];
-  __shared__ int si[8];
-  __shared__ float red[4];
+  __shared__ float red[32];
+  __shared__ float wv[4][16];
+  __shared__ int wi[4][16];
   const int m = blockIdx.y, c = blockIdx.x;
-  const int t0 = c * chunk, t1 = min(V, t0 + chunk);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t0 = c * TK_CHUNK;
   float* dl = nullptr;
   if (dbg_logits) {
     const int b = m / R, j = m % R;
     const int sidx = b * S + sb + j;
     if (st.valid[sidx]) dl = dbg_logits + (size_t)sidx * V;
   }
-  float vals[KMAX];
-  int ids[KMAX];
+  float v[16];
+  int id[16];
+  // thread covers 4 float4 groups: t0 + 4*(threadIdx.x + 256*q) .. +4, q = 0..3
 #pragma unroll
-  for (int k = 0; k < KMAX; ++k) {
-    vals[k] = kNegInf;
-    ids[k] = 0x7fffffff;
-  }
-  float lm = kNegInf, ls = 0.f;
-  for (int t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
-    float z = 0.f;
-    for (int s = 0; s < splits; ++s) z += part[((size_t)s * M + m) * V + t];
-    if (dl) dl[t] = z;
-    if (z > lm) {
-      ls = ls * expf(lm - z) + 1.f;
-      lm = z;
-    } else {
-      ls += expf(z - lm);
+  for (int q = 0; q < 4; ++q) {
+    const int t = t0 + 4 * (threadIdx.x + 256 * q);
+    floatx4 z = {0.f, 0.f, 0.f, 0.f};
+    if (t < V) {
+      for (int s = 0; s < splits; ++s) z += *reinterpret_cast<const floatx4*>(part + ((size_t)s * M + m) * V + t);
+      if (dl) *reinterpret_cast<floatx4*>(dl + t) = z;
     }
-    if (better(z, t, vals[K - 1], ids[K - 1])) {
-      float cvv = z;
-      int cii = t;
 #pragma unroll
-      for (int k = 0; k < KMAX; ++k) {
-        if (k < K && better(cvv, cii, vals[k], ids[k])) {
-          const float tv = vals[k];
-          const int ti = ids[k];
-          vals[k] = cvv;
-          ids[k] = cii;
-          cvv = tv;
-          cii = ti;
-        }
-      }
+    for (int e = 0; e < 4; ++e) {
+      const bool ok = t + e < V;
+      v[4 * q + e] = ok ? z[e] : kNegInf;
+      id[4 * q + e] = ok ? t + e : 0x7fffffff;
     }
   }
-  // chunk (max, sum) with a fixed reduction order
+  // chunk (max, sum e^{z - max})
+  float lm = kNegInf;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) lm = fmaxf(lm, v[i]);
   const float bm = block_max(lm, red);
-  const float scaled = lm == kNegInf ? 0.f : ls * expf(lm - bm);
-  const float tot = block_sum(scaled, red);
-  // chunk top-K: K rounds of block argmax over each thread's sorted head
-  for (int k = 0; k < K; ++k) {
-    float v = vals[0];
-    int id = ids[0];
-    block_argmax(v, id, sv, si);
-    if (ids[0] == id && vals[0] == v && id != 0x7fffffff) {
+  float ls = 0.f;
 #pragma unroll
-      for (int q = 0; q < KMAX - 1; ++q) {
-        vals[q] = vals[q + 1];
-        ids[q] = ids[q + 1];
-      }
-      vals[KMAX - 1] = kNegInf;
-      ids[KMAX - 1] = 0x7fffffff;
-    }
-    if (threadIdx.x == 0) {
-      cv[((size_t)m * n_chunks + c) * K + k] = v;
-      ci[((size_t)m * n_chunks + c) * K + k] = id;
+  for (int i = 0; i < 16; ++i) ls += v[i] == kNegInf ? 0.f : expf(v[i] - bm);
+  const float tot = block_sum(ls, red);
+  // top-K: sort own 16, K rounds per wave, then K rounds over the 4 wave lists
+  sort16(v, id);
+  for (int k = 0; k < K; ++k) {
+    float bv = v[0];
+    int bi = id[0];
+    wave_argmax(bv, bi);
+    if (id[0] == bi && v[0] == bv) pop16(v, id);
+    if (lane == 0) {
+      wv[w][k] = bv;
+      wi[w][k] = bi;
     }
   }
-  if (threadIdx.x == 0) {
-    cmax[(size_t)m * n_chunks + c] = bm;
-    csum[(size_t)m * n_chunks + c] = tot;
+  __syncthreads();
+  if (w == 0) {
+    // lane l < 4*K holds entry (l / K, l % K); heads advance per wave list
+    float hv = kNegInf;
+    int hi = 0x7fffffff;
+    const int nwv = blockDim.x >> 6;
+    if (lane < nwv * K) {
+      hv = wv[lane / K][lane % K];
+      hi = wi[lane / K][lane % K];
+    }
+    for (int k = 0; k < K; ++k) {
+      float bv = hv;
+      int bi = hi;
+      wave_argmax(bv, bi);
+      if (hi == bi && hv == bv) {
+        hv = kNegInf;
+        hi = 0x7fffffff;
+      }
+      if (lane == 0) {
+        cv[((size_t)m * n_chunks + c) * K + k] = bv;
+        ci[((size_t)m * n_chunks + c) * K + k] = bi;
+      }
+    }
+    if (lane == 0) {
+      cmax[(size_t)m * n_chunks + c] = bm;
+      csum[(size_t)m * n_chunks + c] = tot;
+    }
   }
 }
 
-// pass 2: per row, merge the chunks' top-K and (max, sum) in chunk order.
-__global__ __launch_bounds__(256) void k_topk_merge(const float* __restrict__ cv, const int* __restrict__ ci,
-                                                    const float* __restrict__ cmax,
-                                                    const float* __restrict__ csum, int n_chunks, int K,
-                                                    int* __restrict__ top_id, float* __restrict__ top_val,
-                                                    float* __restrict__ lse, int R, int sb, int S,
-                                                    SlotState st, int32_t* dbg_id, float* dbg_val,
-                                                    float* dbg_lse) {
-  __shared__ float sv[8];
-  __shared__ int si[8];
-  __shared__ float s_lse;
+// pass 2: one wave per row merges the chunks' top-K (K rounds of wave argmax over each
+// lane's best remaining candidate) and the chunks' (max, sum) in chunk order.
+__global__ __launch_bounds__(64) void k_topk_merge(const float* __restrict__ cv, const int* __restrict__ ci,
+                                                   const float* __restrict__ cmax,
+                                                   const float* __restrict__ csum, int n_chunks, int K,
+                                                   int* __restrict__ top_id, float* __restrict__ top_val,
+                                                   float* __restrict__ lse, int R, int sb, int S,
+                                                   SlotState st, int32_t* dbg_id, float* dbg_val,
+                                                   float* dbg_lse) {
   const int m = blockIdx.x;
+  const int lane = threadIdx.x;
   const int n = n_chunks * K;
-  if (threadIdx.x == 0) {
-    float mx = kNegInf;
-    for (int c = 0; c < n_chunks; ++c) mx = fmaxf(mx, cmax[(size_t)m * n_chunks + c]);
-    float tot = 0.f;
-    for (int c = 0; c < n_chunks; ++c) {
-      const float cm = cmax[(size_t)m * n_chunks + c];
-      if (cm != kNegInf) tot += csum[(size_t)m * n_chunks + c] * expf(cm - mx);
-    }
-    s_lse = mx + logf(tot);
+  // log-sum-exp over chunks
+  float mx = kNegInf;
+  for (int c = lane; c < n_chunks; c += 64) mx = fmaxf(mx, cmax[(size_t)m * n_chunks + c]);
+  mx = wave_max(mx);
+  float tot = 0.f;
+  for (int c = lane; c < n_chunks; c += 64) {
+    const float cm = cmax[(size_t)m * n_chunks + c];
+    if (cm != kNegInf) tot += csum[(size_t)m * n_chunks + c] * expf(cm - mx);
   }
-  // each thread owns candidates threadIdx.x + 256*q (q < 4 covers n <= 1024)
-  float v_own[4];
-  int i_own[4];
+  tot = wave_sum(tot);
+  const float row_lse = mx + logf(tot);
+  // candidates: lane holds entries lane + 64*q, q < 16 (n <= 1024)
+  float v[16];
+  int id[16];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = threadIdx.x + 256 * q;
-    v_own[q] = e < n ? cv[(size_t)m * n + e] : kNegInf;
-    i_own[q] = e < n ? ci[(size_t)m * n + e] : 0x7fffffff;
+  for (int q = 0; q < 16; ++q) {
+    const int e = lane + 64 * q;
+    v[q] = e < n ? cv[(size_t)m * n + e] : kNegInf;
+    id[q] = e < n ? ci[(size_t)m * n + e] : 0x7fffffff;
   }
   const int b = m / R, j = m % R;
   const int sidx = b * S + sb + j;
   const bool dbg = st.valid[sidx] != 0;
   for (int k = 0; k < K; ++k) {
-    float v = kNegInf;
-    int id = 0x7fffffff;
+    float bv = kNegInf;
+    int bi = 0x7fffffff;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (better(v_own[q], i_own[q], v, id)) {
-        v = v_own[q];
-        id = i_own[q];
+    for (int q = 0; q < 16; ++q)
+      if (better(v[q], id[q], bv, bi)) {
+        bv = v[q];
+        bi = id[q];
       }
-    block_argmax(v, id, sv, si);
+    wave_argmax(bv, bi);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (i_own[q] == id) {
-        v_own[q] = kNegInf;
-        i_own[q] = 0x7fffffff;
+    for (int q = 0; q < 16; ++q)
+      if (id[q] == bi && v[q] == bv) {
+        v[q] = kNegInf;
+        id[q] = 0x7fffffff;
       }
-    if (threadIdx.x == 0) {
-      top_id[(size_t)m * K + k] = id;
-      top_val[(size_t)m * K + k] = v;
-      if (dbg && dbg_id) dbg_id[(size_t)sidx * K + k] = id;
-      if (dbg && dbg_val) dbg_val[(size_t)sidx * K + k] = v;
+    if (lane == 0) {
+      top_id[(size_t)m * K + k] = bi;
+      top_val[(size_t)m * K + k] = bv;
+      if (dbg && dbg_id) dbg_id[(size_t)sidx * K + k] = bi;
+      if (dbg && dbg_val) dbg_val[(size_t)sidx * K + k] = bv;
     }
   }
-  if (threadIdx.x == 0) {
-    lse[m] = s_lse;
-    if (dbg && dbg_lse) dbg_lse[sidx] = s_lse;
+  if (lane == 0) {
+    lse[m] = row_lse;
+    if (dbg && dbg_lse) dbg_lse[sidx] = row_lse;
   }
 }
 
@@ -480,7 +598,7 @@ __global__ __launch_bounds__(256) void k_select(int step, int D, int K, int W, i
 // Workspace plan
 // ---------------------------------------------------------------------------------------
 struct Plan {
-  int B, d, Hq, Hkv, Dh, F, V, D, K, W, N, S, PMAX, Mmax, att_splits, lm_chunk, lm_nchunk;
+  int B, d, Hq, Hkv, Dh, F, V, D, K, W, N, S, PMAX, Mmax, att_splits, lm_nchunk, row_threads;
   size_t gemm_part_elems;
   // pointers (null when measuring)
   SlotState st;
@@ -508,9 +626,9 @@ Plan make_plan(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, int max
   p.S = 1 + (p.D - 1) * p.W;
   p.PMAX = p.K + (p.D - 1) * p.W * p.K;
   p.Mmax = B * (p.W > 1 ? p.W : 1);
-  p.att_splits = e3h::attention_splits(max_prefix, 0);
-  p.lm_chunk = p.V < 4096 ? p.V : 4096;
-  p.lm_nchunk = (p.V + p.lm_chunk - 1) / p.lm_chunk;
+  p.att_splits = e3h::attention_splits(B, p.Hkv, p.Mmax / B * (p.Hq / p.Hkv), max_prefix, 0);
+  p.lm_nchunk = (p.V + TK_CHUNK - 1) / TK_CHUNK;
+  p.row_threads = ((p.d / 8 + 63) / 64) * 64;
   const int es = e3h::elem_size(w->dtype);
   const int nqkv = (p.Hq + 2 * p.Hkv) * p.Dh;
   size_t gp = 0;
@@ -604,7 +722,7 @@ int run_draft(const eagle3_drafter* w, const Plan& p, const void* h_low, const v
     const int M = B * R;
     {
       ProfScope ps("draft_prep", s);
-      hipLaunchKernelGGL(k_prep<T>, dim3(M), dim3(256), 0, s, R, sb, p.S, d, p.V, w->eps, step, p.st,
+      hipLaunchKernelGGL(k_prep<T>, dim3(M), dim3(p.row_threads), 0, s, R, sb, p.S, d, p.V, w->eps, step, p.st,
                          (const T*)w->embed, (const T*)w->g_embed, (const T*)w->g_feat, p.g, p.slot_a,
                          p.f_rows, (T*)p.u, p.row_mask);
       if ((st = launch_status())) return st;
@@ -658,7 +776,7 @@ int run_draft(const eagle3_drafter* w, const Plan& p, const void* h_low, const v
       if ((st = launch_gemm(gp, dt, p.attn, p.Hq * p.Dh, w->w_o, p.gpart, s, "gemm_o"))) return st;
       if ((st = launch_epi_sum(gp, p.gpart, p.h1, p.f_rows, s, "epi_o"))) return st;
       ProfScope ps("rmsnorm", s);
-      hipLaunchKernelGGL(k_rmsnorm<T>, dim3(M), dim3(256), 0, s, p.h1, d, w->eps, (const T*)w->g_mlp,
+      hipLaunchKernelGGL(k_rmsnorm<T>, dim3(M), dim3(p.row_threads), 0, s, p.h1, d, w->eps, (const T*)w->g_mlp,
                          (T*)p.mn, R, sb, p.S, p.st, (float*)nullptr, (float*)nullptr);
       if ((st = launch_status())) return st;
     }
@@ -671,7 +789,7 @@ int run_draft(const eagle3_drafter* w, const Plan& p, const void* h_low, const v
       if ((st = launch_gemm(gd, dt, p.act, p.F, w->w_down, p.gpart, s, "gemm_down"))) return st;
       if ((st = launch_epi_sum(gd, p.gpart, p.a_rows, p.h1, s, "epi_down"))) return st;
       ProfScope ps("rmsnorm", s);
-      hipLaunchKernelGGL(k_rmsnorm<T>, dim3(M), dim3(256), 0, s, p.a_rows, d, w->eps,
+      hipLaunchKernelGGL(k_rmsnorm<T>, dim3(M), dim3(p.row_threads), 0, s, p.a_rows, d, w->eps,
                          (const T*)w->g_final, (T*)p.xl, R, sb, p.S, p.st, p.slot_a,
                          dbg ? dbg->slot_a : (float*)nullptr);
       if ((st = launch_status())) return st;
@@ -683,12 +801,12 @@ int run_draft(const eagle3_drafter* w, const Plan& p, const void* h_low, const v
       {
         ProfScope ps("topk_chunk", s);
         hipLaunchKernelGGL(k_topk_chunk, dim3(p.lm_nchunk, M), dim3(256), 0, s, p.gpart, gp.splits, M,
-                           p.V, p.K, p.lm_chunk, p.lm_nchunk, p.cv, p.ci, p.cmax, p.csum,
+                           p.V, p.K, p.lm_nchunk, p.cv, p.ci, p.cmax, p.csum,
                            dbg ? dbg->slot_logits : (float*)nullptr, R, sb, p.S, p.st);
         if ((st = launch_status())) return st;
       }
       ProfScope ps("topk_merge", s);
-      hipLaunchKernelGGL(k_topk_merge, dim3(M), dim3(256), 0, s, p.cv, p.ci, p.cmax, p.csum,
+      hipLaunchKernelGGL(k_topk_merge, dim3(M), dim3(64), 0, s, p.cv, p.ci, p.cmax, p.csum,
                          p.lm_nchunk, p.K, p.top_id, p.top_val, p.lse, R, sb, p.S, p.st,
                          dbg ? dbg->slot_topk_id : (int32_t*)nullptr,
                          dbg ? dbg->slot_topk_val : (float*)nullptr, dbg ? dbg->slot_lse : (float*)nullptr);
@@ -716,7 +834,7 @@ int draft_check(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, int ma
     return EAGLE3_EINVAL;
   if (w->n_heads_q % w->n_heads_kv) return EAGLE3_EINVAL;
   if (w->head_dim != 64 && w->head_dim != 128) return EAGLE3_EUNSUPPORTED;
-  if (w->d % 8 || w->ffn % 8 || w->vocab % 4) return EAGLE3_EUNSUPPORTED;
+  if (w->d % 8 || w->ffn % 8 || w->vocab % 4 || w->d > 8192) return EAGLE3_EUNSUPPORTED;
   if (!(w->eps > 0.f) || !(w->rope_theta > 0.f)) return EAGLE3_EINVAL;
   if (t->depth < 1 || t->topk < 1 || t->width < 1 || t->n_nodes < 1) return EAGLE3_EINVAL;
   if (t->topk > KMAX || t->topk > w->vocab) return EAGLE3_EUNSUPPORTED;

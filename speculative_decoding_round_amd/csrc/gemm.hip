@@ -1,11 +1,12 @@
 // Weight-streaming GEMM for the drafter's projections and LM head:
 //   Y_part[split][m][n] = sum_{k in split} X[m][k] * W[n][k]
-// X is [M, K] (a handful of rows: the nodes being evaluated), W is [N, K] row-major.
-// The op is bound by streaming W from HBM once, so the layout puts W on the MFMA A operand
-// (16 output features per tile), keeps every byte of W read exactly once, and spreads the
-// work over (n-block, k-split) workgroups of four waves.  Each wave walks its own k-range,
-// holding NT W-tiles and MT X-tiles per 16-byte chunk step; the four waves' partial tiles
-// are summed in LDS in wave order, so results are deterministic.
+// X is [M, K] (the few rows being evaluated), W is [N, K] row-major.  The op is bound by
+// streaming W from HBM exactly once, so W sits on the MFMA A operand (16 output features
+// per tile) and X is kept stationary in registers: a wave loads KCB 16-byte chunks of its
+// X rows once and streams NTB consecutive W tiles against them (X costs 1/(16 NTB) of the
+// load traffic of W), with the next W tile in flight while the current one is multiplied.
+// A workgroup is WK waves that split its k-range (summed in LDS in wave order, so results
+// are deterministic); workgroups tile (n-block, k-split).
 #include "common.h"
 #include "internal.h"
 
@@ -13,34 +14,36 @@ using namespace e3;
 
 namespace {
 
-constexpr int WAVES = 4;
-constexpr int U = 4;  // chunk steps loaded ahead per iteration
-
-template <typename T, int MT, int NT>
-__global__ __launch_bounds__(256) void k_gemm(const T* __restrict__ X, int M, int ldx,
-                                              const T* __restrict__ W, int N, int K,
-                                              float* __restrict__ Y, int n_blocks,
-                                              int chunks_total, int chunks_per_split) {
+// X-stationary variant: each wave keeps KCB chunks of its X rows in registers and streams
+// NTB consecutive 16-row tiles of W against them (W tiles double-buffered), so the X rows
+// cost 16*NTB times less load traffic than W.  The WK waves of a workgroup split the
+// k-range and are summed in LDS in wave order.
+template <typename T, int MT, int NTB, int KCB, int WK>
+__global__ __launch_bounds__(WK * 64) void k_gemm(const T* __restrict__ X, int M, int ldx,
+                                                     const T* __restrict__ W, int N, int K,
+                                                     float* __restrict__ Y, int n_blocks,
+                                                     int chunks_total, int chunks_per_split) {
+  static_assert(NTB % 2 == 0, "NTB must be even");
   constexpr int EPC = Vec<T>::N;
-  constexpr int KPC = Mfma<T>::KPC;  // = 4 * EPC
-  __shared__ floatx4 red[WAVES][NT * MT][64];
-
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  constexpr int KPC = Mfma<T>::KPC;
+  __shared__ floatx4 red[WK][NTB * MT][64];
+  const int lane = threadIdx.x & 63, wk = threadIdx.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int nb = blockIdx.x % n_blocks, ks = blockIdx.x / n_blocks;
   const int cs0 = ks * chunks_per_split;
   const int cs1 = min(chunks_total, cs0 + chunks_per_split);
-  const int per_wave = (cs1 - cs0 + WAVES - 1) / WAVES;
-  const int c0 = cs0 + wid * per_wave;
+  const int per_wave = (cs1 - cs0 + WK - 1) / WK;
+  const int c0 = cs0 + wk * per_wave;
   const int c1 = min(cs1, c0 + per_wave);
+  const u32x4 zero = {0, 0, 0, 0};
 
-  const T* wrow[NT];
-  bool wok[NT];
+  const T* wbase[NTB];
+  bool wok[NTB];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int n = (nb * NT + nt) * 16 + r16;
+  for (int nt = 0; nt < NTB; ++nt) {
+    const int n = (nb * NTB + nt) * 16 + r16;
     wok[nt] = n < N;
-    wrow[nt] = W + (size_t)(wok[nt] ? n : 0) * K + g * EPC;
+    wbase[nt] = W + (size_t)(wok[nt] ? n : 0) * K + g * EPC;
   }
   const T* xrow[MT];
   bool xok[MT];
@@ -50,50 +53,72 @@ __global__ __launch_bounds__(256) void k_gemm(const T* __restrict__ X, int M, in
     xok[mt] = m < M;
     xrow[mt] = X + (size_t)(xok[mt] ? m : 0) * ldx + g * EPC;
   }
-
-  floatx4 acc[NT][MT];
+  floatx4 acc[NTB][MT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+  for (int nt = 0; nt < NTB; ++nt)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const u32x4 zero = {0, 0, 0, 0};
-  for (int c = c0; c < c1; c += U) {
-    u32x4 wv[U][NT], xv[U][MT];
+  for (int cb = c0; cb < c1; cb += KCB) {
+    bool kin[KCB];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kc = c + u;
-      const int koff = kc * KPC;
-      const bool kin = kc < c1 && koff + g * EPC + EPC <= K;
+    for (int u = 0; u < KCB; ++u) kin[u] = cb + u < c1 && (cb + u) * KPC + g * EPC + EPC <= K;
+    u32x4 xv[KCB][MT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) wv[u][nt] = (kin && wok[nt]) ? ld16(wrow[nt] + koff) : zero;
+    for (int u = 0; u < KCB; ++u)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) xv[u][mt] = (kin && xok[mt]) ? ld16(xrow[mt] + koff) : zero;
+      for (int mt = 0; mt < MT; ++mt)
+        xv[u][mt] = (kin[u] && xok[mt]) ? ld16(xrow[mt] + (cb + u) * KPC) : zero;
+    u32x4 wa[KCB], wb[KCB];
+#pragma unroll
+    for (int u = 0; u < KCB; ++u) wa[u] = (kin[u] && wok[0]) ? ld16(wbase[0] + (cb + u) * KPC) : zero;
+#pragma unroll
+    for (int nt = 0; nt < NTB; nt += 2) {
+#pragma unroll
+      for (int u = 0; u < KCB; ++u)
+        wb[u] = (kin[u] && wok[nt + 1]) ? ld16(wbase[nt + 1] + (cb + u) * KPC) : zero;
+#pragma unroll
+      for (int u = 0; u < KCB; ++u)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = Mfma<T>::run(wa[u], xv[u][mt], acc[nt][mt]);
+      if (nt + 2 < NTB) {
+#pragma unroll
+        for (int u = 0; u < KCB; ++u)
+          wa[u] = (kin[u] && wok[nt + 2]) ? ld16(wbase[nt + 2] + (cb + u) * KPC) : zero;
+      }
+#pragma unroll
+      for (int u = 0; u < KCB; ++u)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[nt + 1][mt] = Mfma<T>::run(wb[u], xv[u][mt], acc[nt + 1][mt]);
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = Mfma<T>::run(wv[u][nt], xv[u][mt], acc[nt][mt]);
   }
 
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) red[wid][nt * MT + mt][lane] = acc[nt][mt];
-  __syncthreads();
-  // sum the four waves' tiles in wave order; write 4 consecutive n per (tile, lane)
   float* Ys = Y + (size_t)ks * M * N;
-  for (int e = threadIdx.x; e < NT * MT * 64; e += 256) {
-    const int tile = e / 64, ln = e % 64;
-    const int nt = tile / MT, mt = tile % MT;
-    floatx4 v = red[0][tile][ln];
+  if constexpr (WK == 1) {
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) v += red[w][tile][ln];
-    const int m = mt * 16 + (ln & 15);
-    const int n = (nb * NT + nt) * 16 + 4 * (ln >> 4);
-    if (m < M && n < N) *reinterpret_cast<floatx4*>(Ys + (size_t)m * N + n) = v;
+    for (int nt = 0; nt < NTB; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = mt * 16 + r16;
+        const int n = (nb * NTB + nt) * 16 + 4 * g;
+        if (m < M && n < N) *reinterpret_cast<floatx4*>(Ys + (size_t)m * N + n) = acc[nt][mt];
+      }
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < NTB; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) red[wk][nt * MT + mt][lane] = acc[nt][mt];
+    __syncthreads();
+    for (int e = threadIdx.x; e < NTB * MT * 64; e += WK * 64) {
+      const int tile = e / 64, ln = e % 64;
+      const int nt = tile / MT, mt = tile % MT;
+      floatx4 v = red[0][tile][ln];
+#pragma unroll
+      for (int w = 1; w < WK; ++w) v += red[w][tile][ln];
+      const int m = mt * 16 + (ln & 15);
+      const int n = (nb * NTB + nt) * 16 + 4 * (ln >> 4);
+      if (m < M && n < N) *reinterpret_cast<floatx4*>(Ys + (size_t)m * N + n) = v;
+    }
   }
 }
 
@@ -128,32 +153,50 @@ __global__ __launch_bounds__(256) void k_epi_silu_mul(const float* __restrict__ 
   out[(size_t)m * F + j] = from_f32<T>(act * up);
 }
 
-template <typename T, int MT, int NT>
+template <typename T, int MT, int NTB, int KCB, int WK>
 void launch_gemm_t(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y,
                    hipStream_t s) {
   dim3 grid(p.n_blocks * p.splits);
-  hipLaunchKernelGGL((k_gemm<T, MT, NT>), grid, dim3(256), 0, s, (const T*)X, p.M, ldx,
+  hipLaunchKernelGGL((k_gemm<T, MT, NTB, KCB, WK>), grid, dim3(WK * 64), 0, s, (const T*)X, p.M, ldx,
                      (const T*)W, p.N, p.K, Y, p.n_blocks, p.chunks_total, p.chunks_per_split);
+}
+
+// Per row-tile count MT: (n-tiles per wave, X chunks held per lane).
+constexpr int ntb_for(int mt) { return mt <= 4 ? 8 : 4; }
+constexpr int kcb_for(int mt) { return mt <= 2 ? 8 : (mt <= 4 ? 4 : 2); }
+
+template <typename T, int MT>
+int dispatch_mt(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y,
+                hipStream_t s) {
+  if (p.waves == 1)
+    launch_gemm_t<T, MT, ntb_for(MT), kcb_for(MT), 1>(p, X, ldx, W, Y, s);
+  else
+    launch_gemm_t<T, MT, ntb_for(MT), kcb_for(MT), 4>(p, X, ldx, W, Y, s);
+  return e3h::launch_status();
 }
 
 template <typename T>
 int dispatch_gemm(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y,
                   hipStream_t s) {
-#define E3_CASE(mt, nt)                                   \
-  if (p.MT == mt && p.NT == nt) {                         \
-    launch_gemm_t<T, mt, nt>(p, X, ldx, W, Y, s);         \
-    return e3h::launch_status();                          \
+  switch (p.MT) {
+    case 1: return dispatch_mt<T, 1>(p, X, ldx, W, Y, s);
+    case 2: return dispatch_mt<T, 2>(p, X, ldx, W, Y, s);
+    case 3: return dispatch_mt<T, 3>(p, X, ldx, W, Y, s);
+    case 4: return dispatch_mt<T, 4>(p, X, ldx, W, Y, s);
+    case 6: return dispatch_mt<T, 6>(p, X, ldx, W, Y, s);
+    case 8: return dispatch_mt<T, 8>(p, X, ldx, W, Y, s);
+    case 10: return dispatch_mt<T, 10>(p, X, ldx, W, Y, s);
+    default: return EAGLE3_EUNSUPPORTED;
   }
-  E3_CASE(1, 1) E3_CASE(1, 2) E3_CASE(2, 1) E3_CASE(2, 2) E3_CASE(3, 1) E3_CASE(4, 1)
-  E3_CASE(6, 1) E3_CASE(8, 1) E3_CASE(10, 1)
-#undef E3_CASE
-  return EAGLE3_EUNSUPPORTED;
 }
 
 }  // namespace
 
 namespace e3h {
 
+// Plan: single-wave workgroups when the n-blocks alone fill the chip (the LM head);
+// otherwise four-wave workgroups and a k-split that brings the grid to about 256
+// workgroups, keeping at least one X block of chunks per wave.
 GemmPlan plan_gemm(int M, int N, int K, int dtype) {
   GemmPlan p;
   p.M = M;
@@ -167,20 +210,25 @@ GemmPlan plan_gemm(int M, int N, int K, int dtype) {
       p.MT = v;
       break;
     }
+  const int ntb = p.MT > 0 ? ntb_for(p.MT) : 8;
+  const int kcb = p.MT > 0 ? kcb_for(p.MT) : 8;
+  p.NT = ntb;
   const int ntile = (N + 15) / 16;
-  p.NT = (p.MT <= 2 && ntile >= 4096) ? 2 : 1;
-  p.n_blocks = (ntile + p.NT - 1) / p.NT;
+  p.n_blocks = (ntile + ntb - 1) / ntb;
   const int kpc = dtype == EAGLE3_BF16 ? 32 : 16;
   p.chunks_total = (K + kpc - 1) / kpc;
-  // enough workgroups to keep every CU streaming, but at least 8 chunk steps per wave
-  const int target = 1024;
-  int splits = (target + p.n_blocks - 1) / p.n_blocks;
-  const int max_splits = p.chunks_total / (WAVES * 8) > 0 ? p.chunks_total / (WAVES * 8) : 1;
-  if (splits > max_splits) splits = max_splits;
-  if (splits < 1) splits = 1;
+  int splits = 1;
+  if (p.n_blocks >= 768) {
+    p.waves = 1;
+  } else {
+    p.waves = 4;
+    splits = 256 / p.n_blocks;
+    const int max_splits = p.chunks_total / (p.waves * kcb);
+    if (splits > max_splits) splits = max_splits;
+    if (splits < 1) splits = 1;
+  }
   p.chunks_per_split = (p.chunks_total + splits - 1) / splits;
   p.splits = (p.chunks_total + p.chunks_per_split - 1) / p.chunks_per_split;
-  p.waves = WAVES;
   return p;
 }
 

@@ -31,7 +31,7 @@ struct AttnArgs {
 int launch_tree_attention(const AttnArgs& a, hipStream_t s, const char* tag);
 int launch_lse_merge(int S, int rows, int Dh, const float* o_part, const float* lse_part,
                      int out_dtype, void* o, float* lse, hipStream_t s, const char* tag);
-int attention_splits(int max_prefix, int n_splits);
+int attention_splits(int B, int Hkv, int rows_per_kv, int max_prefix, int n_splits);
 
 // ---- verify ----------------------------------------------------------------------------
 int launch_build_mask(int B, int T, const int32_t* cu_nodes, const int32_t* parents,
@@ -43,6 +43,7 @@ int launch_accept(int B, int T, const int32_t* cu_nodes, const int32_t* tokens,
                   int max_depth, int32_t* accept_len, int32_t* path, int32_t* out_tokens,
                   int32_t* bonus, float* part_v, int* part_i, hipStream_t s);
 size_t accept_workspace(int T, int V);
+int accept_chunks(int V);
 
 // ---- GEMM ------------------------------------------------------------------------------
 // Y_part[split][m][n] = sum over the split's k of X[m][k] * W[n][k]  (fp32 partials).

@@ -119,45 +119,60 @@ __device__ __forceinline__ int find_request(const int32_t* cu, int B, int node) 
 }
 
 // ---------------------------------------------------------------------------------------
-// Acceptance pass 1: per (node, vocab chunk) the best (value, token) of
-// greedy z or z*invT + Gumbel.  Each thread walks groups of four consecutive tokens so one
-// Philox call serves all four.
+// Acceptance pass 1: per (node, chunk of 4096 tokens) the best (value, token) of greedy z
+// or z*invT + Gumbel.  Thread t takes 16 consecutive tokens (vector loads issued together
+// when the row is 16-byte aligned); one Philox call yields the noise of four tokens.
 // ---------------------------------------------------------------------------------------
+constexpr int ACC_CHUNK = 4096;
+
 template <typename T>
-__global__ __launch_bounds__(256) void k_accept_scan(const T* __restrict__ logits, int V, int chunk,
-                                                     int n_chunks, const int32_t* __restrict__ cu_nodes,
+__global__ __launch_bounds__(256) void k_accept_scan(const T* __restrict__ logits, int V, int n_chunks,
+                                                     int aligned, const int32_t* __restrict__ cu_nodes,
                                                      int B, int greedy, float invT, uint32_t seed_lo,
                                                      uint32_t seed_hi, uint32_t rnd,
                                                      float* __restrict__ part_v,
                                                      int* __restrict__ part_i) {
 #pragma clang fp contract(off)
+  constexpr int EPC = Vec<T>::N;
   __shared__ float sv[8];
   __shared__ int si[8];
   const int node = blockIdx.x / n_chunks;
   const int c = blockIdx.x % n_chunks;
-  const int t0 = c * chunk, t1 = min(V, t0 + chunk);
+  const int tb = c * ACC_CHUNK + 16 * threadIdx.x;
   const T* row = logits + (size_t)node * V;
+  float z[16];
+  if (aligned && tb + 16 <= V) {
+#pragma unroll
+    for (int q = 0; q < 16 / EPC; ++q) {
+      const u32x4 v = ld16(row + tb + q * EPC);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) z[q * EPC + e] = chunk_elem<T>(v, e);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) z[e] = tb + e < V ? to_f32(row[tb + e]) : kNegInf;
+  }
   float best = kNegInf;
   int bi = 0x7fffffff;
   if (greedy) {
-    for (int t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
-      float z = to_f32(row[t]);
-      if (better(z, t, best, bi)) {
-        best = z;
-        bi = t;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (tb + e < V && better(z[e], tb + e, best, bi)) {
+        best = z[e];
+        bi = tb + e;
       }
-    }
-  } else {
+  } else if (tb < V) {
     const int b = find_request(cu_nodes, B, node);
     const uint32_t i_local = (uint32_t)(node - cu_nodes[b]);
-    for (int q = (t0 >> 2) + threadIdx.x; q * 4 < t1; q += blockDim.x) {
-      uint32_t ctr[4] = {(uint32_t)q, i_local, (uint32_t)b, rnd};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t ctr[4] = {(uint32_t)((tb >> 2) + q), i_local, (uint32_t)b, rnd};
       philox4x32_10(ctr, seed_lo, seed_hi);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const int t = q * 4 + w;
-        if (t < t0 || t >= t1) continue;
-        const float val = to_f32(row[t]) * invT + gumbel_from_word(ctr[w]);
+        const int t = tb + 4 * q + w;
+        if (t >= V) continue;
+        const float val = z[4 * q + w] * invT + gumbel_from_word(ctr[w]);
         if (better(val, t, best, bi)) {
           best = val;
           bi = t;
@@ -285,7 +300,7 @@ int launch_build_mask(int B, int T, const int32_t* cu_nodes, const int32_t* pare
   return launch_status();
 }
 
-int accept_chunk(int V) { return V < 4096 ? V : 4096; }
+int accept_chunks(int V) { return (V + ACC_CHUNK - 1) / ACC_CHUNK; }
 
 int launch_accept(int B, int T, const int32_t* cu_nodes, const int32_t* tokens,
                   const int32_t* parents, const uint64_t* mask, int W64, const void* logits,
@@ -293,20 +308,21 @@ int launch_accept(int B, int T, const int32_t* cu_nodes, const int32_t* tokens,
                   int max_depth, int32_t* accept_len, int32_t* path, int32_t* out_tokens,
                   int32_t* bonus, float* part_v, int* part_i, hipStream_t s) {
   if (W64 > kMaxW64) return EAGLE3_EUNSUPPORTED;
-  const int chunk = accept_chunk(V);
-  const int n_chunks = (V + chunk - 1) / chunk;
+  const int n_chunks = accept_chunks(V);
   const int greedy = temperature == 0.0f;
   const float invT = greedy ? 1.0f : 1.0f / temperature;
   const uint32_t slo = (uint32_t)seed, shi = (uint32_t)(seed >> 32), rnd = (uint32_t)round;
+  const int es = dtype == EAGLE3_BF16 ? 2 : 4;
+  const int aligned = ((size_t)V * es) % 16 == 0 && ((uintptr_t)logits % 16) == 0;
   {
     ProfScope ps("accept_scan", s);
     dim3 grid((unsigned)((long)n_chunks * T));
     if (dtype == EAGLE3_BF16)
-      hipLaunchKernelGGL(k_accept_scan<bf16>, grid, dim3(256), 0, s, (const bf16*)logits, V, chunk,
-                         n_chunks, cu_nodes, B, greedy, invT, slo, shi, rnd, part_v, part_i);
+      hipLaunchKernelGGL(k_accept_scan<bf16>, grid, dim3(256), 0, s, (const bf16*)logits, V, n_chunks,
+                         aligned, cu_nodes, B, greedy, invT, slo, shi, rnd, part_v, part_i);
     else
       hipLaunchKernelGGL(k_accept_scan<float>, grid, dim3(256), 0, s, (const float*)logits, V,
-                         chunk, n_chunks, cu_nodes, B, greedy, invT, slo, shi, rnd, part_v, part_i);
+                         n_chunks, aligned, cu_nodes, B, greedy, invT, slo, shi, rnd, part_v, part_i);
   }
   int st = launch_status();
   if (st) return st;
@@ -317,8 +333,7 @@ int launch_accept(int B, int T, const int32_t* cu_nodes, const int32_t* tokens,
 }
 
 size_t accept_workspace(int T, int V) {
-  const int chunk = accept_chunk(V);
-  const int n_chunks = (V + chunk - 1) / chunk;
+  const int n_chunks = accept_chunks(V);
   Carve c(nullptr);
   c.take<float>((size_t)T * n_chunks);
   c.take<int>((size_t)T * n_chunks);
