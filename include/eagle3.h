@@ -9,7 +9,8 @@
  *    workspace whose size the matching *_workspace_size() function returns.
  *  - Every call is asynchronous on the caller's HIP stream, passed as `void* stream`
  *    (NULL = the default stream).  No call synchronises the host.
- *  - Tensors are dense, row-major, in the layouts stated per argument.  Float tensors are
+ *  - Tensors are dense, row-major, in the layouts stated per argument; float tensors start
+ *    on a 16-byte boundary (kernels use 16-byte vector loads), else EAGLE3_EINVAL.  Float tensors are
  *    EAGLE3_F32 (IEEE fp32) or EAGLE3_BF16 (bfloat16) as the `dtype` argument says; ids and
  *    indices are int32; tree masks are uint64; log-sum-exp values and attention partials
  *    are always fp32 and use the natural logarithm.

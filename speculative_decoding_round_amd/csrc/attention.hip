@@ -172,8 +172,7 @@ __global__ __launch_bounds__(256) void k_tree_attn(DevArgs a) {
         tmax = fmaxf(tmax, v);
       }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = row_reduce(tmax, OpMax());
     const float m_new = fmaxf(m_run, tmax);
     const float m_use = m_new == kNegInf ? 0.f : m_new;
     const float alpha = exp2f(m_run - m_use);
@@ -224,9 +223,7 @@ __global__ __launch_bounds__(256) void k_tree_attn(DevArgs a) {
     }
   }
 
-  float l = l_run;
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  const float l = row_reduce(l_run, OpAdd());
   if (!row_ok) return;
   const size_t orow = ((size_t)split * a.q_rows_total + qrow) * a.Hq + head;
   const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -240,7 +237,8 @@ __global__ __launch_bounds__(256) void k_tree_attn(DevArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// LSE merge: one thread per (row, 4 dims); partials merged in split order.
+// LSE merge: one thread per (row, 4 dims); partials merged in split order.  The split
+// LSEs are read first (independent loads), then the weighted partials, eight at a time.
 // ---------------------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void k_lse_merge(int S, int rows, int Dh,
@@ -252,18 +250,32 @@ __global__ __launch_bounds__(256) void k_lse_merge(int S, int rows, int Dh,
   if (idx >= (long)rows * d4) return;
   const int row = (int)(idx / d4), q = (int)(idx % d4);
   float m = kNegInf;
-  for (int s = 0; s < S; ++s) m = fmaxf(m, lse_part[(size_t)s * rows + row]);
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float l8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) l8[u] = s0 + u < S ? lse_part[(size_t)(s0 + u) * rows + row] : kNegInf;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = fmaxf(m, l8[u]);
+  }
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (m != kNegInf) {
-    for (int s = 0; s < S; ++s) {
-      const float ls = lse_part[(size_t)s * rows + row];
-      const float w = ls == kNegInf ? 0.f : expf(ls - m);
-      if (w != 0.f) {
-        const floatx4 v = *reinterpret_cast<const floatx4*>(o_part + ((size_t)s * rows + row) * Dh + 4 * q);
-        acc += v * w;
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      float w8[8];
+      floatx4 v8[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool ok = s0 + u < S;
+        const float ls = ok ? lse_part[(size_t)(s0 + u) * rows + row] : kNegInf;
+        w8[u] = ls == kNegInf ? 0.f : expf(ls - m);
+        v8[u] = ok ? *reinterpret_cast<const floatx4*>(o_part + ((size_t)(s0 + u) * rows + row) * Dh + 4 * q)
+                   : floatx4{0.f, 0.f, 0.f, 0.f};
       }
-      wsum += w;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (w8[u] != 0.f) acc += v8[u] * w8[u];
+        wsum += w8[u];
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;

@@ -150,6 +150,8 @@ int eagle3_tree_attention(int B, int T, int Hq, int Hkv, int Dh, int dtype, cons
   if (!q || !k_tree || !v_tree || !cu_nodes || !mask) return EAGLE3_EINVAL;
   if (max_prefix > 0 && (!kpre || !vpre || !cu_prefix)) return EAGLE3_EINVAL;
   if (!o && (!o_part || !lse_part)) return EAGLE3_EINVAL;
+  for (const void* ptr : {q, k_tree, v_tree, kpre, vpre, (const void*)o_part, (const void*)o})
+    if ((uintptr_t)ptr % 16) return EAGLE3_EINVAL;
   const int S = attention_splits(B, Hkv, max_nodes * (Hq / Hkv), max_prefix, n_splits);
   if (!o_part || !lse_part) {
     const size_t need =
@@ -196,6 +198,7 @@ int eagle3_lse_merge(int S, int rows, int Dh, const float* o_part, const float* 
   if (!dtype_ok(out_dtype)) return EAGLE3_EINVAL;
   if (rows == 0) return EAGLE3_OK;
   if (!o_part || !lse_part || !o) return EAGLE3_EINVAL;
+  if ((uintptr_t)o_part % 16) return EAGLE3_EINVAL;
   return launch_lse_merge(S, rows, Dh, o_part, lse_part, out_dtype, o, lse, (hipStream_t)stream,
                           "lse_merge");
 }

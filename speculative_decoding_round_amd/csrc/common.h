@@ -91,18 +91,61 @@ struct Mfma<float> {
 };
 
 // ---------------------------------------------------------------------------------------
-// Wave / block reductions (wave64)
+// Wave / block reductions (wave64), without LDS: quad_perm xor 1 and xor 2, then the
+// half-row and row mirrors (DPP), then the gfx950 row-pair and half-wave swaps.  Every
+// step combines a lane with a partner symmetrically, so all 64 lanes end with the same
+// bits, and the order is fixed, so results are deterministic.
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+// (own, partner) pairs for the cross-row steps: lanes l and l^16 (resp. l^32)
+__device__ __forceinline__ void swap16(uint32_t v, uint32_t& a, uint32_t& b) {
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  a = r[0];
+  b = r[1];
 }
+__device__ __forceinline__ void swap32(uint32_t v, uint32_t& a, uint32_t& b) {
+  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  a = r[0];
+  b = r[1];
+}
+
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = op(v, __uint_as_float(dpp_u<kDppXor1>(__float_as_uint(v))));
+  v = op(v, __uint_as_float(dpp_u<kDppXor2>(__float_as_uint(v))));
+  v = op(v, __uint_as_float(dpp_u<kDppHalfMirror>(__float_as_uint(v))));
+  v = op(v, __uint_as_float(dpp_u<kDppMirror>(__float_as_uint(v))));
+  uint32_t a, b;
+  swap16(__float_as_uint(v), a, b);
+  v = op(__uint_as_float(a), __uint_as_float(b));
+  swap32(__float_as_uint(v), a, b);
+  return op(__uint_as_float(a), __uint_as_float(b));
+}
+
+// Reduction across the four 16-lane rows only (lanes l, l^16, l^32, l^48).
+template <typename Op>
+__device__ __forceinline__ float row_reduce(float v, Op op) {
+  uint32_t a, b;
+  swap16(__float_as_uint(v), a, b);
+  v = op(__uint_as_float(a), __uint_as_float(b));
+  swap32(__float_as_uint(v), a, b);
+  return op(__uint_as_float(a), __uint_as_float(b));
+}
+
+struct OpAdd {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct OpMax {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, OpAdd()); }
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, OpMax()); }
 
 // Block-wide sum with a fixed reduction tree (deterministic for a given block size).
 // `scratch` needs blockDim.x/64 floats.  All threads receive the result.
@@ -134,16 +177,31 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    float ov = __shfl_xor(v, o, 64);
-    int oi = __shfl_xor(i, o, 64);
-    if (better(ov, oi, v, i)) {
-      v = ov;
-      i = oi;
-    }
+__device__ __forceinline__ void argmax_pair(float& v, int& i, float ov, int oi) {
+  if (better(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
   }
+}
+
+// (value desc, index asc) argmax over the wave; every lane receives the winner.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_pair(v, i, __uint_as_float(dpp_u<kDppXor1>(__float_as_uint(v))), (int)dpp_u<kDppXor1>((uint32_t)i));
+  argmax_pair(v, i, __uint_as_float(dpp_u<kDppXor2>(__float_as_uint(v))), (int)dpp_u<kDppXor2>((uint32_t)i));
+  argmax_pair(v, i, __uint_as_float(dpp_u<kDppHalfMirror>(__float_as_uint(v))),
+              (int)dpp_u<kDppHalfMirror>((uint32_t)i));
+  argmax_pair(v, i, __uint_as_float(dpp_u<kDppMirror>(__float_as_uint(v))), (int)dpp_u<kDppMirror>((uint32_t)i));
+  uint32_t va, vb, ia, ib;
+  swap16(__float_as_uint(v), va, vb);
+  swap16((uint32_t)i, ia, ib);
+  v = __uint_as_float(va);
+  i = (int)ia;
+  argmax_pair(v, i, __uint_as_float(vb), (int)ib);
+  swap32(__float_as_uint(v), va, vb);
+  swap32((uint32_t)i, ia, ib);
+  v = __uint_as_float(va);
+  i = (int)ia;
+  argmax_pair(v, i, __uint_as_float(vb), (int)ib);
 }
 
 // Block argmax; scratch needs 2 * blockDim.x/64 words.  All threads receive the result.

@@ -53,10 +53,14 @@ __global__ __launch_bounds__(256) void k_init(int B, int S, int d, int V, const 
     if (dbg_par) dbg_par[i] = st.parent[i];
   }
   if (threadIdx.x == 0) cs.count[b] = 0;
-  for (int k = threadIdx.x; k < d; k += blockDim.x) {
-    xf[(size_t)b * 3 * d + k] = hl[(size_t)b * d + k];
-    xf[(size_t)b * 3 * d + d + k] = hm[(size_t)b * d + k];
-    xf[(size_t)b * 3 * d + 2 * d + k] = hh[(size_t)b * d + k];
+  constexpr int EPC = Vec<T>::N;
+  for (int k = threadIdx.x * EPC; k < d; k += blockDim.x * EPC) {
+    const u32x4 a = ld16(hl + (size_t)b * d + k);
+    const u32x4 m = ld16(hm + (size_t)b * d + k);
+    const u32x4 h = ld16(hh + (size_t)b * d + k);
+    st16(xf + (size_t)b * 3 * d + k, a);
+    st16(xf + (size_t)b * 3 * d + d + k, m);
+    st16(xf + (size_t)b * 3 * d + 2 * d + k, h);
   }
 }
 
@@ -119,28 +123,39 @@ template <typename T>
 __global__ __launch_bounds__(1024) void k_prep(int R, int sb, int S, int d, int V, float eps, int step,
                                                SlotState st, const T* __restrict__ embed,
                                                const T* __restrict__ g_e, const T* __restrict__ g_f,
-                                               const float* __restrict__ gfeat,
+                                               const float* __restrict__ gpart, int gsplits, int B,
                                                const float* __restrict__ slot_a,
                                                float* __restrict__ f_rows, T* __restrict__ u,
-                                               uint64_t* __restrict__ row_mask) {
+                                               uint64_t* __restrict__ row_mask, float* __restrict__ g_dbg) {
   __shared__ float red[32];
   const int r = blockIdx.x;
   const int b = r / R, j = r % R;
   const int si = b * S + sb + j;
   const bool valid = st.valid[si] != 0;
   const int tok = valid ? clampi(st.tok[si], 0, V - 1) : 0;
-  const float* f = nullptr;
-  if (valid) f = step == 0 ? gfeat + (size_t)b * d : slot_a + ((size_t)b * S + clampi(st.parent[si], 0, S - 1)) * d;
   const int k0 = threadIdx.x * 8;
   const bool act = k0 < d;
   float e[8], fv[8], ge[8], gf[8];
   float se = 0.f, sf = 0.f;
   if (act) {
     load8<T>(embed + (size_t)tok * d + k0, e);
-    if (f) load8<float>(f + k0, fv);
-    else
 #pragma unroll
-      for (int i = 0; i < 8; ++i) fv[i] = 0.f;
+    for (int i = 0; i < 8; ++i) fv[i] = 0.f;
+    if (step == 0) {
+      // root: the fused feature g = W_f [h_low; h_mid; h_high], summed over its k-splits
+      for (int s = 0; s < gsplits; ++s) {
+        float t[8];
+        load8<float>(gpart + ((size_t)s * B + b) * d + k0, t);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) fv[i] += t[i];
+      }
+      if (g_dbg) store8<float>(g_dbg + (size_t)b * d + k0, fv);
+      if (!valid)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) fv[i] = 0.f;
+    } else if (valid) {
+      load8<float>(slot_a + ((size_t)b * S + clampi(st.parent[si], 0, S - 1)) * d + k0, fv);
+    }
     load8<T>(g_e + k0, ge);
     load8<T>(g_f + k0, gf);
 #pragma unroll
@@ -166,13 +181,16 @@ __global__ __launch_bounds__(1024) void k_prep(int R, int sb, int S, int d, int 
   if (threadIdx.x == 0) row_mask[r] = valid ? st.mask[si] : 0ull;
 }
 
-// rmsnorm of fp32 rows into dtype rows; optionally keep the fp32 input per slot (the
-// drafter output a that later nodes take as their feature).
+// Residual + RMSNorm over a projection's split-K partials:
+//   y = resid + sum_s part[s] (split order), kept in fp32 as `out` (and per slot in `keep`),
+//   outT = rms(y) * gamma in dtype.
 template <typename T>
-__global__ __launch_bounds__(1024) void k_rmsnorm(const float* __restrict__ in, int d, float eps,
-                                                  const T* __restrict__ gamma, T* __restrict__ out,
-                                                  int R, int sb, int S, SlotState st,
-                                                  float* __restrict__ keep, float* __restrict__ keep_dbg) {
+__global__ __launch_bounds__(1024) void k_resid_norm(const float* __restrict__ part, int splits, int M,
+                                                     int d, const float* __restrict__ resid,
+                                                     const T* __restrict__ gamma, float eps,
+                                                     float* __restrict__ out, T* __restrict__ outT,
+                                                     int R, int sb, int S, SlotState st,
+                                                     float* __restrict__ keep, float* __restrict__ keep_dbg) {
   __shared__ float red[32];
   const int r = blockIdx.x;
   const int k0 = threadIdx.x * 8;
@@ -180,10 +198,21 @@ __global__ __launch_bounds__(1024) void k_rmsnorm(const float* __restrict__ in, 
   float x[8], gm[8];
   float ss = 0.f, dummy = 0.f;
   if (act) {
-    load8<float>(in + (size_t)r * d + k0, x);
+    load8<float>(resid + (size_t)r * d + k0, x);
     load8<T>(gamma + k0, gm);
+    float acc[8];
+    load8<float>(part + (size_t)r * d + k0, acc);
+    for (int s = 1; s < splits; ++s) {
+      float t[8];
+      load8<float>(part + ((size_t)s * M + r) * d + k0, t);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
+      for (int i = 0; i < 8; ++i) acc[i] += t[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[i] += acc[i];
+      ss += x[i] * x[i];
+    }
   }
   block_sum2(ss, dummy, red);
   if (!act) return;
@@ -191,7 +220,8 @@ __global__ __launch_bounds__(1024) void k_rmsnorm(const float* __restrict__ in, 
   float o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = x[i] * inv * gm[i];
-  store8<T>(out + (size_t)r * d + k0, o);
+  store8<float>(out + (size_t)r * d + k0, x);
+  store8<T>(outT + (size_t)r * d + k0, o);
   if (keep) {
     const int b = r / R, j = r % R;
     const int si = b * S + sb + j;
@@ -255,12 +285,12 @@ __global__ __launch_bounds__(256) void k_epi_qkv(const float* __restrict__ part,
 }
 
 // ---------------------------------------------------------------------------------------
-// LM head top-K / log-sum-exp, pass 1: per (row, chunk of 4096 logits) the chunk's top-K
-// (value desc, id asc) and its (max, sum e^{z-max}).  Each thread holds 16 logits (four
-// float4 loads issued together), sorts them with a fixed network, and the K winners are
-// drawn first per wave and then across the four waves, popping sorted heads.
+// LM head top-K / log-sum-exp, pass 1: one wave per (row, chunk of 1024 logits).  Each lane
+// holds 16 logits (four float4 loads issued together) and sorts them with a fixed network;
+// the chunk's K winners (value desc, id asc) are drawn by K wave-argmax rounds over the
+// lanes' sorted heads, and its (max, sum e^{z-max}) by wave reductions.  No block barrier.
 // ---------------------------------------------------------------------------------------
-constexpr int TK_CHUNK = 4096;
+constexpr int TK_CHUNK = 1024;
 
 __device__ __forceinline__ void cswap(float& va, int& ia, float& vb, int& ib) {
   // afterwards (va, ia) is the better of the two
@@ -304,17 +334,45 @@ __device__ __forceinline__ void pop16(float* v, int* id) {
   id[15] = 0x7fffffff;
 }
 
+// Top 16 of two best-first lists of 16, best-first in (v, id): the elementwise better of
+// v[i] and v2[15 - i] is a bitonic sequence holding the 16 best, which a bitonic merge sorts.
+__device__ __forceinline__ void merge16(float* v, int* id, const float* v2, const int* id2) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (better(v2[15 - i], id2[15 - i], v[i], id[i])) {
+      v[i] = v2[15 - i];
+      id[i] = id2[15 - i];
+    }
+#pragma unroll
+  for (int j = 8; j > 0; j >>= 1)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int l = i ^ j;
+      if (l > i) cswap(v[i], id[i], v[l], id[l]);
+    }
+}
+
+// Load one chunk's best-first list of K (padded to 16 with (-inf, max id)).
+__device__ __forceinline__ void load_list(const float* cv, const int* ci, size_t base, int K, bool ok,
+                                          float* v, int* id) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const bool in = ok && k < K;
+    v[k] = in ? cv[base + k] : kNegInf;
+    id[k] = in ? ci[base + k] : 0x7fffffff;
+  }
+}
+
 __global__ __launch_bounds__(256) void k_topk_chunk(const float* __restrict__ part, int splits, int M,
                                                     int V, int K, int n_chunks,
                                                     float* __restrict__ cv, int* __restrict__ ci,
                                                     float* __restrict__ cmax, float* __restrict__ csum,
                                                     float* __restrict__ dbg_logits, int R, int sb, int S,
                                                     SlotState st) {
-  __shared__ float red[32];
-  __shared__ float wv[4][16];
-  __shared__ int wi[4][16];
-  const int m = blockIdx.y, c = blockIdx.x;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int m = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (c >= n_chunks) return;
   const int t0 = c * TK_CHUNK;
   float* dl = nullptr;
   if (dbg_logits) {
@@ -324,10 +382,9 @@ __global__ __launch_bounds__(256) void k_topk_chunk(const float* __restrict__ pa
   }
   float v[16];
   int id[16];
-  // thread covers 4 float4 groups: t0 + 4*(threadIdx.x + 256*q) .. +4, q = 0..3
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int t = t0 + 4 * (threadIdx.x + 256 * q);
+    const int t = t0 + 4 * (lane + 64 * q);
     floatx4 z = {0.f, 0.f, 0.f, 0.f};
     if (t < V) {
       for (int s = 0; s < splits; ++s) z += *reinterpret_cast<const floatx4*>(part + ((size_t)s * M + m) * V + t);
@@ -340,156 +397,128 @@ __global__ __launch_bounds__(256) void k_topk_chunk(const float* __restrict__ pa
       id[4 * q + e] = ok ? t + e : 0x7fffffff;
     }
   }
-  // chunk (max, sum e^{z - max})
   float lm = kNegInf;
 #pragma unroll
   for (int i = 0; i < 16; ++i) lm = fmaxf(lm, v[i]);
-  const float bm = block_max(lm, red);
+  const float bm = wave_max(lm);
   float ls = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) ls += v[i] == kNegInf ? 0.f : expf(v[i] - bm);
-  const float tot = block_sum(ls, red);
-  // top-K: sort own 16, K rounds per wave, then K rounds over the 4 wave lists
+  const float tot = wave_sum(ls);
   sort16(v, id);
+  const size_t base = ((size_t)m * n_chunks + c) * K;
   for (int k = 0; k < K; ++k) {
     float bv = v[0];
     int bi = id[0];
     wave_argmax(bv, bi);
     if (id[0] == bi && v[0] == bv) pop16(v, id);
     if (lane == 0) {
-      wv[w][k] = bv;
-      wi[w][k] = bi;
-    }
-  }
-  __syncthreads();
-  if (w == 0) {
-    // lane l < 4*K holds entry (l / K, l % K); heads advance per wave list
-    float hv = kNegInf;
-    int hi = 0x7fffffff;
-    const int nwv = blockDim.x >> 6;
-    if (lane < nwv * K) {
-      hv = wv[lane / K][lane % K];
-      hi = wi[lane / K][lane % K];
-    }
-    for (int k = 0; k < K; ++k) {
-      float bv = hv;
-      int bi = hi;
-      wave_argmax(bv, bi);
-      if (hi == bi && hv == bv) {
-        hv = kNegInf;
-        hi = 0x7fffffff;
-      }
-      if (lane == 0) {
-        cv[((size_t)m * n_chunks + c) * K + k] = bv;
-        ci[((size_t)m * n_chunks + c) * K + k] = bi;
-      }
-    }
-    if (lane == 0) {
-      cmax[(size_t)m * n_chunks + c] = bm;
-      csum[(size_t)m * n_chunks + c] = tot;
-    }
-  }
-}
-
-// pass 2: one wave per row merges the chunks' top-K (K rounds of wave argmax over each
-// lane's best remaining candidate) and the chunks' (max, sum) in chunk order.
-__global__ __launch_bounds__(64) void k_topk_merge(const float* __restrict__ cv, const int* __restrict__ ci,
-                                                   const float* __restrict__ cmax,
-                                                   const float* __restrict__ csum, int n_chunks, int K,
-                                                   int* __restrict__ top_id, float* __restrict__ top_val,
-                                                   float* __restrict__ lse, int R, int sb, int S,
-                                                   SlotState st, int32_t* dbg_id, float* dbg_val,
-                                                   float* dbg_lse) {
-  const int m = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int n = n_chunks * K;
-  // log-sum-exp over chunks
-  float mx = kNegInf;
-  for (int c = lane; c < n_chunks; c += 64) mx = fmaxf(mx, cmax[(size_t)m * n_chunks + c]);
-  mx = wave_max(mx);
-  float tot = 0.f;
-  for (int c = lane; c < n_chunks; c += 64) {
-    const float cm = cmax[(size_t)m * n_chunks + c];
-    if (cm != kNegInf) tot += csum[(size_t)m * n_chunks + c] * expf(cm - mx);
-  }
-  tot = wave_sum(tot);
-  const float row_lse = mx + logf(tot);
-  // candidates: lane holds entries lane + 64*q, q < 16 (n <= 1024)
-  float v[16];
-  int id[16];
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int e = lane + 64 * q;
-    v[q] = e < n ? cv[(size_t)m * n + e] : kNegInf;
-    id[q] = e < n ? ci[(size_t)m * n + e] : 0x7fffffff;
-  }
-  const int b = m / R, j = m % R;
-  const int sidx = b * S + sb + j;
-  const bool dbg = st.valid[sidx] != 0;
-  for (int k = 0; k < K; ++k) {
-    float bv = kNegInf;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < 16; ++q)
-      if (better(v[q], id[q], bv, bi)) {
-        bv = v[q];
-        bi = id[q];
-      }
-    wave_argmax(bv, bi);
-#pragma unroll
-    for (int q = 0; q < 16; ++q)
-      if (id[q] == bi && v[q] == bv) {
-        v[q] = kNegInf;
-        id[q] = 0x7fffffff;
-      }
-    if (lane == 0) {
-      top_id[(size_t)m * K + k] = bi;
-      top_val[(size_t)m * K + k] = bv;
-      if (dbg && dbg_id) dbg_id[(size_t)sidx * K + k] = bi;
-      if (dbg && dbg_val) dbg_val[(size_t)sidx * K + k] = bv;
+      cv[base + k] = bv;
+      ci[base + k] = bi;
     }
   }
   if (lane == 0) {
-    lse[m] = row_lse;
-    if (dbg && dbg_lse) dbg_lse[sidx] = row_lse;
+    cmax[(size_t)m * n_chunks + c] = bm;
+    csum[(size_t)m * n_chunks + c] = tot;
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// Tree selection for one request per workgroup.  Children of the nodes evaluated at this
-// step get s = s_parent + (z - lse) in fp32; then either the next depth's W best by
-// (s desc, creation asc) become evaluation slots, or (last step) the N best candidates of
-// the pool are kept and relabelled by (depth asc, creation asc).
+// Tree selection for one request per workgroup (one wave per evaluated row).
+// Phase 1: wave j merges row j's chunk winners into its top-K (each lane keeps a sorted
+// list of 16 fed from its chunks, then K wave-argmax rounds) and its log-sum-exp (chunk
+// maxima and sums combined in fixed order).
+// Phase 2: children of the nodes evaluated at this step get s = s_parent + (z - lse) in
+// fp32; then either the next depth's W best by (s desc, creation asc) become evaluation
+// slots, or (last step) the N best candidates of the pool are kept and relabelled by
+// (depth asc, creation asc).
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ bool cand_better(float sa, int ia, float sb_, int ib) {
   return sa > sb_ || (sa == sb_ && ia < ib);
 }
 
-__global__ __launch_bounds__(256) void k_select(int step, int D, int K, int W, int N, int S, int PMAX,
-                                                int R, const int* __restrict__ top_id,
-                                                const float* __restrict__ top_val,
-                                                const float* __restrict__ lse, SlotState st,
-                                                CandState cs, int32_t* __restrict__ out_tok,
-                                                int32_t* __restrict__ out_par,
-                                                int32_t* __restrict__ out_dep, float* __restrict__ out_score,
-                                                int32_t* __restrict__ out_n, int32_t* dbg_tok,
-                                                int32_t* dbg_par) {
+constexpr int SEL_MAXR = 16;   // rows (W) per request handled by one workgroup
+
+__global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, int N, int S, int PMAX,
+                                                 int R, int n_chunks, const float* __restrict__ cv,
+                                                 const int* __restrict__ ci,
+                                                 const float* __restrict__ cmax,
+                                                 const float* __restrict__ csum, SlotState st,
+                                                 CandState cs, int32_t* __restrict__ out_tok,
+                                                 int32_t* __restrict__ out_par,
+                                                 int32_t* __restrict__ out_dep, float* __restrict__ out_score,
+                                                 int32_t* __restrict__ out_n, int32_t* dbg_tok,
+                                                 int32_t* dbg_par, int32_t* dbg_id, float* dbg_val,
+                                                 float* dbg_lse) {
 #pragma clang fp contract(off)
+  __shared__ float s_val[SEL_MAXR][KMAX];
+  __shared__ int s_id[SEL_MAXR][KMAX];
+  __shared__ float s_lse[SEL_MAXR];
   __shared__ float ssc[1024];
   __shared__ int sdep[1024];
   __shared__ int skeep[1024];
   __shared__ int slab[1024];
-  __shared__ int n_eval_s;
+  __shared__ int s_valid[SEL_MAXR];
+  __shared__ float s_score[SEL_MAXR];
+  __shared__ uint64_t s_mask[SEL_MAXR];
+  __shared__ int s_count;
   const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int sb = step == 0 ? 0 : 1 + (step - 1) * W;
-  const int n_before = cs.count[b];
-  if (threadIdx.x == 0) {
-    int ne = 0;
-    for (int j = 0; j < R; ++j) ne += st.valid[b * S + sb + j] ? 1 : 0;
-    n_eval_s = ne;
+  if (threadIdx.x == 0) s_count = cs.count[b];
+
+  // ---- phase 1: per-row top-K merge and log-sum-exp (every load issued first)
+  if (w < R) {
+    const int m = b * R + w;
+    const int sidx = b * S + sb + w;
+    const int valid = st.valid[sidx];
+    const float score0 = st.score[sidx];
+    const uint64_t mk = st.mask[sidx];
+    const bool ok0 = lane < n_chunks, ok1 = lane + 64 < n_chunks;
+    const float cm0 = ok0 ? cmax[(size_t)m * n_chunks + lane] : kNegInf;
+    const float cm1 = ok1 ? cmax[(size_t)m * n_chunks + lane + 64] : kNegInf;
+    const float cs0 = ok0 ? csum[(size_t)m * n_chunks + lane] : 0.f;
+    const float cs1 = ok1 ? csum[(size_t)m * n_chunks + lane + 64] : 0.f;
+    float v[16], v2[16];
+    int id[16], id2[16];
+    load_list(cv, ci, ((size_t)m * n_chunks + lane) * K, K, ok0, v, id);
+    load_list(cv, ci, ((size_t)m * n_chunks + lane + 64) * K, K, ok1, v2, id2);
+    if (lane == 0) {
+      s_valid[w] = valid;
+      s_score[w] = score0;
+      s_mask[w] = mk;
+    }
+    if (valid) {
+      const float mx = wave_max(fmaxf(cm0, cm1));
+      float tot = cm0 != kNegInf ? cs0 * expf(cm0 - mx) : 0.f;
+      if (cm1 != kNegInf) tot += cs1 * expf(cm1 - mx);
+      tot = wave_sum(tot);
+      const float row_lse = mx + logf(tot);
+      merge16(v, id, v2, id2);
+      for (int k = 0; k < K; ++k) {
+        float bv = v[0];
+        int bi = id[0];
+        wave_argmax(bv, bi);
+        if (id[0] == bi && v[0] == bv) pop16(v, id);
+        if (lane == 0) {
+          s_val[w][k] = bv;
+          s_id[w][k] = bi;
+          if (dbg_id) dbg_id[(size_t)sidx * K + k] = bi;
+          if (dbg_val) dbg_val[(size_t)sidx * K + k] = bv;
+        }
+      }
+      if (lane == 0) {
+        s_lse[w] = row_lse;
+        if (dbg_lse) dbg_lse[sidx] = row_lse;
+      }
+    }
   }
   __syncthreads();
-  const int nE = n_eval_s;  // valid slots form a prefix of the step's slots
+
+  // ---- phase 2: children, then the next frontier or the final prune
+  const int n_before = s_count;
+  int nE = 0;  // valid slots form a prefix of the step's slots
+  for (int j = 0; j < R; ++j) nE += s_valid[j] ? 1 : 0;
   const int n_new = nE * K;
   const int n_total = n_before + n_new;
   int32_t* ctok = cs.tok + (size_t)b * PMAX;
@@ -499,23 +528,21 @@ __global__ __launch_bounds__(256) void k_select(int step, int D, int K, int W, i
   for (int e = threadIdx.x; e < n_new; e += blockDim.x) {
     const int j = e / K, rk = e % K;
     const int slot = sb + j;
-    const int row = b * R + j;
     const int ci_ = n_before + e;
-    const float val = top_val[(size_t)row * K + rk];
-    const float lp = val - lse[row];
-    ctok[ci_] = top_id[(size_t)row * K + rk];
+    const float lp = s_val[j][rk] - s_lse[j];
+    const float sc = s_score[j] + lp;
+    ctok[ci_] = s_id[j][rk];
     cps[ci_] = slot;
     cdep[ci_] = step + 1;
-    csc[ci_] = st.score[b * S + slot] + lp;
-    ssc[ci_] = csc[ci_];
+    csc[ci_] = sc;
+    ssc[ci_] = sc;
+    sdep[ci_] = step + 1;
   }
-  // earlier candidates' scores into LDS for the final ranking
   if (step + 1 == D) {
     for (int e = threadIdx.x; e < n_before; e += blockDim.x) {
       ssc[e] = csc[e];
       sdep[e] = cdep[e];
     }
-    for (int e = threadIdx.x; e < n_new; e += blockDim.x) sdep[n_before + e] = step + 1;
   }
   __syncthreads();
   if (step + 1 < D) {
@@ -535,7 +562,7 @@ __global__ __launch_bounds__(256) void k_select(int step, int D, int K, int W, i
         st.valid[i] = 1;
         st.score[i] = sa;
         st.cand[i] = ia;
-        st.mask[i] = st.mask[b * S + ps] | (1ull << slot);
+        st.mask[i] = s_mask[ps - sb] | (1ull << slot);
         if (dbg_tok) dbg_tok[i] = ctok[ia];
         if (dbg_par) dbg_par[i] = ps;
       }
@@ -603,8 +630,8 @@ struct Plan {
   // pointers (null when measuring)
   SlotState st;
   CandState cs;
-  float *g, *slot_a, *f_rows, *h1, *a_rows, *gpart, *att_o, *att_lse, *cv, *cmax, *csum, *top_val, *lse;
-  int *ci, *top_id;
+  float *gfuse, *slot_a, *f_rows, *h1, *a_rows, *gpart, *att_o, *att_lse, *cv, *cmax, *csum;
+  int* ci;
   uint64_t* row_mask;
   void *xf, *u, *q_rows, *kslot, *vslot, *attn, *mn, *act, *xl;
   size_t bytes;
@@ -637,7 +664,6 @@ Plan make_plan(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, int max
     size_t e = (size_t)gpl.splits * M * N_;
     if (e > gp) gp = e;
   };
-  upd(B, p.d, 3 * p.d);
   for (int M : {B, p.Mmax}) {
     upd(M, nqkv, 2 * p.d);
     upd(M, p.d, p.Hq * p.Dh);
@@ -659,7 +685,6 @@ Plan make_plan(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, int max
   p.cs.depth = c.take<int32_t>(BP);
   p.cs.score = c.take<float>(BP);
   p.cs.count = c.take<int32_t>(B);
-  p.g = c.take<float>((size_t)B * p.d);
   p.xf = c.take<char>((size_t)B * 3 * p.d * es);
   p.slot_a = c.take<float>(BS * p.d);
   p.kslot = c.take<char>(BS * p.Hkv * p.Dh * es);
@@ -676,15 +701,16 @@ Plan make_plan(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, int max
   p.a_rows = c.take<float>(M * p.d);
   p.xl = c.take<char>(M * p.d * es);
   p.gpart = c.take<float>(gp);
+  {
+    e3h::GemmPlan gfp = e3h::plan_gemm(B, p.d, 3 * p.d, w->dtype);
+    p.gfuse = c.take<float>((size_t)gfp.splits * B * p.d);
+  }
   p.att_o = c.take<float>((size_t)(p.att_splits + 1) * M * p.Hq * p.Dh);
   p.att_lse = c.take<float>((size_t)(p.att_splits + 1) * M * p.Hq);
   p.cv = c.take<float>(M * p.lm_nchunk * p.K);
   p.ci = c.take<int>(M * p.lm_nchunk * p.K);
   p.cmax = c.take<float>(M * p.lm_nchunk);
   p.csum = c.take<float>(M * p.lm_nchunk);
-  p.top_id = c.take<int>(M * p.K);
-  p.top_val = c.take<float>(M * p.K);
-  p.lse = c.take<float>(M);
   p.bytes = c.size();
   return p;
 }
@@ -707,15 +733,9 @@ int run_draft(const eagle3_drafter* w, const Plan& p, const void* h_low, const v
                        (const T*)h_low, (const T*)h_mid, (const T*)h_high, (T*)p.xf, dbg_tok, dbg_par);
     if ((st = launch_status())) return st;
   }
-  // feature fusion g = W_f [h_low; h_mid; h_high]
-  {
-    GemmPlan gp = plan_gemm(B, d, 3 * d, dt);
-    if ((st = launch_gemm(gp, dt, p.xf, 3 * d, w->w_fuse, p.gpart, s, "gemm_fuse"))) return st;
-    if ((st = launch_epi_sum(gp, p.gpart, p.g, nullptr, s, "epi_fuse"))) return st;
-    if (dbg && dbg->g)
-      if (hipMemcpyAsync(dbg->g, p.g, (size_t)B * d * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
-        return EAGLE3_EHIP;
-  }
+  // feature fusion g = W_f [h_low; h_mid; h_high] (its k-splits are summed by the step-0 prep)
+  GemmPlan gf = plan_gemm(B, d, 3 * d, dt);
+  if ((st = launch_gemm(gf, dt, p.xf, 3 * d, w->w_fuse, p.gfuse, s, "gemm_fuse"))) return st;
   for (int step = 0; step < p.D; ++step) {
     const int R = step == 0 ? 1 : p.W;
     const int sb = step == 0 ? 0 : 1 + (step - 1) * p.W;
@@ -723,8 +743,8 @@ int run_draft(const eagle3_drafter* w, const Plan& p, const void* h_low, const v
     {
       ProfScope ps("draft_prep", s);
       hipLaunchKernelGGL(k_prep<T>, dim3(M), dim3(p.row_threads), 0, s, R, sb, p.S, d, p.V, w->eps, step, p.st,
-                         (const T*)w->embed, (const T*)w->g_embed, (const T*)w->g_feat, p.g, p.slot_a,
-                         p.f_rows, (T*)p.u, p.row_mask);
+                         (const T*)w->embed, (const T*)w->g_embed, (const T*)w->g_feat, p.gfuse, gf.splits, B,
+                         p.slot_a, p.f_rows, (T*)p.u, p.row_mask, dbg ? dbg->g : (float*)nullptr);
       if ((st = launch_status())) return st;
     }
     // QKV + RoPE
@@ -770,53 +790,44 @@ int run_draft(const eagle3_drafter* w, const Plan& p, const void* h_low, const v
                                  nullptr, s, "draft_lse_merge")))
         return st;
     }
-    // O projection + residual
+    // O projection + residual, RMSNorm
     {
       GemmPlan gp = plan_gemm(M, d, p.Hq * p.Dh, dt);
       if ((st = launch_gemm(gp, dt, p.attn, p.Hq * p.Dh, w->w_o, p.gpart, s, "gemm_o"))) return st;
-      if ((st = launch_epi_sum(gp, p.gpart, p.h1, p.f_rows, s, "epi_o"))) return st;
-      ProfScope ps("rmsnorm", s);
-      hipLaunchKernelGGL(k_rmsnorm<T>, dim3(M), dim3(p.row_threads), 0, s, p.h1, d, w->eps, (const T*)w->g_mlp,
-                         (T*)p.mn, R, sb, p.S, p.st, (float*)nullptr, (float*)nullptr);
+      ProfScope ps("resid_norm", s);
+      hipLaunchKernelGGL(k_resid_norm<T>, dim3(M), dim3(p.row_threads), 0, s, p.gpart, gp.splits, M, d,
+                         p.f_rows, (const T*)w->g_mlp, w->eps, p.h1, (T*)p.mn, R, sb, p.S, p.st,
+                         (float*)nullptr, (float*)nullptr);
       if ((st = launch_status())) return st;
     }
-    // SiLU-gated MLP + residual
+    // SiLU-gated MLP + residual, final RMSNorm
     {
-      GemmPlan gp = plan_gemm(M, 2 * p.F, d, dt);
-      if ((st = launch_gemm(gp, dt, p.mn, d, w->w_gate_up, p.gpart, s, "gemm_gate_up"))) return st;
-      if ((st = launch_epi_silu_mul(gp, p.gpart, dt, p.act, s, "epi_silu_mul"))) return st;
+      GemmPlan gp = plan_gemm(M, 2 * p.F, d, dt, true);
+      if ((st = launch_gemm(gp, dt, p.mn, d, w->w_gate_up, p.gpart, s, "gemm_gate_up", p.act))) return st;
       GemmPlan gd = plan_gemm(M, d, p.F, dt);
       if ((st = launch_gemm(gd, dt, p.act, p.F, w->w_down, p.gpart, s, "gemm_down"))) return st;
-      if ((st = launch_epi_sum(gd, p.gpart, p.a_rows, p.h1, s, "epi_down"))) return st;
-      ProfScope ps("rmsnorm", s);
-      hipLaunchKernelGGL(k_rmsnorm<T>, dim3(M), dim3(p.row_threads), 0, s, p.a_rows, d, w->eps,
-                         (const T*)w->g_final, (T*)p.xl, R, sb, p.S, p.st, p.slot_a,
+      ProfScope ps("resid_norm", s);
+      hipLaunchKernelGGL(k_resid_norm<T>, dim3(M), dim3(p.row_threads), 0, s, p.gpart, gd.splits, M, d, p.h1,
+                         (const T*)w->g_final, w->eps, p.a_rows, (T*)p.xl, R, sb, p.S, p.st, p.slot_a,
                          dbg ? dbg->slot_a : (float*)nullptr);
       if ((st = launch_status())) return st;
     }
-    // LM head, top-K and log-sum-exp
+    // LM head, top-K and log-sum-exp, then the tree selection
     {
       GemmPlan gp = plan_gemm(M, p.V, d, dt);
       if ((st = launch_gemm(gp, dt, p.xl, d, w->w_lm, p.gpart, s, "gemm_lm_head"))) return st;
       {
         ProfScope ps("topk_chunk", s);
-        hipLaunchKernelGGL(k_topk_chunk, dim3(p.lm_nchunk, M), dim3(256), 0, s, p.gpart, gp.splits, M,
-                           p.V, p.K, p.lm_nchunk, p.cv, p.ci, p.cmax, p.csum,
+        hipLaunchKernelGGL(k_topk_chunk, dim3((p.lm_nchunk + 3) / 4, M), dim3(256), 0, s, p.gpart,
+                           gp.splits, M, p.V, p.K, p.lm_nchunk, p.cv, p.ci, p.cmax, p.csum,
                            dbg ? dbg->slot_logits : (float*)nullptr, R, sb, p.S, p.st);
         if ((st = launch_status())) return st;
       }
-      ProfScope ps("topk_merge", s);
-      hipLaunchKernelGGL(k_topk_merge, dim3(M), dim3(64), 0, s, p.cv, p.ci, p.cmax, p.csum,
-                         p.lm_nchunk, p.K, p.top_id, p.top_val, p.lse, R, sb, p.S, p.st,
-                         dbg ? dbg->slot_topk_id : (int32_t*)nullptr,
-                         dbg ? dbg->slot_topk_val : (float*)nullptr, dbg ? dbg->slot_lse : (float*)nullptr);
-      if ((st = launch_status())) return st;
-    }
-    {
       ProfScope ps("draft_select", s);
-      hipLaunchKernelGGL(k_select, dim3(B), dim3(256), 0, s, step, p.D, p.K, p.W, p.N, p.S, p.PMAX, R,
-                         p.top_id, p.top_val, p.lse, p.st, p.cs, tokens, parents, depth, score, n_nodes,
-                         dbg_tok, dbg_par);
+      hipLaunchKernelGGL(k_select, dim3(B), dim3(64 * (R > 4 ? R : 4)), 0, s, step, p.D, p.K, p.W, p.N, p.S, p.PMAX, R,
+                         p.lm_nchunk, p.cv, p.ci, p.cmax, p.csum, p.st, p.cs, tokens, parents, depth,
+                         score, n_nodes, dbg_tok, dbg_par, dbg ? dbg->slot_topk_id : (int32_t*)nullptr,
+                         dbg ? dbg->slot_topk_val : (float*)nullptr, dbg ? dbg->slot_lse : (float*)nullptr);
       if ((st = launch_status())) return st;
     }
   }
@@ -842,8 +853,8 @@ int draft_check(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, int ma
   if ((long)t->topk + (long)(t->depth - 1) * t->width * t->topk > 1024) return EAGLE3_EUNSUPPORTED;
   if (t->n_nodes > 255) return EAGLE3_EUNSUPPORTED;
   if ((long)B * (t->width > 1 ? t->width : 1) > 160) return EAGLE3_EUNSUPPORTED;
-  const long nch = (w->vocab + 4095) / 4096;
-  if (nch * t->topk > 1024) return EAGLE3_EUNSUPPORTED;
+  if (t->width > SEL_MAXR) return EAGLE3_EUNSUPPORTED;
+  if (w->vocab > 128 * TK_CHUNK) return EAGLE3_EUNSUPPORTED;
   if (!w->embed || !w->w_fuse || !w->g_embed || !w->g_feat || !w->g_mlp || !w->g_final ||
       !w->w_qkv || !w->w_o || !w->w_gate_up || !w->w_down || !w->w_lm)
     return EAGLE3_EINVAL;
@@ -866,6 +877,9 @@ int draft_expand(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, const
       !score || !n_nodes)
     return EAGLE3_EINVAL;
   if (max_prefix > 0 && (!kpre || !vpre)) return EAGLE3_EINVAL;
+  for (const void* ptr : {h_low, h_mid, h_high, kpre, vpre, w->embed, w->w_fuse, w->g_embed, w->g_feat,
+                          w->g_mlp, w->g_final, w->w_qkv, w->w_o, w->w_gate_up, w->w_down, w->w_lm})
+    if ((uintptr_t)ptr % 16) return EAGLE3_EINVAL;
   Plan p = make_plan(w, t, B, max_prefix, nullptr);
   if (!ws || ws_bytes < p.bytes) return EAGLE3_EWORKSPACE;
   p = make_plan(w, t, B, max_prefix, ws);

@@ -18,11 +18,39 @@ namespace {
 // NTB consecutive 16-row tiles of W against them (W tiles double-buffered), so the X rows
 // cost 16*NTB times less load traffic than W.  The WK waves of a workgroup split the
 // k-range and are summed in LDS in wave order.
-template <typename T, int MT, int NTB, int KCB, int WK>
+// SILU: W is [2F, K] with the gate rows first and the up rows second.  A wave takes NTB/2
+// gate tiles and the NTB/2 matching up tiles, and writes act[m][j] = silu(gate) * up in T
+// (needs a single k-split).
+template <int NTB, bool SILU>
+__device__ __forceinline__ int tile_row0(int nb, int t, int F) {
+  if constexpr (!SILU) {
+    return (nb * NTB + t) * 16;
+  } else {
+    constexpr int H = NTB / 2;
+    return t < H ? (nb * H + t) * 16 : F + (nb * H + t - H) * 16;
+  }
+}
+
+template <typename T, bool SILU>
+__device__ __forceinline__ void store_out(float* Ys, void* act, int M, int N, int F, int m, int n_gate,
+                                          floatx4 g, floatx4 u) {
+  if constexpr (!SILU) {
+    if (m < M && n_gate < N) *reinterpret_cast<floatx4*>(Ys + (size_t)m * N + n_gate) = g;
+  } else {
+    if (m < M && n_gate < F) {
+      T* o = reinterpret_cast<T*>(act) + (size_t)m * F + n_gate;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(g[e] / (1.f + expf(-g[e])) * u[e]);
+    }
+  }
+}
+
+template <typename T, int MT, int NTB, int KCB, int WK, bool SILU = false>
 __global__ __launch_bounds__(WK * 64) void k_gemm(const T* __restrict__ X, int M, int ldx,
                                                      const T* __restrict__ W, int N, int K,
                                                      float* __restrict__ Y, int n_blocks,
-                                                     int chunks_total, int chunks_per_split) {
+                                                     int chunks_total, int chunks_per_split,
+                                                     void* __restrict__ act, int F) {
   static_assert(NTB % 2 == 0, "NTB must be even");
   constexpr int EPC = Vec<T>::N;
   constexpr int KPC = Mfma<T>::KPC;
@@ -41,7 +69,7 @@ __global__ __launch_bounds__(WK * 64) void k_gemm(const T* __restrict__ X, int M
   bool wok[NTB];
 #pragma unroll
   for (int nt = 0; nt < NTB; ++nt) {
-    const int n = (nb * NTB + nt) * 16 + r16;
+    const int n = tile_row0<NTB, SILU>(nb, nt, F) + r16;
     wok[nt] = n < N;
     wbase[nt] = W + (size_t)(wok[nt] ? n : 0) * K + g * EPC;
   }
@@ -94,14 +122,15 @@ __global__ __launch_bounds__(WK * 64) void k_gemm(const T* __restrict__ X, int M
   }
 
   float* Ys = Y + (size_t)ks * M * N;
+  constexpr int NOUT = SILU ? NTB / 2 : NTB;   // output tiles per wave
   if constexpr (WK == 1) {
 #pragma unroll
-    for (int nt = 0; nt < NTB; ++nt)
+    for (int nt = 0; nt < NOUT; ++nt)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int m = mt * 16 + r16;
-        const int n = (nb * NTB + nt) * 16 + 4 * g;
-        if (m < M && n < N) *reinterpret_cast<floatx4*>(Ys + (size_t)m * N + n) = acc[nt][mt];
+        const int n = tile_row0<NTB, SILU>(nb, nt, F) + 4 * g;
+        store_out<T, SILU>(Ys, act, M, N, F, m, n, acc[nt][mt], acc[SILU ? nt + NOUT : nt][mt]);
       }
   } else {
 #pragma unroll
@@ -109,15 +138,19 @@ __global__ __launch_bounds__(WK * 64) void k_gemm(const T* __restrict__ X, int M
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) red[wk][nt * MT + mt][lane] = acc[nt][mt];
     __syncthreads();
-    for (int e = threadIdx.x; e < NTB * MT * 64; e += WK * 64) {
+    for (int e = threadIdx.x; e < NOUT * MT * 64; e += WK * 64) {
       const int tile = e / 64, ln = e % 64;
       const int nt = tile / MT, mt = tile % MT;
-      floatx4 v = red[0][tile][ln];
+      const int tile2 = (SILU ? nt + NOUT : nt) * MT + mt;
+      floatx4 v = red[0][tile][ln], u = red[0][tile2][ln];
 #pragma unroll
-      for (int w = 1; w < WK; ++w) v += red[w][tile][ln];
+      for (int w = 1; w < WK; ++w) {
+        v += red[w][tile][ln];
+        if constexpr (SILU) u += red[w][tile2][ln];
+      }
       const int m = mt * 16 + (ln & 15);
-      const int n = (nb * NTB + nt) * 16 + 4 * (ln >> 4);
-      if (m < M && n < N) *reinterpret_cast<floatx4*>(Ys + (size_t)m * N + n) = v;
+      const int n = tile_row0<NTB, SILU>(nb, nt, F) + 4 * (ln >> 4);
+      store_out<T, SILU>(Ys, act, M, N, F, m, n, v, u);
     }
   }
 }
@@ -136,29 +169,13 @@ __global__ __launch_bounds__(256) void k_epi_sum(const float* __restrict__ part,
   reinterpret_cast<floatx4*>(out)[i4] = v;
 }
 
-// gate/up: N = 2F; out[m][j] = silu(y[m][j]) * y[m][F + j]
-template <typename T>
-__global__ __launch_bounds__(256) void k_epi_silu_mul(const float* __restrict__ part, int S, int M,
-                                                      int N, T* __restrict__ out) {
-  const int F = N / 2;
-  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (long)M * F) return;
-  const int m = (int)(idx / F), j = (int)(idx % F);
-  float gt = 0.f, up = 0.f;
-  for (int s = 0; s < S; ++s) {
-    gt += part[((size_t)s * M + m) * N + j];
-    up += part[((size_t)s * M + m) * N + F + j];
-  }
-  const float act = gt / (1.f + expf(-gt));
-  out[(size_t)m * F + j] = from_f32<T>(act * up);
-}
-
-template <typename T, int MT, int NTB, int KCB, int WK>
+template <typename T, int MT, int NTB, int KCB, int WK, bool SILU>
 void launch_gemm_t(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y,
-                   hipStream_t s) {
+                   void* act, hipStream_t s) {
   dim3 grid(p.n_blocks * p.splits);
-  hipLaunchKernelGGL((k_gemm<T, MT, NTB, KCB, WK>), grid, dim3(WK * 64), 0, s, (const T*)X, p.M, ldx,
-                     (const T*)W, p.N, p.K, Y, p.n_blocks, p.chunks_total, p.chunks_per_split);
+  hipLaunchKernelGGL((k_gemm<T, MT, NTB, KCB, WK, SILU>), grid, dim3(WK * 64), 0, s, (const T*)X, p.M,
+                     ldx, (const T*)W, p.N, p.K, Y, p.n_blocks, p.chunks_total, p.chunks_per_split,
+                     act, p.N / 2);
 }
 
 // Per row-tile count MT: (n-tiles per wave, X chunks held per lane).
@@ -166,26 +183,33 @@ constexpr int ntb_for(int mt) { return mt <= 4 ? 8 : 4; }
 constexpr int kcb_for(int mt) { return mt <= 2 ? 8 : (mt <= 4 ? 4 : 2); }
 
 template <typename T, int MT>
-int dispatch_mt(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y,
+int dispatch_mt(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y, void* act,
                 hipStream_t s) {
-  if (p.waves == 1)
-    launch_gemm_t<T, MT, ntb_for(MT), kcb_for(MT), 1>(p, X, ldx, W, Y, s);
-  else
-    launch_gemm_t<T, MT, ntb_for(MT), kcb_for(MT), 4>(p, X, ldx, W, Y, s);
+  if (p.silu) {
+    if (p.waves == 1)
+      launch_gemm_t<T, MT, ntb_for(MT), kcb_for(MT), 1, true>(p, X, ldx, W, Y, act, s);
+    else
+      launch_gemm_t<T, MT, ntb_for(MT), kcb_for(MT), 4, true>(p, X, ldx, W, Y, act, s);
+  } else {
+    if (p.waves == 1)
+      launch_gemm_t<T, MT, ntb_for(MT), kcb_for(MT), 1, false>(p, X, ldx, W, Y, act, s);
+    else
+      launch_gemm_t<T, MT, ntb_for(MT), kcb_for(MT), 4, false>(p, X, ldx, W, Y, act, s);
+  }
   return e3h::launch_status();
 }
 
 template <typename T>
 int dispatch_gemm(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y,
-                  hipStream_t s) {
+                  void* act, hipStream_t s) {
   switch (p.MT) {
-    case 1: return dispatch_mt<T, 1>(p, X, ldx, W, Y, s);
-    case 2: return dispatch_mt<T, 2>(p, X, ldx, W, Y, s);
-    case 3: return dispatch_mt<T, 3>(p, X, ldx, W, Y, s);
-    case 4: return dispatch_mt<T, 4>(p, X, ldx, W, Y, s);
-    case 6: return dispatch_mt<T, 6>(p, X, ldx, W, Y, s);
-    case 8: return dispatch_mt<T, 8>(p, X, ldx, W, Y, s);
-    case 10: return dispatch_mt<T, 10>(p, X, ldx, W, Y, s);
+    case 1: return dispatch_mt<T, 1>(p, X, ldx, W, Y, act, s);
+    case 2: return dispatch_mt<T, 2>(p, X, ldx, W, Y, act, s);
+    case 3: return dispatch_mt<T, 3>(p, X, ldx, W, Y, act, s);
+    case 4: return dispatch_mt<T, 4>(p, X, ldx, W, Y, act, s);
+    case 6: return dispatch_mt<T, 6>(p, X, ldx, W, Y, act, s);
+    case 8: return dispatch_mt<T, 8>(p, X, ldx, W, Y, act, s);
+    case 10: return dispatch_mt<T, 10>(p, X, ldx, W, Y, act, s);
     default: return EAGLE3_EUNSUPPORTED;
   }
 }
@@ -197,8 +221,9 @@ namespace e3h {
 // Plan: single-wave workgroups when the n-blocks alone fill the chip (the LM head);
 // otherwise four-wave workgroups and a k-split that brings the grid to about 256
 // workgroups, keeping at least one X block of chunks per wave.
-GemmPlan plan_gemm(int M, int N, int K, int dtype) {
+GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu) {
   GemmPlan p;
+  p.silu = silu;
   p.M = M;
   p.N = N;
   p.K = K;
@@ -227,17 +252,24 @@ GemmPlan plan_gemm(int M, int N, int K, int dtype) {
     if (splits > max_splits) splits = max_splits;
     if (splits < 1) splits = 1;
   }
+  if (silu) {
+    // gate/up pairs: NTB/2 gate tiles per wave and one k-split
+    p.n_blocks = (N / 2 + 16 * (ntb / 2) - 1) / (16 * (ntb / 2));
+    p.waves = p.n_blocks >= 768 ? 1 : 4;
+    splits = 1;
+  }
   p.chunks_per_split = (p.chunks_total + splits - 1) / splits;
   p.splits = (p.chunks_total + p.chunks_per_split - 1) / p.chunks_per_split;
   return p;
 }
 
 int launch_gemm(const GemmPlan& p, int dtype, const void* X, int ldx, const void* W, float* Ypart,
-                hipStream_t s, const char* tag) {
+                hipStream_t s, const char* tag, void* act) {
   if (p.MT == 0) return EAGLE3_EUNSUPPORTED;
+  if (p.silu && (!act || (p.N / 2) % (16 * (p.NT / 2)))) return EAGLE3_EUNSUPPORTED;
   ProfScope ps(tag, s);
-  if (dtype == EAGLE3_BF16) return dispatch_gemm<bf16>(p, X, ldx, W, Ypart, s);
-  return dispatch_gemm<float>(p, X, ldx, W, Ypart, s);
+  if (dtype == EAGLE3_BF16) return dispatch_gemm<bf16>(p, X, ldx, W, Ypart, act, s);
+  return dispatch_gemm<float>(p, X, ldx, W, Ypart, act, s);
 }
 
 int launch_epi_sum(const GemmPlan& p, const float* part, float* out, const float* resid,
@@ -246,20 +278,6 @@ int launch_epi_sum(const GemmPlan& p, const float* part, float* out, const float
   const long total = (long)p.M * p.N / 4;
   hipLaunchKernelGGL(k_epi_sum, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part,
                      p.splits, p.M, p.N, out, resid);
-  return launch_status();
-}
-
-int launch_epi_silu_mul(const GemmPlan& p, const float* part, int dtype, void* out, hipStream_t s,
-                        const char* tag) {
-  ProfScope ps(tag, s);
-  const long total = (long)p.M * (p.N / 2);
-  dim3 grid((unsigned)((total + 255) / 256));
-  if (dtype == EAGLE3_BF16)
-    hipLaunchKernelGGL(k_epi_silu_mul<bf16>, grid, dim3(256), 0, s, part, p.splits, p.M, p.N,
-                       (bf16*)out);
-  else
-    hipLaunchKernelGGL(k_epi_silu_mul<float>, grid, dim3(256), 0, s, part, p.splits, p.M, p.N,
-                       (float*)out);
   return launch_status();
 }
 

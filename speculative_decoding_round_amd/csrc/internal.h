@@ -46,18 +46,18 @@ size_t accept_workspace(int T, int V);
 int accept_chunks(int V);
 
 // ---- GEMM ------------------------------------------------------------------------------
-// Y_part[split][m][n] = sum over the split's k of X[m][k] * W[n][k]  (fp32 partials).
+// Y_part[split][m][n] = sum over the split's k of X[m][k] * W[n][k]  (fp32 partials), or
+// with silu: W = [gate; up] ([2F, K]) and act[m][j] = silu(gate) * up written in dtype.
 struct GemmPlan {
   int M, N, K, MT, NT, n_blocks, splits, chunks_total, chunks_per_split, waves;
+  bool silu;
 };
-GemmPlan plan_gemm(int M, int N, int K, int dtype);
+GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu = false);
 int launch_gemm(const GemmPlan& p, int dtype, const void* X, int ldx, const void* W, float* Ypart,
-                hipStream_t s, const char* tag);
+                hipStream_t s, const char* tag, void* act = nullptr);
 
-// Epilogues over the split partials (all sums in split order).
+// out[m][n] = (resid ? resid[m][n] : 0) + sum_s part[s][m][n]  (split order)
 int launch_epi_sum(const GemmPlan& p, const float* part, float* out, const float* resid,
                    hipStream_t s, const char* tag);
-int launch_epi_silu_mul(const GemmPlan& p, const float* part, int dtype, void* out,
-                        hipStream_t s, const char* tag);
 
 }  // namespace e3h

@@ -222,13 +222,23 @@ __global__ __launch_bounds__(256) void k_accept_path(
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
     const float* pv = part_v + (size_t)(n0 + i) * n_chunks;
     const int* pi = part_i + (size_t)(n0 + i) * n_chunks;
-    float bv = pv[0];
-    int bi = pi[0];
-    for (int c = 1; c < n_chunks; ++c)
-      if (better(pv[c], pi[c], bv, bi)) {
-        bv = pv[c];
-        bi = pi[c];
+    float bv = kNegInf;
+    int bi = 0x7fffffff;
+    for (int c0 = 0; c0 < n_chunks; c0 += 8) {
+      float v8[8];
+      int i8[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        v8[u] = c0 + u < n_chunks ? pv[c0 + u] : kNegInf;
+        i8[u] = c0 + u < n_chunks ? pi[c0 + u] : 0x7fffffff;
       }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (better(v8[u], i8[u], bv, bi)) {
+          bv = v8[u];
+          bi = i8[u];
+        }
+    }
     y[i] = bi;
   }
   __syncthreads();

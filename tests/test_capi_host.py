@@ -92,11 +92,14 @@ def test_draft_validation_and_workspace(lib):
     assert 0 < ws < 512 << 20
     t_bad = Eagle3TreeCfg(depth=8, topk=10, width=10, n_nodes=60)   # 71 slots > 64
     assert lib.eagle3_draft_expand_workspace_size(ctypes.byref(w), ctypes.byref(t_bad), 1, 2048) == 0
-    st = lib.eagle3_draft_expand(ctypes.byref(w), ctypes.byref(t_bad), 1, 8, 8, 8, 8, 8, 8, 8, 2048,
-                                 8, 8, 8, 8, 8, None, 8, 1 << 30, None)
+    st = lib.eagle3_draft_expand(ctypes.byref(w), ctypes.byref(t_bad), 1, 256, 256, 256, 256, 256, 256,
+                                 256, 2048, 256, 256, 256, 256, 256, None, 256, 1 << 30, None)
     assert st == -2
-    st = lib.eagle3_draft_expand(ctypes.byref(w), ctypes.byref(t), 1, 8, 8, 8, 8, 8, 8, 8, 2048,
-                                 8, 8, 8, 8, 8, None, 8, 16, None)
+    st = lib.eagle3_draft_expand(ctypes.byref(w), ctypes.byref(t), 1, 256, 256, 256, 256, 256, 256,
+                                 256, 2048, 256, 256, 256, 256, 256, None, 256, 16, None)
     assert st == -3
+    st = lib.eagle3_draft_expand(ctypes.byref(w), ctypes.byref(t), 1, 264, 256, 256, 256, 256, 256,
+                                 256, 2048, 256, 256, 256, 256, 256, None, 256, 1 << 30, None)
+    assert st == -1   # misaligned h_low
     w.head_dim = 80
     assert lib.eagle3_draft_expand_workspace_size(ctypes.byref(w), ctypes.byref(t), 1, 2048) == 0
