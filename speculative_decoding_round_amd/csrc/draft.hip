@@ -439,6 +439,19 @@ __device__ __forceinline__ bool cand_better(float sa, int ia, float sb_, int ib)
 
 constexpr int SEL_MAXR = 16;   // rows (W) per request handled by one workgroup
 
+// Number of entries f in [lo, hi) that beat entry e (score desc, index asc); `sc` is LDS,
+// 16-byte aligned at lo (a multiple of 4), padded with -inf up to a multiple of 4.
+__device__ __forceinline__ int rank_of(const float* sc, int lo, int hi, float sa, int e) {
+  int rank = 0;
+#pragma unroll 4
+  for (int f = lo; f < hi; f += 4) {
+    const floatx4 v = *reinterpret_cast<const floatx4*>(sc + f);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rank += (v[q] > sa || (v[q] == sa && f + q < e)) ? 1 : 0;
+  }
+  return rank;
+}
+
 __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, int N, int S, int PMAX,
                                                  int R, int n_chunks, const float* __restrict__ cv,
                                                  const int* __restrict__ ci,
@@ -454,18 +467,35 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
   __shared__ float s_val[SEL_MAXR][KMAX];
   __shared__ int s_id[SEL_MAXR][KMAX];
   __shared__ float s_lse[SEL_MAXR];
-  __shared__ float ssc[1024];
+  __shared__ __attribute__((aligned(16))) float ssc[1024 + 4];
   __shared__ int sdep[1024];
-  __shared__ int skeep[1024];
+  __shared__ int stok[1024];
+  __shared__ int sps[1024];
   __shared__ int slab[1024];
+  __shared__ int s_wave_cnt[16];
   __shared__ int s_valid[SEL_MAXR];
   __shared__ float s_score[SEL_MAXR];
   __shared__ uint64_t s_mask[SEL_MAXR];
+  __shared__ int s_cand[SEL_MAXR];
   __shared__ int s_count;
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int sb = step == 0 ? 0 : 1 + (step - 1) * W;
-  if (threadIdx.x == 0) s_count = cs.count[b];
+  const bool last = step + 1 == D;
+  const int n_before = cs.count[b];
+  int32_t* ctok = cs.tok + (size_t)b * PMAX;
+  int32_t* cps = cs.pslot + (size_t)b * PMAX;
+  int32_t* cdep = cs.depth + (size_t)b * PMAX;
+  float* csc = cs.score + (size_t)b * PMAX;
+  // the last step ranks the whole pool: stage the earlier candidates in LDS now
+  if (last) {
+    for (int e = threadIdx.x; e < n_before; e += blockDim.x) {
+      ssc[e] = csc[e];
+      sdep[e] = cdep[e];
+      stok[e] = ctok[e];
+      sps[e] = cps[e];
+    }
+  }
 
   // ---- phase 1: per-row top-K merge and log-sum-exp (every load issued first)
   if (w < R) {
@@ -474,6 +504,7 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
     const int valid = st.valid[sidx];
     const float score0 = st.score[sidx];
     const uint64_t mk = st.mask[sidx];
+    const int cand0 = st.cand[sidx];
     const bool ok0 = lane < n_chunks, ok1 = lane + 64 < n_chunks;
     const float cm0 = ok0 ? cmax[(size_t)m * n_chunks + lane] : kNegInf;
     const float cm1 = ok1 ? cmax[(size_t)m * n_chunks + lane + 64] : kNegInf;
@@ -487,6 +518,7 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
       s_valid[w] = valid;
       s_score[w] = score0;
       s_mask[w] = mk;
+      s_cand[w] = cand0;
     }
     if (valid) {
       const float mx = wave_max(fmaxf(cm0, cm1));
@@ -515,92 +547,85 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
   }
   __syncthreads();
 
-  // ---- phase 2: children, then the next frontier or the final prune
-  const int n_before = s_count;
+  // ---- phase 2: children of this step's nodes (LDS), then the next frontier or the prune
   int nE = 0;  // valid slots form a prefix of the step's slots
   for (int j = 0; j < R; ++j) nE += s_valid[j] ? 1 : 0;
   const int n_new = nE * K;
   const int n_total = n_before + n_new;
-  int32_t* ctok = cs.tok + (size_t)b * PMAX;
-  int32_t* cps = cs.pslot + (size_t)b * PMAX;
-  int32_t* cdep = cs.depth + (size_t)b * PMAX;
-  float* csc = cs.score + (size_t)b * PMAX;
   for (int e = threadIdx.x; e < n_new; e += blockDim.x) {
     const int j = e / K, rk = e % K;
-    const int slot = sb + j;
     const int ci_ = n_before + e;
-    const float lp = s_val[j][rk] - s_lse[j];
-    const float sc = s_score[j] + lp;
-    ctok[ci_] = s_id[j][rk];
-    cps[ci_] = slot;
-    cdep[ci_] = step + 1;
-    csc[ci_] = sc;
-    ssc[ci_] = sc;
+    ssc[ci_] = s_score[j] + (s_val[j][rk] - s_lse[j]);
     sdep[ci_] = step + 1;
+    stok[ci_] = s_id[j][rk];
+    sps[ci_] = sb + j;
   }
-  if (step + 1 == D) {
-    for (int e = threadIdx.x; e < n_before; e += blockDim.x) {
-      ssc[e] = csc[e];
-      sdep[e] = cdep[e];
-    }
-  }
+  if (threadIdx.x < 4) ssc[n_total + threadIdx.x] = kNegInf;
   __syncthreads();
-  if (step + 1 < D) {
+  if (!last) {
     // rank the new candidates; the W best take the next step's slots
     const int nsb = 1 + step * W;
+    const int lo = n_before & ~3;
     for (int e = threadIdx.x; e < n_new; e += blockDim.x) {
       const int ia = n_before + e;
       const float sa = ssc[ia];
-      int rank = 0;
-      for (int f = 0; f < n_new; ++f) rank += cand_better(ssc[n_before + f], n_before + f, sa, ia) ? 1 : 0;
+      // entries [lo, n_before) are not new candidates; rank_of counts them, so they are
+      // counted again with the same test and removed
+      int rank = rank_of(ssc, lo, n_total, sa, ia);
+      for (int f = lo; f < n_before; ++f) rank -= (ssc[f] > sa || (ssc[f] == sa && f < ia)) ? 1 : 0;
       if (rank < W) {
         const int slot = nsb + rank;
         const int i = b * S + slot;
-        const int ps = cps[ia];
-        st.tok[i] = ctok[ia];
+        const int ps = sps[ia];
+        st.tok[i] = stok[ia];
         st.parent[i] = ps;
         st.valid[i] = 1;
         st.score[i] = sa;
         st.cand[i] = ia;
         st.mask[i] = s_mask[ps - sb] | (1ull << slot);
-        if (dbg_tok) dbg_tok[i] = ctok[ia];
+        if (dbg_tok) dbg_tok[i] = stok[ia];
         if (dbg_par) dbg_par[i] = ps;
       }
+      ctok[ia] = stok[ia];
+      cps[ia] = sps[ia];
+      cdep[ia] = step + 1;
+      csc[ia] = sa;
     }
     if (threadIdx.x == 0) cs.count[b] = n_total;
     return;
   }
-  // final prune: keep the N best of the whole pool, relabel in level order
-  for (int e = threadIdx.x; e < n_total; e += blockDim.x) {
-    const float sa = ssc[e];
-    int rank = 0;
-    for (int f = 0; f < n_total; ++f) rank += cand_better(ssc[f], f, sa, e) ? 1 : 0;
-    skeep[e] = rank < N ? 1 : 0;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < n_total; e += blockDim.x) {
-    int lab = -1;
-    if (skeep[e]) {
-      lab = 1;
-      const int de = sdep[e];
-      for (int f = 0; f < n_total; ++f)
-        if (skeep[f] && (sdep[f] < de || (sdep[f] == de && f < e))) ++lab;
+  // final prune: keep the N best of the whole pool.  Candidates are created depth by depth,
+  // so (depth asc, creation asc) order is creation order and the new labels are 1 + the
+  // number of kept candidates created earlier (a ballot prefix count).
+  for (int base = 0; base < n_total; base += blockDim.x) {
+    const int e = base + threadIdx.x;
+    bool keep = false;
+    if (e < n_total) keep = rank_of(ssc, 0, n_total, ssc[e], e) < N;
+    const uint64_t bal = __ballot(keep);
+    if (lane == 0) s_wave_cnt[w] = __popcll(bal);
+    __syncthreads();
+    int before = base == 0 ? 0 : slab[base - 1] + 1;
+    for (int q = 0; q < w; ++q) before += s_wave_cnt[q];
+    const int within = __popcll(bal & ((1ull << lane) - 1ull));
+    if (e < n_total) {
+      if (!keep) sdep[e] = -1;  // -1 marks dropped
+      slab[e] = before + within + (keep ? 1 : 0) - 1;
     }
-    slab[e] = lab;
+    __syncthreads();
   }
-  __syncthreads();
   const int n_keep = min(N, n_total);
   const size_t ob = (size_t)b * (N + 1);
   for (int e = threadIdx.x; e < n_total; e += blockDim.x) {
-    if (!skeep[e]) continue;
-    const int lab = slab[e];
-    const int ps = cps[e];
+    if (sdep[e] < 0) continue;
+    const int lab = slab[e] + 1;
+    const int ps = sps[e];
     int plab = 0;
     if (ps > 0) {
-      const int pc = st.cand[b * S + ps];
-      plab = (pc >= 0 && pc < n_total) ? slab[pc] : -1;
+      // the parent slot's candidate: a slot of this step (LDS) or of an earlier one
+      const int pc = (ps >= sb && ps < sb + R) ? s_cand[ps - sb] : st.cand[b * S + ps];
+      plab = (pc >= 0 && pc < n_total && sdep[pc] >= 0) ? slab[pc] + 1 : -1;
     }
-    out_tok[ob + lab] = ctok[e];
+    out_tok[ob + lab] = stok[e];
     out_par[ob + lab] = plab;
     out_dep[ob + lab] = sdep[e];
     out_score[ob + lab] = ssc[e];
