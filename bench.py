@@ -33,6 +33,9 @@ def parse():
     ap.add_argument("--workload", default="llama8b", choices=["llama8b", "batch16", "llama70b", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel", default="gemm_lm_head", help="kernel timed for the roofline")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (for scaling HBM byte "
+                         "counters against a kernel of known traffic)")
     return ap.parse_args()
 
 
@@ -105,6 +108,19 @@ class Round:
                         seed=20260101, round=self.round, max_depth=s.depth, workspace=self.ws_acc,
                         out=self.acc_out)
         self.round += 1
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per LM-head launch measured by rocprofv3 counters (profiles/), or None if
+    they were taken on another workload or on a different GEMM kernel source."""
+    from speculative_decoding_round_amd import profsum
+    path = os.path.join(ROOT, "profiles", f"gemm_lm_head_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = dict(line.split(": ", 1) for line in open(path).read().splitlines() if ": " in line)
+    if kv.get("gemm_source_sha256_16") != profsum.gemm_source_hash():
+        return None
+    return int(kv["traffic_bytes_per_launch"])
 
 
 def lm_head_bytes(shape, M):
@@ -217,10 +233,17 @@ def main():
                    "verified_nodes_per_round": n_verified, "temperature": shape.temperature},
         "roofline": {"kernel": args.kernel, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_launch_us": round(k_avg_ms * 1e3, 2),
+                     "traffic": recorded_traffic(args.workload), "avg_launch_us": round(k_avg_ms * 1e3, 2),
                      "launches": k_n, "algorithmic_bytes_per_launch": int(bytes_avg)},
         "wall_s_timed": round(wall, 3),
     }
+    if args.copy_calibration_mb > 0:
+        n = args.copy_calibration_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = n
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(rnd)
     print(json.dumps(line), flush=True)
