@@ -164,7 +164,7 @@ def cpu_baseline(rnd: Round):
         def filt(b, P, sp=sp):
             keep = np.zeros(P, dtype=bool)
             if sp < S:
-                ch = -(-P // S)
+                ch = (-(-P // S) + 127) // 128 * 128
                 keep[min(P, sp * ch):min(P, sp * ch + ch)] = True
             return keep, np.full(rnd.n1, sp == S)
         o, l = O.tree_attention(vi["q"], vi["k_tree"], vi["v_tree"], cu, mask, vi["kpre"],

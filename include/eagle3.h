@@ -185,16 +185,18 @@ EAGLE3_API int eagle3_build_tree_mask(int B, int T, const int32_t* cu_nodes, con
  * prefix keys 0..P_b-1 (all visible) and the tree keys j with mask bit j set, scores
  * scale * q.k.  The prefix is cut into S splits, the tree keys form one more partial:
  *  o_part [S+1, T, Hq, Dh] fp32 and lse_part [S+1, T, Hq] fp32 receive the partials
- *  (partial s < S covers prefix keys [s*ceil(P_b/S), (s+1)*ceil(P_b/S)); partial S covers
- *  the tree keys); an empty partial has O = 0, LSE = -inf.  If `o` is not NULL the partials
+ *  (with C_b = ceil(P_b/S) rounded up to a multiple of 128, partial s < S covers prefix
+ *  keys [s*C_b, (s+1)*C_b) clipped to P_b; partial S covers the tree keys); an empty
+ *  partial has O = 0, LSE = -inf.  If `o` is not NULL the partials
  *  are also merged (as eagle3_lse_merge) into o [T, Hq, Dh] (dtype) and lse [T, Hq] fp32;
  *  then o_part/lse_part may be NULL and the workspace holds them.
  *
  *  q [T, Hq, Dh], k_tree, v_tree [T, Hkv, Dh], kpre, vpre [sum P_b, Hkv, Dh]: dtype
  *  cu_nodes [B+1], cu_prefix [B+1]: int32 device; mask [T, W64] as built above
- *  max_nodes, max_prefix: host upper bounds per request; n_splits: S (0 = automatic: about
- *  1024 workgroups, at least 128 keys per split and 64-row block; the same arguments give
- *  the same S in eagle3_tree_attention_num_splits).  Dh must be 64 or 128.
+ *  max_nodes, max_prefix: host upper bounds per request; n_splits: S in 1..256 (0 =
+ *  automatic: about as many workgroups as the chip holds at once, each split at least one
+ *  key tile and twice as many keys as its row block has query rows; the same arguments
+ *  give the same S in eagle3_tree_attention_num_splits).  Dh must be 64 or 128.
  * ------------------------------------------------------------------------------------ */
 EAGLE3_API int eagle3_tree_attention_num_splits(int B, int Hq, int Hkv, int max_nodes,
                                                 int max_prefix, int n_splits);
@@ -216,7 +218,8 @@ EAGLE3_API int eagle3_tree_attention(int B, int T, int Hq, int Hkv, int Dh, int 
  * LSE = m + ln sum_s w_s.  Partials with LSE = -inf weigh 0; a row whose partials are all
  * -inf gives O = 0 and LSE = -inf.
  *  o_part [S, rows, Dh] fp32, lse_part [S, rows] fp32 -> o [rows, Dh] (out_dtype),
- *  lse [rows] fp32 (may be NULL).  S >= 1; Dh % 4 == 0.
+ *  lse [rows] fp32 (may be NULL).  1 <= S <= 512; Dh % 4 == 0 and Dh <= 128 (else
+ *  EAGLE3_EUNSUPPORTED).
  * ------------------------------------------------------------------------------------ */
 EAGLE3_API int eagle3_lse_merge(int S, int rows, int Dh, const float* o_part, const float* lse_part,
                      int out_dtype, void* o, float* lse, void* stream);

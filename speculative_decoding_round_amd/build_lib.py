@@ -31,9 +31,16 @@ CFLAGS = [
 ]
 
 
+# Per-file additions.  attention.hip: keep MFMA accumulators in VGPRs (its kernels fit in
+# 256 VGPRs; the AGPR form costs a copy for every softmax rescale and score read).
+FILE_FLAGS = {
+    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC] + CFLAGS + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + CFLAGS + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -6,6 +6,8 @@
 // S^T = K Q^T with 16x16 MFMA so that every lane owns one query row, the online softmax
 // runs in the log2 domain, and O^T += V^T P^T consumes the probabilities straight from the
 // score registers.  Tree keys are masked per row by the ancestor bitmask.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -14,6 +16,10 @@ using namespace e3;
 namespace {
 
 constexpr int KT = 64;     // keys per tile
+
+// Keys per prefix split: ceil(P / S) rounded up to a multiple of 128, so that every split
+// but the last is a whole number of key tiles of either kernel.
+__device__ __forceinline__ int split_keys(int P, int S) { return ((P + S - 1) / S + 127) / 128 * 128; }
 constexpr int ROWS = 64;   // query rows per workgroup (16 per wave)
 
 template <typename T, int DH>
@@ -43,6 +49,7 @@ struct DevArgs {
   const int32_t* p_cu;
   float scale_log2;
   int S;
+  int n_rb;   // row blocks per (request, KV head) (bf16 kernel)
   float* o_part;
   float* lse_part;
 };
@@ -73,7 +80,7 @@ __global__ __launch_bounds__(256) void k_tree_attn(DevArgs a) {
   if (!tree) {
     const int p0 = a.p_cu ? a.p_cu[b] : 0;
     const int P = a.p_cu ? a.p_cu[b + 1] - p0 : 0;
-    const int chunk = (P + a.S - 1) / a.S;
+    const int chunk = split_keys(P, a.S);
     k_lo = min(P, split * chunk);
     k_hi = min(P, k_lo + chunk);
     kbase = reinterpret_cast<const T*>(a.kp) + ((size_t)p0 * a.Hkv + c) * DH;
@@ -237,53 +244,440 @@ __global__ __launch_bounds__(256) void k_tree_attn(DevArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// LSE merge: one thread per (row, 4 dims); partials merged in split order.  The split
-// LSEs are read first (independent loads), then the weighted partials, eight at a time.
+// bf16 attention with LDS-DMA staged K/V (gfx950).
+//
+// K and V tiles go from HBM straight into LDS (global_load_lds, 16 bytes per lane, no
+// register staging) through an NST-deep ring of stages, so several tiles are in flight
+// per workgroup.  A stage holds WK sub-tiles of KTW keys, one per key group of waves;
+// the WR = 4 / WK waves of a key group own disjoint query-row tiles and share its
+// sub-tile.  With WK > 1 the key groups keep separate softmax states for the same rows,
+// combined in LDS at the end.
+//
+// A key row's 16-byte chunks are stored XOR-swizzled (chunk c of key k at position
+// c ^ swz(k)) so that both LDS read patterns are bank-conflict free: the 16 keys of one
+// K operand read at a fixed chunk, and the 4 keys x 2 chunks of one transpose read.
+// V is consumed through ds_read_b64_tr_b16: within each 16-lane group, the lane at
+// (key row r, dim quad q) supplies the address of V[key0 + r][dim0 + 4q], and lane j of
+// the group receives V[key0 .. key0+3][dim0 + j], which is the MFMA operand layout
+// (4 consecutive keys of one dimension) without a transpose on store.
+//
+// Scores: S^T = K Q^T (16x16x32 MFMA, K from LDS as operand A, the wave's query rows
+// stationary as operand B), so lane l holds row l % 16, keys 4*(l/16) + i of each 16-key
+// block.  P^T feeds O^T += V^T P^T with the k-order {4g..4g+3, 16+4g..16+4g+3} on both
+// operands.  The softmax runs in the log2 domain.
 // ---------------------------------------------------------------------------------------
-template <typename T>
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int CPR>
+__device__ __forceinline__ int kv_swz(int key) {
+  if constexpr (CPR == 16) return ((key & 7) << 1) | ((key >> 3) & 1);
+  else return ((key & 3) << 1) | ((key >> 2) & 1);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// all of this wave's LDS reads done, then the workgroup barrier (no global-memory wait)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int DH, int QT, int WK, int KTW, int NST>
+struct DmaCfg {
+  static constexpr int CPR = DH / 8;                        // 16-byte chunks per key row
+  static constexpr int WR = 4 / WK;                         // row waves per key group
+  static constexpr int ROWS = WR * QT * 16;                 // query rows per workgroup
+  static constexpr int KITER = WK * KTW;                    // keys per iteration
+  static constexpr int SUB = KTW * CPR * 16;                // bytes of one K (or V) sub-tile
+  static constexpr int STAGE = WK * 2 * SUB;                // bytes per stage
+  static constexpr int PER = STAGE / 4096;                  // DMA instructions per thread per stage
+  static constexpr int MERGE = (WK - 1) * WR * QT * (DH / 16) * 64 * 16 + 2 * (WK - 1) * WR * QT * 64 * 4;
+  static constexpr int LDS = NST * STAGE > MERGE ? NST * STAGE : MERGE;
+  static_assert(STAGE % 4096 == 0, "stage must be a whole number of 4 KB rounds");
+  static_assert(KTW % 32 == 0, "sub-tile must hold whole 32-key PV steps");
+  static_assert(PER <= 16 && PER * (NST - 1) <= 63, "outstanding DMA must fit the vmcnt counter");
+  static_assert(NST >= 2 && NST <= 4, "the wait schedule covers 2..4 stages");
+};
+
+// Softmax reference: rows keep a reference max m (log2 domain) and exponentiate against
+// it; m is raised (and O, l rescaled) only when some row of the wave sees a score more
+// than 2^8 above its reference, so p <= 2^8 and the accumulator is rarely touched.
+constexpr float kRescaleLog2 = 8.f;
+
+template <int DH, int QT, int WK, int KTW, int NST>
+__global__ __launch_bounds__(256) void k_tree_attn_dma(DevArgs a) {
+  using C = DmaCfg<DH, QT, WK, KTW, NST>;
+  constexpr int CPR = C::CPR, WR = C::WR, NDT = DH / 16, NDC = DH / 32, NST16 = KTW / 16;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  __shared__ uint64_t smask[4][QT][16][4];
+
+  // Workgroups that share K/V (the row blocks of one request, KV head and split) are
+  // numbered so that they fall on the same XCD (workgroups go to XCDs round-robin), where
+  // they share that XCD's L2.
+  const int n_groups = a.B * a.Hkv * (a.S + 1);
+  const int id = blockIdx.x, xcd = id % 8, t = id / 8;
+  const int rbk = t % a.n_rb;
+  const int grp = (t / a.n_rb) * 8 + xcd;
+  if (grp >= n_groups) return;
+  const int split = grp % (a.S + 1);
+  const int bc = grp / (a.S + 1);
+  const int b = bc / a.Hkv;
+  const int c = bc % a.Hkv;
+  const int q0 = a.q_cu ? a.q_cu[b] : b * a.q_stride;
+  const int nq = a.q_cu ? a.q_cu[b + 1] - q0 : a.q_stride;
+  const int R = nq * a.G;
+  const int rb0 = rbk * C::ROWS;
+  if (rb0 >= R) return;
+
+  const bool tree = split == a.S;
+  int k_lo = 0, k_hi = 0;
+  const bf16* kbase;
+  const bf16* vbase;
+  if (!tree) {
+    const int p0 = a.p_cu ? a.p_cu[b] : 0;
+    const int P = a.p_cu ? a.p_cu[b + 1] - p0 : 0;
+    const int chunk = split_keys(P, a.S);
+    k_lo = min(P, split * chunk);
+    k_hi = min(P, k_lo + chunk);
+    kbase = reinterpret_cast<const bf16*>(a.kp) + ((size_t)p0 * a.Hkv + c) * DH;
+    vbase = reinterpret_cast<const bf16*>(a.vp) + ((size_t)p0 * a.Hkv + c) * DH;
+  } else {
+    const int t0 = a.kt_cu ? a.kt_cu[b] : b * a.kt_stride;
+    k_hi = a.kt_cu ? a.kt_cu[b + 1] - t0 : a.kt_count;
+    kbase = reinterpret_cast<const bf16*>(a.kt) + ((size_t)t0 * a.Hkv + c) * DH;
+    vbase = reinterpret_cast<const bf16*>(a.vt) + ((size_t)t0 * a.Hkv + c) * DH;
+  }
+  const int kstride = a.Hkv * DH;   // elements between consecutive keys
+  const int n_it = k_hi > k_lo ? (k_hi - k_lo + C::KITER - 1) / C::KITER : 0;
+  const float sc = a.scale_log2;    // > 0
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wk = w / WR, wr = w % WR;
+  const int r16 = lane & 15, g = lane >> 4;
+
+  // this wave's query rows (operand B of S^T = K Q^T); in the tree split, their mask words
+  // go to this wave's own LDS slots (one word is read back per key tile)
+  u32x4 qv[QT][NDC];
+  int rowid[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int r = rb0 + (wr * QT + qt) * 16 + r16;
+    const bool ok = r < R;
+    rowid[qt] = ok ? r : -1;
+    const int node = ok ? r / a.G : 0;
+    const int head = c * a.G + (ok ? r % a.G : 0);
+    const bf16* qp = reinterpret_cast<const bf16*>(a.q) + ((size_t)(q0 + node) * a.Hq + head) * DH;
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) qv[qt][dc] = ok ? ld16(qp + dc * 32 + g * 8) : u32x4{0, 0, 0, 0};
+    if (tree) smask[w][qt][r16][g] = (ok && g < a.W64) ? a.mask[(size_t)(q0 + node) * a.W64 + g] : 0ull;
+  }
+
+  // DMA: thread chunk q = (u*4 + w)*64 + lane of a stage, decoded as (key group, K|V,
+  // key, position); position p holds the key's chunk p ^ swz(key).  src[u] walks the
+  // stream one iteration at a time; the last iteration clamps keys to the range end.
+  const bf16* src[C::PER];
+  int relk[C::PER];
+#pragma unroll
+  for (int u = 0; u < C::PER; ++u) {
+    const int q = (u * 4 + w) * 64 + lane;
+    const int pos = q % CPR;
+    const int key = (q / CPR) % KTW;
+    const int tv = (q / (CPR * KTW)) % 2;
+    const int kg = q / (2 * CPR * KTW);
+    relk[u] = kg * KTW + key;
+    src[u] = (tv ? vbase : kbase) + (pos ^ kv_swz<CPR>(key)) * 8;
+  }
+  auto issue = [&](int it) {
+    char* st = smem + (it % NST) * C::STAGE;
+    const int t0 = k_lo + it * C::KITER;
+    const bool whole = t0 + C::KITER <= k_hi;
+#pragma unroll
+    for (int u = 0; u < C::PER; ++u) {
+      const int kabs = whole ? t0 + relk[u] : min(t0 + relk[u], k_hi - 1);
+      const bf16* p = src[u] + (uint32_t)kabs * (uint32_t)kstride;
+      __builtin_amdgcn_global_load_lds((const void*)p, (lds_void*)(st + (u * 4 + w) * 1024), 16, 0, 0);
+    }
+  };
+
+  floatx4 acc[QT][NDT];
+  float m_ref[QT], l_run[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m_ref[qt] = kNegInf;
+    l_run[qt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // per-lane LDS offsets (bytes within a sub-tile) of the K operand reads and V transpose reads
+  int koff[NST16][NDC];
+#pragma unroll
+  for (int st = 0; st < NST16; ++st)
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) {
+      const int key = st * 16 + r16;
+      koff[st][dc] = (key * CPR + ((dc * 4 + g) ^ kv_swz<CPR>(key))) * 16;
+    }
+  const int kr = (lane & 15) >> 2, dq = lane & 3;
+
+#pragma unroll
+  for (int s0 = 0; s0 < NST - 1; ++s0)
+    if (s0 < n_it) issue(s0);
+
+  for (int it = 0; it < n_it; ++it) {
+    if constexpr (NST >= 3) {
+      if (it + NST - 2 < n_it) wait_vm<C::PER * (NST - 2)>();
+      else if (it + 1 < n_it) wait_vm<C::PER * (NST - 3 > 0 ? NST - 3 : 0)>();
+      else wait_vm<0>();
+    } else {
+      wait_vm<0>();
+    }
+    lds_barrier();  // stage it complete for every wave; stage it-1 fully consumed
+    if (it + NST - 1 < n_it) issue(it + NST - 1);
+
+    const char* ks = smem + (it % NST) * C::STAGE + (wk * 2) * C::SUB;
+    const char* vs = ks + C::SUB;
+    const int kbase_it = k_lo + it * C::KITER + wk * KTW;
+
+    // raw scores S^T for NST16 blocks of 16 keys
+    floatx4 s[QT][NST16];
+#pragma unroll
+    for (int st = 0; st < NST16; ++st) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) s[qt][st] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(ks + koff[st][dc]);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) s[qt][st] = Mfma<bf16>::run(kv, qv[qt][dc], s[qt][st]);
+      }
+    }
+    // keys past the range end or outside the row's ancestor set -> -inf; whole prefix
+    // tiles need no mask
+    const int lim = k_hi - kbase_it;
+    if (tree || lim < KTW) {
+      const int word = (kbase_it >> 6) & 3, sh = kbase_it & 63;  // a sub-tile lies in one word
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const uint64_t bits = tree ? (smask[w][qt][r16][word] >> sh) >> (4 * g) : ~0ull;
+#pragma unroll
+        for (int st = 0; st < NST16; ++st)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool vis = st * 16 + 4 * g + i < lim && ((bits >> (st * 16 + i)) & 1ull);
+            if (!vis) s[qt][st][i] = kNegInf;
+          }
+      }
+    }
+    // online softmax against the reference max (scale > 0 is folded into the exponent)
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float tmax = kNegInf;
+#pragma unroll
+      for (int st = 0; st < NST16; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[qt][st][i]);
+      tmax = row_reduce(tmax, OpMax()) * sc;
+      if (__any(tmax > m_ref[qt] + kRescaleLog2)) {
+        const float m_new = fmaxf(m_ref[qt], tmax);
+        const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_ref[qt] - m_new);
+        l_run[qt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] *= alpha;
+        m_ref[qt] = m_new;
+      }
+      const float nm = m_ref[qt] == kNegInf ? 0.f : -m_ref[qt];
+      float psum = 0.f;
+#pragma unroll
+      for (int st = 0; st < NST16; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][st][i], sc, nm));
+          s[qt][st][i] = p;
+          psum += p;
+        }
+      l_run[qt] += psum;
+    }
+    // O^T += V^T P^T, 32 keys per step
+#pragma unroll
+    for (int pc = 0; pc < KTW / 32; ++pc) {
+      u32x4 pb[QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        bf16x8 p8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p8[i] = static_cast<bf16>(s[qt][2 * pc][i]);
+          p8[4 + i] = static_cast<bf16>(s[qt][2 * pc + 1][i]);
+        }
+        pb[qt] = __builtin_bit_cast(u32x4, p8);
+      }
+      const int ka = pc * 32 + 4 * g + kr, kb = ka + 16;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int gc = 2 * dt + (dq >> 1);
+        const int off = (dq & 1) * 8;
+        const char* pa = vs + (ka * CPR + (gc ^ kv_swz<CPR>(ka))) * 16 + off;
+        const char* pbp = vs + (kb * CPR + (gc ^ kv_swz<CPR>(kb))) * 16 + off;
+        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(pa));
+        const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(pbp));
+        const uint2 lu = __builtin_bit_cast(uint2, lo), hu = __builtin_bit_cast(uint2, hi);
+        const u32x4 va = u32x4{lu.x, lu.y, hu.x, hu.y};
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) acc[qt][dt] = Mfma<bf16>::run(va, pb[qt], acc[qt][dt]);
+      }
+    }
+  }
+
+  float l_tot[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) l_tot[qt] = row_reduce(l_run[qt], OpAdd());
+
+  if constexpr (WK > 1) {
+    // key groups 1.. hand their (m, l, O) to group 0 through LDS
+    __syncthreads();
+    floatx4* mo = reinterpret_cast<floatx4*>(smem);
+    float* ml = reinterpret_cast<float*>(smem + (WK - 1) * WR * QT * NDT * 64 * 16);
+    if (wk > 0) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const int slot = ((wk - 1) * WR + wr) * QT + qt;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) mo[(slot * NDT + dt) * 64 + lane] = acc[qt][dt];
+        ml[(2 * slot) * 64 + lane] = m_ref[qt];
+        ml[(2 * slot + 1) * 64 + lane] = l_tot[qt];
+      }
+    }
+    __syncthreads();
+    if (wk > 0) return;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float mm = m_ref[qt];
+#pragma unroll
+      for (int o = 1; o < WK; ++o) mm = fmaxf(mm, ml[(2 * (((o - 1) * WR + wr) * QT + qt)) * 64 + lane]);
+      const float e0 = m_ref[qt] == kNegInf ? 0.f : exp2f(m_ref[qt] - mm);
+      float lt = l_tot[qt] * e0;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] *= e0;
+#pragma unroll
+      for (int o = 1; o < WK; ++o) {
+        const int slot = ((o - 1) * WR + wr) * QT + qt;
+        const float mo_ = ml[(2 * slot) * 64 + lane];
+        const float eo = mo_ == kNegInf ? 0.f : exp2f(mo_ - mm);
+        lt += ml[(2 * slot + 1) * 64 + lane] * eo;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] += mo[(slot * NDT + dt) * 64 + lane] * eo;
+      }
+      m_ref[qt] = mm;
+      l_tot[qt] = lt;
+    }
+  }
+
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int r = rowid[qt];
+    if (r < 0) continue;
+    const int node = r / a.G;
+    const int head = c * a.G + r % a.G;
+    const size_t orow = ((size_t)split * a.q_rows_total + q0 + node) * a.Hq + head;
+    const float l = l_tot[qt];
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float* op = a.o_part + orow * DH;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<floatx4*>(op + dt * 16 + 4 * g) = acc[qt][dt] * inv;
+    if (g == 0) a.lse_part[orow] = l > 0.f ? (m_ref[qt] + log2f(l)) * kLn2 : kNegInf;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// LSE merge.  A row's split LSEs are read at once (one per lane or thread), giving
+// m = max and the weights w_s = e^{LSE_s - m} in LDS; the weighted partials are then
+// summed with eight loads in flight.  WPR = waves per row: with few splits one wave takes
+// a row (four rows per workgroup); with many, the four waves of a workgroup take the
+// splits s = w, w+4, ... of one row and their sums are added in wave order.  Every order
+// is fixed, so the result is deterministic.
+// ---------------------------------------------------------------------------------------
+constexpr int MERGE_MAX_S = 512;
+constexpr int MERGE_FEW_S = 16;   // up to this many splits: one wave per row
+
+template <typename T, int WPR>
 __global__ __launch_bounds__(256) void k_lse_merge(int S, int rows, int Dh,
                                                    const float* __restrict__ o_part,
                                                    const float* __restrict__ lse_part,
                                                    T* __restrict__ o, float* __restrict__ lse) {
-  const int d4 = Dh / 4;
-  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (long)rows * d4) return;
-  const int row = (int)(idx / d4), q = (int)(idx % d4);
-  float m = kNegInf;
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    float l8[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) l8[u] = s0 + u < S ? lse_part[(size_t)(s0 + u) * rows + row] : kNegInf;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) m = fmaxf(m, l8[u]);
+  constexpr int SW = WPR == 1 ? MERGE_FEW_S : MERGE_MAX_S;
+  __shared__ float sw[4 / WPR][SW];
+  __shared__ float red[32];
+  __shared__ floatx4 part[4][32];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int row = WPR == 1 ? blockIdx.x * 4 + w : blockIdx.x;
+  const int slot = WPR == 1 ? w : 0;
+  float m, wsum;
+  if constexpr (WPR == 1) {
+    if (row >= rows) return;   // whole wave; no block barrier below
+    const float l0 = lane < S ? lse_part[(size_t)lane * rows + row] : kNegInf;
+    m = wave_max(l0);
+    const float w0 = (m == kNegInf || l0 == kNegInf) ? 0.f : expf(l0 - m);
+    if (lane < S) sw[slot][lane] = w0;
+    wsum = wave_sum(w0);
+  } else {
+    const float l0 = tid < S ? lse_part[(size_t)tid * rows + row] : kNegInf;
+    const float l1 = tid + 256 < S ? lse_part[(size_t)(tid + 256) * rows + row] : kNegInf;
+    m = block_max(fmaxf(l0, l1), red);
+    const float w0 = (m == kNegInf || l0 == kNegInf) ? 0.f : expf(l0 - m);
+    const float w1 = (m == kNegInf || l1 == kNegInf) ? 0.f : expf(l1 - m);
+    if (tid < S) sw[0][tid] = w0;
+    if (tid + 256 < S) sw[0][tid + 256] = w1;
+    wsum = block_sum(w0 + w1, red);   // its barriers also order the LDS weights
   }
+  const int d4 = Dh / 4;                          // float4 columns of a row (<= 32)
+  const int s_first = WPR == 1 ? 0 : w, s_step = WPR == 1 ? 1 : 4;
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  if (m != kNegInf) {
-    for (int s0 = 0; s0 < S; s0 += 8) {
-      float w8[8];
-      floatx4 v8[8];
+  if (lane < d4) {
+    const float* base = o_part + (size_t)row * Dh + 4 * lane;
+    for (int s0 = s_first; s0 < S; s0 += 8 * s_step) {
+      floatx4 v[8];
+      float ww[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const bool ok = s0 + u < S;
-        const float ls = ok ? lse_part[(size_t)(s0 + u) * rows + row] : kNegInf;
-        w8[u] = ls == kNegInf ? 0.f : expf(ls - m);
-        v8[u] = ok ? *reinterpret_cast<const floatx4*>(o_part + ((size_t)(s0 + u) * rows + row) * Dh + 4 * q)
-                   : floatx4{0.f, 0.f, 0.f, 0.f};
+        const int sp = s0 + s_step * u;
+        ww[u] = sp < S ? sw[slot][sp] : 0.f;
+        v[u] = (sp < S && ww[u] != 0.f) ? *reinterpret_cast<const floatx4*>(base + (size_t)sp * rows * Dh)
+                                        : floatx4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (w8[u] != 0.f) acc += v8[u] * w8[u];
-        wsum += w8[u];
-      }
+      for (int u = 0; u < 8; ++u) acc += v[u] * ww[u];
     }
   }
+  if constexpr (WPR > 1) {
+    if (lane < d4) part[w][lane] = acc;
+    __syncthreads();
+    if (w != 0) return;
+    if (lane < d4) {
+      acc = part[0][lane] + part[1][lane];
+      acc += part[2][lane];
+      acc += part[3][lane];
+    }
+  }
+  if (lane >= d4) return;
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  T* op = o + (size_t)row * Dh + 4 * q;
+  T* op = o + (size_t)row * Dh + 4 * lane;
 #pragma unroll
   for (int i = 0; i < 4; ++i) op[i] = from_f32<T>(acc[i] * inv);
-  if (lse && q == 0) lse[row] = wsum > 0.f ? m + logf(wsum) : kNegInf;
+  if (lse && lane == 0) lse[row] = wsum > 0.f ? m + logf(wsum) : kNegInf;
 }
+
+// Workgroup shape of the bf16 kernel by query rows per (request, KV head):
+// 0: 32 rows, keys split over the 4 waves (one workgroup per CU);
+// 1: 64 rows, one 16-row tile per wave, keys shared (two workgroups per CU);
+// 2: 128 rows, two 16-row tiles per wave, keys shared (two workgroups per CU).
+inline int attn_cfg(int rows) { return rows <= 32 ? 0 : rows <= 64 ? 1 : 2; }
+inline int attn_cfg_rows(int cfg) { return cfg == 0 ? 32 : cfg == 1 ? 64 : 128; }
+inline int attn_cfg_keys(int cfg) { return cfg == 0 ? 128 : 32; }
+inline int attn_cfg_wgs(int cfg) { return cfg == 0 ? 256 : 512; }   // resident workgroups on the chip
 
 template <typename T, int DH>
 int launch_attn_t(const e3h::AttnArgs& h, hipStream_t s) {
@@ -310,9 +704,24 @@ int launch_attn_t(const e3h::AttnArgs& h, hipStream_t s) {
   a.S = h.S;
   a.o_part = h.o_part;
   a.lse_part = h.lse_part;
-  const int rb = (h.max_q_per_req * a.G + ROWS - 1) / ROWS;
-  dim3 grid(rb, h.B * h.Hkv, h.S + 1);
-  hipLaunchKernelGGL((k_tree_attn<T, DH>), grid, dim3(256), 0, s, a);
+  const int rows = h.max_q_per_req * a.G;
+  if constexpr (sizeof(T) == 2) {
+    auto go = [&](auto kern, int rows_wg) {
+      a.n_rb = (rows + rows_wg - 1) / rows_wg;
+      const long groups = (long)h.B * h.Hkv * (h.S + 1);
+      const long n = (groups + 7) / 8 * 8 * a.n_rb;
+      hipLaunchKernelGGL(kern, dim3((unsigned)n), dim3(256), 0, s, a);
+    };
+    switch (attn_cfg(rows)) {
+      case 0: go(k_tree_attn_dma<DH, 2, 4, 32, 2>, DmaCfg<DH, 2, 4, 32, 2>::ROWS); break;
+      case 1: go(k_tree_attn_dma<DH, 1, 1, 32, 4>, DmaCfg<DH, 1, 1, 32, 4>::ROWS); break;
+      default: go(k_tree_attn_dma<DH, 2, 1, 32, 4>, DmaCfg<DH, 2, 1, 32, 4>::ROWS); break;
+    }
+  } else {
+    const int rb = (rows + ROWS - 1) / ROWS;
+    dim3 grid(rb, h.B * h.Hkv, h.S + 1);
+    hipLaunchKernelGGL((k_tree_attn<T, DH>), grid, dim3(256), 0, s, a);
+  }
   return e3h::launch_status();
 }
 
@@ -320,16 +729,20 @@ int launch_attn_t(const e3h::AttnArgs& h, hipStream_t s) {
 
 namespace e3h {
 
-// Prefix splits: aim at ~1024 workgroups in total, but give every split at least
-// 128 keys per 64-row block so that a split's fp32 partial (64 rows x Dh x 4 B per row
-// block) stays at or below half of the bf16 K+V bytes it streams.
+// Prefix splits: about as many workgroups as the chip holds at once, but every split
+// keeps at least one iteration of keys and at least twice as many keys as the row block
+// has rows, so a split's fp32 partial stays at or below half of the bf16 K+V bytes it
+// streams.
 int attention_splits(int B, int Hkv, int rows_per_kv, int max_prefix, int n_splits) {
   if (n_splits > 0) return n_splits;
   if (max_prefix <= 0 || B <= 0 || Hkv <= 0) return 1;
-  const int rb = rows_per_kv > 0 ? (rows_per_kv + ROWS - 1) / ROWS : 1;
+  const int rows = rows_per_kv > 0 ? rows_per_kv : 1;
+  const int cfg = attn_cfg(rows);
+  const int rows_wg = attn_cfg_rows(cfg), kiter = attn_cfg_keys(cfg);
+  const long rb = (rows + rows_wg - 1) / rows_wg;
   const long base = (long)B * Hkv * rb;
-  long s = (1024 + base - 1) / base;
-  const long min_keys = 128L * rb;
+  long s = (attn_cfg_wgs(cfg) + base - 1) / base;
+  const long min_keys = std::max<long>(kiter, 2L * std::min(rows, rows_wg));
   const long max_s = (max_prefix + min_keys - 1) / min_keys;
   if (s > max_s) s = max_s;
   if (s > 256) s = 256;
@@ -353,15 +766,17 @@ int launch_tree_attention(const AttnArgs& a, hipStream_t s, const char* tag) {
 int launch_lse_merge(int S, int rows, int Dh, const float* o_part, const float* lse_part,
                      int out_dtype, void* o, float* lse, hipStream_t s, const char* tag) {
   if (rows <= 0) return EAGLE3_OK;
+  if (S > MERGE_MAX_S || Dh > 128 || Dh % 4) return EAGLE3_EUNSUPPORTED;
   ProfScope ps(tag, s);
-  const long n = (long)rows * (Dh / 4);
-  dim3 grid((unsigned)((n + 255) / 256));
-  if (out_dtype == EAGLE3_BF16)
-    hipLaunchKernelGGL(k_lse_merge<bf16>, grid, dim3(256), 0, s, S, rows, Dh, o_part, lse_part,
-                       (bf16*)o, lse);
-  else
-    hipLaunchKernelGGL(k_lse_merge<float>, grid, dim3(256), 0, s, S, rows, Dh, o_part, lse_part,
-                       (float*)o, lse);
+  const bool few = S <= MERGE_FEW_S;
+  const dim3 grid(few ? (rows + 3) / 4 : rows);
+  if (out_dtype == EAGLE3_BF16) {
+    if (few) hipLaunchKernelGGL((k_lse_merge<bf16, 1>), grid, dim3(256), 0, s, S, rows, Dh, o_part, lse_part, (bf16*)o, lse);
+    else hipLaunchKernelGGL((k_lse_merge<bf16, 4>), grid, dim3(256), 0, s, S, rows, Dh, o_part, lse_part, (bf16*)o, lse);
+  } else {
+    if (few) hipLaunchKernelGGL((k_lse_merge<float, 1>), grid, dim3(256), 0, s, S, rows, Dh, o_part, lse_part, (float*)o, lse);
+    else hipLaunchKernelGGL((k_lse_merge<float, 4>), grid, dim3(256), 0, s, S, rows, Dh, o_part, lse_part, (float*)o, lse);
+  }
   return launch_status();
 }
 

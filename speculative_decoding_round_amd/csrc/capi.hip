@@ -120,6 +120,7 @@ int eagle3_tree_attention_num_splits(int B, int Hq, int Hkv, int max_nodes, int 
                                      int n_splits) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || max_nodes < 0 || max_prefix < 0 || n_splits < 0)
     return EAGLE3_EINVAL;
+  if (n_splits > 256) return EAGLE3_EUNSUPPORTED;
   return attention_splits(B, Hkv, max_nodes * (Hq / Hkv), max_prefix, n_splits);
 }
 
@@ -144,7 +145,7 @@ int eagle3_tree_attention(int B, int T, int Hq, int Hkv, int Dh, int dtype, cons
     return EAGLE3_EINVAL;
   if (!dtype_ok(dtype)) return EAGLE3_EINVAL;
   if (Dh != 64 && Dh != 128) return EAGLE3_EUNSUPPORTED;
-  if (W64 > 4 || max_nodes > 64 * W64) return EAGLE3_EUNSUPPORTED;
+  if (W64 > 4 || max_nodes > 64 * W64 || n_splits > 256) return EAGLE3_EUNSUPPORTED;
   if (!(scale > 0.f)) return EAGLE3_EINVAL;
   if (T == 0) return EAGLE3_OK;
   if (!q || !k_tree || !v_tree || !cu_nodes || !mask) return EAGLE3_EINVAL;
@@ -195,6 +196,7 @@ int eagle3_tree_attention(int B, int T, int Hq, int Hkv, int Dh, int dtype, cons
 int eagle3_lse_merge(int S, int rows, int Dh, const float* o_part, const float* lse_part,
                      int out_dtype, void* o, float* lse, void* stream) {
   if (S < 1 || rows < 0 || Dh <= 0 || Dh % 4) return EAGLE3_EINVAL;
+  if (S > 512 || Dh > 128) return EAGLE3_EUNSUPPORTED;
   if (!dtype_ok(out_dtype)) return EAGLE3_EINVAL;
   if (rows == 0) return EAGLE3_OK;
   if (!o_part || !lse_part || !o) return EAGLE3_EINVAL;

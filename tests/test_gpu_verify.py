@@ -131,7 +131,7 @@ def test_tree_attention_matches_oracle(name, dt, Hq, Hkv, Dh, sizes, prefix, spl
         def filt(b, P, s=s):
             keep = np.zeros(P, dtype=bool)
             if s < S:
-                ch = -(-P // S)
+                ch = (-(-P // S) + 127) // 128 * 128   # split size: ceil(P/S) up to a multiple of 128
                 keep[min(P, s * ch):min(P, s * ch + ch)] = True
             return keep, np.full(sizes[b], s == S)
         o_s, l_s = O.tree_attention(vi["q"].cpu(), vi["k_tree"].cpu(), vi["v_tree"].cpu(),
