@@ -186,6 +186,53 @@ def test_draft_llama8b_full_size_sampled():
     check_teacher_forced(shape, w, di, out, 1, prefix, slots_per_request=chains)
 
 
+def test_draft_llama70b_full_size_sampled():
+    """The 70B-shaped drafter (d 8192, 64 q / 8 kv heads, FFN 28672, fusion 24576 -> 8192) for
+    4 requests over 8192-token prefixes: top-K and selection checked on every slot of every
+    request; floats teacher-forced on the root-to-leaf chain of one deepest slot each."""
+    need_gpu()
+    shape = synth.LLAMA70B
+    prefix = synth.prefix_lengths(shape, seed=71)
+    w, di, out = run_gpu(shape, prefix, 7070, 7071)
+    check_topk_on_gpu_logits(shape, out["debug"], shape.B)
+    check_selection_replay(shape, out, shape.B)
+    assert out["n_nodes"].tolist() == [shape.n_nodes + 1] * shape.B
+
+    def chain(b, nodes):
+        by = {n["slot"]: n for n in nodes}
+        s = [n["slot"] for n in nodes if n["depth"] == shape.depth - 1][0]
+        keep = set()
+        while s >= 0:
+            keep.add(s)
+            s = by[s]["parent_slot"]
+        return [by[x] for x in sorted(keep)]
+    check_teacher_forced(shape, w, di, out, shape.B, prefix, slots_per_request=chain)
+
+
+def test_draft_batch16_full_size_sampled():
+    """16 requests with the 8B-shaped drafter over ragged prefixes (uniform 512..4096):
+    160 evaluated rows per step.  Top-K and selection on every slot of every request; floats
+    teacher-forced on one root-to-leaf chain of requests 0, 7 and 15."""
+    need_gpu()
+    shape = synth.BATCH16
+    prefix = synth.prefix_lengths(shape, seed=161)
+    w, di, out = run_gpu(shape, prefix, 1616, 1617)
+    check_topk_on_gpu_logits(shape, out["debug"], shape.B)
+    check_selection_replay(shape, out, shape.B)
+
+    def chain(b, nodes):
+        if b not in (0, 7, 15):
+            return []
+        by = {n["slot"]: n for n in nodes}
+        s = max(nodes, key=lambda n: (n["depth"], -n["slot"]))["slot"]
+        keep = set()
+        while s >= 0:
+            keep.add(s)
+            s = by[s]["parent_slot"]
+        return [by[x] for x in sorted(keep)]
+    check_teacher_forced(shape, w, di, out, shape.B, prefix, slots_per_request=chain)
+
+
 def test_draft_ignores_stale_workspace_contents():
     """Unused evaluation slots sit inside the drafter's tree-key range (masked out); the
     round must not depend on what the workspace held before (here: all NaN bytes)."""
