@@ -285,72 +285,83 @@ __global__ __launch_bounds__(256) void k_epi_qkv(const float* __restrict__ part,
 }
 
 // ---------------------------------------------------------------------------------------
-// LM head top-K / log-sum-exp, pass 1: one wave per (row, chunk of 1024 logits).  Each lane
-// holds 16 logits (four float4 loads issued together) and sorts them with a fixed network;
-// the chunk's K winners (value desc, id asc) are drawn by K wave-argmax rounds over the
-// lanes' sorted heads, and its (max, sum e^{z-max}) by wave reductions.  No block barrier.
+// Exact top-K (value desc, id asc) over a wave, NV pairs per lane.
+// The threshold tau is the K-th largest lane maximum (K rounds of wave max; the lanes that
+// hold a round's maximum drop out), a lower bound on the K-th largest value, so the top K
+// are among the pairs with value >= tau.  When at most TK_CAP pairs pass, they are
+// compacted into this wave's LDS slots (positions from per-element ballots) and each is
+// ranked against all of them; the pair of rank r < K goes to out(r, ...).  Otherwise (many
+// ties at tau, or fewer than K finite lane maxima) K exact argmax rounds over all pairs are
+// used.  Ids must be distinct across the wave, except for padding pairs (value -inf).
+// `sv`, `si` hold TK_CAP entries of this wave's LDS.
 // ---------------------------------------------------------------------------------------
-constexpr int TK_CHUNK = 1024;
+constexpr int TK_CAP = 64;
 
-__device__ __forceinline__ void cswap(float& va, int& ia, float& vb, int& ib) {
-  // afterwards (va, ia) is the better of the two
-  if (better(vb, ib, va, ia)) {
-    const float tv = va;
-    const int ti = ia;
-    va = vb;
-    ia = ib;
-    vb = tv;
-    ib = ti;
+template <int NV, typename IdOf, typename Out>
+__device__ __forceinline__ void wave_topk(const float* v, IdOf id_of, int K, float* sv, int* si, Out out) {
+  const int lane = threadIdx.x & 63;
+  float lm = kNegInf;
+#pragma unroll
+  for (int e = 0; e < NV; ++e) lm = fmaxf(lm, v[e]);
+  float x = lm, tau = kNegInf;
+  for (int k = 0; k < K; ++k) {
+    tau = wave_max(x);
+    if (x == tau) x = kNegInf;
   }
-}
-
-// Sort 16 (value, id) pairs best-first with a bitonic network (static indices only).
-__device__ __forceinline__ void sort16(float* v, int* id) {
+  uint64_t bal[NV];
+  int total = 0;
 #pragma unroll
-  for (int k = 2; k <= 16; k <<= 1) {
+  for (int e = 0; e < NV; ++e) {
+    bal[e] = __ballot(v[e] >= tau);
+    total += __popcll(bal[e]);
+  }
+  if (total <= TK_CAP) {
+    int off = 0;
+    const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int l = i ^ j;
-        if (l > i) {
-          if ((i & k) == 0)
-            cswap(v[i], id[i], v[l], id[l]);
-          else
-            cswap(v[l], id[l], v[i], id[i]);
-        }
+    for (int e = 0; e < NV; ++e) {
+      if (v[e] >= tau) {
+        const int p = off + __popcll(bal[e] & below);
+        sv[p] = v[e];
+        si[p] = id_of(e);
       }
+      off += __popcll(bal[e]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < total) {
+      const float a = sv[lane];
+      const int ia = si[lane];
+      int r = 0;
+      for (int j = 0; j < total; ++j) r += better(sv[j], si[j], a, ia) ? 1 : 0;
+      if (r < K) out(r, a, ia);
+    }
+  } else {
+    // a pair that won a round is taken out by its bit, so that when fewer than K finite
+    // values exist the -inf padding is drawn in id order, each pair once
+    uint32_t gone = 0;
+    for (int k = 0; k < K; ++k) {
+      float bv = kNegInf;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int e = 0; e < NV; ++e)
+        if (!((gone >> e) & 1u)) argmax_pair(bv, bi, v[e], id_of(e));
+      wave_argmax(bv, bi);
+      if (lane == 0) out(k, bv, bi);
+#pragma unroll
+      for (int e = 0; e < NV; ++e)
+        if (id_of(e) == bi && v[e] == bv) gone |= 1u << e;
     }
   }
 }
 
-__device__ __forceinline__ void pop16(float* v, int* id) {
-#pragma unroll
-  for (int q = 0; q < 15; ++q) {
-    v[q] = v[q + 1];
-    id[q] = id[q + 1];
-  }
-  v[15] = kNegInf;
-  id[15] = 0x7fffffff;
-}
-
-// Top 16 of two best-first lists of 16, best-first in (v, id): the elementwise better of
-// v[i] and v2[15 - i] is a bitonic sequence holding the 16 best, which a bitonic merge sorts.
-__device__ __forceinline__ void merge16(float* v, int* id, const float* v2, const int* id2) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    if (better(v2[15 - i], id2[15 - i], v[i], id[i])) {
-      v[i] = v2[15 - i];
-      id[i] = id2[15 - i];
-    }
-#pragma unroll
-  for (int j = 8; j > 0; j >>= 1)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int l = i ^ j;
-      if (l > i) cswap(v[i], id[i], v[l], id[l]);
-    }
-}
+// ---------------------------------------------------------------------------------------
+// LM head top-K / log-sum-exp, pass 1: one workgroup per (row, chunk of 4096 logits).  Each
+// wave takes 1024 logits, 16 per lane (four float4 loads issued together): its K winners
+// from wave_topk and its (max, sum e^{z-max}) from wave reductions go to LDS; wave 0 then
+// draws the chunk's K winners (best first) from the 4K wave winners, one per lane, and
+// combines the four (max, sum) pairs in wave order.
+// ---------------------------------------------------------------------------------------
+constexpr int TK_CHUNK = 4096;
 
 // Load one chunk's best-first list of K (padded to 16 with (-inf, max id)).
 __device__ __forceinline__ void load_list(const float* cv, const int* ci, size_t base, int K, bool ok,
@@ -369,11 +380,14 @@ __global__ __launch_bounds__(256) void k_topk_chunk(const float* __restrict__ pa
                                                     float* __restrict__ cmax, float* __restrict__ csum,
                                                     float* __restrict__ dbg_logits, int R, int sb, int S,
                                                     SlotState st) {
-  const int m = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (c >= n_chunks) return;
-  const int t0 = c * TK_CHUNK;
+  __shared__ float sv[4][TK_CAP];
+  __shared__ int si[4][TK_CAP];
+  __shared__ float wv[4 * KMAX];
+  __shared__ int wi[4 * KMAX];
+  __shared__ float wmax[4], wsum[4];
+  const int m = blockIdx.y, c = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t0 = c * TK_CHUNK + w * 1024;
   float* dl = nullptr;
   if (dbg_logits) {
     const int b = m / R, j = m % R;
@@ -381,7 +395,6 @@ __global__ __launch_bounds__(256) void k_topk_chunk(const float* __restrict__ pa
     if (st.valid[sidx]) dl = dbg_logits + (size_t)sidx * V;
   }
   float v[16];
-  int id[16];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int t = t0 + 4 * (lane + 64 * q);
@@ -391,35 +404,47 @@ __global__ __launch_bounds__(256) void k_topk_chunk(const float* __restrict__ pa
       if (dl) *reinterpret_cast<floatx4*>(dl + t) = z;
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool ok = t + e < V;
-      v[4 * q + e] = ok ? z[e] : kNegInf;
-      id[4 * q + e] = ok ? t + e : 0x7fffffff;
-    }
+    for (int e = 0; e < 4; ++e) v[4 * q + e] = t + e < V ? z[e] : kNegInf;
   }
   float lm = kNegInf;
 #pragma unroll
   for (int i = 0; i < 16; ++i) lm = fmaxf(lm, v[i]);
   const float bm = wave_max(lm);
   float ls = 0.f;
+  if (bm != kNegInf)
 #pragma unroll
-  for (int i = 0; i < 16; ++i) ls += v[i] == kNegInf ? 0.f : expf(v[i] - bm);
+    for (int i = 0; i < 16; ++i) ls += __builtin_amdgcn_exp2f((v[i] - bm) * kLog2e);
   const float tot = wave_sum(ls);
-  sort16(v, id);
-  const size_t base = ((size_t)m * n_chunks + c) * K;
-  for (int k = 0; k < K; ++k) {
-    float bv = v[0];
-    int bi = id[0];
-    wave_argmax(bv, bi);
-    if (id[0] == bi && v[0] == bv) pop16(v, id);
-    if (lane == 0) {
-      cv[base + k] = bv;
-      ci[base + k] = bi;
-    }
+  if (lane < K) {
+    wv[w * K + lane] = kNegInf;   // a wave with fewer than K finite logits leaves padding
+    wi[w * K + lane] = 0x7fffffff;
   }
+  wave_topk<16>(v, [&](int e) { return t0 + 4 * (lane + 64 * (e >> 2)) + (e & 3); }, K, sv[w], si[w],
+                [&](int r, float val, int id) {
+                  wv[w * K + r] = val;
+                  wi[w * K + r] = id;
+                });
   if (lane == 0) {
-    cmax[(size_t)m * n_chunks + c] = bm;
-    csum[(size_t)m * n_chunks + c] = tot;
+    wmax[w] = bm;
+    wsum[w] = tot;
+  }
+  __syncthreads();
+  if (w != 0) return;
+  const float x = lane < 4 * K ? wv[lane] : kNegInf;
+  const int xi = lane < 4 * K ? wi[lane] : 0x7fffffff - lane;   // padding ids kept distinct
+  const size_t base = ((size_t)m * n_chunks + c) * K;
+  wave_topk<1>(&x, [&](int) { return xi; }, K, sv[0], si[0], [&](int r, float val, int id) {
+    cv[base + r] = val;
+    ci[base + r] = id;
+  });
+  if (lane == 0) {
+    float mx = wmax[0];
+    for (int i = 1; i < 4; ++i) mx = fmaxf(mx, wmax[i]);
+    float sm = 0.f;
+    for (int i = 0; i < 4; ++i)
+      if (wmax[i] != kNegInf) sm += wsum[i] * __builtin_amdgcn_exp2f((wmax[i] - mx) * kLog2e);
+    cmax[(size_t)m * n_chunks + c] = mx;
+    csum[(size_t)m * n_chunks + c] = sm;
   }
 }
 
@@ -467,6 +492,8 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
   __shared__ float s_val[SEL_MAXR][KMAX];
   __shared__ int s_id[SEL_MAXR][KMAX];
   __shared__ float s_lse[SEL_MAXR];
+  __shared__ float s_cv[SEL_MAXR][TK_CAP];
+  __shared__ int s_ci[SEL_MAXR][TK_CAP];
   __shared__ __attribute__((aligned(16))) float ssc[1024 + 4];
   __shared__ int sdep[1024];
   __shared__ int stok[1024];
@@ -497,7 +524,8 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
     }
   }
 
-  // ---- phase 1: per-row top-K merge and log-sum-exp (every load issued first)
+  // ---- phase 1: per-row top-K over the chunks' lists (lane l holds chunk l's list) and
+  // log-sum-exp from the chunks' (max, sum), combined in lane order
   if (w < R) {
     const int m = b * R + w;
     const int sidx = b * S + sb + w;
@@ -505,15 +533,12 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
     const float score0 = st.score[sidx];
     const uint64_t mk = st.mask[sidx];
     const int cand0 = st.cand[sidx];
-    const bool ok0 = lane < n_chunks, ok1 = lane + 64 < n_chunks;
-    const float cm0 = ok0 ? cmax[(size_t)m * n_chunks + lane] : kNegInf;
-    const float cm1 = ok1 ? cmax[(size_t)m * n_chunks + lane + 64] : kNegInf;
-    const float cs0 = ok0 ? csum[(size_t)m * n_chunks + lane] : 0.f;
-    const float cs1 = ok1 ? csum[(size_t)m * n_chunks + lane + 64] : 0.f;
-    float v[16], v2[16];
-    int id[16], id2[16];
-    load_list(cv, ci, ((size_t)m * n_chunks + lane) * K, K, ok0, v, id);
-    load_list(cv, ci, ((size_t)m * n_chunks + lane + 64) * K, K, ok1, v2, id2);
+    const bool ok = lane < n_chunks;
+    const float cm = ok ? cmax[(size_t)m * n_chunks + lane] : kNegInf;
+    const float cs_ = ok ? csum[(size_t)m * n_chunks + lane] : 0.f;
+    float v[16];
+    int id[16];
+    load_list(cv, ci, ((size_t)m * n_chunks + lane) * K, K, ok, v, id);
     if (lane == 0) {
       s_valid[w] = valid;
       s_score[w] = score0;
@@ -521,24 +546,15 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
       s_cand[w] = cand0;
     }
     if (valid) {
-      const float mx = wave_max(fmaxf(cm0, cm1));
-      float tot = cm0 != kNegInf ? cs0 * expf(cm0 - mx) : 0.f;
-      if (cm1 != kNegInf) tot += cs1 * expf(cm1 - mx);
-      tot = wave_sum(tot);
+      const float mx = wave_max(cm);
+      const float tot = wave_sum(cm != kNegInf ? cs_ * expf(cm - mx) : 0.f);
       const float row_lse = mx + logf(tot);
-      merge16(v, id, v2, id2);
-      for (int k = 0; k < K; ++k) {
-        float bv = v[0];
-        int bi = id[0];
-        wave_argmax(bv, bi);
-        if (id[0] == bi && v[0] == bv) pop16(v, id);
-        if (lane == 0) {
-          s_val[w][k] = bv;
-          s_id[w][k] = bi;
-          if (dbg_id) dbg_id[(size_t)sidx * K + k] = bi;
-          if (dbg_val) dbg_val[(size_t)sidx * K + k] = bv;
-        }
-      }
+      wave_topk<16>(v, [&](int e) { return id[e]; }, K, s_cv[w], s_ci[w], [&](int r, float val, int idv) {
+        s_val[w][r] = val;
+        s_id[w][r] = idv;
+        if (dbg_id) dbg_id[(size_t)sidx * K + r] = idv;
+        if (dbg_val) dbg_val[(size_t)sidx * K + r] = val;
+      });
       if (lane == 0) {
         s_lse[w] = row_lse;
         if (dbg_lse) dbg_lse[sidx] = row_lse;
@@ -752,15 +768,15 @@ int run_draft(const eagle3_drafter* w, const Plan& p, const void* h_low, const v
   int32_t* dbg_tok = dbg ? dbg->slot_token : nullptr;
   int32_t* dbg_par = dbg ? dbg->slot_parent : nullptr;
   int st;
+  GemmPlan gf = plan_gemm(B, d, 3 * d, dt);
   {
     ProfScope ps("draft_init", s);
     hipLaunchKernelGGL(k_init<T>, dim3(B), dim3(256), 0, s, B, p.S, d, p.V, root_tok, p.st, p.cs,
                        (const T*)h_low, (const T*)h_mid, (const T*)h_high, (T*)p.xf, dbg_tok, dbg_par);
     if ((st = launch_status())) return st;
+    // feature fusion g = W_f [h_low; h_mid; h_high] (its k-splits are summed by the step-0 prep)
+    if ((st = launch_gemm(gf, dt, p.xf, 3 * d, w->w_fuse, p.gfuse, s, "gemm_fuse"))) return st;
   }
-  // feature fusion g = W_f [h_low; h_mid; h_high] (its k-splits are summed by the step-0 prep)
-  GemmPlan gf = plan_gemm(B, d, 3 * d, dt);
-  if ((st = launch_gemm(gf, dt, p.xf, 3 * d, w->w_fuse, p.gfuse, s, "gemm_fuse"))) return st;
   for (int step = 0; step < p.D; ++step) {
     const int R = step == 0 ? 1 : p.W;
     const int sb = step == 0 ? 0 : 1 + (step - 1) * p.W;
@@ -843,7 +859,7 @@ int run_draft(const eagle3_drafter* w, const Plan& p, const void* h_low, const v
       if ((st = launch_gemm(gp, dt, p.xl, d, w->w_lm, p.gpart, s, "gemm_lm_head"))) return st;
       {
         ProfScope ps("topk_chunk", s);
-        hipLaunchKernelGGL(k_topk_chunk, dim3((p.lm_nchunk + 3) / 4, M), dim3(256), 0, s, p.gpart,
+        hipLaunchKernelGGL(k_topk_chunk, dim3(p.lm_nchunk, M), dim3(256), 0, s, p.gpart,
                            gp.splits, M, p.V, p.K, p.lm_nchunk, p.cv, p.ci, p.cmax, p.csum,
                            dbg ? dbg->slot_logits : (float*)nullptr, R, sb, p.S, p.st);
         if ((st = launch_status())) return st;
@@ -879,7 +895,7 @@ int draft_check(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, int ma
   if (t->n_nodes > 255) return EAGLE3_EUNSUPPORTED;
   if ((long)B * (t->width > 1 ? t->width : 1) > 160) return EAGLE3_EUNSUPPORTED;
   if (t->width > SEL_MAXR) return EAGLE3_EUNSUPPORTED;
-  if (w->vocab > 128 * TK_CHUNK) return EAGLE3_EUNSUPPORTED;
+  if (w->vocab > 64 * TK_CHUNK) return EAGLE3_EUNSUPPORTED;
   if (!w->embed || !w->w_fuse || !w->g_embed || !w->g_feat || !w->g_mlp || !w->g_final ||
       !w->w_qkv || !w->w_o || !w->w_gate_up || !w->w_down || !w->w_lm)
     return EAGLE3_EINVAL;

@@ -255,3 +255,39 @@ def test_draft_ignores_stale_workspace_contents():
     for k in ("tokens", "parents", "depth", "score", "n_nodes"):
         assert torch.equal(outs[0][k], outs[1][k]), k
     assert torch.isfinite(outs[0]["score"][:, :shape.n_nodes + 1]).all()
+
+
+def _tied_lm_head(w, kind):
+    """Rewrite the LM head so that its logits tie: "periodic3" gives every row only three
+    distinct logit values (ids t = r mod 3 tie), "paired" makes rows 2j and 2j+1 equal (each
+    value appears twice, at adjacent ids)."""
+    lm = w["w_lm"]
+    if kind == "periodic3":
+        base = lm[:3].clone()
+        lm.copy_(base.repeat((lm.shape[0] + 2) // 3, 1)[:lm.shape[0]])
+    elif kind == "paired":
+        lm[1::2].copy_(lm[0::2][:lm[1::2].shape[0]])
+
+
+@pytest.mark.parametrize("kind,V", [("periodic3", 8192), ("paired", 8192), ("plain", 4104),
+                                    ("paired", 4104)])
+def test_draft_topk_with_tied_logits_and_short_tail_chunk(kind, V):
+    """Top-K ids (value desc, id asc) stay exact when logits tie heavily (every wave falls
+    back to exact argmax rounds), when ties sit at the selection threshold, and when the
+    last 4096-logit chunk holds fewer than K logits (V = 4104, K = 10)."""
+    need_gpu()
+    shape = synth.scaled(SMALL_BF16, V=V, B=2, depth=3, topk=10, width=4, n_nodes=20)
+    prefix = [100, 257]
+    w = synth.drafter_weights(shape, seed=31, device=DEV)
+    _tied_lm_head(w, kind)
+    di = synth.draft_inputs(shape, seed=32, device=DEV, prefix=prefix)
+    dr = capi.make_drafter(w, shape.Hq, shape.Hkv, shape.Dh)
+    tree = capi.Eagle3TreeCfg(depth=shape.depth, topk=shape.topk, width=shape.width,
+                              n_nodes=shape.n_nodes)
+    out = capi.eagle3_draft_expand(dr, tree, di["h_low"], di["h_mid"], di["h_high"], di["root_tok"],
+                                   di["kpre"], di["vpre"], di["cu_prefix"], max(prefix), debug=True,
+                                   debug_logits=True)
+    torch.cuda.synchronize()
+    check_topk_on_gpu_logits(shape, out["debug"], shape.B)
+    check_selection_replay(shape, out, shape.B)
+    check_teacher_forced(shape, w, di, out, shape.B, prefix)
