@@ -32,6 +32,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b", choices=["llama8b", "batch16", "llama70b", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ops", action="store_true", help="skip the per-op roofline measurements")
+    ap.add_argument("--only-ops", action="store_true",
+                    help="measure only the per-op rooflines (no round, no CPU baseline)")
     ap.add_argument("--kernel", default="gemm_lm_head", help="kernel timed for the roofline")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (for scaling HBM byte "
@@ -180,6 +183,210 @@ def cpu_baseline(rnd: Round):
                       f"tree tokens) in {dt:.2f} s, float64 numpy oracle"}
 
 
+# ---------------------------------------------------------------------------------------
+# Per-op rooflines.  Each op is one library call on the shapes of the other workloads,
+# timed by the library's HIP event pair on the launch stream (eagle3_profile_*), over
+# `reps` launches that cycle through enough input copies that the reads miss the 256 MB
+# Infinity Cache.  `bytes` / `flops` are algorithmic: what the method itself must read and
+# write (or multiply-add), never the split partials the kernels add.
+# ---------------------------------------------------------------------------------------
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+INFINITY_CACHE_BYTES = 256 << 20
+
+
+def _copies(nbytes: int, want: int = 2) -> int:
+    """Enough rotating copies of an nbytes working set to exceed the Infinity Cache twice."""
+    return max(want, -(-2 * INFINITY_CACHE_BYTES // max(nbytes, 1)))
+
+
+def _time_tag(capi, tag: str, fn, reps: int) -> float:
+    """Average device time (us) of the library launches tagged `tag` over reps calls."""
+    import torch
+    for i in range(3):
+        fn(i)
+    torch.cuda.synchronize()
+    capi.eagle3_profile_reset()
+    capi.eagle3_profile_enable(True, only_kernel=tag)
+    for i in range(reps):
+        fn(i)
+    torch.cuda.synchronize()
+    capi.eagle3_profile_enable(False)
+    ms, n = capi.eagle3_profile_read(tag)
+    capi.eagle3_profile_reset()
+    return ms / max(n, 1) * 1e3
+
+
+def _entry(op, workload, kernel, us, bound, bytes_=None, flops=None, **extra):
+    e = {"op": op, "workload": workload, "kernel": kernel, "bound": bound,
+         "avg_launch_us": round(us, 2)}
+    if bytes_ is not None:
+        gbs = bytes_ / (us * 1e-6) / 1e9
+        e.update({"algorithmic_bytes": int(bytes_), "achieved_gbs": round(gbs, 1),
+                  "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+    if flops is not None:
+        tfs = flops / (us * 1e-6) / 1e12
+        e.update({"algorithmic_flops": int(flops), "achieved_tflops": round(tfs, 1),
+                  "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4)})
+    if bound == "hbm":
+        e.update({"achieved": e["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": e["hbm_frac"]})
+    elif bound == "mfma":
+        e.update({"achieved": e["achieved_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                  "unit": "TFLOP/s", "frac": e["mfma_frac"]})
+    e.update(extra)
+    return e
+
+
+def _tree_depths(parents):
+    dep = []
+    for p in parents:
+        dep.append(0 if p < 0 else dep[p] + 1)
+    return dep
+
+
+def attention_op(capi, synth, shape, trees, prefix, bound, reps=20, seed=500):
+    """Verify tree attention (the partial-producing kernel alone) on one workload."""
+    import numpy as np
+    import torch
+    dev = "cuda:0"
+    vi = synth.verify_inputs(shape, trees, prefix, seed=seed, device=dev, with_logits=False)
+    maxn = max(len(t) for t in trees)
+    mk = capi.eagle3_build_tree_mask(vi["cu_nodes"], vi["parents"], vi["cu_prefix"], max_nodes=maxn)
+    es = 2
+    kv_bytes = sum(prefix) * shape.Hkv * shape.Dh * 2 * es
+    ncopy = _copies(kv_bytes)
+    kp = [vi["kpre"]] + [synth.normal(tuple(vi["kpre"].shape), 1.0, seed + 10 + c, vi["kpre"].dtype, dev)
+                         for c in range(ncopy - 1)]
+    vp = [vi["vpre"]] + [synth.normal(tuple(vi["vpre"].shape), 1.0, seed + 50 + c, vi["vpre"].dtype, dev)
+                         for c in range(ncopy - 1)]
+    S = capi.eagle3_tree_attention_num_splits(len(trees), shape.Hq, shape.Hkv, maxn, max(prefix), 0)
+    T = vi["T"]
+    part = {"o_part": torch.empty((S + 1, T, shape.Hq, shape.Dh), dtype=torch.float32, device=dev),
+            "lse_part": torch.empty((S + 1, T, shape.Hq), dtype=torch.float32, device=dev)}
+    scale = float(1.0 / math.sqrt(shape.Dh))
+
+    def run(i):
+        capi.eagle3_tree_attention(vi["q"], vi["k_tree"], vi["v_tree"], vi["cu_nodes"], maxn, mk["mask"],
+                                   kp[i % ncopy], vp[i % ncopy], vi["cu_prefix"], max(prefix), scale,
+                                   out=part)
+    us = _time_tag(capi, "tree_attention", run, reps)
+    n_nodes = [len(t) for t in trees]
+    tree_bytes = T * shape.Hkv * shape.Dh * 2 * es
+    q_bytes = T * shape.Hq * shape.Dh * es
+    out_bytes = T * shape.Hq * (shape.Dh * es + 4)
+    flops = 0
+    for t, P in zip(trees, prefix):
+        anc = [d + 1 for d in _tree_depths(t)]          # ancestors-or-self of each node
+        flops += shape.Hq * 4 * shape.Dh * (len(t) * P + sum(anc))
+    rows_per_kv = max(n_nodes) * shape.Hq // shape.Hkv
+    return _entry("tree_attention", shape.name, "k_tree_attn_dma", us, bound,
+                  bytes_=kv_bytes + tree_bytes + q_bytes + out_bytes, flops=flops,
+                  splits=S, rows_per_kv_head=rows_per_kv, prefix_tokens=sum(prefix),
+                  rotating_copies=ncopy)
+
+
+def op_rooflines(reps=20):
+    import numpy as np
+    import torch
+    from speculative_decoding_round_amd import capi, synth
+    dev = "cuda:0"
+    ops = []
+    # long-context branch: 7 chain queries over a 65536-token prefix (HBM-bound)
+    sh = synth.LONGCTX
+    ops.append(attention_op(capi, synth, sh, [synth.chain_tree(sh.branch)], [65536], "hbm", reps))
+    # batched serving: 16 random trees of <= 48 nodes, prefixes uniform in [512, 4096] (HBM-bound)
+    sh = synth.BATCH16
+    prefix = synth.prefix_lengths(sh, seed=31)
+    rng = np.random.default_rng(31)
+    trees = [synth.random_tree(int(rng.integers(1, sh.verify_max_nodes + 1)), sh.verify_max_depth, 3100 + i)
+             for i in range(sh.B)]
+    ops.append(attention_op(capi, synth, sh, trees, prefix, "hbm", reps))
+    # 70B-shaped verify: 4 x (root + 60 nodes), 488 query rows per KV head (MFMA-bound)
+    sh = synth.LLAMA70B
+    trees = [synth.random_tree(61, sh.depth, 4100 + i) for i in range(sh.B)]
+    ops.append(attention_op(capi, synth, sh, trees, synth.prefix_lengths(sh, 41), "mfma", reps))
+    # 8B-shaped verify (60-node tree over 2048 keys): latency-sized, reported for both bounds
+    sh = synth.LLAMA8B
+    ops.append(attention_op(capi, synth, sh, [synth.random_tree(61, sh.depth, 4200)], [2048], "hbm", reps))
+
+    # LSE merge at the long-context training scale: two partials of 65536 x 32 rows
+    rows, Dh = 65536 * 32, 128
+    o_part = synth.normal((2, rows, Dh), 1.0, 900, torch.float32, dev)
+    lse_part = synth.normal((2, rows), 1.0, 901, torch.float32, dev)
+    mo = {"o": torch.empty((rows, Dh), dtype=torch.bfloat16, device=dev),
+          "lse": torch.empty((rows,), dtype=torch.float32, device=dev)}
+    us = _time_tag(capi, "lse_merge", lambda i: capi.eagle3_lse_merge(o_part, lse_part, out=mo), reps)
+    ops.append(_entry("lse_merge", "2 partials x 65536 positions x 32 heads x 128 (fp32 -> bf16)",
+                      "k_lse_merge", us, "hbm", bytes_=2 * rows * (Dh + 1) * 4 + rows * (Dh * 2 + 4)))
+    del o_part, lse_part, mo
+
+    # acceptance: greedy at the 8B shape (61 nodes x 128256 bf16 logits), T = 0.7 at the 70B
+    # shape (4 x 61 nodes)
+    for sh, B, temp in ((synth.LLAMA8B, 1, 0.0), (synth.LLAMA70B, 4, 0.7)):
+        trees = [synth.random_tree(61, sh.depth, 4300 + i) for i in range(B)]
+        vi = synth.verify_inputs(sh, trees, [0] * B, seed=950, device=dev, with_logits=False)
+        mk = capi.eagle3_build_tree_mask(vi["cu_nodes"], vi["parents"], None, max_nodes=61)
+        T, V = vi["T"], sh.V
+        lbytes = T * V * 2
+        ncopy = _copies(lbytes)
+        logits = [synth.normal((T, V), 1.0, 960 + c, torch.bfloat16, dev) for c in range(ncopy)]
+        ws = torch.empty(capi.lib().eagle3_accept_workspace_size(T, V), dtype=torch.uint8, device=dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        ao = {"accept_len": torch.empty((B,), **i32), "path": torch.empty((B, sh.depth + 1), **i32),
+              "out_tokens": torch.empty((B, sh.depth + 1), **i32), "bonus": torch.empty((B,), **i32)}
+
+        def run(i, vi=vi, mk=mk, logits=logits, ws=ws, ao=ao, temp=temp, sh=sh):
+            capi.eagle3_accept(vi["cu_nodes"], vi["tokens"], vi["parents"], mk["mask"], logits[i % len(logits)],
+                               temp, seed=7, round=i, max_depth=sh.depth, workspace=ws, out=ao)
+        us_scan = _time_tag(capi, "accept_scan", run, reps)
+        us_path = _time_tag(capi, "accept_path", run, reps)
+        name = "greedy" if temp == 0 else f"T={temp}"
+        ops.append(_entry(f"accept_scan ({name})", f"{sh.name}: {T} nodes x {V} logits", "k_accept_scan",
+                          us_scan, "hbm", bytes_=lbytes, accept_path_us=round(us_path, 2),
+                          rotating_copies=ncopy,
+                          logits_per_s=round(T * V / (us_scan * 1e-6) / 1e9, 2)))
+        del logits
+    torch.cuda.empty_cache()
+    return ops
+
+
+def gemm_rooflines(rnd: "Round", steps: int):
+    """Per-projection GEMM times inside the round (every launch timed by its event pair)."""
+    import torch
+    capi, s = rnd.capi, rnd.shape
+    capi.eagle3_profile_reset()
+    capi.eagle3_profile_enable(True)
+    for _ in range(steps):
+        rnd.step()
+    torch.cuda.synchronize()
+    capi.eagle3_profile_enable(False)
+    es = 2 if s.dtype == "bf16" else 4
+    d, F, V = s.d, s.F, s.V
+    nqkv = (s.Hq + 2 * s.Hkv) * s.Dh
+    rows = [s.B] + [s.B * s.width] * (s.depth - 1)
+    avg_m = sum(rows) / len(rows)
+    # weights once + activations in (dtype) + outputs (fp32 partial sums once, or dtype for
+    # the SiLU product), at the average row count of the round's steps
+    spec = {
+        "gemm_fuse": (d * 3 * d, s.B, 3 * d, d, 4),
+        "gemm_qkv": (nqkv * 2 * d, avg_m, 2 * d, nqkv, 4),
+        "gemm_o": (d * s.Hq * s.Dh, avg_m, s.Hq * s.Dh, d, 4),
+        "gemm_gate_up": (2 * F * d, avg_m, d, F, es),
+        "gemm_down": (d * F, avg_m, F, d, 4),
+        "gemm_lm_head": (V * d, avg_m, d, V, 4),
+    }
+    out = []
+    for tag, (wn, m, kin, nout, oes) in spec.items():
+        ms, n = capi.eagle3_profile_read(tag)
+        if n == 0:
+            continue
+        us = ms / n * 1e3
+        b = wn * es + m * kin * es + m * nout * oes
+        out.append(_entry(tag, s.name, "k_gemm", us, "hbm", bytes_=b, launches=n))
+    capi.eagle3_profile_reset()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -189,6 +396,9 @@ def main():
     import torch
     from speculative_decoding_round_amd import capi, synth
     dev = "cuda:0"
+    if args.only_ops:
+        print(json.dumps({"ops": op_rooflines()}), flush=True)
+        return
     shape = {"llama8b": synth.LLAMA8B, "batch16": synth.BATCH16, "llama70b": synth.LLAMA70B,
              "tiny": synth.TINY}[args.workload]
     rnd = Round(shape, dev)
@@ -247,6 +457,8 @@ def main():
         "wall_s_timed": round(wall, 3),
         "ms_per_step_with_kernel_events": round(ms_ev, 4),
     }
+    if not args.no_ops:
+        line["gemms"] = gemm_rooflines(rnd, args.steps)
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -254,8 +466,13 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         line["copy_calibration_bytes"] = n
+        del src, dst
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(rnd)
+    if not args.no_ops:
+        del rnd
+        torch.cuda.empty_cache()
+        line["ops"] = op_rooflines()
     print(json.dumps(line), flush=True)
 
 

@@ -770,10 +770,12 @@ int run_draft(const eagle3_drafter* w, const Plan& p, const void* h_low, const v
   int st;
   GemmPlan gf = plan_gemm(B, d, 3 * d, dt);
   {
-    ProfScope ps("draft_init", s);
-    hipLaunchKernelGGL(k_init<T>, dim3(B), dim3(256), 0, s, B, p.S, d, p.V, root_tok, p.st, p.cs,
-                       (const T*)h_low, (const T*)h_mid, (const T*)h_high, (T*)p.xf, dbg_tok, dbg_par);
-    if ((st = launch_status())) return st;
+    {
+      ProfScope ps("draft_init", s);
+      hipLaunchKernelGGL(k_init<T>, dim3(B), dim3(256), 0, s, B, p.S, d, p.V, root_tok, p.st, p.cs,
+                         (const T*)h_low, (const T*)h_mid, (const T*)h_high, (T*)p.xf, dbg_tok, dbg_par);
+      if ((st = launch_status())) return st;
+    }
     // feature fusion g = W_f [h_low; h_mid; h_high] (its k-splits are summed by the step-0 prep)
     if ((st = launch_gemm(gf, dt, p.xf, 3 * d, w->w_fuse, p.gfuse, s, "gemm_fuse"))) return st;
   }
