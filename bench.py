@@ -200,7 +200,10 @@ def _copies(nbytes: int, want: int = 2) -> int:
 
 
 def _time_tag(capi, tag: str, fn, reps: int) -> float:
-    """Average device time (us) of the library launches tagged `tag` over reps calls."""
+    """Average device time (us) of the library launches tagged `tag` over reps calls.  A
+    short device-side spin precedes each call, so that the launch's opening event does not
+    fire on an idle queue before the host has enqueued the kernel (the event pair then
+    brackets the kernel alone, not the host's enqueue latency)."""
     import torch
     for i in range(3):
         fn(i)
@@ -208,6 +211,7 @@ def _time_tag(capi, tag: str, fn, reps: int) -> float:
     capi.eagle3_profile_reset()
     capi.eagle3_profile_enable(True, only_kernel=tag)
     for i in range(reps):
+        torch.cuda._sleep(200_000)
         fn(i)
     torch.cuda.synchronize()
     capi.eagle3_profile_enable(False)

@@ -194,9 +194,10 @@ EAGLE3_API int eagle3_build_tree_mask(int B, int T, const int32_t* cu_nodes, con
  *  q [T, Hq, Dh], k_tree, v_tree [T, Hkv, Dh], kpre, vpre [sum P_b, Hkv, Dh]: dtype
  *  cu_nodes [B+1], cu_prefix [B+1]: int32 device; mask [T, W64] as built above
  *  max_nodes, max_prefix: host upper bounds per request; n_splits: S in 1..256 (0 =
- *  automatic: about as many workgroups as the chip holds at once, each split at least one
- *  key tile and twice as many keys as its row block has query rows; the same arguments
- *  give the same S in eagle3_tree_attention_num_splits).  Dh must be 64 or 128.
+ *  automatic: enough workgroups for the kernel shape chosen by the query rows per KV head,
+ *  each split at least one key tile and four times as many keys as its row block has
+ *  query rows; the same arguments give the same S in eagle3_tree_attention_num_splits).
+ *  Dh must be 64 or 128.
  * ------------------------------------------------------------------------------------ */
 EAGLE3_API int eagle3_tree_attention_num_splits(int B, int Hq, int Hkv, int max_nodes,
                                                 int max_prefix, int n_splits);

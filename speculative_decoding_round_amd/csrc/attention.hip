@@ -269,6 +269,28 @@ __global__ __launch_bounds__(256) void k_tree_attn(DevArgs a) {
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const char lds_cchar;
+
+// Byte address of a __shared__ object in the workgroup's LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_cchar*)p;
+}
+
+// One 16-byte-per-lane LDS DMA: lane l's 16 bytes land at LDS byte lds_base + 16 l.
+// Non-temporal: the K/V stream is read once.  Written as inline assembly so that the
+// compiler does not see an outstanding LDS write: it would otherwise drain every DMA
+// (s_waitcnt vmcnt(0)) before each later LDS read, including the reads of stages whose
+// data arrived long ago, and no stage could be in flight during the math.  Completion is
+// ordered explicitly instead (wait_vm + barrier before a stage is read).
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(0) with expcnt and lgkmcnt left open.
+constexpr int kWaitVm0 = 0x0F70;
+
+// Address = wave-uniform base (SGPRs) + this lane's 32-bit byte offset.
+__device__ __forceinline__ void dma16_nt_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase),
+               "s"(lds_base)
+               : "memory", "m0");
+}
 
 template <int CPR>
 __device__ __forceinline__ int kv_swz(int key) {
@@ -376,29 +398,42 @@ __global__ __launch_bounds__(256) void k_tree_attn_dma(DevArgs a) {
   }
 
   // DMA: thread chunk q = (u*4 + w)*64 + lane of a stage, decoded as (key group, K|V,
-  // key, position); position p holds the key's chunk p ^ swz(key).  src[u] walks the
-  // stream one iteration at a time; the last iteration clamps keys to the range end.
-  const bf16* src[C::PER];
+  // key, position); position p holds the key's chunk p ^ swz(key).  A lane's byte offset
+  // from the iteration's first key is the same in every iteration, and the K|V choice of
+  // instruction u is the same for all lanes of a wave (CPR * KTW >= 64), so the stream
+  // position lives in two scalar bases that advance by one iteration of keys; only the
+  // last iteration clamps keys to the range end.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  uint32_t voff[C::PER], vpos[C::PER];
   int relk[C::PER];
+  bool isv[C::PER];
 #pragma unroll
   for (int u = 0; u < C::PER; ++u) {
-    const int q = (u * 4 + w) * 64 + lane;
+    const int q = (u * 4 + wu) * 64 + lane;
     const int pos = q % CPR;
     const int key = (q / CPR) % KTW;
-    const int tv = (q / (CPR * KTW)) % 2;
+    isv[u] = ((u * 4 + wu) * 64 / (CPR * KTW)) % 2 != 0;
     const int kg = q / (2 * CPR * KTW);
     relk[u] = kg * KTW + key;
-    src[u] = (tv ? vbase : kbase) + (pos ^ kv_swz<CPR>(key)) * 8;
+    vpos[u] = (uint32_t)(pos ^ kv_swz<CPR>(key)) * 16u;
+    voff[u] = (uint32_t)relk[u] * (uint32_t)kstride * 2u + vpos[u];
   }
+  const uint32_t smem_lds = lds_addr(smem);
+  const char* kstream = reinterpret_cast<const char*>(kbase);
+  const char* vstream = reinterpret_cast<const char*>(vbase);
+  const size_t it_bytes = (size_t)C::KITER * kstride * 2;
   auto issue = [&](int it) {
-    char* st = smem + (it % NST) * C::STAGE;
+    const uint32_t st = smem_lds + (it % NST) * C::STAGE;
     const int t0 = k_lo + it * C::KITER;
     const bool whole = t0 + C::KITER <= k_hi;
+    const size_t adv = (size_t)k_lo * kstride * 2 + (size_t)it * it_bytes;
+    const char* kb = kstream + adv;
+    const char* vb = vstream + adv;
 #pragma unroll
     for (int u = 0; u < C::PER; ++u) {
-      const int kabs = whole ? t0 + relk[u] : min(t0 + relk[u], k_hi - 1);
-      const bf16* p = src[u] + (uint32_t)kabs * (uint32_t)kstride;
-      __builtin_amdgcn_global_load_lds((const void*)p, (lds_void*)(st + (u * 4 + w) * 1024), 16, 0, 0);
+      uint32_t off = voff[u];
+      if (!whole) off = (uint32_t)min(relk[u], k_hi - 1 - t0) * (uint32_t)kstride * 2u + vpos[u];
+      dma16_nt_s(isv[u] ? vb : kb, off, st + (u * 4 + wu) * 1024);
     }
   };
 
@@ -423,6 +458,11 @@ __global__ __launch_bounds__(256) void k_tree_attn_dma(DevArgs a) {
     }
   const int kr = (lane & 15) >> 2, dq = lane & 3;
 
+  // The query rows (and mask words) are in registers / LDS before the stream starts.  This
+  // wait is a real instruction the compiler accounts for: without it, the compiler (which
+  // does not count the assembly DMAs) would keep the query loads pending and drain the
+  // whole DMA ring (vmcnt(0)) before the first MFMA of every tile.
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
 #pragma unroll
   for (int s0 = 0; s0 < NST - 1; ++s0)
     if (s0 < n_it) issue(s0);
@@ -671,13 +711,16 @@ __global__ __launch_bounds__(256) void k_lse_merge(int S, int rows, int Dh,
 }
 
 // Workgroup shape of the bf16 kernel by query rows per (request, KV head):
-// 0: 32 rows, keys split over the 4 waves (one workgroup per CU);
-// 1: 64 rows, one 16-row tile per wave, keys shared (two workgroups per CU);
-// 2: 128 rows, two 16-row tiles per wave, keys shared (two workgroups per CU).
-inline int attn_cfg(int rows) { return rows <= 32 ? 0 : rows <= 64 ? 1 : 2; }
+// 0: <= 32 rows: 32 rows per workgroup, keys split over the 4 waves (one workgroup per CU);
+// 1: <= 256 rows: 64 rows per workgroup, one 16-row tile per wave, keys shared;
+// 2: more: 128 rows per workgroup, two 16-row tiles per wave, keys shared.
+// Workgroups aimed for per launch: one per CU for shape 0; for shape 1 several rounds of
+// the two resident per CU, which evens out ragged requests; for shape 2 (hundreds of rows,
+// math-bound) one round.
+inline int attn_cfg(int rows) { return rows <= 32 ? 0 : rows <= 256 ? 1 : 2; }
 inline int attn_cfg_rows(int cfg) { return cfg == 0 ? 32 : cfg == 1 ? 64 : 128; }
 inline int attn_cfg_keys(int cfg) { return cfg == 0 ? 128 : 32; }
-inline int attn_cfg_wgs(int cfg) { return cfg == 0 ? 256 : 512; }   // resident workgroups on the chip
+inline int attn_cfg_wgs(int cfg) { return cfg == 0 ? 256 : cfg == 1 ? 2048 : 512; }
 
 template <typename T, int DH>
 int launch_attn_t(const e3h::AttnArgs& h, hipStream_t s) {
@@ -729,10 +772,10 @@ int launch_attn_t(const e3h::AttnArgs& h, hipStream_t s) {
 
 namespace e3h {
 
-// Prefix splits: about as many workgroups as the chip holds at once, but every split
-// keeps at least one iteration of keys and at least twice as many keys as the row block
-// has rows, so a split's fp32 partial stays at or below half of the bf16 K+V bytes it
-// streams.
+// Prefix splits: enough workgroups for the launch target of the workgroup shape, but every
+// split keeps at least one iteration of keys and at least four times as many keys as its
+// row block has rows, so a split's fp32 partial stays at or below a quarter of the bf16
+// K+V bytes it streams.
 int attention_splits(int B, int Hkv, int rows_per_kv, int max_prefix, int n_splits) {
   if (n_splits > 0) return n_splits;
   if (max_prefix <= 0 || B <= 0 || Hkv <= 0) return 1;
@@ -742,7 +785,7 @@ int attention_splits(int B, int Hkv, int rows_per_kv, int max_prefix, int n_spli
   const long rb = (rows + rows_wg - 1) / rows_wg;
   const long base = (long)B * Hkv * rb;
   long s = (attn_cfg_wgs(cfg) + base - 1) / base;
-  const long min_keys = std::max<long>(kiter, 2L * std::min(rows, rows_wg));
+  const long min_keys = std::max<long>(kiter, 4L * std::min(rows, rows_wg));
   const long max_s = (max_prefix + min_keys - 1) / min_keys;
   if (s > max_s) s = max_s;
   if (s > 256) s = 256;
