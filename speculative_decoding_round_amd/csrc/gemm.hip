@@ -155,6 +155,144 @@ __global__ __launch_bounds__(WK * 64) void k_gemm(const T* __restrict__ X, int M
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// bf16 weight streaming through an LDS ring (one wave per workgroup).
+//
+// A tile is 16 rows x 8 chunks (a 512-byte row segment).  It moves from HBM to a slot of
+// this wave's LDS ring by eight LDS-DMA instructions, each taking two whole 512-byte row
+// segments (lanes 0-31 and 32-63), so every HBM line is fetched whole, non-temporally.  A
+// row's 16-byte pieces are stored XOR-swizzled (piece p at position p ^ row), which keeps
+// the MFMA operand reads (16 rows at one piece) free of bank conflicts.  Per 8-chunk k-block
+// the stream is MT tiles of X (the evaluated rows, kept in registers for the block) and then
+// NTB tiles of W; NST slots are in flight.  W feeds operand A (16 output features), X
+// operand B, accumulation in fp32.  Needs K % 32 == 0 and MT <= 2.
+// ---------------------------------------------------------------------------------------
+constexpr int RING_TILE = 16 * 512;
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// 16 bytes per lane into LDS at lds_base + 16 * lane, non-temporal.  Issued as assembly so
+// that the compiler does not see an outstanding LDS write (it would drain every DMA before
+// each later LDS read); completion is ordered by the explicit vmcnt waits of the ring.
+__device__ __forceinline__ void ring_dma(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(gptr), "s"(lds_base)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void ring_wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int MT, int NTB, int NST, bool SILU>
+__global__ __launch_bounds__(64) void k_gemm_ring(const bf16* __restrict__ X, int M, int ldx,
+                                                  const bf16* __restrict__ W, int N, int K,
+                                                  float* __restrict__ Y, int n_blocks,
+                                                  int chunks_total, int chunks_per_split,
+                                                  void* __restrict__ act, int F) {
+  static_assert(MT >= 1 && MT <= 2, "X is held in registers for one k-block");
+  static_assert(NST >= 2 && 8 * (NST - 2) <= 63, "outstanding DMA must fit the vmcnt counter");
+  constexpr int SPK = MT + NTB;   // ring stages per k-block
+  __shared__ __attribute__((aligned(16))) char ring[NST * RING_TILE];
+  const int lane = threadIdx.x;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int nb = blockIdx.x % n_blocks, ks = blockIdx.x / n_blocks;
+  const int cs0 = ks * chunks_per_split;
+  const int cs1 = min(chunks_total, cs0 + chunks_per_split);
+  const int n_kb = cs1 > cs0 ? (cs1 - cs0 + 7) / 8 : 0;
+  const int total = n_kb * SPK;
+  const uint32_t ring0 = lds_u32(ring);
+
+  // DMA of stage s (k-block s / SPK; X tile, or W tile of this workgroup's n-block)
+  auto issue = [&](int s) {
+    const int j = s / SPK, r = s - j * SPK;
+    const int c0 = cs0 + j * 8;
+    const int lastp = min(8, cs1 - c0) * 4 - 1;
+    const uint32_t slot = ring0 + (uint32_t)(s % NST) * RING_TILE;
+    const bf16* base;
+    int ld, row0, rmax;
+    if (r < MT) {
+      base = X;
+      ld = ldx;
+      row0 = r * 16;
+      rmax = M - 1;
+    } else {
+      base = W;
+      ld = K;
+      row0 = tile_row0<NTB, SILU>(nb, r - MT, F);
+      rmax = N - 1;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the slot's last reads are done
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rt = 2 * i + (lane >> 5);
+      const int row = min(row0 + rt, rmax);
+      const int pc = min((lane & 31) ^ rt, lastp);
+      ring_dma(base + (size_t)row * ld + c0 * 32 + pc * 8, slot + i * 1024);
+    }
+  };
+
+  floatx4 acc[NTB][MT];
+#pragma unroll
+  for (int nt = 0; nt < NTB; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  u32x4 xv[8][MT];
+
+  // LDS byte offset of this lane's operand piece for chunk u: row r16, piece 4u + g
+  auto opoff = [&](int u) { return (uint32_t)(r16 * 512 + (((4 * u + g) ^ r16) * 16)); };
+
+#pragma unroll
+  for (int s0 = 0; s0 < NST - 1; ++s0)
+    if (s0 < total) issue(s0);
+
+  int s = 0;
+  for (int j = 0; j < n_kb; ++j) {
+    const int nvalid = min(8, cs1 - (cs0 + j * 8));
+#pragma unroll
+    for (int r = 0; r < SPK; ++r, ++s) {
+      if (s + NST - 2 < total) ring_wait_vm<8 * (NST - 2)>();
+      else ring_wait_vm<0>();
+      const char* slot = ring + (s % NST) * RING_TILE;
+      if (r < MT) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(slot + opoff(u));
+          xv[u][r] = u < nvalid ? v : u32x4{0, 0, 0, 0};
+        }
+      } else {
+        u32x4 wv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) wv[u] = *reinterpret_cast<const u32x4*>(slot + opoff(u));
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[r - MT][mt] = Mfma<bf16>::run(wv[u], xv[u][mt], acc[r - MT][mt]);
+      }
+      if (s + NST - 1 < total) issue(s + NST - 1);
+    }
+  }
+
+  float* Ys = Y + (size_t)ks * M * N;
+  constexpr int NOUT = SILU ? NTB / 2 : NTB;
+#pragma unroll
+  for (int nt = 0; nt < NOUT; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + r16;
+      const int n = tile_row0<NTB, SILU>(nb, nt, F) + 4 * g;
+      store_out<bf16, SILU>(Ys, act, M, N, F, m, n, acc[nt][mt], acc[SILU ? nt + NOUT : nt][mt]);
+    }
+}
+
+// Ring kernel shape: 8 W tiles (128 output features) per workgroup, 4 ring slots (32 KB
+// of LDS, five workgroups per CU).
+constexpr int kRingNTB = 8, kRingNST = 4;
+// Workgroups aimed for by the k-split of ring launches (about four per CU).
+constexpr int kRingTargetWgs = 800;
+
 // out[m][n] = (resid ? resid[m][n] : 0) + sum_s part[s][m][n]
 __global__ __launch_bounds__(256) void k_epi_sum(const float* __restrict__ part, int S, int M, int N,
                                                  float* __restrict__ out,
@@ -199,9 +337,20 @@ int dispatch_mt(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, f
   return e3h::launch_status();
 }
 
+template <int MT>
+int launch_ring(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm_ring<MT, kRingNTB, kRingNST, false>), dim3(p.n_blocks * p.splits), dim3(64), 0,
+                     s, (const bf16*)X, p.M, ldx, (const bf16*)W, p.N, p.K, Y, p.n_blocks, p.chunks_total,
+                     p.chunks_per_split, nullptr, p.N / 2);
+  return e3h::launch_status();
+}
+
 template <typename T>
 int dispatch_gemm(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y,
                   void* act, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    if (p.ring) return p.MT == 1 ? launch_ring<1>(p, X, ldx, W, Y, s) : launch_ring<2>(p, X, ldx, W, Y, s);
+  }
   switch (p.MT) {
     case 1: return dispatch_mt<T, 1>(p, X, ldx, W, Y, act, s);
     case 2: return dispatch_mt<T, 2>(p, X, ldx, W, Y, act, s);
@@ -224,10 +373,27 @@ namespace e3h {
 GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu) {
   GemmPlan p;
   p.silu = silu;
+  p.ring = false;
   p.M = M;
   p.N = N;
   p.K = K;
   const int mt_need = (M + 15) / 16;
+  if (dtype == EAGLE3_BF16 && !silu && mt_need <= 2 && K % 32 == 0) {
+    // LDS-ring kernel: 128 output features per workgroup and a k-split in whole 8-chunk
+    // blocks that brings the grid to about kRingTargetWgs workgroups
+    p.ring = true;
+    p.MT = mt_need < 1 ? 1 : mt_need;
+    p.NT = kRingNTB;
+    p.waves = 1;
+    p.n_blocks = ((N + 15) / 16 + kRingNTB - 1) / kRingNTB;
+    p.chunks_total = K / 32;
+    int splits = (kRingTargetWgs + p.n_blocks - 1) / p.n_blocks;
+    int cps = (p.chunks_total + splits - 1) / splits;
+    cps = (cps + 7) / 8 * 8;
+    p.chunks_per_split = cps;
+    p.splits = (p.chunks_total + cps - 1) / cps;
+    return p;
+  }
   static const int mts[] = {1, 2, 3, 4, 6, 8, 10};
   p.MT = 0;
   for (int v : mts)

@@ -21,7 +21,7 @@ import sys
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LM_HEAD_KERNEL = re.compile(r"k_gemm<[^>]*, 8, 8, 1, false>")   # the single-wave LM-head variant
+LM_HEAD_KERNEL = re.compile(r"k_gemm_ring<1, 8, 4, false>")   # the LM head (one 16-row tile of rows)
 
 
 def gemm_source_hash() -> str:
