@@ -394,17 +394,31 @@ __global__ __launch_bounds__(256) void k_topk_chunk(const float* __restrict__ pa
     const int sidx = b * S + sb + j;
     if (st.valid[sidx]) dl = dbg_logits + (size_t)sidx * V;
   }
+  // the four float4 loads of a split are issued together, splits summed in order
   float v[16];
+  floatx4 z[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int t = t0 + 4 * (lane + 64 * q);
-    floatx4 z = {0.f, 0.f, 0.f, 0.f};
-    if (t < V) {
-      for (int s = 0; s < splits; ++s) z += *reinterpret_cast<const floatx4*>(part + ((size_t)s * M + m) * V + t);
-      if (dl) *reinterpret_cast<floatx4*>(dl + t) = z;
+    z[q] = t < V ? *reinterpret_cast<const floatx4*>(part + (size_t)m * V + t) : floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int s = 1; s < splits; ++s) {
+    floatx4 y[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t = t0 + 4 * (lane + 64 * q);
+      y[q] = t < V ? *reinterpret_cast<const floatx4*>(part + ((size_t)s * M + m) * V + t)
+                   : floatx4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[4 * q + e] = t + e < V ? z[e] : kNegInf;
+    for (int q = 0; q < 4; ++q) z[q] += y[q];
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int t = t0 + 4 * (lane + 64 * q);
+    if (dl && t < V) *reinterpret_cast<floatx4*>(dl + t) = z[q];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[4 * q + e] = t + e < V ? z[q][e] : kNegInf;
   }
   float lm = kNegInf;
 #pragma unroll
@@ -419,11 +433,14 @@ __global__ __launch_bounds__(256) void k_topk_chunk(const float* __restrict__ pa
     wv[w * K + lane] = kNegInf;   // a wave with fewer than K finite logits leaves padding
     wi[w * K + lane] = 0x7fffffff;
   }
-  wave_topk<16>(v, [&](int e) { return t0 + 4 * (lane + 64 * (e >> 2)) + (e & 3); }, K, sv[w], si[w],
-                [&](int r, float val, int id) {
-                  wv[w * K + r] = val;
-                  wi[w * K + r] = id;
-                });
+  // a wave wholly past the vocabulary end keeps the padding written above (its list would be
+  // K of its -inf pairs; with K <= V they never reach a row's top K)
+  if (t0 < V)
+    wave_topk<16>(v, [&](int e) { return t0 + 4 * (lane + 64 * (e >> 2)) + (e & 3); }, K, sv[w], si[w],
+                  [&](int r, float val, int id) {
+                    wv[w * K + r] = val;
+                    wi[w * K + r] = id;
+                  });
   if (lane == 0) {
     wmax[w] = bm;
     wsum[w] = tot;
