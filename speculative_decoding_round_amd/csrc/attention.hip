@@ -636,9 +636,10 @@ __global__ __launch_bounds__(256) void k_tree_attn_dma(DevArgs a) {
 // LSE merge.  A row's split LSEs are read at once (one per lane or thread), giving
 // m = max and the weights w_s = e^{LSE_s - m} in LDS; the weighted partials are then
 // summed with eight loads in flight.  WPR = waves per row: with few splits one wave takes
-// a row (four rows per workgroup); with many, the four waves of a workgroup take the
-// splits s = w, w+4, ... of one row and their sums are added in wave order.  Every order
-// is fixed, so the result is deterministic.
+// a row (four rows per workgroup; used when the head size has no thread-per-row kernel
+// below); with many, the four waves of a workgroup take the splits s = w, w+4, ... of one
+// row and their sums are added in wave order.  Every order is fixed, so the result is
+// deterministic.
 // ---------------------------------------------------------------------------------------
 constexpr int MERGE_MAX_S = 512;
 constexpr int MERGE_FEW_S = 16;   // up to this many splits: one wave per row
@@ -708,6 +709,66 @@ __global__ __launch_bounds__(256) void k_lse_merge(int S, int rows, int Dh,
 #pragma unroll
   for (int i = 0; i < 4; ++i) op[i] = from_f32<T>(acc[i] * inv);
   if (lse && lane == 0) lse[row] = wsum > 0.f ? m + logf(wsum) : kNegInf;
+}
+
+// LSE merge with few partials (S <= MERGE_FEW_S): a thread owns 4 output dimensions of one
+// row.  It reads the row's S split LSEs into registers (the same words for all threads of the
+// row), forms m = max and the weights itself, issues all S partial loads at once and sums them
+// in split order; nothing is exchanged between lanes.  S is a template argument: with a
+// run-time count the guarded loads are issued one after another.
+template <typename T, int DH, int S>
+__global__ __launch_bounds__(256) void k_lse_merge_rows(int rows, const float* __restrict__ o_part,
+                                                        const float* __restrict__ lse_part,
+                                                        T* __restrict__ o, float* __restrict__ lse) {
+  constexpr int TPR = DH / 4;   // threads per row
+  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+  const long row = gid / TPR;
+  const int c = (int)(gid % TPR);
+  if (row >= rows) return;
+  float l[S];
+  floatx4 v[S];
+#pragma unroll
+  for (int sp = 0; sp < S; ++sp) {
+    l[sp] = lse_part[(size_t)sp * rows + row];
+    v[sp] = __builtin_nontemporal_load(
+        reinterpret_cast<const floatx4*>(o_part + ((size_t)sp * rows + row) * DH + 4 * c));
+  }
+  float m = kNegInf;
+#pragma unroll
+  for (int sp = 0; sp < S; ++sp) m = fmaxf(m, l[sp]);
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (m != kNegInf) {
+#pragma unroll
+    for (int sp = 0; sp < S; ++sp) {
+      const float w = l[sp] == kNegInf ? 0.f : expf(l[sp] - m);
+      wsum += w;
+      acc += v[sp] * w;
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  T* op = o + (size_t)row * DH + 4 * c;
+  if constexpr (sizeof(T) == 2) {
+    typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+    bf16x4v ov;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ov[i] = static_cast<bf16>(acc[i] * inv);
+    *reinterpret_cast<bf16x4v*>(op) = ov;      // one 8-byte store
+  } else {
+    *reinterpret_cast<floatx4*>(op) = acc * inv;
+  }
+  if (lse && c == 0) lse[row] = wsum > 0.f ? m + logf(wsum) : kNegInf;
+}
+
+template <typename T, int DH, int S>
+void launch_merge_rows(int S_rt, int rows, const float* o_part, const float* lse_part, void* o, float* lse,
+                       hipStream_t st) {
+  if constexpr (S > 1) {
+    if (S_rt < S) return launch_merge_rows<T, DH, S - 1>(S_rt, rows, o_part, lse_part, o, lse, st);
+  }
+  const long threads = (long)rows * (DH / 4);
+  hipLaunchKernelGGL((k_lse_merge_rows<T, DH, S>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                     rows, o_part, lse_part, (T*)o, lse);
 }
 
 // Workgroup shape of the bf16 kernel by query rows per (request, KV head):
@@ -811,6 +872,16 @@ int launch_lse_merge(int S, int rows, int Dh, const float* o_part, const float* 
   if (rows <= 0) return EAGLE3_OK;
   if (S > MERGE_MAX_S || Dh > 128 || Dh % 4) return EAGLE3_EUNSUPPORTED;
   ProfScope ps(tag, s);
+  if (S <= MERGE_FEW_S && (Dh == 128 || Dh == 64)) {
+    if (out_dtype == EAGLE3_BF16) {
+      if (Dh == 128) launch_merge_rows<bf16, 128, MERGE_FEW_S>(S, rows, o_part, lse_part, o, lse, s);
+      else launch_merge_rows<bf16, 64, MERGE_FEW_S>(S, rows, o_part, lse_part, o, lse, s);
+    } else {
+      if (Dh == 128) launch_merge_rows<float, 128, MERGE_FEW_S>(S, rows, o_part, lse_part, o, lse, s);
+      else launch_merge_rows<float, 64, MERGE_FEW_S>(S, rows, o_part, lse_part, o, lse, s);
+    }
+    return launch_status();
+  }
   const bool few = S <= MERGE_FEW_S;
   const dim3 grid(few ? (rows + 3) / 4 : rows);
   if (out_dtype == EAGLE3_BF16) {

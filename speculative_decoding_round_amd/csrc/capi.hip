@@ -200,7 +200,7 @@ int eagle3_lse_merge(int S, int rows, int Dh, const float* o_part, const float* 
   if (!dtype_ok(out_dtype)) return EAGLE3_EINVAL;
   if (rows == 0) return EAGLE3_OK;
   if (!o_part || !lse_part || !o) return EAGLE3_EINVAL;
-  if ((uintptr_t)o_part % 16) return EAGLE3_EINVAL;
+  if ((uintptr_t)o_part % 16 || (uintptr_t)o % 16) return EAGLE3_EINVAL;
   return launch_lse_merge(S, rows, Dh, o_part, lse_part, out_dtype, o, lse, (hipStream_t)stream,
                           "lse_merge");
 }

@@ -75,6 +75,7 @@ def test_host_validation_rejects_before_launch(lib):
     # merge
     assert L.eagle3_lse_merge(0, 4, 8, 8, 8, 0, 8, None, None) == -1
     assert L.eagle3_lse_merge(2, 4, 6, 8, 8, 0, 8, None, None) == -1
+    assert L.eagle3_lse_merge(2, 4, 8, 16, 16, 0, 24, None, None) == -1   # output not 16-byte aligned
     # accept: workspace too small, negative temperature
     assert L.eagle3_accept(1, 3, 8, 8, 8, 8, 1, 8, 100, 1, 0.0, 0, 0, 2, 8, 8, 8, 8, None, 0, None) == -3
     assert L.eagle3_accept(1, 3, 8, 8, 8, 8, 1, 8, 100, 1, -1.0, 0, 0, 2, 8, 8, 8, 8, 8, 1 << 20, None) == -1
