@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--no-ops", action="store_true", help="skip the per-op roofline measurements")
     ap.add_argument("--only-ops", action="store_true",
                     help="measure only the per-op rooflines (no round, no CPU baseline)")
+    ap.add_argument("--ops", default=",".join(OP_KEYS),
+                    help="comma-separated per-op measurements to run")
     ap.add_argument("--kernel", default="gemm_lm_head", help="kernel timed for the roofline")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (for scaling HBM byte "
@@ -113,17 +115,31 @@ class Round:
         self.round += 1
 
 
-def recorded_traffic(workload: str):
-    """HBM bytes per LM-head launch measured by rocprofv3 counters (profiles/), or None if
-    they were taken on another workload or on a different GEMM kernel source."""
+def recorded(name: str, field: str):
+    """A figure stored under profiles/<name>.txt by profsum (rocprofv3 counters), or None if
+    it is missing or was measured on a different source of the kernel."""
     from speculative_decoding_round_amd import profsum
-    path = os.path.join(ROOT, "profiles", f"gemm_lm_head_{workload}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"{name}.txt")
     if not os.path.exists(path):
         return None
     kv = dict(line.split(": ", 1) for line in open(path).read().splitlines() if ": " in line)
-    if kv.get("gemm_source_sha256_16") != profsum.gemm_source_hash():
+    if kv.get("source_sha256_16") != profsum.source_hash(profsum.sources_for(kv.get("kernel", ""))):
         return None
-    return int(kv["traffic_bytes_per_launch"])
+    return int(kv[field]) if field in kv else None
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per LM-head launch measured by rocprofv3 counters (profiles/)."""
+    return recorded(f"gemm_lm_head_{workload}_traffic", "traffic_bytes_per_launch")
+
+
+# counters stored per op (profiles/<name>.txt): HBM traffic per launch, VALU instructions
+OP_PROFILES = {"attn_longctx": "tree_attention_longctx_traffic", "merge": "lse_merge_longctx_training_traffic",
+               "accept_greedy": "accept_scan_llama8b_greedy_traffic"}
+VALU_PROFILE = {"accept_t07": "accept_scan_llama70b_t07_valu"}
+# one full-rate wave64 VALU instruction per SIMD every 4 clocks: 256 CUs x 4 SIMDs x 16 lanes
+# x 2.4 GHz lane-instructions per second
+VALU_PEAK_LANE_INSTR = 256 * 4 * 16 * 2.4e9
 
 
 def lm_head_bytes(shape, M):
@@ -289,44 +305,56 @@ def attention_op(capi, synth, shape, trees, prefix, bound, reps=20, seed=500):
                   rotating_copies=ncopy)
 
 
-def op_rooflines(reps=20):
+OP_KEYS = ("attn_longctx", "attn_batch16", "attn_70b", "attn_8b", "merge", "accept_greedy", "accept_t07")
+
+
+def op_rooflines(reps=20, keys=OP_KEYS):
     import numpy as np
     import torch
     from speculative_decoding_round_amd import capi, synth
     dev = "cuda:0"
     ops = []
-    # long-context branch: 7 chain queries over a 65536-token prefix (HBM-bound)
-    sh = synth.LONGCTX
-    ops.append(attention_op(capi, synth, sh, [synth.chain_tree(sh.branch)], [65536], "hbm", reps))
-    # batched serving: 16 random trees of <= 48 nodes, prefixes uniform in [512, 4096] (HBM-bound)
-    sh = synth.BATCH16
-    prefix = synth.prefix_lengths(sh, seed=31)
-    rng = np.random.default_rng(31)
-    trees = [synth.random_tree(int(rng.integers(1, sh.verify_max_nodes + 1)), sh.verify_max_depth, 3100 + i)
-             for i in range(sh.B)]
-    ops.append(attention_op(capi, synth, sh, trees, prefix, "hbm", reps))
-    # 70B-shaped verify: 4 x (root + 60 nodes), 488 query rows per KV head (MFMA-bound)
-    sh = synth.LLAMA70B
-    trees = [synth.random_tree(61, sh.depth, 4100 + i) for i in range(sh.B)]
-    ops.append(attention_op(capi, synth, sh, trees, synth.prefix_lengths(sh, 41), "mfma", reps))
-    # 8B-shaped verify (60-node tree over 2048 keys): latency-sized, reported for both bounds
-    sh = synth.LLAMA8B
-    ops.append(attention_op(capi, synth, sh, [synth.random_tree(61, sh.depth, 4200)], [2048], "hbm", reps))
-
-    # LSE merge at the long-context training scale: two partials of 65536 x 32 rows
-    rows, Dh = 65536 * 32, 128
-    o_part = synth.normal((2, rows, Dh), 1.0, 900, torch.float32, dev)
-    lse_part = synth.normal((2, rows), 1.0, 901, torch.float32, dev)
-    mo = {"o": torch.empty((rows, Dh), dtype=torch.bfloat16, device=dev),
-          "lse": torch.empty((rows,), dtype=torch.float32, device=dev)}
-    us = _time_tag(capi, "lse_merge", lambda i: capi.eagle3_lse_merge(o_part, lse_part, out=mo), reps)
-    ops.append(_entry("lse_merge", "2 partials x 65536 positions x 32 heads x 128 (fp32 -> bf16)",
-                      "k_lse_merge", us, "hbm", bytes_=2 * rows * (Dh + 1) * 4 + rows * (Dh * 2 + 4)))
-    del o_part, lse_part, mo
-
+    if "attn_longctx" in keys:
+        # long-context branch: 7 chain queries over a 65536-token prefix (HBM-bound)
+        sh = synth.LONGCTX
+        e = attention_op(capi, synth, sh, [synth.chain_tree(sh.branch)], [65536], "hbm", reps)
+        ops.append(dict(key="attn_longctx", **e))
+    if "attn_batch16" in keys:
+        # batched serving: 16 random trees of <= 48 nodes, prefixes uniform in [512, 4096] (HBM-bound)
+        sh = synth.BATCH16
+        prefix = synth.prefix_lengths(sh, seed=31)
+        rng = np.random.default_rng(31)
+        trees = [synth.random_tree(int(rng.integers(1, sh.verify_max_nodes + 1)), sh.verify_max_depth, 3100 + i)
+                 for i in range(sh.B)]
+        ops.append(dict(key="attn_batch16", **attention_op(capi, synth, sh, trees, prefix, "hbm", reps)))
+    if "attn_70b" in keys:
+        # 70B-shaped verify: 4 x (root + 60 nodes), 488 query rows per KV head (MFMA-bound)
+        sh = synth.LLAMA70B
+        trees = [synth.random_tree(61, sh.depth, 4100 + i) for i in range(sh.B)]
+        ops.append(dict(key="attn_70b", **attention_op(capi, synth, sh, trees, synth.prefix_lengths(sh, 41),
+                                                        "mfma", reps)))
+    if "attn_8b" in keys:
+        # 8B-shaped verify (60-node tree over 2048 keys): latency-sized, reported for both bounds
+        sh = synth.LLAMA8B
+        ops.append(dict(key="attn_8b", **attention_op(capi, synth, sh, [synth.random_tree(61, sh.depth, 4200)],
+                                                       [2048], "hbm", reps)))
+    if "merge" in keys:
+        # LSE merge at the long-context training scale: two partials of 65536 x 32 rows
+        rows, Dh = 65536 * 32, 128
+        o_part = synth.normal((2, rows, Dh), 1.0, 900, torch.float32, dev)
+        lse_part = synth.normal((2, rows), 1.0, 901, torch.float32, dev)
+        mo = {"o": torch.empty((rows, Dh), dtype=torch.bfloat16, device=dev),
+              "lse": torch.empty((rows,), dtype=torch.float32, device=dev)}
+        us = _time_tag(capi, "lse_merge", lambda i: capi.eagle3_lse_merge(o_part, lse_part, out=mo), reps)
+        ops.append(dict(key="merge", **_entry("lse_merge", "2 partials x 65536 positions x 32 heads x 128 "
+                                              "(fp32 -> bf16)", "k_lse_merge_rows", us, "hbm",
+                                              bytes_=2 * rows * (Dh + 1) * 4 + rows * (Dh * 2 + 4))))
+        del o_part, lse_part, mo
     # acceptance: greedy at the 8B shape (61 nodes x 128256 bf16 logits), T = 0.7 at the 70B
     # shape (4 x 61 nodes)
-    for sh, B, temp in ((synth.LLAMA8B, 1, 0.0), (synth.LLAMA70B, 4, 0.7)):
+    for key, sh, B, temp in (("accept_greedy", synth.LLAMA8B, 1, 0.0), ("accept_t07", synth.LLAMA70B, 4, 0.7)):
+        if key not in keys:
+            continue
         trees = [synth.random_tree(61, sh.depth, 4300 + i) for i in range(B)]
         vi = synth.verify_inputs(sh, trees, [0] * B, seed=950, device=dev, with_logits=False)
         mk = capi.eagle3_build_tree_mask(vi["cu_nodes"], vi["parents"], None, max_nodes=61)
@@ -345,12 +373,23 @@ def op_rooflines(reps=20):
         us_scan = _time_tag(capi, "accept_scan", run, reps)
         us_path = _time_tag(capi, "accept_path", run, reps)
         name = "greedy" if temp == 0 else f"T={temp}"
-        ops.append(_entry(f"accept_scan ({name})", f"{sh.name}: {T} nodes x {V} logits", "k_accept_scan",
-                          us_scan, "hbm", bytes_=lbytes, accept_path_us=round(us_path, 2),
-                          rotating_copies=ncopy,
-                          logits_per_s=round(T * V / (us_scan * 1e-6) / 1e9, 2)))
+        ops.append(dict(key=key, **_entry(f"accept_scan ({name})", f"{sh.name}: {T} nodes x {V} logits",
+                                          "k_accept_scan", us_scan, "hbm", bytes_=lbytes,
+                                          accept_path_us=round(us_path, 2), rotating_copies=ncopy,
+                                          logits_per_s=round(T * V / (us_scan * 1e-6) / 1e9, 2))))
         del logits
     torch.cuda.empty_cache()
+    for o in ops:
+        if o["key"] in OP_PROFILES:
+            o["traffic"] = recorded(OP_PROFILES[o["key"]], "traffic_bytes_per_launch")
+        if o["key"] in VALU_PROFILE:
+            n = recorded(VALU_PROFILE[o["key"]], "sq_insts_valu_per_launch")
+            if n is not None:
+                # the scan is bound by its arithmetic (Philox + two float32 logs per logit)
+                ach = n * 64 / (o["avg_launch_us"] * 1e-6)
+                o.update({"bound": "alu", "achieved": round(ach / 1e12, 2), "peak": round(VALU_PEAK_LANE_INSTR / 1e12, 2),
+                          "unit": "T VALU lane-instr/s", "frac": round(ach / VALU_PEAK_LANE_INSTR, 4),
+                          "valu_wave_instr_per_launch": n})
     return ops
 
 
@@ -400,8 +439,17 @@ def main():
     import torch
     from speculative_decoding_round_amd import capi, synth
     dev = "cuda:0"
+    keys = tuple(k for k in args.ops.split(",") if k)
     if args.only_ops:
-        print(json.dumps({"ops": op_rooflines()}), flush=True)
+        out = {"ops": op_rooflines(keys=keys)}
+        if args.copy_calibration_mb > 0:
+            n = args.copy_calibration_mb << 20
+            src = torch.empty(n, dtype=torch.uint8, device=dev)
+            dst = torch.empty(n, dtype=torch.uint8, device=dev)
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            out["copy_calibration_bytes"] = n
+        print(json.dumps(out), flush=True)
         return
     shape = {"llama8b": synth.LLAMA8B, "batch16": synth.BATCH16, "llama70b": synth.LLAMA70B,
              "tiny": synth.TINY}[args.workload]
@@ -476,7 +524,7 @@ def main():
     if not args.no_ops:
         del rnd
         torch.cuda.empty_cache()
-        line["ops"] = op_rooflines()
+        line["ops"] = op_rooflines(keys=keys)
     print(json.dumps(line), flush=True)
 
 

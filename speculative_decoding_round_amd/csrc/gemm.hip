@@ -7,6 +7,8 @@
 // load traffic of W), with the next W tile in flight while the current one is multiplied.
 // A workgroup is WK waves that split its k-range (summed in LDS in wave order, so results
 // are deterministic); workgroups tile (n-block, k-split).
+#include <cstring>
+
 #include "common.h"
 #include "internal.h"
 
@@ -186,24 +188,38 @@ __device__ __forceinline__ void ring_wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int MT, int NTB, int NST, bool SILU>
-__global__ __launch_bounds__(64) void k_gemm_ring(const bf16* __restrict__ X, int M, int ldx,
-                                                  const bf16* __restrict__ W, int N, int K,
-                                                  float* __restrict__ Y, int n_blocks,
-                                                  int chunks_total, int chunks_per_split,
-                                                  void* __restrict__ act, int F) {
+// ROLE names the projection (0 other, 1 LM head, 2 QKV, 3 O, 4 MLP down, 5 fusion, 6 MLP
+// gate/up).  It does not change the code; each projection gets its own kernel symbol, so that
+// profiles and hardware counters attribute launches to projections.
+// WK waves share a workgroup's n-block: wave w streams the w-th part of the workgroup's
+// k-range through its own ring, and the WK partial tiles are summed in LDS in wave order at
+// the end (deterministic), so a k-split over WK waves costs no partial-sum traffic.
+template <int MT, int NTB, int NST, bool SILU, int ROLE, int WK>
+__global__ __launch_bounds__(64 * WK) void k_gemm_ring(const bf16* __restrict__ X, int M, int ldx,
+                                                       const bf16* __restrict__ W, int N, int K,
+                                                       float* __restrict__ Y, int n_blocks,
+                                                       int chunks_total, int chunks_per_split,
+                                                       void* __restrict__ act, int F) {
   static_assert(MT >= 1 && MT <= 2, "X is held in registers for one k-block");
   static_assert(NST >= 2 && 8 * (NST - 2) <= 63, "outstanding DMA must fit the vmcnt counter");
+  static_assert((WK - 1) * NTB * MT * 64 * 16 <= WK * NST * RING_TILE, "reduction fits the rings");
   constexpr int SPK = MT + NTB;   // ring stages per k-block
-  __shared__ __attribute__((aligned(16))) char ring[NST * RING_TILE];
-  const int lane = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) char ring[WK * NST * RING_TILE];
+  const int lane = threadIdx.x & 63;
+  const int wv_id = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int nb = blockIdx.x % n_blocks, ks = blockIdx.x / n_blocks;
-  const int cs0 = ks * chunks_per_split;
-  const int cs1 = min(chunks_total, cs0 + chunks_per_split);
+  // this wave's chunk range: the workgroup's split, cut into WK parts of whole 8-chunk blocks
+  const int ws0 = ks * chunks_per_split;
+  const int ws1 = min(chunks_total, ws0 + chunks_per_split);
+  const int wblocks = ws1 > ws0 ? (ws1 - ws0 + 7) / 8 : 0;
+  const int per_wave = (wblocks + WK - 1) / WK;
+  const int cs0 = min(ws1, ws0 + wv_id * per_wave * 8);
+  const int cs1 = min(ws1, cs0 + per_wave * 8);
   const int n_kb = cs1 > cs0 ? (cs1 - cs0 + 7) / 8 : 0;
   const int total = n_kb * SPK;
-  const uint32_t ring0 = lds_u32(ring);
+  const uint32_t ring0 = lds_u32(ring) + (uint32_t)wv_id * (NST * RING_TILE);
+  char* myring = ring + wv_id * (NST * RING_TILE);
 
   // DMA of stage s (k-block s / SPK; X tile, or W tile of this workgroup's n-block)
   auto issue = [&](int s) {
@@ -255,7 +271,7 @@ __global__ __launch_bounds__(64) void k_gemm_ring(const bf16* __restrict__ X, in
     for (int r = 0; r < SPK; ++r, ++s) {
       if (s + NST - 2 < total) ring_wait_vm<8 * (NST - 2)>();
       else ring_wait_vm<0>();
-      const char* slot = ring + (s % NST) * RING_TILE;
+      const char* slot = myring + (s % NST) * RING_TILE;
       if (r < MT) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -275,6 +291,27 @@ __global__ __launch_bounds__(64) void k_gemm_ring(const bf16* __restrict__ X, in
     }
   }
 
+  if constexpr (WK > 1) {
+    // waves 1.. hand their tiles to wave 0 through LDS (the rings are drained: every wave's
+    // last stage waited for vmcnt(0) before it was read)
+    floatx4* red = reinterpret_cast<floatx4*>(ring);
+    __syncthreads();
+    if (wv_id > 0) {
+#pragma unroll
+      for (int nt = 0; nt < NTB; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) red[(((wv_id - 1) * NTB + nt) * MT + mt) * 64 + lane] = acc[nt][mt];
+    }
+    __syncthreads();
+    if (wv_id > 0) return;
+#pragma unroll
+    for (int w = 1; w < WK; ++w)
+#pragma unroll
+      for (int nt = 0; nt < NTB; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[nt][mt] += red[(((w - 1) * NTB + nt) * MT + mt) * 64 + lane];
+  }
+
   float* Ys = Y + (size_t)ks * M * N;
   constexpr int NOUT = SILU ? NTB / 2 : NTB;
 #pragma unroll
@@ -287,11 +324,11 @@ __global__ __launch_bounds__(64) void k_gemm_ring(const bf16* __restrict__ X, in
     }
 }
 
-// Ring kernel shape: 8 W tiles (128 output features) per workgroup, 4 ring slots (32 KB
-// of LDS, five workgroups per CU).
+// Ring kernel shape: 8 W tiles (128 output features) per workgroup, 4 ring slots of 8 KB per
+// wave (five one-wave workgroups per CU).
 constexpr int kRingNTB = 8, kRingNST = 4;
-// Workgroups aimed for by the k-split of ring launches (about four per CU).
-constexpr int kRingTargetWgs = 800;
+// Waves aimed for by the k-split of the projections. ring launches (four per CU).
+constexpr int kRingTargetWgs = 1024;
 
 // out[m][n] = (resid ? resid[m][n] : 0) + sum_s part[s][m][n]
 __global__ __launch_bounds__(256) void k_epi_sum(const float* __restrict__ part, int S, int M, int N,
@@ -337,19 +374,47 @@ int dispatch_mt(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, f
   return e3h::launch_status();
 }
 
-template <int MT>
-int launch_ring(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm_ring<MT, kRingNTB, kRingNST, false>), dim3(p.n_blocks * p.splits), dim3(64), 0,
-                     s, (const bf16*)X, p.M, ldx, (const bf16*)W, p.N, p.K, Y, p.n_blocks, p.chunks_total,
-                     p.chunks_per_split, nullptr, p.N / 2);
+template <int MT, int ROLE, int WK, bool SILU>
+int launch_ring_r(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y, void* act,
+                  hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm_ring<MT, kRingNTB, kRingNST, SILU, ROLE, WK>), dim3(p.n_blocks * p.splits),
+                     dim3(64 * WK), 0, s, (const bf16*)X, p.M, ldx, (const bf16*)W, p.N, p.K, Y, p.n_blocks,
+                     p.chunks_total, p.chunks_per_split, act, p.N / 2);
   return e3h::launch_status();
+}
+
+inline int gemm_role(const char* tag) {
+  static const char* names[] = {"gemm_lm_head", "gemm_qkv", "gemm_o", "gemm_down", "gemm_fuse", "gemm_gate_up"};
+  for (int i = 0; i < 6; ++i)
+    if (tag && strcmp(tag, names[i]) == 0) return i + 1;
+  return 0;
+}
+
+// Instantiated shapes: the LM head one wave per workgroup; the other projections two; the
+// SiLU gate/up four.
+template <int MT>
+int launch_ring(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y, void* act,
+                hipStream_t s, int role) {
+  if (p.silu) return launch_ring_r<MT, 6, 4, true>(p, X, ldx, W, Y, act, s);
+  if (p.waves == 1) return launch_ring_r<MT, 1, 1, false>(p, X, ldx, W, Y, act, s);
+  switch (role) {
+    case 2: return launch_ring_r<MT, 2, 2, false>(p, X, ldx, W, Y, act, s);
+    case 3: return launch_ring_r<MT, 3, 2, false>(p, X, ldx, W, Y, act, s);
+    case 4: return launch_ring_r<MT, 4, 2, false>(p, X, ldx, W, Y, act, s);
+    case 5: return launch_ring_r<MT, 5, 2, false>(p, X, ldx, W, Y, act, s);
+    default: return launch_ring_r<MT, 0, 2, false>(p, X, ldx, W, Y, act, s);
+  }
 }
 
 template <typename T>
 int dispatch_gemm(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y,
-                  void* act, hipStream_t s) {
+                  void* act, hipStream_t s, const char* tag) {
   if constexpr (sizeof(T) == 2) {
-    if (p.ring) return p.MT == 1 ? launch_ring<1>(p, X, ldx, W, Y, s) : launch_ring<2>(p, X, ldx, W, Y, s);
+    if (p.ring) {
+      const int role = gemm_role(tag);
+      return p.MT == 1 ? launch_ring<1>(p, X, ldx, W, Y, act, s, role)
+                       : launch_ring<2>(p, X, ldx, W, Y, act, s, role);
+    }
   }
   switch (p.MT) {
     case 1: return dispatch_mt<T, 1>(p, X, ldx, W, Y, act, s);
@@ -378,18 +443,27 @@ GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu) {
   p.N = N;
   p.K = K;
   const int mt_need = (M + 15) / 16;
-  if (dtype == EAGLE3_BF16 && !silu && mt_need <= 2 && K % 32 == 0) {
-    // LDS-ring kernel: 128 output features per workgroup and a k-split in whole 8-chunk
-    // blocks that brings the grid to about kRingTargetWgs workgroups
+  if (dtype == EAGLE3_BF16 && mt_need <= 2 && K % 32 == 0 &&
+      (!silu || (N / 2) % (16 * (kRingNTB / 2)) == 0)) {
+    // LDS-ring kernel, 128 output features (or 64 gate + 64 up) per workgroup.  The LM head
+    // has enough n-blocks for one wave per workgroup and no k-split; the SiLU gate/up needs
+    // the whole k-range in one workgroup (four waves); the other projections use two waves
+    // and a k-split in whole blocks to about kRingTargetWgs waves.
     p.ring = true;
     p.MT = mt_need < 1 ? 1 : mt_need;
     p.NT = kRingNTB;
-    p.waves = 1;
-    p.n_blocks = ((N + 15) / 16 + kRingNTB - 1) / kRingNTB;
     p.chunks_total = K / 32;
-    int splits = (kRingTargetWgs + p.n_blocks - 1) / p.n_blocks;
+    int splits = 1;
+    if (silu) {
+      p.n_blocks = (N / 2) / (16 * (kRingNTB / 2));
+      p.waves = 4;
+    } else {
+      p.n_blocks = ((N + 15) / 16 + kRingNTB - 1) / kRingNTB;
+      p.waves = p.n_blocks >= 512 ? 1 : 2;
+      splits = (kRingTargetWgs + p.n_blocks * p.waves - 1) / (p.n_blocks * p.waves);
+    }
     int cps = (p.chunks_total + splits - 1) / splits;
-    cps = (cps + 7) / 8 * 8;
+    cps = (cps + 8 * p.waves - 1) / (8 * p.waves) * (8 * p.waves);
     p.chunks_per_split = cps;
     p.splits = (p.chunks_total + cps - 1) / cps;
     return p;
@@ -434,8 +508,8 @@ int launch_gemm(const GemmPlan& p, int dtype, const void* X, int ldx, const void
   if (p.MT == 0) return EAGLE3_EUNSUPPORTED;
   if (p.silu && (!act || (p.N / 2) % (16 * (p.NT / 2)))) return EAGLE3_EUNSUPPORTED;
   ProfScope ps(tag, s);
-  if (dtype == EAGLE3_BF16) return dispatch_gemm<bf16>(p, X, ldx, W, Ypart, act, s);
-  return dispatch_gemm<float>(p, X, ldx, W, Ypart, act, s);
+  if (dtype == EAGLE3_BF16) return dispatch_gemm<bf16>(p, X, ldx, W, Ypart, act, s, tag);
+  return dispatch_gemm<float>(p, X, ldx, W, Ypart, act, s, tag);
 }
 
 int launch_epi_sum(const GemmPlan& p, const float* part, float* out, const float* resid,

@@ -79,7 +79,7 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32
 
 // ln v for positive normal v: v = 2^e m, m in [sqrt(1/2), sqrt(2)); s = (m-1)/(m+1);
 // ln v = e*ln2_hi + (e*ln2_lo + 2*(s + s^3 (1/3 + s^2 (1/5 + s^2 (1/7 + s^2/9))))).
-__device__ __noinline__ float ln_fixed(float v) {
+__device__ __forceinline__ float ln_fixed(float v) {
 #pragma clang fp contract(off)
   const uint32_t bits = __float_as_uint(v);
   int e = (int)((bits >> 23) & 0xffu) - 127;

@@ -1,14 +1,20 @@
 """Turn rocprofv3 CSV output into the short text summaries kept under profiles/.
 
     python -m speculative_decoding_round_amd.profsum stats  KERNEL_STATS_CSV BENCH_JSON OUT.txt CMD
-    python -m speculative_decoding_round_amd.profsum traffic FETCH_CSV WRITE_CSV OUT.txt CMD
+    python -m speculative_decoding_round_amd.profsum opstats KERNEL_STATS_CSV OPS_JSON OUT.txt CMD
+    python -m speculative_decoding_round_amd.profsum traffic FETCH_CSV WRITE_CSV OUT.txt CMD [KERNEL_RE [TITLE]]
+    python -m speculative_decoding_round_amd.profsum counter CSV OUT.txt CMD KERNEL_RE COUNTER
 
 `stats` lists the kernels of a `rocprofv3 --kernel-trace --stats` run with their average
 duration, marks the LM-head GEMM and puts bench.py's own event-timed average beside it.
+`opstats` does the same for a `bench.py --only-ops --ops KEY` run (one op's kernels) and puts
+the op's event-timed average and roofline fraction beside the profiler's average.
 `traffic` reads one `--pmc FETCH_SIZE` and one `--pmc WRITE_SIZE` run (KiB per dispatch),
 scales both by what the same counter reads for the plain 1 GiB device copy that
-`bench.py --copy-calibration-mb 1024` adds, and records the HBM bytes per LM-head launch
-with a hash of the GEMM kernel source, so bench.py can tell when they went stale.
+`bench.py --copy-calibration-mb 1024` adds, and records the HBM bytes per launch of the
+kernel matching KERNEL_RE (default: the LM head) with a hash of the kernel sources, so
+bench.py can tell when they went stale.  `counter` records the per-dispatch average of any
+one counter for one kernel (e.g. SQ_INSTS_VALU).
 """
 from __future__ import annotations
 
@@ -21,20 +27,51 @@ import sys
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LM_HEAD_KERNEL = re.compile(r"k_gemm_ring<1, 8, 4, false>")   # the LM head (one 16-row tile of rows)
+LM_HEAD_KERNEL = re.compile(r"k_gemm_ring<1, 8, 4, false, 1, 1>")   # the LM head (role 1), one row tile
 
 
-def gemm_source_hash() -> str:
+def source_hash(files=("gemm.hip", "common.h")) -> str:
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.h"):
+    for f in files:
         with open(os.path.join(PKG, "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
+def gemm_source_hash() -> str:
+    return source_hash(("gemm.hip", "common.h"))
+
+
+# kernel name pattern -> the sources its code comes from (for staleness of stored counters)
+KERNEL_SOURCES = {"k_gemm_ring": ("gemm.hip", "common.h"),
+                  "k_tree_attn_dma": ("attention.hip", "common.h"),
+                  "k_lse_merge": ("attention.hip", "common.h"),
+                  "k_accept_scan": ("verify.hip", "common.h")}
+
+
+def sources_for(kernel_re: str):
+    for k, v in KERNEL_SOURCES.items():
+        if k in kernel_re:
+            return v
+    return ("gemm.hip", "common.h")
+
+
+RING_ROLES = {"1": "LM head", "2": "QKV", "3": "O projection", "4": "MLP down", "5": "feature fusion",
+              "6": "MLP gate/up (SiLU)"}
+
+
 def _short(name: str) -> str:
     m = re.search(r"(k_[a-z_0-9]+)(<[^()]*>)?", name)
     return (m.group(1) + (m.group(2) or "")) if m else name[:60]
+
+
+def _role(name: str) -> str:
+    m = re.search(r"k_gemm_ring<\d+, \d+, \d+, (?:false|true), (\d+), \d+>", name)
+    if m and m.group(1) in RING_ROLES:
+        return "  <- " + RING_ROLES[m.group(1)]
+    if re.search(r"k_gemm<[^>]*true>", name):
+        return "  <- MLP gate/up (SiLU)"
+    return ""
 
 
 def stats(csv_path, bench_json, out, cmd):
@@ -43,7 +80,7 @@ def stats(csv_path, bench_json, out, cmd):
     lines = [f"# rocprofv3 kernel stats, {bench['config']['workload']}", f"command: {cmd}", "",
              f"{'calls':>6} {'avg_us':>10} {'total_%':>8}  kernel"]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"]))[:24]:
-        mark = "  <- LM head" if LM_HEAD_KERNEL.search(r["Name"]) else ""
+        mark = _role(r["Name"])
         lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
                      f"{float(r['Percentage']):8.2f}  {_short(r['Name'])}{mark}")
     lm = [r for r in rows if LM_HEAD_KERNEL.search(r["Name"])]
@@ -55,6 +92,21 @@ def stats(csv_path, bench_json, out, cmd):
     open(out, "w").write("\n".join(lines) + "\n")
 
 
+def opstats(csv_path, ops_json, out, cmd):
+    rows = list(csv.DictReader(open(csv_path)))
+    ops = json.loads(open(ops_json).read().strip().splitlines()[-1])["ops"]
+    lines = [f"# rocprofv3 kernel stats, per-op measurement: " + ", ".join(o["op"] + " on " + o["workload"] for o in ops),
+             f"command: {cmd}", "", f"{'calls':>6} {'avg_us':>10} {'total_%':>8}  kernel"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"]))[:12]:
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['Percentage']):8.2f}  {_short(r['Name'])}")
+    lines.append("")
+    for o in ops:
+        lines.append(f"bench.py (HIP events, same run): {o['op']} on {o['workload']}: {o['avg_launch_us']} us, "
+                     f"{o.get('achieved')} {o.get('unit')} = {o.get('frac')} of peak ({o['bound']}-bound)")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
 def _per_kernel(csv_path):
     agg = defaultdict(list)
     for r in csv.DictReader(open(csv_path)):
@@ -62,17 +114,19 @@ def _per_kernel(csv_path):
     return agg
 
 
-def traffic(fetch_csv, write_csv, out, cmd):
+def traffic(fetch_csv, write_csv, out, cmd, kernel_re=None, title=None):
+    pat = re.compile(kernel_re) if kernel_re else LM_HEAD_KERNEL
     f, w = _per_kernel(fetch_csv), _per_kernel(write_csv)
     copy = [k for k in f if "copyBuffer" in k]
     known = 1 << 20                                     # KiB moved each way by the 1 GiB copy
     f_copy = max(max(f[k]) for k in copy)
     w_copy = max(max(w[k]) for k in copy)
     ff, wf = known / f_copy, known / w_copy
-    lm = [k for k in f if LM_HEAD_KERNEL.search(k)][0]
+    lm = [k for k in f if pat.search(k)][0]
     fetch = sum(f[lm]) / len(f[lm]) * ff * 1024
     write = sum(w[lm]) / len(w[lm]) * wf * 1024
-    lines = ["# HBM traffic of the LM-head GEMM (rocprofv3 --pmc), llama8b workload",
+    lines = [f"# HBM traffic of {title or 'the LM-head GEMM, llama8b workload'} (rocprofv3 --pmc)",
+             f"kernel: {_short(lm)}",
              f"command_fetch: {cmd.format(counter='FETCH_SIZE')}",
              f"command_write: {cmd.format(counter='WRITE_SIZE')}",
              f"copy_calibration: 1 GiB device copy reads {f_copy:.0f} KiB by FETCH_SIZE and writes "
@@ -81,7 +135,18 @@ def traffic(fetch_csv, write_csv, out, cmd):
              f"launches: {len(f[lm])}",
              f"fetch_bytes_per_launch: {fetch:.0f}", f"write_bytes_per_launch: {write:.0f}",
              f"traffic_bytes_per_launch: {fetch + write:.0f}",
-             f"gemm_source_sha256_16: {gemm_source_hash()}"]
+             f"source_sha256_16: {source_hash(sources_for(_short(lm)))}"]
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+def counter(csv_path, out, cmd, kernel_re, name):
+    pat = re.compile(kernel_re)
+    agg = _per_kernel(csv_path)
+    k = [k for k in agg if pat.search(k)][0]
+    avg = sum(agg[k]) / len(agg[k])
+    lines = [f"# {name} per dispatch of {_short(k)} (rocprofv3 --pmc)", f"command: {cmd}",
+             f"kernel: {_short(k)}", f"launches: {len(agg[k])}", f"{name.lower()}_per_launch: {avg:.0f}",
+             f"source_sha256_16: {source_hash(sources_for(_short(k)))}"]
     open(out, "w").write("\n".join(lines) + "\n")
 
 
@@ -89,7 +154,11 @@ if __name__ == "__main__":
     mode = sys.argv[1]
     if mode == "stats":
         stats(*sys.argv[2:6])
+    elif mode == "opstats":
+        opstats(*sys.argv[2:6])
     elif mode == "traffic":
-        traffic(*sys.argv[2:6])
+        traffic(*sys.argv[2:8])
+    elif mode == "counter":
+        counter(*sys.argv[2:7])
     else:
         raise SystemExit(__doc__)

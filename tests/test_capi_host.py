@@ -104,3 +104,29 @@ def test_draft_validation_and_workspace(lib):
     assert st == -1   # misaligned h_low
     w.head_dim = 80
     assert lib.eagle3_draft_expand_workspace_size(ctypes.byref(w), ctypes.byref(t), 1, 2048) == 0
+
+
+def test_draft_workspace_is_a_function_of_the_shapes(lib):
+    """The workspace size (and so every launch plan behind it) depends on the shapes alone:
+    the same shapes give the same size whatever was computed before and whatever the
+    weight addresses are.  Covers the fp32 path, bf16 with few rows (LDS-ring GEMMs) and bf16
+    with 160 rows (register-stationary GEMMs)."""
+    from speculative_decoding_round_amd.capi import Eagle3Drafter, Eagle3TreeCfg
+
+    def size(d, hq, hkv, dh, f, v, dt, b, tree, prefix, base):
+        w = Eagle3Drafter(d=d, n_heads_q=hq, n_heads_kv=hkv, head_dim=dh, ffn=f, vocab=v, dtype=dt,
+                          eps=1e-5, rope_theta=5e5)
+        for i, k in enumerate(capi.WEIGHT_KEYS):
+            setattr(w, k, base + 4096 * i)
+        t = Eagle3TreeCfg(*tree)
+        return lib.eagle3_draft_expand_workspace_size(ctypes.byref(w), ctypes.byref(t), b, prefix)
+
+    shapes = [(256, 4, 4, 64, 1024, 1024, 0, 1, (3, 2, 4, 14), 128),
+              (4096, 32, 8, 128, 14336, 128256, 1, 1, (6, 10, 10, 60), 2048),
+              (4096, 32, 8, 128, 14336, 128256, 1, 16, (6, 10, 10, 48), 4096),
+              (512, 8, 8, 64, 1536, 8192, 0, 2, (4, 5, 6, 20), 513)]
+    first = [size(*s, base=1 << 20) for s in shapes]
+    assert all(x > 0 for x in first)
+    for rep in range(3):
+        again = [size(*s, base=(1 << 40) + rep * (1 << 24)) for s in reversed(shapes)][::-1]
+        assert again == first
