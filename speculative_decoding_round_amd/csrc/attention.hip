@@ -286,11 +286,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 constexpr int kWaitVm0 = 0x0F70;
 
 // Address = wave-uniform base (SGPRs) + this lane's 32-bit byte offset.
+// M0 is written by the asm and named as clobbered; the compiler does not preserve reserved
+// registers across asm (hence its warning), which is harmless: nothing else in these
+// kernels keeps a value in M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16_nt_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase),
                "s"(lds_base)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 template <int CPR>
 __device__ __forceinline__ int kv_swz(int key) {

@@ -172,9 +172,10 @@ __device__ __forceinline__ float block_max(float v, float* scratch) {
   return t;
 }
 
-// (value desc, index asc) ordering used by every argmax / top-K in the library.
+// (value desc, index asc) ordering used by every argmax / top-K in the library.  Written with
+// non-short-circuit operators: the short-circuit form compiles to exec-mask branches in loops.
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
+  return (va > vb) | ((va == vb) & (ia < ib));
 }
 
 __device__ __forceinline__ void argmax_pair(float& v, int& i, float ov, int oi) {

@@ -12,6 +12,8 @@ using namespace e3;
 
 namespace {
 
+typedef int intx4 __attribute__((ext_vector_type(4)));
+
 constexpr int KMAX = 16;     // largest top-K
 constexpr int SMAX = 64;     // largest slot count (one mask word)
 
@@ -29,6 +31,9 @@ struct CandState {
   int32_t* depth;    // [B*PMAX]
   float* score;      // [B*PMAX]
   int32_t* count;    // [B]
+  int32_t* topn;     // [B*N]  the N best candidates so far (candidate index), best first
+  float* topsc;      // [B*N]  their scores
+  int32_t* ntop;     // [B]
 };
 
 // ---------------------------------------------------------------------------------------
@@ -52,7 +57,10 @@ __global__ __launch_bounds__(256) void k_init(int B, int S, int d, int V, const 
     if (dbg_tok) dbg_tok[i] = st.tok[i];
     if (dbg_par) dbg_par[i] = st.parent[i];
   }
-  if (threadIdx.x == 0) cs.count[b] = 0;
+  if (threadIdx.x == 0) {
+    cs.count[b] = 0;
+    cs.ntop[b] = 0;
+  }
   constexpr int EPC = Vec<T>::N;
   for (int k = threadIdx.x * EPC; k < d; k += blockDim.x * EPC) {
     const u32x4 a = ld16(hl + (size_t)b * d + k);
@@ -293,7 +301,7 @@ __global__ __launch_bounds__(256) void k_epi_qkv(const float* __restrict__ part,
 // ranked against all of them; the pair of rank r < K goes to out(r, ...).  Otherwise (many
 // ties at tau, or fewer than K finite lane maxima) K exact argmax rounds over all pairs are
 // used.  Ids must be distinct across the wave, except for padding pairs (value -inf).
-// `sv`, `si` hold TK_CAP entries of this wave's LDS.
+// `sv`, `si` hold TK_CAP entries of this wave's LDS, 16-byte aligned.
 // ---------------------------------------------------------------------------------------
 constexpr int TK_CAP = 64;
 
@@ -327,12 +335,24 @@ __device__ __forceinline__ void wave_topk(const float* v, IdOf id_of, int K, flo
       }
       off += __popcll(bal[e]);
     }
+    // pad to a multiple of four with (-inf, INT_MAX), which beats no entry, and rank each
+    // compacted pair against four entries per LDS read
+    const int total4 = (total + 3) & ~3;
+    if (lane >= total && lane < total4) {
+      sv[lane] = kNegInf;
+      si[lane] = 0x7fffffff;
+    }
     __builtin_amdgcn_wave_barrier();
     if (lane < total) {
       const float a = sv[lane];
       const int ia = si[lane];
       int r = 0;
-      for (int j = 0; j < total; ++j) r += better(sv[j], si[j], a, ia) ? 1 : 0;
+      for (int j = 0; j < total4; j += 4) {
+        const floatx4 bv = *reinterpret_cast<const floatx4*>(sv + j);
+        const intx4 bi = *reinterpret_cast<const intx4*>(si + j);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r += (int)((bv[q] > a) | ((bv[q] == a) & (bi[q] < ia)));
+      }
       if (r < K) out(r, a, ia);
     }
   } else {
@@ -380,8 +400,8 @@ __global__ __launch_bounds__(256) void k_topk_chunk(const float* __restrict__ pa
                                                     float* __restrict__ cmax, float* __restrict__ csum,
                                                     float* __restrict__ dbg_logits, int R, int sb, int S,
                                                     SlotState st) {
-  __shared__ float sv[4][TK_CAP];
-  __shared__ int si[4][TK_CAP];
+  __shared__ __attribute__((aligned(16))) float sv[4][TK_CAP];
+  __shared__ __attribute__((aligned(16))) int si[4][TK_CAP];
   __shared__ float wv[4 * KMAX];
   __shared__ int wi[4 * KMAX];
   __shared__ float wmax[4], wsum[4];
@@ -475,25 +495,43 @@ __global__ __launch_bounds__(256) void k_topk_chunk(const float* __restrict__ pa
 // slots, or (last step) the N best candidates of the pool are kept and relabelled by
 // (depth asc, creation asc).
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ bool cand_better(float sa, int ia, float sb_, int ib) {
-  return sa > sb_ || (sa == sb_ && ia < ib);
-}
-
 constexpr int SEL_MAXR = 16;   // rows (W) per request handled by one workgroup
 
-// Number of entries f in [lo, hi) that beat entry e (score desc, index asc); `sc` is LDS,
-// 16-byte aligned at lo (a multiple of 4), padded with -inf up to a multiple of 4.
+// Number of entries f in [lo, hi) that beat (sa, e) by (score desc, index asc) where an
+// entry's index is its position; `sc` is LDS, 16-byte aligned at lo (a multiple of 4),
+// padded with -inf up to a multiple of 4.
 __device__ __forceinline__ int rank_of(const float* sc, int lo, int hi, float sa, int e) {
   int rank = 0;
 #pragma unroll 4
   for (int f = lo; f < hi; f += 4) {
     const floatx4 v = *reinterpret_cast<const floatx4*>(sc + f);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) rank += (v[q] > sa || (v[q] == sa && f + q < e)) ? 1 : 0;
+    for (int q = 0; q < 4; ++q) rank += (int)((v[q] > sa) | ((v[q] == sa) & (f + q < e)));
   }
   return rank;
 }
 
+// Number of entries of [0, hi) that beat (sa, ia) by (score desc, index asc), the indices
+// given in `ix`; both LDS arrays 16-byte aligned, padded with (-inf, INT_MAX) to a multiple
+// of 4.
+__device__ __forceinline__ int rank_idx(const float* sc, const int* ix, int hi, float sa, int ia) {
+  int rank = 0;
+#pragma unroll 4
+  for (int f = 0; f < hi; f += 4) {
+    const floatx4 v = *reinterpret_cast<const floatx4*>(sc + f);
+    const intx4 i = *reinterpret_cast<const intx4*>(ix + f);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rank += (int)((v[q] > sa) | ((v[q] == sa) & (i[q] < ia)));
+  }
+  return rank;
+}
+
+constexpr int SEL_MAXNEW = SEL_MAXR * KMAX;   // new candidates per step
+constexpr int SEL_MAXTOP = 256;               // N <= 255
+
+// Phase 2 keeps a running list of the N best candidates created so far: the N best of all
+// candidates are the N best of (the previous list and the new candidates), so each step ranks
+// at most N + W*K entries, and the last step relabels the final list.
 __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, int N, int S, int PMAX,
                                                  int R, int n_chunks, const float* __restrict__ cv,
                                                  const int* __restrict__ ci,
@@ -509,36 +547,35 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
   __shared__ float s_val[SEL_MAXR][KMAX];
   __shared__ int s_id[SEL_MAXR][KMAX];
   __shared__ float s_lse[SEL_MAXR];
-  __shared__ float s_cv[SEL_MAXR][TK_CAP];
-  __shared__ int s_ci[SEL_MAXR][TK_CAP];
-  __shared__ __attribute__((aligned(16))) float ssc[1024 + 4];
-  __shared__ int sdep[1024];
-  __shared__ int stok[1024];
-  __shared__ int sps[1024];
-  __shared__ int slab[1024];
-  __shared__ int s_wave_cnt[16];
+  __shared__ __attribute__((aligned(16))) float s_cv[SEL_MAXR][TK_CAP];
+  __shared__ __attribute__((aligned(16))) int s_ci[SEL_MAXR][TK_CAP];
+  __shared__ __attribute__((aligned(16))) float nsc[SEL_MAXNEW + 4];   // new candidates, creation order
+  __shared__ int ntok[SEL_MAXNEW];
+  __shared__ int nps[SEL_MAXNEW];
+  __shared__ __attribute__((aligned(16))) float msc[SEL_MAXTOP + SEL_MAXNEW + 4];   // list, then new
+  __shared__ __attribute__((aligned(16))) int midx[SEL_MAXTOP + SEL_MAXNEW + 4];
+  __shared__ int ktop[SEL_MAXTOP];
+  __shared__ float ktsc[SEL_MAXTOP];
+  __shared__ int lab_of[1024];
   __shared__ int s_valid[SEL_MAXR];
   __shared__ float s_score[SEL_MAXR];
   __shared__ uint64_t s_mask[SEL_MAXR];
   __shared__ int s_cand[SEL_MAXR];
-  __shared__ int s_count;
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int sb = step == 0 ? 0 : 1 + (step - 1) * W;
   const bool last = step + 1 == D;
   const int n_before = cs.count[b];
+  const int ntop = cs.ntop[b];
   int32_t* ctok = cs.tok + (size_t)b * PMAX;
   int32_t* cps = cs.pslot + (size_t)b * PMAX;
   int32_t* cdep = cs.depth + (size_t)b * PMAX;
   float* csc = cs.score + (size_t)b * PMAX;
-  // the last step ranks the whole pool: stage the earlier candidates in LDS now
-  if (last) {
-    for (int e = threadIdx.x; e < n_before; e += blockDim.x) {
-      ssc[e] = csc[e];
-      sdep[e] = cdep[e];
-      stok[e] = ctok[e];
-      sps[e] = cps[e];
-    }
+  int32_t* topn = cs.topn + (size_t)b * N;
+  float* topsc = cs.topsc + (size_t)b * N;
+  for (int i = threadIdx.x; i < ntop; i += blockDim.x) {
+    msc[i] = topsc[i];
+    midx[i] = topn[i];
   }
 
   // ---- phase 1: per-row top-K over the chunks' lists (lane l holds chunk l's list) and
@@ -580,88 +617,110 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
   }
   __syncthreads();
 
-  // ---- phase 2: children of this step's nodes (LDS), then the next frontier or the prune
+  // ---- phase 2: children of this step's nodes, s = s_parent + (z - lse) in fp32, recorded in
+  // creation order (evaluation rank of the parent, then child rank)
   int nE = 0;  // valid slots form a prefix of the step's slots
   for (int j = 0; j < R; ++j) nE += s_valid[j] ? 1 : 0;
   const int n_new = nE * K;
   const int n_total = n_before + n_new;
+  const int m_total = ntop + n_new;
   for (int e = threadIdx.x; e < n_new; e += blockDim.x) {
     const int j = e / K, rk = e % K;
-    const int ci_ = n_before + e;
-    ssc[ci_] = s_score[j] + (s_val[j][rk] - s_lse[j]);
-    sdep[ci_] = step + 1;
-    stok[ci_] = s_id[j][rk];
-    sps[ci_] = sb + j;
+    const float sc = s_score[j] + (s_val[j][rk] - s_lse[j]);
+    const int tk = s_id[j][rk];
+    nsc[e] = sc;
+    ntok[e] = tk;
+    nps[e] = sb + j;
+    msc[ntop + e] = sc;
+    midx[ntop + e] = n_before + e;
+    ctok[n_before + e] = tk;
+    cps[n_before + e] = sb + j;
+    cdep[n_before + e] = step + 1;
+    csc[n_before + e] = sc;
   }
-  if (threadIdx.x < 4) ssc[n_total + threadIdx.x] = kNegInf;
+  if (threadIdx.x < 4) {
+    nsc[n_new + threadIdx.x] = kNegInf;
+    msc[m_total + threadIdx.x] = kNegInf;
+    midx[m_total + threadIdx.x] = 0x7fffffff;
+  }
   __syncthreads();
   if (!last) {
-    // rank the new candidates; the W best take the next step's slots
+    // the W best new candidates (score desc, creation asc) take the next step's slots
     const int nsb = 1 + step * W;
-    const int lo = n_before & ~3;
     for (int e = threadIdx.x; e < n_new; e += blockDim.x) {
-      const int ia = n_before + e;
-      const float sa = ssc[ia];
-      // entries [lo, n_before) are not new candidates; rank_of counts them, so they are
-      // counted again with the same test and removed
-      int rank = rank_of(ssc, lo, n_total, sa, ia);
-      for (int f = lo; f < n_before; ++f) rank -= (ssc[f] > sa || (ssc[f] == sa && f < ia)) ? 1 : 0;
+      const float sa = nsc[e];
+      const int rank = rank_of(nsc, 0, n_new, sa, e);
       if (rank < W) {
         const int slot = nsb + rank;
         const int i = b * S + slot;
-        const int ps = sps[ia];
-        st.tok[i] = stok[ia];
+        const int ps = nps[e];
+        st.tok[i] = ntok[e];
         st.parent[i] = ps;
         st.valid[i] = 1;
         st.score[i] = sa;
-        st.cand[i] = ia;
+        st.cand[i] = n_before + e;
         st.mask[i] = s_mask[ps - sb] | (1ull << slot);
-        if (dbg_tok) dbg_tok[i] = stok[ia];
+        if (dbg_tok) dbg_tok[i] = ntok[e];
         if (dbg_par) dbg_par[i] = ps;
       }
-      ctok[ia] = stok[ia];
-      cps[ia] = sps[ia];
-      cdep[ia] = step + 1;
-      csc[ia] = sa;
     }
-    if (threadIdx.x == 0) cs.count[b] = n_total;
+  }
+  // the running list: the N best of (list, new)
+  for (int i = threadIdx.x; i < m_total; i += blockDim.x) {
+    const int r = rank_idx(msc, midx, m_total, msc[i], midx[i]);
+    if (r < N) {
+      ktop[r] = midx[i];
+      ktsc[r] = msc[i];
+    }
+  }
+  for (int i = threadIdx.x; i < n_total; i += blockDim.x) lab_of[i] = -1;
+  __syncthreads();
+  const int n_keep = min(N, m_total);
+  if (!last) {
+    for (int i = threadIdx.x; i < n_keep; i += blockDim.x) {
+      topn[i] = ktop[i];
+      topsc[i] = ktsc[i];
+    }
+    if (threadIdx.x == 0) {
+      cs.ntop[b] = n_keep;
+      cs.count[b] = n_total;
+    }
     return;
   }
-  // final prune: keep the N best of the whole pool.  Candidates are created depth by depth,
-  // so (depth asc, creation asc) order is creation order and the new labels are 1 + the
-  // number of kept candidates created earlier (a ballot prefix count).
-  for (int base = 0; base < n_total; base += blockDim.x) {
-    const int e = base + threadIdx.x;
-    bool keep = false;
-    if (e < n_total) keep = rank_of(ssc, 0, n_total, ssc[e], e) < N;
-    const uint64_t bal = __ballot(keep);
-    if (lane == 0) s_wave_cnt[w] = __popcll(bal);
-    __syncthreads();
-    int before = base == 0 ? 0 : slab[base - 1] + 1;
-    for (int q = 0; q < w; ++q) before += s_wave_cnt[q];
-    const int within = __popcll(bal & ((1ull << lane) - 1ull));
-    if (e < n_total) {
-      if (!keep) sdep[e] = -1;  // -1 marks dropped
-      slab[e] = before + within + (keep ? 1 : 0) - 1;
-    }
-    __syncthreads();
+  // final: relabel the kept candidates by (depth asc, creation asc), which is creation order
+  // since candidates are created depth by depth; root = 0
+  for (int i = threadIdx.x; i < n_keep; i += blockDim.x) {
+    const int idx = ktop[i];
+    int lab = 1;
+    for (int k = 0; k < n_keep; ++k) lab += (int)(ktop[k] < idx);
+    lab_of[idx] = lab;
   }
-  const int n_keep = min(N, n_total);
+  __syncthreads();
   const size_t ob = (size_t)b * (N + 1);
-  for (int e = threadIdx.x; e < n_total; e += blockDim.x) {
-    if (sdep[e] < 0) continue;
-    const int lab = slab[e] + 1;
-    const int ps = sps[e];
+  for (int i = threadIdx.x; i < n_keep; i += blockDim.x) {
+    const int idx = ktop[i];
+    const int lab = lab_of[idx];
+    int tk, ps, dep;
+    if (idx >= n_before) {
+      tk = ntok[idx - n_before];
+      ps = nps[idx - n_before];
+      dep = step + 1;
+    } else {
+      tk = ctok[idx];
+      ps = cps[idx];
+      dep = cdep[idx];
+    }
     int plab = 0;
     if (ps > 0) {
-      // the parent slot's candidate: a slot of this step (LDS) or of an earlier one
+      // the parent slot's candidate: a slot of this step (LDS) or of an earlier one; it is kept
+      // (a child's score never exceeds its parent's and a parent is created first)
       const int pc = (ps >= sb && ps < sb + R) ? s_cand[ps - sb] : st.cand[b * S + ps];
-      plab = (pc >= 0 && pc < n_total && sdep[pc] >= 0) ? slab[pc] + 1 : -1;
+      plab = (pc >= 0 && pc < n_total) ? lab_of[pc] : -1;
     }
-    out_tok[ob + lab] = stok[e];
+    out_tok[ob + lab] = tk;
     out_par[ob + lab] = plab;
-    out_dep[ob + lab] = sdep[e];
-    out_score[ob + lab] = ssc[e];
+    out_dep[ob + lab] = dep;
+    out_score[ob + lab] = ktsc[i];
   }
   for (int l = n_keep + 1 + threadIdx.x; l <= N; l += blockDim.x) {
     out_tok[ob + l] = -1;
@@ -676,6 +735,7 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
     out_score[ob] = 0.f;
     out_n[b] = 1 + n_keep;
     cs.count[b] = n_total;
+    cs.ntop[b] = n_keep;
   }
 }
 
@@ -743,6 +803,9 @@ Plan make_plan(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, int max
   p.cs.depth = c.take<int32_t>(BP);
   p.cs.score = c.take<float>(BP);
   p.cs.count = c.take<int32_t>(B);
+  p.cs.topn = c.take<int32_t>((size_t)B * p.N);
+  p.cs.topsc = c.take<float>((size_t)B * p.N);
+  p.cs.ntop = c.take<int32_t>(B);
   p.xf = c.take<char>((size_t)B * 3 * p.d * es);
   p.slot_a = c.take<float>(BS * p.d);
   p.kslot = c.take<char>(BS * p.Hkv * p.Dh * es);

@@ -178,10 +178,16 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
 // 16 bytes per lane into LDS at lds_base + 16 * lane, non-temporal.  Issued as assembly so
 // that the compiler does not see an outstanding LDS write (it would drain every DMA before
 // each later LDS read); completion is ordered by the explicit vmcnt waits of the ring.
+// M0 is written by the asm and named as clobbered; the compiler does not preserve reserved
+// registers across asm (hence its warning), which is harmless: nothing else in these
+// kernels keeps a value in M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void ring_dma(const void* gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(gptr), "s"(lds_base)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 template <int N>
 __device__ __forceinline__ void ring_wait_vm() {
