@@ -137,9 +137,11 @@ def recorded_traffic(workload: str):
 OP_PROFILES = {"attn_longctx": "tree_attention_longctx_traffic", "merge": "lse_merge_longctx_training_traffic",
                "accept_greedy": "accept_scan_llama8b_greedy_traffic"}
 VALU_PROFILE = {"accept_t07": "accept_scan_llama70b_t07_valu"}
-# one full-rate wave64 VALU instruction per SIMD every 4 clocks: 256 CUs x 4 SIMDs x 16 lanes
-# x 2.4 GHz lane-instructions per second
-VALU_PEAK_LANE_INSTR = 256 * 4 * 16 * 2.4e9
+# VALU lane-instructions per second at the published fp32 vector peak (157.3 TFLOP/s, two
+# flops per FMA lane-instruction): 256 CUs x 128 lanes x 2.4 GHz.  Quarter-rate instructions
+# (64-bit integer multiply-add, reciprocal, the division helpers) take four issue slots, so a
+# mix with them stays below this.
+VALU_PEAK_LANE_INSTR = 157.3e12 / 2
 
 
 def lm_head_bytes(shape, M):
@@ -215,25 +217,25 @@ def _copies(nbytes: int, want: int = 2) -> int:
     return max(want, -(-2 * INFINITY_CACHE_BYTES // max(nbytes, 1)))
 
 
-def _time_tag(capi, tag: str, fn, reps: int) -> float:
-    """Average device time (us) of the library launches tagged `tag` over reps calls.  A
-    short device-side spin precedes each call, so that the launch's opening event does not
-    fire on an idle queue before the host has enqueued the kernel (the event pair then
-    brackets the kernel alone, not the host's enqueue latency)."""
+def _time_b2b(fn, reps: int) -> float:
+    """Average device time (us) of one call of fn, over reps calls run back to back: a device
+    spin long enough for the host to enqueue every call holds the stream, one event pair on
+    the launch stream brackets the calls, so the time is the kernels' own (plus the
+    dispatch gaps between them), not the host's enqueue latency or per-launch events."""
     import torch
     for i in range(3):
         fn(i)
     torch.cuda.synchronize()
-    capi.eagle3_profile_reset()
-    capi.eagle3_profile_enable(True, only_kernel=tag)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(20_000_000)          # several ms at the shader clock
+    e0.record(stream)
     for i in range(reps):
-        torch.cuda._sleep(200_000)
         fn(i)
+    e1.record(stream)
     torch.cuda.synchronize()
-    capi.eagle3_profile_enable(False)
-    ms, n = capi.eagle3_profile_read(tag)
-    capi.eagle3_profile_reset()
-    return ms / max(n, 1) * 1e3
+    return e0.elapsed_time(e1) / reps * 1e3
 
 
 def _entry(op, workload, kernel, us, bound, bytes_=None, flops=None, **extra):
@@ -289,7 +291,7 @@ def attention_op(capi, synth, shape, trees, prefix, bound, reps=20, seed=500):
         capi.eagle3_tree_attention(vi["q"], vi["k_tree"], vi["v_tree"], vi["cu_nodes"], maxn, mk["mask"],
                                    kp[i % ncopy], vp[i % ncopy], vi["cu_prefix"], max(prefix), scale,
                                    out=part)
-    us = _time_tag(capi, "tree_attention", run, reps)
+    us = _time_b2b(run, reps)
     n_nodes = [len(t) for t in trees]
     tree_bytes = T * shape.Hkv * shape.Dh * 2 * es
     q_bytes = T * shape.Hq * shape.Dh * es
@@ -345,7 +347,7 @@ def op_rooflines(reps=20, keys=OP_KEYS):
         lse_part = synth.normal((2, rows), 1.0, 901, torch.float32, dev)
         mo = {"o": torch.empty((rows, Dh), dtype=torch.bfloat16, device=dev),
               "lse": torch.empty((rows,), dtype=torch.float32, device=dev)}
-        us = _time_tag(capi, "lse_merge", lambda i: capi.eagle3_lse_merge(o_part, lse_part, out=mo), reps)
+        us = _time_b2b(lambda i: capi.eagle3_lse_merge(o_part, lse_part, out=mo), reps)
         ops.append(dict(key="merge", **_entry("lse_merge", "2 partials x 65536 positions x 32 heads x 128 "
                                               "(fp32 -> bf16)", "k_lse_merge_rows", us, "hbm",
                                               bytes_=2 * rows * (Dh + 1) * 4 + rows * (Dh * 2 + 4))))
@@ -370,13 +372,12 @@ def op_rooflines(reps=20, keys=OP_KEYS):
         def run(i, vi=vi, mk=mk, logits=logits, ws=ws, ao=ao, temp=temp, sh=sh):
             capi.eagle3_accept(vi["cu_nodes"], vi["tokens"], vi["parents"], mk["mask"], logits[i % len(logits)],
                                temp, seed=7, round=i, max_depth=sh.depth, workspace=ws, out=ao)
-        us_scan = _time_tag(capi, "accept_scan", run, reps)
-        us_path = _time_tag(capi, "accept_path", run, reps)
+        us = _time_b2b(run, reps)
         name = "greedy" if temp == 0 else f"T={temp}"
-        ops.append(dict(key=key, **_entry(f"accept_scan ({name})", f"{sh.name}: {T} nodes x {V} logits",
-                                          "k_accept_scan", us_scan, "hbm", bytes_=lbytes,
-                                          accept_path_us=round(us_path, 2), rotating_copies=ncopy,
-                                          logits_per_s=round(T * V / (us_scan * 1e-6) / 1e9, 2))))
+        ops.append(dict(key=key, **_entry(f"accept ({name})", f"{sh.name}: {T} nodes x {V} logits",
+                                          "k_accept_scan + k_accept_path", us, "hbm", bytes_=lbytes,
+                                          rotating_copies=ncopy,
+                                          logits_per_s=round(T * V / (us * 1e-6) / 1e9, 2))))
         del logits
     torch.cuda.empty_cache()
     for o in ops:
@@ -385,7 +386,8 @@ def op_rooflines(reps=20, keys=OP_KEYS):
         if o["key"] in VALU_PROFILE:
             n = recorded(VALU_PROFILE[o["key"]], "sq_insts_valu_per_launch")
             if n is not None:
-                # the scan is bound by its arithmetic (Philox + two float32 logs per logit)
+                # the scan is bound by its arithmetic (Philox + two float32 logs per logit); the
+                # time covers the whole call (scan and path kernels), the count the scan alone
                 ach = n * 64 / (o["avg_launch_us"] * 1e-6)
                 o.update({"bound": "alu", "achieved": round(ach / 1e12, 2), "peak": round(VALU_PEAK_LANE_INSTR / 1e12, 2),
                           "unit": "T VALU lane-instr/s", "frac": round(ach / VALU_PEAK_LANE_INSTR, 4),
