@@ -307,7 +307,39 @@ def attention_op(capi, synth, shape, trees, prefix, bound, reps=20, seed=500):
                   rotating_copies=ncopy)
 
 
-OP_KEYS = ("attn_longctx", "attn_batch16", "attn_70b", "attn_8b", "merge", "accept_greedy", "accept_t07")
+OP_KEYS = ("attn_longctx", "attn_batch16", "attn_70b", "attn_8b", "merge", "accept_greedy", "accept_t07",
+           "gemm_sweep")
+
+
+def gemm_sweep(capi, synth, reps):
+    """The drafter projections' GEMM (eagle3_linear) over the number of rows: at the QKV
+    shape (N = 6144, K = 8192) for M = 1 .. 8192, and at M = 2048 (a prompt's worth of rows)
+    for the MLP-down and LM-head shapes.  Few rows are bound by streaming W (HBM), many by
+    the matrix cores (bf16 MFMA)."""
+    import torch
+    dev = "cuda:0"
+    out = []
+    cases = [(m, 6144, 8192, "QKV") for m in (1, 10, 160, 1024, 2048, 8192)]
+    cases += [(2048, 4096, 14336, "MLP down"), (2048, 128256, 4096, "LM head")]
+    for M, N, K, name in cases:
+        wbytes = N * K * 2
+        ncopy = _copies(wbytes) if M <= 160 else 1
+        ws = [synth.normal((N, K), K ** -0.5, 70 + c, torch.bfloat16, dev) for c in range(ncopy)]
+        x = synth.normal((M, K), 1.0, 71, torch.bfloat16, dev)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        need = capi.lib().eagle3_linear_workspace_size(M, N, K, capi.EAGLE3_BF16)
+        wk = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+
+        def run(i, ws=ws, x=x, y=y, wk=wk):
+            capi.eagle3_linear(x, ws[i % len(ws)], out=y, workspace=wk)
+        us = _time_b2b(run, reps if M <= 2048 else max(4, reps // 4))
+        bound = "hbm" if M <= 160 else "mfma"
+        e = _entry(f"linear ({name})", f"M={M} N={N} K={K} bf16", "k_gemm_ring" if M <= 32 else
+                   ("k_gemm" if M <= 160 else "k_gemm_tile"), us, bound,
+                   bytes_=wbytes + M * K * 2 + M * N * 4, flops=2 * M * N * K)
+        out.append(dict(key="gemm_sweep", **e))
+        del ws, x, y, wk
+    return out
 
 
 def op_rooflines(reps=20, keys=OP_KEYS):
@@ -379,6 +411,8 @@ def op_rooflines(reps=20, keys=OP_KEYS):
                                           rotating_copies=ncopy,
                                           logits_per_s=round(T * V / (us * 1e-6) / 1e9, 2))))
         del logits
+    if "gemm_sweep" in keys:
+        ops += gemm_sweep(capi, synth, reps)
     torch.cuda.empty_cache()
     for o in ops:
         if o["key"] in OP_PROFILES:

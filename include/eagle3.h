@@ -195,7 +195,7 @@ EAGLE3_API int eagle3_build_tree_mask(int B, int T, const int32_t* cu_nodes, con
  *  cu_nodes [B+1], cu_prefix [B+1]: int32 device; mask [T, W64] as built above
  *  max_nodes, max_prefix: host upper bounds per request; n_splits: S in 1..256 (0 =
  *  automatic: enough workgroups for the kernel shape chosen by the query rows per KV head,
- *  each split at least one key tile and four times as many keys as its row block has
+ *  each split at least one key tile and three times as many keys as its row block has
  *  query rows; the same arguments give the same S in eagle3_tree_attention_num_splits).
  *  Dh must be 64 or 128.
  * ------------------------------------------------------------------------------------ */
@@ -251,6 +251,24 @@ EAGLE3_API int eagle3_accept(int B, int T, const int32_t* cu_nodes, const int32_
                   int V, int dtype, float temperature, uint64_t seed, uint64_t round,
                   int max_depth, int32_t* accept_len, int32_t* path, int32_t* out_tokens,
                   int32_t* bonus, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * eagle3_linear -- Y = X W^T through the GEMM kernels of the drafter's projections.
+ * Every step of the drafter multiplies rows by a weight matrix stored [out_features,
+ * in_features]: the fusion W_f ([P3] 多层特征融合到底融合了什么), the decoder layer's QKV, O and
+ * MLP projections ([P1] 训练细节: a single decoder layer) and the LM head.  The kernel is
+ * chosen by M: a few rows (M <= 32, bf16) stream W through LDS; up to 160 rows hold X in
+ * registers; many rows (M >= 256, bf16, K % 64 == 0) use 256 x 256 matrix-core tiles.
+ *
+ *  X [M, K] dtype, row stride ldx >= K elements; W [N, K] dtype; Y [M, N] fp32 (written
+ *  whole).  N % 4 == 0, K % 8 == 0; M in 1..160 for any dtype, or M >= 256 for bf16 with
+ *  K % 64 == 0 (else EAGLE3_EUNSUPPORTED).  Pointers 16-byte aligned (ldx * element size a
+ *  multiple of 16).  workspace: eagle3_linear_workspace_size() bytes (split-K partial sums;
+ *  0 when none are needed, then workspace may be NULL).
+ * ------------------------------------------------------------------------------------ */
+EAGLE3_API size_t eagle3_linear_workspace_size(int M, int N, int K, int dtype);
+EAGLE3_API int eagle3_linear(int M, int N, int K, int dtype, const void* X, int ldx, const void* W,
+                             float* Y, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * Launch timing.  While enabled, the library records a HIP event pair on the launch stream

@@ -68,6 +68,13 @@ def silu(x: np.ndarray) -> np.ndarray:
     return x / (1.0 + np.exp(-x))
 
 
+def project(x, w) -> np.ndarray:
+    """One projection of the drafter, y = x W^T with W stored [out, in] (the fusion W_f of
+    [P3] 多层特征融合到底融合了什么; the QKV, O and MLP projections of the single decoder
+    layer and the LM head, [P1] 训练细节), in float64 on the exact upcast of the inputs."""
+    return f64(x) @ f64(w).T
+
+
 def fuse_features(h_low, h_mid, h_high, w_fuse) -> np.ndarray:
     """[P3] 多层特征融合到底融合了什么 / [P1] 推理流程: concatenate the low, middle and
     high target features (3k wide) and project back to k with one fully connected layer:

@@ -65,6 +65,9 @@ EXPORTS = {
                                       c_size_t, c_void_p]),
     "eagle3_lse_merge": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_int, c_void_p,
                                  c_void_p, c_void_p]),
+    "eagle3_linear_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int]),
+    "eagle3_linear": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p, c_void_p,
+                              c_size_t, c_void_p]),
     "eagle3_accept_workspace_size": (c_size_t, [c_int, c_int]),
     "eagle3_accept": (c_int, [c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
                               c_void_p, c_int, c_int, c_float, c_uint64, c_uint64, c_int,
@@ -345,6 +348,34 @@ def eagle3_accept(cu_nodes, tokens, parents, mask, logits, temperature: float, s
                              out["out_tokens"].data_ptr(), out["bonus"].data_ptr(),
                              workspace.data_ptr(), workspace.numel(), _stream(stream))
     _check("eagle3_accept", st)
+    return out
+
+
+# ---------------------------------------------------------------------------------------
+# Projections' GEMM
+# ---------------------------------------------------------------------------------------
+
+
+def eagle3_linear(x, w, out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """Y = X W^T in fp32 through the drafter's GEMM kernels; x [M, K], w [N, K] (same dtype)."""
+    _dev(w, "w")
+    if not (isinstance(x, torch.Tensor) and x.is_cuda and x.dim() == 2 and x.stride(1) == 1):
+        raise ValueError("x must be a 2-D device tensor with unit column stride")
+    if x.dtype != w.dtype:
+        raise ValueError("x and w must have the same dtype")
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    dt = dtype_code(x.dtype)
+    need = lib().eagle3_linear_workspace_size(M, N, K, dt)
+    if workspace is None and need > 0:
+        workspace = _workspace(need, x.device)
+    st = lib().eagle3_linear(M, N, K, dt, x.data_ptr(), x.stride(0), w.data_ptr(), out.data_ptr(),
+                             _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream))
+    _check("eagle3_linear", st)
     return out
 
 

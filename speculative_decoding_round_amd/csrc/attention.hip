@@ -473,6 +473,7 @@ __global__ __launch_bounds__(256) void k_tree_attn_dma(DevArgs a) {
   for (int s0 = 0; s0 < NST - 1; ++s0)
     if (s0 < n_it) issue(s0);
 
+  const bool wave_active = rb0 + wr * QT * 16 < R;
   for (int it = 0; it < n_it; ++it) {
     if constexpr (NST >= 3) {
       if (it + NST - 2 < n_it) wait_vm<C::PER * (NST - 2)>();
@@ -483,6 +484,8 @@ __global__ __launch_bounds__(256) void k_tree_attn_dma(DevArgs a) {
     }
     lds_barrier();  // stage it complete for every wave; stage it-1 fully consumed
     if (it + NST - 1 < n_it) issue(it + NST - 1);
+    // a wave whose row tiles all lie past the last row only moves data and meets the barriers
+    if (!wave_active) continue;
 
     const char* ks = smem + (it % NST) * C::STAGE + (wk * 2) * C::SUB;
     const char* vs = ks + C::SUB;
@@ -840,9 +843,9 @@ int launch_attn_t(const e3h::AttnArgs& h, hipStream_t s) {
 namespace e3h {
 
 // Prefix splits: enough workgroups for the launch target of the workgroup shape, but every
-// split keeps at least one iteration of keys and at least four times as many keys as its
-// row block has rows, so a split's fp32 partial stays at or below a quarter of the bf16
-// K+V bytes it streams.
+// split keeps at least one iteration of keys and at least three times as many keys as its
+// row block has rows, so a split's fp32 partial stays at or below a third of the bf16 K+V
+// bytes it streams.
 int attention_splits(int B, int Hkv, int rows_per_kv, int max_prefix, int n_splits) {
   if (n_splits > 0) return n_splits;
   if (max_prefix <= 0 || B <= 0 || Hkv <= 0) return 1;
@@ -852,7 +855,7 @@ int attention_splits(int B, int Hkv, int rows_per_kv, int max_prefix, int n_spli
   const long rb = (rows + rows_wg - 1) / rows_wg;
   const long base = (long)B * Hkv * rb;
   long s = (attn_cfg_wgs(cfg) + base - 1) / base;
-  const long min_keys = std::max<long>(kiter, 4L * std::min(rows, rows_wg));
+  const long min_keys = std::max<long>(kiter, 3L * std::min(rows, rows_wg));
   const long max_s = (max_prefix + min_keys - 1) / min_keys;
   if (s > max_s) s = max_s;
   if (s > 256) s = 256;

@@ -205,6 +205,42 @@ int eagle3_lse_merge(int S, int rows, int Dh, const float* o_part, const float* 
                           "lse_merge");
 }
 
+// ---- linear (the projections' GEMM) ----------------------------------------------------
+namespace {
+bool linear_shape_ok(int M, int N, int K, int dtype) {
+  if (M <= 0 || N <= 0 || K <= 0 || !dtype_ok(dtype)) return false;
+  return true;
+}
+}  // namespace
+
+size_t eagle3_linear_workspace_size(int M, int N, int K, int dtype) {
+  if (!linear_shape_ok(M, N, K, dtype)) return 0;
+  const GemmPlan p = plan_gemm(M, N, K, dtype);
+  if (p.splits <= 1) return 0;
+  Carve c(nullptr);
+  c.take<float>((size_t)p.splits * M * N);
+  return c.size();
+}
+
+int eagle3_linear(int M, int N, int K, int dtype, const void* X, int ldx, const void* W, float* Y,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (!linear_shape_ok(M, N, K, dtype) || ldx < K) return EAGLE3_EINVAL;
+  if (N % 4 || K % 8) return EAGLE3_EUNSUPPORTED;
+  if (!X || !W || !Y) return EAGLE3_EINVAL;
+  if ((uintptr_t)X % 16 || (uintptr_t)W % 16 || (uintptr_t)Y % 16 || ((size_t)ldx * elem_size(dtype)) % 16)
+    return EAGLE3_EINVAL;
+  const GemmPlan p = plan_gemm(M, N, K, dtype);
+  if (!p.tile && (p.MT == 0 || M > 160)) return EAGLE3_EUNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  if (p.splits <= 1) return launch_gemm(p, dtype, X, ldx, W, Y, s, "linear");
+  const size_t need = eagle3_linear_workspace_size(M, N, K, dtype);
+  if (!workspace || workspace_bytes < need) return EAGLE3_EWORKSPACE;
+  float* part = static_cast<float*>(workspace);
+  int st = launch_gemm(p, dtype, X, ldx, W, part, s, "linear");
+  if (st) return st;
+  return launch_epi_sum(p, part, Y, nullptr, s, "linear_sum");
+}
+
 // ---- accept ---------------------------------------------------------------------------
 size_t eagle3_accept_workspace_size(int T, int V) {
   if (T < 0 || V <= 0) return 0;

@@ -330,6 +330,123 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_ring(const bf16* __restrict__ 
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// bf16 GEMM for many rows (M >= 256), bound by the matrix cores:
+//   Y[m][n] = sum_k X[m][k] W[n][k], fp32 out.
+// A workgroup owns a 256 (n) x 256 (m) output tile; its four waves each hold a 128 x 128
+// sub-tile in accumulators (4 x 4 tiles of v_mfma_f32_32x32x16_bf16, 256 fp32 per lane).
+// Both operands are k-major rows, so a k-step of 64 brings 256 rows x 128 bytes of W and of
+// X into LDS by LDS-DMA (eight whole 128-byte row pieces per instruction, non-temporal); the
+// 16-byte pieces of row r are stored at p ^ (r & 7), which makes the operand reads (32 rows at
+// one piece) conflict-free.  Two stages of 64 KB; the next stage's DMA is in flight during
+// the current stage's 64 MFMAs per wave.
+// ---------------------------------------------------------------------------------------
+constexpr int TILE_B = 256;                    // output rows (of W) and columns (rows of X) per tile
+constexpr int TILE_K = 64;                     // k per stage
+constexpr int TILE_HALF = TILE_B * TILE_K * 2; // bytes of the W (or X) part of a stage: 32 KB
+constexpr int TILE_STAGE = 2 * TILE_HALF;      // 64 KB
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256) void k_gemm_tile(const bf16* __restrict__ X, int M, int ldx,
+                                                   const bf16* __restrict__ W, int N, int K,
+                                                   float* __restrict__ Y, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * TILE_STAGE];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tn = blockIdx.x % tiles_n, tm = blockIdx.x / tiles_n;
+  const int n0 = tn * TILE_B, m0 = tm * TILE_B;
+  const int wn = w & 1, wm = w >> 1;             // this wave: W rows n0 + 128 wn, X rows m0 + 128 wm
+  const int n_k = K / TILE_K;
+  const uint32_t lds0 = lds_u32(lds);
+
+  // DMA: a stage is 64 instructions of 1 KB: j < 32 take W rows 8j .. 8j+7, j >= 32 X rows;
+  // wave w issues j = 16 w .. 16 w + 15.  Lane l: row 8 (j % 32) + l / 8, 16-byte piece
+  // (l % 8) ^ (row % 8) of the row's 128-byte segment.  Offsets are fixed across stages.
+  uint32_t goff[16];
+  const bf16* gbase[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int j = w * 16 + u;
+    const int r = 8 * (j % 32) + (lane >> 3);
+    const int piece = (lane & 7) ^ (r & 7);
+    if (j < 32) {
+      gbase[u] = W;
+      goff[u] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K * 2u + piece * 16;
+    } else {
+      gbase[u] = X;
+      goff[u] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)ldx * 2u + piece * 16;
+    }
+  }
+  auto issue = [&](int kt) {
+    const uint32_t st = lds0 + (uint32_t)(kt & 1) * TILE_STAGE;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const char* g = reinterpret_cast<const char*>(gbase[u]) + goff[u] + (size_t)kt * (TILE_K * 2);
+      ring_dma(g, st + (uint32_t)(w * 16 + u) * 1024);
+    }
+  };
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // operand read offsets: fragment row base rb (32 rows), lane row rb + l % 32, piece
+  // 2 kk + l / 32 of k16 block kk
+  const int lr = lane & 31, lh = lane >> 5;
+  auto frag = [&](const char* half, int rb, int kk) {
+    const int row = rb + lr;
+    const int piece = (2 * kk + lh) ^ (row & 7);
+    return *reinterpret_cast<const u32x4*>(half + row * (TILE_K * 2) + piece * 16);
+  };
+
+  issue(0);
+  for (int kt = 0; kt < n_k; ++kt) {
+    ring_wait_vm<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stage kt landed for all waves
+    if (kt + 1 < n_k) issue(kt + 1);
+    const char* wst = lds + (kt & 1) * TILE_STAGE;
+    const char* xst = wst + TILE_HALF;
+#pragma unroll
+    for (int kk = 0; kk < TILE_K / 16; ++kk) {
+      u32x4 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = frag(wst, wn * 128 + i * 32, kk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = frag(xst, wm * 128 + j * 32, kk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i]),
+                                                              __builtin_bit_cast(bf16x8, b[j]),
+                                                              acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // D[n][m] of fragment (i, j): lane holds m = l % 32; register 4 q + e holds
+  // n = 8 q + 4 (l / 32) + e
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + wm * 128 + j * 32 + lr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * 128 + i * 32 + 8 * q + 4 * lh;
+        if (n < N)
+          *reinterpret_cast<floatx4*>(Y + (size_t)m * N + n) =
+              floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+      }
+  }
+}
+
 // Ring kernel shape: 8 W tiles (128 output features) per workgroup, 4 ring slots of 8 KB per
 // wave (five one-wave workgroups per CU).
 constexpr int kRingNTB = 8, kRingNST = 4;
@@ -445,10 +562,23 @@ GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu) {
   GemmPlan p;
   p.silu = silu;
   p.ring = false;
+  p.tile = false;
   p.M = M;
   p.N = N;
   p.K = K;
   const int mt_need = (M + 15) / 16;
+  if (dtype == EAGLE3_BF16 && !silu && M >= 256 && K % TILE_K == 0 && N % 4 == 0) {
+    // many rows: the matrix cores bound it; 256 x 256 output tiles, whole k-range per tile
+    p.tile = true;
+    p.MT = 0;
+    p.NT = 0;
+    p.n_blocks = (N + TILE_B - 1) / TILE_B;
+    p.chunks_total = K / 32;
+    p.chunks_per_split = p.chunks_total;
+    p.splits = 1;
+    p.waves = 4;
+    return p;
+  }
   if (dtype == EAGLE3_BF16 && mt_need <= 2 && K % 32 == 0 &&
       (!silu || (N / 2) % (16 * (kRingNTB / 2)) == 0)) {
     // LDS-ring kernel, 128 output features (or 64 gate + 64 up) per workgroup.  The LM head
@@ -511,6 +641,14 @@ GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu) {
 
 int launch_gemm(const GemmPlan& p, int dtype, const void* X, int ldx, const void* W, float* Ypart,
                 hipStream_t s, const char* tag, void* act) {
+  if (p.tile) {
+    if (dtype != EAGLE3_BF16) return EAGLE3_EUNSUPPORTED;
+    ProfScope ps(tag, s);
+    const int tiles_m = (p.M + TILE_B - 1) / TILE_B;
+    hipLaunchKernelGGL(k_gemm_tile, dim3(p.n_blocks * tiles_m), dim3(256), 0, s, (const bf16*)X, p.M, ldx,
+                       (const bf16*)W, p.N, p.K, Ypart, p.n_blocks);
+    return launch_status();
+  }
   if (p.MT == 0) return EAGLE3_EUNSUPPORTED;
   if (p.silu && (!act || (p.N / 2) % (16 * (p.NT / 2)))) return EAGLE3_EUNSUPPORTED;
   ProfScope ps(tag, s);

@@ -27,6 +27,28 @@ def test_fusion_identity_block():
     np.testing.assert_allclose(O.fuse_features(*h, wf), 2 * h[1] - h[2])
 
 
+def test_projection_against_explicit_sums():
+    """y[m][n] = sum_k x[m][k] W[n][k] with W stored [out, in]: each output is checked as an
+    explicit sum over k, an identity block returns the selected inputs, and a transposed
+    weight (the usual mistake for this layout) is told apart."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((3, 7))
+    w = rng.standard_normal((5, 7))
+    y = O.project(x, w)
+    assert y.shape == (3, 5)
+    for m in range(3):
+        for n in range(5):
+            ref = 0.0
+            for k in range(7):
+                ref += x[m, k] * w[n, k]
+            assert abs(y[m, n] - ref) <= 1e-12 * max(1.0, abs(ref))
+    eye = np.zeros((4, 7))
+    eye[np.arange(4), [6, 0, 3, 2]] = 1.0
+    np.testing.assert_array_equal(O.project(x, eye), x[:, [6, 0, 3, 2]])
+    sq = rng.standard_normal((7, 7))
+    assert not np.allclose(O.project(x, sq), x @ sq)
+
+
 def test_rope_properties():
     rng = np.random.default_rng(1)
     q, k = rng.standard_normal(64), rng.standard_normal(64)
