@@ -320,7 +320,8 @@ def gemm_sweep(capi, synth, reps):
     dev = "cuda:0"
     out = []
     cases = [(m, 6144, 8192, "QKV") for m in (1, 10, 160, 1024, 2048, 8192)]
-    cases += [(2048, 4096, 14336, "MLP down"), (2048, 128256, 4096, "LM head")]
+    cases += [(2048, 4096, 12288, "feature fusion"), (2048, 4096, 14336, "MLP down"),
+              (2048, 128256, 4096, "LM head")]
     for M, N, K, name in cases:
         wbytes = N * K * 2
         ncopy = _copies(wbytes) if M <= 160 else 1

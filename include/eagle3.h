@@ -258,13 +258,16 @@ EAGLE3_API int eagle3_accept(int B, int T, const int32_t* cu_nodes, const int32_
  * in_features]: the fusion W_f ([P3] 多层特征融合到底融合了什么), the decoder layer's QKV, O and
  * MLP projections ([P1] 训练细节: a single decoder layer) and the LM head.  The kernel is
  * chosen by M: a few rows (M <= 32, bf16) stream W through LDS; up to 160 rows hold X in
- * registers; many rows (M >= 256, bf16, K % 64 == 0) use 256 x 256 matrix-core tiles.
+ * registers; more rows (M > 160, bf16, K % 64 == 0) use 256 x 256 matrix-core tiles, with the
+ * k-range split over workgroups when there are fewer tiles than compute units.
  *
  *  X [M, K] dtype, row stride ldx >= K elements; W [N, K] dtype; Y [M, N] fp32 (written
- *  whole).  N % 4 == 0, K % 8 == 0; M in 1..160 for any dtype, or M >= 256 for bf16 with
- *  K % 64 == 0 (else EAGLE3_EUNSUPPORTED).  Pointers 16-byte aligned (ldx * element size a
- *  multiple of 16).  workspace: eagle3_linear_workspace_size() bytes (split-K partial sums;
- *  0 when none are needed, then workspace may be NULL).
+ *  whole).  N % 4 == 0, K % 8 == 0; M in 1..160 for any dtype, or M > 160 for bf16 with
+ *  K % 64 == 0, N * K * 2 and M * ldx * 2 below 4 GiB (else EAGLE3_EUNSUPPORTED).  Pointers
+ *  16-byte aligned (ldx * element size a multiple of 16).  workspace:
+ *  eagle3_linear_workspace_size() bytes (split-K partial sums; 0 when none are needed, then
+ *  workspace may be NULL).  Split-K sums are added in split order, so results are
+ *  deterministic for a given shape.
  * ------------------------------------------------------------------------------------ */
 EAGLE3_API size_t eagle3_linear_workspace_size(int M, int N, int K, int dtype);
 EAGLE3_API int eagle3_linear(int M, int N, int K, int dtype, const void* X, int ldx, const void* W,

@@ -333,59 +333,95 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_ring(const bf16* __restrict__ 
 // ---------------------------------------------------------------------------------------
 // bf16 GEMM for many rows (M >= 256), bound by the matrix cores:
 //   Y[m][n] = sum_k X[m][k] W[n][k], fp32 out.
-// A workgroup owns a 256 (n) x 256 (m) output tile; its four waves each hold a 128 x 128
-// sub-tile in accumulators (4 x 4 tiles of v_mfma_f32_32x32x16_bf16, 256 fp32 per lane).
-// Both operands are k-major rows, so a k-step of 64 brings 256 rows x 128 bytes of W and of
-// X into LDS by LDS-DMA (eight whole 128-byte row pieces per instruction, non-temporal); the
-// 16-byte pieces of row r are stored at p ^ (r & 7), which makes the operand reads (32 rows at
-// one piece) conflict-free.  Two stages of 64 KB; the next stage's DMA is in flight during
-// the current stage's 64 MFMAs per wave.
+// A workgroup owns a 256 (n) x 256 (m) output tile; its four waves (one per SIMD) each hold
+// a 128 x 128 sub-tile in accumulators (4 x 4 tiles of v_mfma_f32_32x32x16_bf16, 256 fp32 per
+// lane), which is the largest sub-tile the register file allows and so the fewest LDS operand
+// reads per MFMA.  Both operands are k-major rows; a k-step of 64 brings 256 rows x 128 bytes
+// of W and of X into LDS by LDS-DMA (one instruction moves eight 128-byte row pieces).
+//
+// Pipeline.  Two stages of 64 KB.  A k-step is four sub-steps of 16 MFMAs per wave; during
+// each sub-step the wave reads the next sub-step's 8 operand fragments from LDS (one read
+// after each of the first 8 MFMAs), so LDS latency hides under the MFMAs.  The DMA of stage
+// s + 1 is issued during stage s, spread over its first two sub-steps (one instruction after
+// every second MFMA): issued all at once behind the barrier, the 64 instructions of a stage
+// back up in the CU's load path and hold every wave's MFMA issue for about half the stage.
+// One barrier per stage, before the last sub-step, orders both hazards: stage s + 1 has
+// landed for all waves (each waited for its own DMA), and every wave has finished reading
+// stage s - 1's buffer, which the next DMA overwrites.
+//
+// LDS layout: the 16-byte piece p of row r sits at position p ^ (r & 7) ^ ((r >> 3) & 1) of
+// the row's 128 bytes.  An operand read takes 16 rows at one piece per LDS cycle; the XOR
+// places those 16 reads in distinct banks (two rows per 256-byte bank line).
+//
+// Tile order: consecutive workgroups go to different XCDs, so workgroup b is remapped to
+// XCD-major order first, and each XCD walks its range in groups of 8 tile rows (m) per tile
+// column (n), so the workgroups resident on one XCD share W and X tiles in its L2.
+// With fewer tiles than CUs the k-range is split over workgroups (fp32 partial sums, added in
+// split order by the sum epilogue).
 // ---------------------------------------------------------------------------------------
 constexpr int TILE_B = 256;                    // output rows (of W) and columns (rows of X) per tile
 constexpr int TILE_K = 64;                     // k per stage
-constexpr int TILE_HALF = TILE_B * TILE_K * 2; // bytes of the W (or X) part of a stage: 32 KB
+constexpr int TILE_RB = TILE_K * 2;            // bytes of one row per stage
+constexpr int TILE_HALF = TILE_B * TILE_RB;    // bytes of the W (or X) part of a stage: 32 KB
 constexpr int TILE_STAGE = 2 * TILE_HALF;      // 64 KB
+constexpr int TILE_DPW = TILE_STAGE / 1024 / 4;   // DMA instructions per wave per stage: 16
+constexpr int TILE_GROUP_M = 8;
+constexpr int kTileCUs = 256;                  // MI355X compute units
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
+__device__ __forceinline__ int tile_swz(int row) { return (row ^ ((row >> 3) & 1)) & 7; }
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from sbase + voff into LDS at lds_base + 16 * lane (cached: the tiles are
+// re-read by other workgroups through L2).
+__device__ __forceinline__ void tile_dma(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 __global__ __launch_bounds__(256) void k_gemm_tile(const bf16* __restrict__ X, int M, int ldx,
                                                    const bf16* __restrict__ W, int N, int K,
-                                                   float* __restrict__ Y, int tiles_n) {
+                                                   float* __restrict__ Y, int tiles_n, int tiles_m,
+                                                   int kps) {
   __shared__ __attribute__((aligned(16))) char lds[2 * TILE_STAGE];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tn = blockIdx.x % tiles_n, tm = blockIdx.x / tiles_n;
+  int b = blockIdx.x;
+  const int total = tiles_n * tiles_m;
+  if (gridDim.x % 8 == 0) b = (b % 8) * (gridDim.x / 8) + b / 8;
+  // split over k: workgroups total * ks .. hold k-steps [ks * kps, (ks + 1) * kps) of every
+  // tile and write their partial sums to Y + ks * M * N
+  const int ks = b / total;
+  b -= ks * total;
+  Y += (size_t)ks * M * N;
+  const int gsz = TILE_GROUP_M * tiles_n;
+  const int g = b / gsz, rem = b % gsz;
+  const int gm = min(TILE_GROUP_M, tiles_m - g * TILE_GROUP_M);
+  const int tm = g * TILE_GROUP_M + rem % gm, tn = rem / gm;
   const int n0 = tn * TILE_B, m0 = tm * TILE_B;
   const int wn = w & 1, wm = w >> 1;             // this wave: W rows n0 + 128 wn, X rows m0 + 128 wm
-  const int n_k = K / TILE_K;
+  const int k_first = ks * kps;
+  const int n_k = min(kps, K / TILE_K - k_first);
   const uint32_t lds0 = lds_u32(lds);
 
-  // DMA: a stage is 64 instructions of 1 KB: j < 32 take W rows 8j .. 8j+7, j >= 32 X rows;
-  // wave w issues j = 16 w .. 16 w + 15.  Lane l: row 8 (j % 32) + l / 8, 16-byte piece
-  // (l % 8) ^ (row % 8) of the row's 128-byte segment.  Offsets are fixed across stages.
-  uint32_t goff[16];
-  const bf16* gbase[16];
+  // DMA: a stage is 64 instructions of 1 KB (8 rows each): j < 32 cover W rows 8j .. 8j+7,
+  // j >= 32 X rows; wave w issues j = 16 w .. 16 w + 15 (waves 0, 1: W; 2, 3: X).  Lane l:
+  // row 8 (j % 32) + l / 8, LDS position l % 8, which holds piece (l % 8) ^ swz(row).
+  const char* gb = reinterpret_cast<const char*>(w < 2 ? W : X) + (size_t)k_first * TILE_RB;
+  uint32_t goff[TILE_DPW];
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int j = w * 16 + u;
-    const int r = 8 * (j % 32) + (lane >> 3);
-    const int piece = (lane & 7) ^ (r & 7);
-    if (j < 32) {
-      gbase[u] = W;
-      goff[u] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K * 2u + piece * 16;
-    } else {
-      gbase[u] = X;
-      goff[u] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)ldx * 2u + piece * 16;
-    }
+  for (int u = 0; u < TILE_DPW; ++u) {
+    const int r = 8 * ((w * TILE_DPW + u) % 32) + (lane >> 3);
+    const int p = (lane & 7) ^ tile_swz(r);
+    goff[u] = (w < 2 ? (uint32_t)min(n0 + r, N - 1) * (uint32_t)K * 2u
+                     : (uint32_t)min(m0 + r, M - 1) * (uint32_t)ldx * 2u) + p * 16;
   }
-  auto issue = [&](int kt) {
-    const uint32_t st = lds0 + (uint32_t)(kt & 1) * TILE_STAGE;
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const char* g = reinterpret_cast<const char*>(gbase[u]) + goff[u] + (size_t)kt * (TILE_K * 2);
-      ring_dma(g, st + (uint32_t)(w * 16 + u) * 1024);
-    }
+  auto dma_one = [&](int stage, int u) {
+    tile_dma(gb + (size_t)stage * TILE_RB, goff[u],
+             lds0 + (uint32_t)(stage & 1) * TILE_STAGE + (uint32_t)(w * TILE_DPW + u) * 1024);
   };
 
   floatx16 acc[4][4];
@@ -396,38 +432,59 @@ __global__ __launch_bounds__(256) void k_gemm_tile(const bf16* __restrict__ X, i
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // operand read offsets: fragment row base rb (32 rows), lane row rb + l % 32, piece
-  // 2 kk + l / 32 of k16 block kk
+  // operand fragments: lane l reads row rb + l % 32, piece 2 kk + l / 32 of k16 block kk
+  // (swz(row) = swz(l % 32): fragment bases are multiples of 32 rows)
   const int lr = lane & 31, lh = lane >> 5;
-  auto frag = [&](const char* half, int rb, int kk) {
-    const int row = rb + lr;
-    const int piece = (2 * kk + lh) ^ (row & 7);
-    return *reinterpret_cast<const u32x4*>(half + row * (TILE_K * 2) + piece * 16);
+  uint32_t ra[4], rx[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ra[i] = (uint32_t)(wn * 128 + i * 32 + lr) * TILE_RB;
+    rx[i] = (uint32_t)(TILE_HALF + (wm * 128 + i * 32 + lr) * TILE_RB);
+  }
+  const int sw = tile_swz(lr);
+  u32x4 fa[2][4], fb[2][4];
+  auto read_one = [&](int nb, int t, int buf, int kk) {
+    const char* st = lds + buf * TILE_STAGE + ((2 * kk + lh) ^ sw) * 16;
+    if (t < 4) fa[nb][t] = *reinterpret_cast<const u32x4*>(st + ra[t]);
+    else fb[nb][t - 4] = *reinterpret_cast<const u32x4*>(st + rx[t - 4]);
+  };
+  // sub-step: the 16 MFMAs of fragment set cb, with the reads of the next set (buf, kk) after
+  // MFMAs 0..7 and DMA instructions lo.. of stage dstage after the odd MFMAs.  The explicit
+  // order is kept by scheduling barriers.
+  auto step = [&](int cb, int buf, int kk, bool dma_ok, int dstage, int lo, int hi) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int i = t >> 2, j = t & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[cb][i]),
+                                                          __builtin_bit_cast(bf16x8, fb[cb][j]), acc[i][j], 0, 0, 0);
+      if (t < 8) read_one(cb ^ 1, t, buf, kk);
+      if ((t & 1) && lo + (t >> 1) < hi && dma_ok) dma_one(dstage, lo + (t >> 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
-  issue(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no compiler-tracked load outstanding
+#pragma unroll
+  for (int u = 0; u < TILE_DPW; ++u) dma_one(0, u);
+  ring_wait_vm<0>();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+  for (int t = 0; t < 8; ++t) read_one(0, t, 0, 0);
+
   for (int kt = 0; kt < n_k; ++kt) {
-    ring_wait_vm<0>();
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stage kt landed for all waves
-    if (kt + 1 < n_k) issue(kt + 1);
-    const char* wst = lds + (kt & 1) * TILE_STAGE;
-    const char* xst = wst + TILE_HALF;
-#pragma unroll
-    for (int kk = 0; kk < TILE_K / 16; ++kk) {
-      u32x4 a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = frag(wst, wn * 128 + i * 32, kk);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = frag(xst, wm * 128 + j * 32, kk);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i]),
-                                                              __builtin_bit_cast(bf16x8, b[j]),
-                                                              acc[i][j], 0, 0, 0);
+    const int buf = kt & 1;
+    const bool dma_ok = kt + 1 < n_k;            // stage kt + 1 goes to buffer buf ^ 1
+    step(0, buf, 1, dma_ok, kt + 1, 0, 8);
+    step(1, buf, 2, dma_ok, kt + 1, 8, 16);
+    step(0, buf, 3, false, 0, 0, 0);
+    if (dma_ok) {
+      ring_wait_vm<0>();
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
+    __builtin_amdgcn_sched_barrier(0);
+    step(1, buf ^ 1, 0, false, 0, 0, 0);   // past the last stage these reads are unused
   }
+  ring_wait_vm<0>();
 
   // D[n][m] of fragment (i, j): lane holds m = l % 32; register 4 q + e holds
   // n = 8 q + 4 (l / 32) + e
@@ -567,16 +624,37 @@ GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu) {
   p.N = N;
   p.K = K;
   const int mt_need = (M + 15) / 16;
-  if (dtype == EAGLE3_BF16 && !silu && M >= 256 && K % TILE_K == 0 && N % 4 == 0) {
-    // many rows: the matrix cores bound it; 256 x 256 output tiles, whole k-range per tile
+  if (dtype == EAGLE3_BF16 && !silu && M > 160 && K % TILE_K == 0 && N % 4 == 0 &&
+      (size_t)N * (size_t)K * 2 <= 0xFFFFFFFFull) {
+    // many rows: the matrix cores bound it; 256 x 256 output tiles.  With fewer tiles than
+    // CUs the k-range is split: pick the split count that minimises (rounds of workgroups over
+    // the CUs) x (work per workgroup) + the partial sums' write and read, with the tile kernel
+    // at ~1.2 PFLOP/s and the partial-sum traffic at ~5 TB/s.
     p.tile = true;
     p.MT = 0;
     p.NT = 0;
     p.n_blocks = (N + TILE_B - 1) / TILE_B;
     p.chunks_total = K / 32;
-    p.chunks_per_split = p.chunks_total;
-    p.splits = 1;
     p.waves = 4;
+    const int n_k = K / TILE_K;
+    const long tiles = (long)p.n_blocks * ((M + TILE_B - 1) / TILE_B);
+    double best = 0;
+    int best_s = 1;
+    for (int sp = 1; sp <= 8 && sp <= n_k; ++sp) {
+      const int kps = (n_k + sp - 1) / sp;
+      const int s_eff = (n_k + kps - 1) / kps;
+      const long wgs = tiles * s_eff;
+      const long rounds = (wgs + kTileCUs - 1) / kTileCUs;
+      const double t = (double)rounds * 2.0 * TILE_B * TILE_B * TILE_K * kps / (1.2e15 / kTileCUs) +
+                       (s_eff > 1 ? 2.0 * s_eff * (double)M * N * 4 / 5e12 : 0.0);
+      if (sp == 1 || t < best * 0.97) {
+        best = t;
+        best_s = s_eff;
+      }
+    }
+    const int kps = (n_k + best_s - 1) / best_s;
+    p.chunks_per_split = 2 * kps;
+    p.splits = (n_k + kps - 1) / kps;
     return p;
   }
   if (dtype == EAGLE3_BF16 && mt_need <= 2 && K % 32 == 0 &&
@@ -643,10 +721,13 @@ int launch_gemm(const GemmPlan& p, int dtype, const void* X, int ldx, const void
                 hipStream_t s, const char* tag, void* act) {
   if (p.tile) {
     if (dtype != EAGLE3_BF16) return EAGLE3_EUNSUPPORTED;
+    // row offsets are 32-bit byte offsets from the operand base
+    if ((size_t)p.M * (size_t)ldx * 2 > 0xFFFFFFFFull) return EAGLE3_EUNSUPPORTED;
     ProfScope ps(tag, s);
     const int tiles_m = (p.M + TILE_B - 1) / TILE_B;
-    hipLaunchKernelGGL(k_gemm_tile, dim3(p.n_blocks * tiles_m), dim3(256), 0, s, (const bf16*)X, p.M, ldx,
-                       (const bf16*)W, p.N, p.K, Ypart, p.n_blocks);
+    hipLaunchKernelGGL(k_gemm_tile, dim3(p.n_blocks * tiles_m * p.splits), dim3(256), 0, s, (const bf16*)X,
+                       p.M, ldx, (const bf16*)W, p.N, p.K, Ypart, p.n_blocks, tiles_m,
+                       p.chunks_per_split / 2);
     return launch_status();
   }
   if (p.MT == 0) return EAGLE3_EUNSUPPORTED;

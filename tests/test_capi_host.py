@@ -138,10 +138,13 @@ def test_linear_validation(lib):
     assert lib.eagle3_linear(0, 8, 8, 1, P, 8, P, P, None, 0, None) == -1          # M = 0
     assert lib.eagle3_linear(4, 8, 8, 1, P, 4, P, P, None, 0, None) == -1          # ldx < K
     assert lib.eagle3_linear(4, 6, 8, 1, P, 8, P, P, None, 0, None) == -2          # N % 4
-    assert lib.eagle3_linear(200, 8, 8, 1, P, 8, P, P, None, 0, None) == -2        # 160 < M < 256
+    assert lib.eagle3_linear(200, 8, 8, 1, P, 8, P, P, None, 0, None) == -2        # tiled needs K % 64
     assert lib.eagle3_linear(256, 8, 40, 1, P, 40, P, P, None, 0, None) == -2      # tiled needs K % 64
     assert lib.eagle3_linear(256, 8, 64, 0, P, 64, P, P, None, 0, None) == -2      # tiled is bf16 only
     assert lib.eagle3_linear(4, 8, 8, 1, P + 8, 8, P, P, None, 0, None) == -1      # misaligned X
     need = lib.eagle3_linear_workspace_size(10, 4096, 4096, 1)
     assert need > 0 and lib.eagle3_linear_workspace_size(2048, 6144, 8192, 1) == 0
+    # tiles: 192 output tiles of 256 x 256 keep the k-range whole; 96 tiles (fewer than half
+    # the compute units) split it in two, one fp32 partial [M, N] per split
+    assert lib.eagle3_linear_workspace_size(1024, 6144, 8192, 1) == 2 * 1024 * 6144 * 4
     assert lib.eagle3_linear(10, 4096, 4096, 1, P, 4096, P, P, None, 0, None) == -3  # no workspace
