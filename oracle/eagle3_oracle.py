@@ -382,6 +382,42 @@ def draft_round(drafter: Drafter, D: int, K: int, W: int, N: int,
 
 
 # =======================================================================================
+# After acceptance: commit the accepted path's KV ([P5] 一棵候选树怎样被验证, step 5) and
+# rebuild the drafter's prefix KV of the committed positions from the target's real
+# features ([P3] 第二步为什么没有“正确隐藏状态”可用)
+# =======================================================================================
+
+
+def commit_kv(cu_nodes, path, accept_len, k_tree, v_tree, dst_row, k_cache, v_cache):
+    """[P5] 一棵候选树怎样被验证, step 5: only the KV of the accepted path is committed and
+    the other branches are released.  For request b the path's nodes path[b][0..accept_len[b]]
+    (root first) are tree rows cu_nodes[b] + path[b][i]; their K and V rows are copied, in
+    path order, to cache rows dst_row[b] + i.  Every other cache row is left as it was.
+    Returns new (k_cache, v_cache) arrays."""
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    for b in range(len(cu_nodes) - 1):
+        for i in range(int(accept_len[b]) + 1):
+            src = int(cu_nodes[b]) + int(path[b][i])
+            kc[int(dst_row[b]) + i] = k_tree[src]
+            vc[int(dst_row[b]) + i] = v_tree[src]
+    return kc, vc
+
+
+def drafter_catchup(drafter: "Drafter", tokens, h_low, h_mid, h_high, pos):
+    """Drafter catch-up over committed positions.  [P3] 第二步为什么没有“正确隐藏状态”可用:
+    the first draft step reads the real fused target feature g with its token; later steps
+    substitute the drafter's own output a only because the target has not run on the drafted
+    tokens yet.  Once the target has verified positions, their real features exist, and the
+    drafter's prefix KV for them is built as for a first step: per row,
+    g = W_f [h_low; h_mid; h_high] ([P3] 多层特征融合到底融合了什么),
+    u = [rms(E[x]) g_e ; rms(g) g_f], and the layer's key (RoPE at the row's position) and
+    value.  Returns (g [n, d], k [n, Hkv, Dh], v [n, Hkv, Dh]) in float64."""
+    g = fuse_features(f64(h_low), f64(h_mid), f64(h_high), drafter.w_fuse)
+    _, k, v = drafter.qkv([int(t) for t in tokens], g, [int(p) for p in pos])
+    return g, k, v
+
+
+# =======================================================================================
 # O4: tree mask, depth, positions ([P2] 树因果掩码, [P3] 每个节点只能关注它的祖先路径,
 #     [P5] 给节点分配 position / 节点只能看到自己的祖先)
 # =======================================================================================
