@@ -308,7 +308,7 @@ def attention_op(capi, synth, shape, trees, prefix, bound, reps=20, seed=500):
 
 
 OP_KEYS = ("attn_longctx", "attn_batch16", "attn_70b", "attn_8b", "merge", "accept_greedy", "accept_t07",
-           "gemm_sweep")
+           "gemm_sweep", "catchup", "commit")
 
 
 def gemm_sweep(capi, synth, reps):
@@ -341,6 +341,74 @@ def gemm_sweep(capi, synth, reps):
         out.append(dict(key="gemm_sweep", **e))
         del ws, x, y, wk
     return out
+
+
+def catchup_ops(capi, synth, reps):
+    """The step after acceptance at the 8B shapes: drafter catch-up over a 2048-token prompt
+    (fusion 12288 -> 4096 and the K/V rows of the QKV projection, 8192 -> 2048, on the matrix
+    cores) and over one round's committed path (accept_len + 1 = 7 rows, streaming the same
+    weights), and the commit of a 7-node path (8 KV heads x 128, bf16)."""
+    import torch
+    dev = "cuda:0"
+    shape = synth.LLAMA8B
+    d, Hkv, Dh = shape.d, shape.Hkv, shape.Dh
+    nkv = 2 * Hkv * Dh
+    out = []
+    w = synth.drafter_weights(shape, seed=81, device=dev)
+    wbytes = (3 * d * d + 2 * d * nkv) * 2
+    # rotating copies of the two weights the catch-up streams, so the 7-row case reads HBM
+    drs, keep = [], []
+    for c in range(_copies(wbytes)):
+        wc = dict(w)
+        if c:
+            wc["w_fuse"] = w["w_fuse"].clone()
+            wc["w_qkv"] = w["w_qkv"].clone()
+            keep.append(wc)
+        drs.append(capi.make_drafter(wc, shape.Hq, shape.Hkv, shape.Dh))
+    for n, bound in ((2048, "mfma"), (7, "hbm")):
+        h = [synth.normal((n, d), 1.0, 90 + i, torch.bfloat16, dev) for i in range(3)]
+        tok = synth.uniform_int(n, shape.V, 93, dev).to(torch.int32)
+        pos = torch.arange(n, device=dev, dtype=torch.int32)
+        dst = torch.arange(n, device=dev, dtype=torch.int32)
+        kc = torch.empty((n, Hkv, Dh), dtype=torch.bfloat16, device=dev)
+        vc = torch.empty_like(kc)
+        g = torch.empty((n, d), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(capi.eagle3_drafter_catchup_workspace_size(drs[0], n), 256), dtype=torch.uint8,
+                         device=dev)
+
+        def run(i, h=h, tok=tok, pos=pos, dst=dst, kc=kc, vc=vc, g=g, ws=ws):
+            capi.eagle3_drafter_catchup(drs[i % len(drs)], tok, pos, *h, dst, kc, vc, g_out=g, workspace=ws)
+        us = _time_b2b(run, reps)
+        flops = 2 * n * (3 * d * d + 2 * d * nkv)
+        byts = wbytes + n * (3 * d * 2 + 4 * d + 2 * nkv) + n * d * 2
+        e = _entry("drafter catch-up", f"8B shapes, {n} committed positions",
+                   "k_gemm_tile + prep + rope" if n > 160 else "k_gemm_ring + prep + rope", us, bound,
+                   bytes_=byts, flops=flops)
+        out.append(dict(key="catchup", **e))
+        del h, kc, vc, g, ws
+    del w, keep, drs
+    return out
+
+
+def commit_ops(capi, synth, reps):
+    import torch
+    dev = "cuda:0"
+    T, Hkv, Dh, D = 61, 8, 128, 6
+    k_tree = synth.normal((T, Hkv, Dh), 1.0, 1, torch.bfloat16, dev)
+    v_tree = synth.normal((T, Hkv, Dh), 1.0, 2, torch.bfloat16, dev)
+    kc = torch.zeros((4096, Hkv, Dh), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    path = torch.tensor([[0, 1, 11, 21, 31, 41, 51]], dtype=torch.int32, device=dev)
+    acc = torch.tensor([D], dtype=torch.int32, device=dev)
+    dst = torch.tensor([2048], dtype=torch.int32, device=dev)
+
+    def run(i):
+        capi.eagle3_commit_kv(cu, path, acc, k_tree, v_tree, dst, kc, vc)
+    us = _time_b2b(run, reps)
+    byts = 2 * 2 * (D + 1) * Hkv * Dh * 2
+    return [dict(key="commit", **_entry("commit accepted KV", "7-node path, 8 KV heads x 128, bf16",
+                                        "k_commit_kv", us, "latency", bytes_=byts))]
 
 
 def op_rooflines(reps=20, keys=OP_KEYS):
@@ -414,6 +482,10 @@ def op_rooflines(reps=20, keys=OP_KEYS):
         del logits
     if "gemm_sweep" in keys:
         ops += gemm_sweep(capi, synth, reps)
+    if "catchup" in keys:
+        ops += catchup_ops(capi, synth, reps)
+    if "commit" in keys:
+        ops += commit_ops(capi, synth, reps)
     torch.cuda.empty_cache()
     for o in ops:
         if o["key"] in OP_PROFILES:

@@ -62,6 +62,8 @@ extern "C" {
 #define EAGLE3_DEV_BAD_PARENT 1  /* parent[i] not in [0, i) (or root parent != -1)      */
 #define EAGLE3_DEV_TOO_DEEP 2    /* a request has more nodes than the mask can hold     */
 #define EAGLE3_DEV_BAD_TOKEN 4   /* a token id outside [0, vocab)                       */
+#define EAGLE3_DEV_BAD_PATH 8    /* accept_len or a path node outside its request       */
+#define EAGLE3_DEV_BAD_ROW 16    /* a destination row outside the cache                 */
 
 EAGLE3_API int eagle3_abi_version(void);
 EAGLE3_API const char* eagle3_status_string(int status);
@@ -251,6 +253,58 @@ EAGLE3_API int eagle3_accept(int B, int T, const int32_t* cu_nodes, const int32_
                   int V, int dtype, float temperature, uint64_t seed, uint64_t round,
                   int max_depth, int32_t* accept_len, int32_t* path, int32_t* out_tokens,
                   int32_t* bonus, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * eagle3_commit_kv -- commit the accepted path's KV.  [P5] 一棵候选树怎样被验证, step 5
+ * (commit only the KV on the accepted path, release the other branches); [P2]
+ * 二、EAGLE-2动态草稿树 (fall back to the last accepted node, where the next round starts).
+ * For request b the path nodes path[b * path_stride + i], i = 0 .. accept_len[b] (root
+ * first, as eagle3_accept returns them), are tree rows cu_nodes[b] + node; their K and V
+ * rows are copied to cache rows dst_row[b] + i.  No other cache row is written: the rows of
+ * rejected branches are released by not being copied.
+ *
+ *  Hkv, Dh >= 1 with Hkv * Dh * element size a multiple of 16 bytes; path_stride >= 1
+ *  cu_nodes [B+1], path [B, path_stride], accept_len [B], dst_row [B]: int32 (device)
+ *  k_tree, v_tree [T, Hkv, Dh] dtype; k_cache, v_cache [cache_rows, Hkv, Dh] dtype, written
+ *  in place (they must not overlap the tree rows).
+ *  dev_status: EAGLE3_DEV_BAD_PATH (accept_len outside [0, path_stride) or a node outside
+ *  its request: those rows are skipped), EAGLE3_DEV_BAD_ROW (destination outside
+ *  [0, cache_rows): skipped).
+ * ------------------------------------------------------------------------------------ */
+EAGLE3_API int eagle3_commit_kv(int B, int Hkv, int Dh, int dtype, int path_stride,
+                                const int32_t* cu_nodes, const int32_t* path,
+                                const int32_t* accept_len, const void* k_tree, const void* v_tree,
+                                const int32_t* dst_row, int64_t cache_rows, void* k_cache,
+                                void* v_cache, int32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * eagle3_drafter_catchup -- the drafter's prefix KV of committed positions, from the
+ * target's real features.  [P3] 第二步为什么没有“正确隐藏状态”可用 (a draft step reads the
+ * real fused target feature only where the target has already run; drafted steps
+ * substitute the drafter's own output), [P3] 多层特征融合到底融合了什么 (g = W_f [h_low;
+ * h_mid; h_high]).  Row r (one committed position) is formed as the draft round's root:
+ * g_r = W_f [h_low_r; h_mid_r; h_high_r], u_r = [rms(E[tokens_r]) g_e ; rms(g_r) g_f], and
+ * its key (RoPE at pos_r) and value (the K and V rows of w_qkv) go to cache row dst_row[r].
+ * g_r is returned in fp32: the last committed position's g is the next round's root
+ * feature.  Rows may belong to different requests; n = P rows catch the drafter up over a
+ * whole prompt (the fusion and K/V projections then run on the matrix-core tiles).
+ *
+ *  w: the drafter, as for eagle3_draft_expand; n >= 1
+ *  tokens, pos, dst_row [n] int32 (device); h_low, h_mid, h_high [n, d] dtype
+ *  k_cache, v_cache [cache_rows, Hkv, Dh] dtype (the drafter prefix KV), written in place
+ *  g_out [n, d] fp32, may be NULL
+ *  dev_status: EAGLE3_DEV_BAD_TOKEN (token clamped into the vocabulary),
+ *  EAGLE3_DEV_BAD_ROW (destination outside [0, cache_rows): row skipped)
+ *  workspace: eagle3_drafter_catchup_workspace_size(w, n) bytes.
+ *  bf16: any n (n > 160 needs d % 64 == 0); fp32: n <= 160; else EAGLE3_EUNSUPPORTED.
+ * ------------------------------------------------------------------------------------ */
+EAGLE3_API size_t eagle3_drafter_catchup_workspace_size(const eagle3_drafter* w, int n);
+EAGLE3_API int eagle3_drafter_catchup(const eagle3_drafter* w, int n, const int32_t* tokens,
+                                      const int32_t* pos, const void* h_low, const void* h_mid,
+                                      const void* h_high, const int32_t* dst_row, int64_t cache_rows,
+                                      void* k_cache, void* v_cache, float* g_out,
+                                      int32_t* dev_status, void* workspace, size_t workspace_bytes,
+                                      void* stream);
 
 /* ------------------------------------------------------------------------------------
  * eagle3_linear -- Y = X W^T through the GEMM kernels of the drafter's projections.

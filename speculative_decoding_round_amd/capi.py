@@ -68,6 +68,13 @@ EXPORTS = {
     "eagle3_linear_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int]),
     "eagle3_linear": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p, c_void_p,
                               c_size_t, c_void_p]),
+    "eagle3_commit_kv": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                 c_void_p, c_void_p, c_void_p, ctypes.c_int64, c_void_p, c_void_p,
+                                 c_void_p, c_void_p]),
+    "eagle3_drafter_catchup_workspace_size": (c_size_t, [c_void_p, c_int]),
+    "eagle3_drafter_catchup": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_void_p, c_void_p, ctypes.c_int64, c_void_p, c_void_p,
+                                       c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "eagle3_accept_workspace_size": (c_size_t, [c_int, c_int]),
     "eagle3_accept": (c_int, [c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
                               c_void_p, c_int, c_int, c_float, c_uint64, c_uint64, c_int,
@@ -349,6 +356,61 @@ def eagle3_accept(cu_nodes, tokens, parents, mask, logits, temperature: float, s
                              workspace.data_ptr(), workspace.numel(), _stream(stream))
     _check("eagle3_accept", st)
     return out
+
+
+# ---------------------------------------------------------------------------------------
+# After acceptance: commit and drafter catch-up
+# ---------------------------------------------------------------------------------------
+
+
+def eagle3_commit_kv(cu_nodes, path, accept_len, k_tree, v_tree, dst_row, k_cache, v_cache,
+                     dev_status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Copy the accepted path's tree K/V rows (path [B, path_stride] from eagle3_accept) into
+    the caches at rows dst_row[b] + i, in place."""
+    for n, t in (("cu_nodes", cu_nodes), ("path", path), ("accept_len", accept_len),
+                 ("dst_row", dst_row)):
+        _dev(t, n, torch.int32)
+    dt = k_tree.dtype
+    for n, t in (("k_tree", k_tree), ("v_tree", v_tree), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(t, n, dt)
+    B = cu_nodes.numel() - 1
+    _, Hkv, Dh = k_tree.shape
+    st = lib().eagle3_commit_kv(B, Hkv, Dh, dtype_code(dt), path.shape[1], cu_nodes.data_ptr(),
+                                path.data_ptr(), accept_len.data_ptr(), k_tree.data_ptr(),
+                                v_tree.data_ptr(), dst_row.data_ptr(), k_cache.shape[0],
+                                k_cache.data_ptr(), v_cache.data_ptr(), _ptr(dev_status), _stream(stream))
+    _check("eagle3_commit_kv", st)
+
+
+def eagle3_drafter_catchup_workspace_size(drafter: Eagle3Drafter, n: int) -> int:
+    return lib().eagle3_drafter_catchup_workspace_size(ctypes.byref(drafter), n)
+
+
+def eagle3_drafter_catchup(drafter: Eagle3Drafter, tokens, pos, h_low, h_mid, h_high, dst_row,
+                           k_cache, v_cache, g_out: Optional[torch.Tensor] = None,
+                           dev_status: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Drafter keys/values of committed positions (rows) into the drafter prefix caches at
+    dst_row, from the real target features; returns the fused features g [n, d] (fp32)."""
+    for n, t in (("tokens", tokens), ("pos", pos), ("dst_row", dst_row)):
+        _dev(t, n, torch.int32)
+    dt = h_low.dtype
+    for n, t in (("h_low", h_low), ("h_mid", h_mid), ("h_high", h_high), ("k_cache", k_cache),
+                 ("v_cache", v_cache)):
+        _dev(t, n, dt)
+    n_rows = tokens.numel()
+    if g_out is None:
+        g_out = torch.empty((n_rows, drafter.d), dtype=torch.float32, device=h_low.device)
+    _dev(g_out, "g_out", torch.float32)
+    if workspace is None:
+        workspace = _workspace(eagle3_drafter_catchup_workspace_size(drafter, n_rows), h_low.device)
+    st = lib().eagle3_drafter_catchup(ctypes.byref(drafter), n_rows, tokens.data_ptr(), pos.data_ptr(),
+                                      h_low.data_ptr(), h_mid.data_ptr(), h_high.data_ptr(),
+                                      dst_row.data_ptr(), k_cache.shape[0], k_cache.data_ptr(),
+                                      v_cache.data_ptr(), g_out.data_ptr(), _ptr(dev_status),
+                                      workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _check("eagle3_drafter_catchup", st)
+    return g_out
 
 
 # ---------------------------------------------------------------------------------------

@@ -242,6 +242,45 @@ int eagle3_linear(int M, int N, int K, int dtype, const void* X, int ldx, const 
 }
 
 // ---- accept ---------------------------------------------------------------------------
+int eagle3_commit_kv(int B, int Hkv, int Dh, int dtype, int path_stride, const int32_t* cu_nodes,
+                     const int32_t* path, const int32_t* accept_len, const void* k_tree, const void* v_tree,
+                     const int32_t* dst_row, int64_t cache_rows, void* k_cache, void* v_cache,
+                     int32_t* dev_status, void* stream) {
+  if (B <= 0 || Hkv <= 0 || Dh <= 0 || path_stride <= 0 || cache_rows < 0) return EAGLE3_EINVAL;
+  if (!dtype_ok(dtype)) return EAGLE3_EINVAL;
+  if (!cu_nodes || !path || !accept_len || !k_tree || !v_tree || !dst_row || !k_cache || !v_cache)
+    return EAGLE3_EINVAL;
+  const long row_bytes = (long)Hkv * Dh * elem_size(dtype);
+  if (row_bytes % 16) return EAGLE3_EINVAL;
+  if ((uintptr_t)k_tree % 16 || (uintptr_t)v_tree % 16 || (uintptr_t)k_cache % 16 || (uintptr_t)v_cache % 16)
+    return EAGLE3_EINVAL;
+  if (path_stride > 65535 || B > 65535) return EAGLE3_EUNSUPPORTED;
+  return launch_commit_kv(B, Hkv * Dh, dtype, path_stride, cu_nodes, path, accept_len, k_tree, v_tree, dst_row,
+                          (long)cache_rows, k_cache, v_cache, dev_status, (hipStream_t)stream);
+}
+
+size_t eagle3_drafter_catchup_workspace_size(const eagle3_drafter* w, int n) {
+  if (drafter_check(w) != EAGLE3_OK || n <= 0) return 0;
+  return catchup_workspace(w, n);
+}
+
+int eagle3_drafter_catchup(const eagle3_drafter* w, int n, const int32_t* tokens, const int32_t* pos,
+                           const void* h_low, const void* h_mid, const void* h_high, const int32_t* dst_row,
+                           int64_t cache_rows, void* k_cache, void* v_cache, float* g_out, int32_t* dev_status,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (const int st = drafter_check(w)) return st;
+  if (n <= 0 || cache_rows < 0) return EAGLE3_EINVAL;
+  if (!tokens || !pos || !h_low || !h_mid || !h_high || !dst_row || !k_cache || !v_cache) return EAGLE3_EINVAL;
+  if ((uintptr_t)h_low % 16 || (uintptr_t)h_mid % 16 || (uintptr_t)h_high % 16 || (uintptr_t)k_cache % 16 ||
+      (uintptr_t)v_cache % 16 || (uintptr_t)g_out % 16)
+    return EAGLE3_EINVAL;
+  if (!catchup_supported(w, n)) return EAGLE3_EUNSUPPORTED;
+  const size_t need = catchup_workspace(w, n);
+  if (!workspace || workspace_bytes < need) return EAGLE3_EWORKSPACE;
+  return launch_catchup(w, n, tokens, pos, h_low, h_mid, h_high, dst_row, (long)cache_rows, k_cache, v_cache,
+                        g_out, dev_status, workspace, (hipStream_t)stream);
+}
+
 size_t eagle3_accept_workspace_size(int T, int V) {
   if (T < 0 || V <= 0) return 0;
   return accept_workspace(T, V);

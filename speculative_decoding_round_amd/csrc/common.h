@@ -226,6 +226,57 @@ __device__ __forceinline__ void block_argmax(float& v, int& i, float* sv, int* s
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// Row helpers: 8 consecutive elements of a row as float (one or two 16-byte accesses).
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* v);
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* v) {
+  const u32x4 a = ld16(p), b = ld16(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = __uint_as_float(a[i]);
+    v[4 + i] = __uint_as_float(b[i]);
+  }
+}
+template <>
+__device__ __forceinline__ void load8<bf16>(const bf16* p, float* v) {
+  const u32x4 a = ld16(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = chunk_elem<bf16>(a, i);
+}
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float* v);
+template <>
+__device__ __forceinline__ void store8<float>(float* p, const float* v) {
+  st16(p, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
+  st16(p + 4, u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])});
+}
+template <>
+__device__ __forceinline__ void store8<bf16>(bf16* p, const float* v) {
+  bf16x8 o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = static_cast<bf16>(v[i]);
+  st16(p, __builtin_bit_cast(u32x4, o));
+}
+
+// Sum of two values over the block (fixed order); scratch needs 2 * 16 floats.
+__device__ __forceinline__ void block_sum2(float& a, float& b, float* scratch) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  a = wave_sum(a);
+  b = wave_sum(b);
+  if (lane == 0) {
+    scratch[w] = a;
+    scratch[16 + w] = b;
+  }
+  __syncthreads();
+  a = 0.f;
+  b = 0.f;
+  for (int i = 0; i < nw; ++i) {
+    a += scratch[i];
+    b += scratch[16 + i];
+  }
+}
+
 }  // namespace e3
 
 // ---------------------------------------------------------------------------------------

@@ -76,56 +76,6 @@ __global__ __launch_bounds__(256) void k_init(int B, int S, int d, int V, const 
 // Row kernels.  One workgroup per row, one thread per 8-element chunk (d <= 8 * 1024), every
 // load issued before any arithmetic so a row costs one memory round trip.
 // ---------------------------------------------------------------------------------------
-template <typename T>
-__device__ __forceinline__ void load8(const T* p, float* v);
-template <>
-__device__ __forceinline__ void load8<float>(const float* p, float* v) {
-  const u32x4 a = ld16(p), b = ld16(p + 4);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[i] = __uint_as_float(a[i]);
-    v[4 + i] = __uint_as_float(b[i]);
-  }
-}
-template <>
-__device__ __forceinline__ void load8<bf16>(const bf16* p, float* v) {
-  const u32x4 a = ld16(p);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = chunk_elem<bf16>(a, i);
-}
-template <typename T>
-__device__ __forceinline__ void store8(T* p, const float* v);
-template <>
-__device__ __forceinline__ void store8<float>(float* p, const float* v) {
-  st16(p, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
-  st16(p + 4, u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])});
-}
-template <>
-__device__ __forceinline__ void store8<bf16>(bf16* p, const float* v) {
-  bf16x8 o;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = static_cast<bf16>(v[i]);
-  st16(p, __builtin_bit_cast(u32x4, o));
-}
-
-// Sum of two values over the block (fixed order); scratch needs 2 * 16 floats.
-__device__ __forceinline__ void block_sum2(float& a, float& b, float* scratch) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  a = wave_sum(a);
-  b = wave_sum(b);
-  if (lane == 0) {
-    scratch[w] = a;
-    scratch[16 + w] = b;
-  }
-  __syncthreads();
-  a = 0.f;
-  b = 0.f;
-  for (int i = 0; i < nw; ++i) {
-    a += scratch[i];
-    b += scratch[16 + i];
-  }
-}
-
 // prep: u = [rms(E[x]) * g_e ; rms(f) * g_f], f = g (root) or a of the parent slot.
 template <typename T>
 __global__ __launch_bounds__(1024) void k_prep(int R, int sb, int S, int d, int V, float eps, int step,
@@ -961,8 +911,8 @@ int run_draft(const eagle3_drafter* w, const Plan& p, const void* h_low, const v
 
 namespace e3h {
 
-int draft_check(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, int max_prefix) {
-  if (!w || !t || B <= 0 || max_prefix < 0) return EAGLE3_EINVAL;
+int drafter_check(const eagle3_drafter* w) {
+  if (!w) return EAGLE3_EINVAL;
   if (!dtype_ok(w->dtype)) return EAGLE3_EINVAL;
   if (w->d <= 0 || w->n_heads_q <= 0 || w->n_heads_kv <= 0 || w->ffn <= 0 || w->vocab <= 0)
     return EAGLE3_EINVAL;
@@ -970,6 +920,15 @@ int draft_check(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, int ma
   if (w->head_dim != 64 && w->head_dim != 128) return EAGLE3_EUNSUPPORTED;
   if (w->d % 8 || w->ffn % 8 || w->vocab % 4 || w->d > 8192) return EAGLE3_EUNSUPPORTED;
   if (!(w->eps > 0.f) || !(w->rope_theta > 0.f)) return EAGLE3_EINVAL;
+  if (!w->embed || !w->w_fuse || !w->g_embed || !w->g_feat || !w->g_mlp || !w->g_final ||
+      !w->w_qkv || !w->w_o || !w->w_gate_up || !w->w_down || !w->w_lm)
+    return EAGLE3_EINVAL;
+  return EAGLE3_OK;
+}
+
+int draft_check(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, int max_prefix) {
+  if (!w || !t || B <= 0 || max_prefix < 0) return EAGLE3_EINVAL;
+  if (const int st = drafter_check(w)) return st;
   if (t->depth < 1 || t->topk < 1 || t->width < 1 || t->n_nodes < 1) return EAGLE3_EINVAL;
   if (t->topk > KMAX || t->topk > w->vocab) return EAGLE3_EUNSUPPORTED;
   if (1 + (long)(t->depth - 1) * t->width > SMAX) return EAGLE3_EUNSUPPORTED;
@@ -978,9 +937,6 @@ int draft_check(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, int ma
   if ((long)B * (t->width > 1 ? t->width : 1) > 160) return EAGLE3_EUNSUPPORTED;
   if (t->width > SEL_MAXR) return EAGLE3_EUNSUPPORTED;
   if (w->vocab > 64 * TK_CHUNK) return EAGLE3_EUNSUPPORTED;
-  if (!w->embed || !w->w_fuse || !w->g_embed || !w->g_feat || !w->g_mlp || !w->g_final ||
-      !w->w_qkv || !w->w_o || !w->w_gate_up || !w->w_down || !w->w_lm)
-    return EAGLE3_EINVAL;
   return EAGLE3_OK;
 }
 

@@ -62,4 +62,17 @@ int launch_gemm(const GemmPlan& p, int dtype, const void* X, int ldx, const void
 int launch_epi_sum(const GemmPlan& p, const float* part, float* out, const float* resid,
                    hipStream_t s, const char* tag);
 
+// ---- commit and drafter catch-up ------------------------------------------------------
+int drafter_check(const eagle3_drafter* w);
+int launch_commit_kv(int B, int row_elems, int dtype, int path_stride, const int32_t* cu_nodes,
+                     const int32_t* path, const int32_t* accept_len, const void* k_tree,
+                     const void* v_tree, const int32_t* dst_row, long cache_rows, void* k_cache,
+                     void* v_cache, int32_t* dev_status, hipStream_t s);
+size_t catchup_workspace(const eagle3_drafter* w, int n);
+int catchup_supported(const eagle3_drafter* w, int n);
+int launch_catchup(const eagle3_drafter* w, int n, const int32_t* tokens, const int32_t* pos,
+                   const void* h_low, const void* h_mid, const void* h_high, const int32_t* dst_row,
+                   long cache_rows, void* k_cache, void* v_cache, float* g_out, int32_t* dev_status,
+                   void* ws, hipStream_t s);
+
 }  // namespace e3h

@@ -148,3 +148,24 @@ def test_linear_validation(lib):
     # the compute units) split it in two, one fp32 partial [M, N] per split
     assert lib.eagle3_linear_workspace_size(1024, 6144, 8192, 1) == 2 * 1024 * 6144 * 4
     assert lib.eagle3_linear(10, 4096, 4096, 1, P, 4096, P, P, None, 0, None) == -3  # no workspace
+
+
+def test_commit_and_catchup_validation(lib):
+    """Host-side checks of eagle3_commit_kv and eagle3_drafter_catchup."""
+    P = 1 << 12
+    # commit: B, Hkv, Dh, dtype, path_stride, cu_nodes, path, accept_len, k_tree, v_tree,
+    # dst_row, cache_rows, k_cache, v_cache, dev_status, stream
+    args = [2, 8, 128, 1, 7, P, P, P, P, P, P, 100, P, P, None, None]
+    bad = list(args); bad[0] = 0
+    assert lib.eagle3_commit_kv(*bad) == -1                       # no request
+    bad = list(args); bad[3] = 5
+    assert lib.eagle3_commit_kv(*bad) == -1                       # dtype
+    bad = list(args); bad[1] = 1; bad[2] = 3
+    assert lib.eagle3_commit_kv(*bad) == -1                       # row of 6 bytes: not 16-aligned
+    bad = list(args); bad[12] = P + 4
+    assert lib.eagle3_commit_kv(*bad) == -1                       # misaligned cache
+    bad = list(args); bad[6] = None
+    assert lib.eagle3_commit_kv(*bad) == -1                       # null path
+    assert lib.eagle3_drafter_catchup_workspace_size(None, 4) == 0
+    assert lib.eagle3_drafter_catchup(None, 4, P, P, P, P, P, P, 10, P, P, None, None, P, 1 << 20,
+                                      None) == -1
