@@ -633,13 +633,14 @@ def draws_over_rounds(z_row, temperature: float, seed: int, rounds: np.ndarray, 
     z = np.asarray(z_row, dtype=np.float32)
     V = z.shape[0]
     R = rounds.shape[0]
-    t = np.tile(np.arange(V, dtype=np.uint64), R)
-    rr = np.repeat(np.asarray(rounds, dtype=np.uint64), V)
-    c0 = t >> np.uint64(2)
-    w = philox4x32_10(c0, np.full(t.shape, i), np.full(t.shape, b), rr & np.uint64(MASK32),
-                      np.full(t.shape, seed & MASK32), np.full(t.shape, (seed >> 32) & MASK32))
-    x = np.choose((t & np.uint64(3)).astype(np.int64), w)
-    g = (-ln_spec(-ln_spec(uniform23(x)))).astype(np.float32).reshape(R, V)
+    # one Philox block per (round, counter t >> 2): its four words serve tokens 4c .. 4c+3
+    C = (V + 3) // 4
+    c0 = np.tile(np.arange(C, dtype=np.uint64), R)
+    rr = np.repeat(np.asarray(rounds, dtype=np.uint64), C)
+    w = philox4x32_10(c0, np.full(c0.shape, i), np.full(c0.shape, b), rr & np.uint64(MASK32),
+                      np.full(c0.shape, seed & MASK32), np.full(c0.shape, (seed >> 32) & MASK32))
+    x = np.stack(w, axis=-1).reshape(R, 4 * C)[:, :V]
+    g = (-ln_spec(-ln_spec(uniform23(x.reshape(-1))))).astype(np.float32).reshape(R, V)
     invT = np.float32(1.0) / np.float32(temperature)
     vals = (z[None, :] * invT + g).astype(np.float32)
     return np.argmax(vals, axis=1)

@@ -138,7 +138,7 @@ def test_sampler_consistent_with_vectorised_draws():
 def test_chi_square_lossless():
     """Speculative sampling must reproduce the target distribution: on the K=3 two-level
     tree with V=16 and T=1, the first emitted token follows softmax(z_root), and the
-    second token, conditioned on accepting child c, follows softmax(z_c); 1e6 draws,
+    second token, conditioned on accepting child c, follows softmax(z_c); 3e5 draws,
     chi-square p > 0.01."""
     V, T = 16, 1.0
     rng = np.random.default_rng(5)
@@ -147,7 +147,7 @@ def test_chi_square_lossless():
     tok = [0] + [int(x) for x in rng.choice(V, 3, replace=False)] + \
         [int(x) for x in rng.integers(0, V, 9)]
     z = (rng.standard_normal((n, V)) * 1.2).astype(np.float32)
-    rounds = np.arange(1_000_000, dtype=np.uint64)
+    rounds = np.arange(300_000, dtype=np.uint64)
     seed = 20260601
     y_root = O.draws_over_rounds(z[0], T, seed, rounds, 0, 0)
 
