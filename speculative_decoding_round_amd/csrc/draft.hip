@@ -461,13 +461,13 @@ __device__ __forceinline__ int rank_of(const float* sc, int lo, int hi, float sa
   return rank;
 }
 
-// Number of entries of [0, hi) that beat (sa, ia) by (score desc, index asc), the indices
-// given in `ix`; both LDS arrays 16-byte aligned, padded with (-inf, INT_MAX) to a multiple
-// of 4.
-__device__ __forceinline__ int rank_idx(const float* sc, const int* ix, int hi, float sa, int ia) {
+// Number of entries of [lo, hi) that beat (sa, ia) by (score desc, index asc), the indices
+// given in `ix`; lo a multiple of 4; both LDS arrays 16-byte aligned, padded with
+// (-inf, INT_MAX) to a multiple of 4.
+__device__ __forceinline__ int rank_idx(const float* sc, const int* ix, int lo, int hi, float sa, int ia) {
   int rank = 0;
 #pragma unroll 4
-  for (int f = 0; f < hi; f += 4) {
+  for (int f = lo; f < hi; f += 4) {
     const floatx4 v = *reinterpret_cast<const floatx4*>(sc + f);
     const intx4 i = *reinterpret_cast<const intx4*>(ix + f);
 #pragma unroll
@@ -511,6 +511,8 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
   __shared__ float s_score[SEL_MAXR];
   __shared__ uint64_t s_mask[SEL_MAXR];
   __shared__ int s_cand[SEL_MAXR];
+  __shared__ int fr_e[SEL_MAXR];
+  __shared__ int s_rank[SEL_MAXNEW + SEL_MAXTOP + SEL_MAXNEW];   // frontier ranks, then list ranks
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int sb = step == 0 ? 0 : 1 + (step - 1) * W;
@@ -583,50 +585,74 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
     nps[e] = sb + j;
     msc[ntop + e] = sc;
     midx[ntop + e] = n_before + e;
-    ctok[n_before + e] = tk;
-    cps[n_before + e] = sb + j;
-    cdep[n_before + e] = step + 1;
-    csc[n_before + e] = sc;
   }
   if (threadIdx.x < 4) {
     nsc[n_new + threadIdx.x] = kNegInf;
     msc[m_total + threadIdx.x] = kNegInf;
     midx[m_total + threadIdx.x] = 0x7fffffff;
   }
+  for (int i = threadIdx.x; i < SEL_MAXNEW + m_total; i += blockDim.x) s_rank[i] = 0;
+  for (int i = threadIdx.x; i < n_total; i += blockDim.x) lab_of[i] = -1;
   __syncthreads();
-  if (!last) {
-    // the W best new candidates (score desc, creation asc) take the next step's slots
-    const int nsb = 1 + step * W;
-    for (int e = threadIdx.x; e < n_new; e += blockDim.x) {
-      const float sa = nsc[e];
-      const int rank = rank_of(nsc, 0, n_new, sa, e);
-      if (rank < W) {
-        const int slot = nsb + rank;
-        const int i = b * S + slot;
-        const int ps = nps[e];
-        st.tok[i] = ntok[e];
-        st.parent[i] = ps;
-        st.valid[i] = 1;
-        st.score[i] = sa;
-        st.cand[i] = n_before + e;
-        st.mask[i] = s_mask[ps - sb] | (1ull << slot);
-        if (dbg_tok) dbg_tok[i] = ntok[e];
-        if (dbg_par) dbg_par[i] = ps;
+  // Ranks by (score desc, creation asc): of the new candidates among themselves (the W best
+  // take the next step's slots) and of the running list with the new candidates (the N best
+  // are kept).  The whole workgroup works on (entry, 16-entry chunk) pairs; the integer
+  // partial counts are summed by LDS atomics, whose order does not matter.
+  {
+    constexpr int CH = 16;
+    const int cf = last ? 0 : (n_new + CH - 1) / CH;
+    const int cl = (m_total + CH - 1) / CH;
+    const int items_f = n_new * cf, items = items_f + m_total * cl;
+    for (int it = threadIdx.x; it < items; it += blockDim.x) {
+      if (it < items_f) {
+        const int e = it % n_new, lo = (it / n_new) * CH;
+        const int part = rank_of(nsc, lo, min(lo + CH, n_new), nsc[e], e);
+        if (part) atomicAdd(&s_rank[e], part);
+      } else {
+        const int jt = it - items_f;
+        const int i = jt % m_total, lo = (jt / m_total) * CH;
+        const int part = rank_idx(msc, midx, lo, min(lo + CH, m_total), msc[i], midx[i]);
+        if (part) atomicAdd(&s_rank[SEL_MAXNEW + i], part);
       }
     }
   }
-  // the running list: the N best of (list, new)
+  __syncthreads();
+  if (!last)
+    for (int e = threadIdx.x; e < n_new; e += blockDim.x)
+      if (s_rank[e] < W) fr_e[s_rank[e]] = e;   // slots written at the end (a barrier after global stores waits for them)
   for (int i = threadIdx.x; i < m_total; i += blockDim.x) {
-    const int r = rank_idx(msc, midx, m_total, msc[i], midx[i]);
+    const int r = s_rank[SEL_MAXNEW + i];
     if (r < N) {
       ktop[r] = midx[i];
       ktsc[r] = msc[i];
     }
   }
-  for (int i = threadIdx.x; i < n_total; i += blockDim.x) lab_of[i] = -1;
   __syncthreads();
   const int n_keep = min(N, m_total);
+  // this step's candidates into the pool
+  for (int e = threadIdx.x; e < n_new; e += blockDim.x) {
+    ctok[n_before + e] = ntok[e];
+    cps[n_before + e] = nps[e];
+    cdep[n_before + e] = step + 1;
+    csc[n_before + e] = nsc[e];
+  }
   if (!last) {
+    const int nsb = 1 + step * W;
+    const int n_fr = min(W, n_new);
+    for (int r = threadIdx.x; r < n_fr; r += blockDim.x) {
+      const int e = fr_e[r];
+      const int slot = nsb + r;
+      const int i = b * S + slot;
+      const int ps = nps[e];
+      st.tok[i] = ntok[e];
+      st.parent[i] = ps;
+      st.valid[i] = 1;
+      st.score[i] = nsc[e];
+      st.cand[i] = n_before + e;
+      st.mask[i] = s_mask[ps - sb] | (1ull << slot);
+      if (dbg_tok) dbg_tok[i] = ntok[e];
+      if (dbg_par) dbg_par[i] = ps;
+    }
     for (int i = threadIdx.x; i < n_keep; i += blockDim.x) {
       topn[i] = ktop[i];
       topsc[i] = ktsc[i];
@@ -897,7 +923,7 @@ int run_draft(const eagle3_drafter* w, const Plan& p, const void* h_low, const v
         if ((st = launch_status())) return st;
       }
       ProfScope ps("draft_select", s);
-      hipLaunchKernelGGL(k_select, dim3(B), dim3(64 * (R > 4 ? R : 4)), 0, s, step, p.D, p.K, p.W, p.N, p.S, p.PMAX, R,
+      hipLaunchKernelGGL(k_select, dim3(B), dim3(1024), 0, s, step, p.D, p.K, p.W, p.N, p.S, p.PMAX, R,
                          p.lm_nchunk, p.cv, p.ci, p.cmax, p.csum, p.st, p.cs, tokens, parents, depth,
                          score, n_nodes, dbg_tok, dbg_par, dbg ? dbg->slot_topk_id : (int32_t*)nullptr,
                          dbg ? dbg->slot_topk_val : (float*)nullptr, dbg ? dbg->slot_lse : (float*)nullptr);

@@ -577,6 +577,15 @@ int launch_ring(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, f
                 hipStream_t s, int role) {
   if (p.silu) return launch_ring_r<MT, 6, 4, true>(p, X, ldx, W, Y, act, s);
   if (p.waves == 1) return launch_ring_r<MT, 1, 1, false>(p, X, ldx, W, Y, act, s);
+  if (p.waves == 4) {
+    switch (role) {
+      case 2: return launch_ring_r<MT, 2, 4, false>(p, X, ldx, W, Y, act, s);
+      case 3: return launch_ring_r<MT, 3, 4, false>(p, X, ldx, W, Y, act, s);
+      case 4: return launch_ring_r<MT, 4, 4, false>(p, X, ldx, W, Y, act, s);
+      case 5: return launch_ring_r<MT, 5, 4, false>(p, X, ldx, W, Y, act, s);
+      default: return launch_ring_r<MT, 0, 4, false>(p, X, ldx, W, Y, act, s);
+    }
+  }
   switch (role) {
     case 2: return launch_ring_r<MT, 2, 2, false>(p, X, ldx, W, Y, act, s);
     case 3: return launch_ring_r<MT, 3, 2, false>(p, X, ldx, W, Y, act, s);
@@ -674,6 +683,14 @@ GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu) {
     } else {
       p.n_blocks = ((N + 15) / 16 + kRingNTB - 1) / kRingNTB;
       p.waves = p.n_blocks >= 512 ? 1 : 2;
+      // four waves per workgroup halve the split count (fewer fp32 partials for the
+      // epilogue to read) when the workgroups, one per CU at 128 KB of LDS, still cover
+      // three quarters of the CUs
+      if (p.waves == 2 && p.n_blocks <= 64) {
+        const int s4 = (kRingTargetWgs + p.n_blocks * 4 - 1) / (p.n_blocks * 4);
+        const int c4 = ((p.chunks_total + s4 - 1) / s4 + 31) / 32 * 32;
+        if ((long)p.n_blocks * ((p.chunks_total + c4 - 1) / c4) >= 192) p.waves = 4;
+      }
       splits = (kRingTargetWgs + p.n_blocks * p.waves - 1) / (p.n_blocks * p.waves);
     }
     int cps = (p.chunks_total + splits - 1) / splits;
