@@ -308,7 +308,7 @@ def attention_op(capi, synth, shape, trees, prefix, bound, reps=20, seed=500):
 
 
 OP_KEYS = ("attn_longctx", "attn_batch16", "attn_70b", "attn_8b", "merge", "accept_greedy", "accept_t07",
-           "gemm_sweep", "catchup", "commit")
+           "gemm_sweep", "catchup", "commit", "tree_budgets")
 
 
 def gemm_sweep(capi, synth, reps):
@@ -411,6 +411,40 @@ def commit_ops(capi, synth, reps):
                                         "k_commit_kv", us, "latency", bytes_=byts))]
 
 
+def tree_budget_ops(steps=10):
+    """Whole rounds at the 8B shapes for other tree budgets: EAGLE-2's depth 6 and EAGLE-3's
+    depth 8 at 60, 50 and 48 kept nodes (K = W = 10).  The round streams the fusion weights
+    once and the layer and LM-head weights at every depth step (HBM-bound)."""
+    import torch
+    from speculative_decoding_round_amd import synth
+    dev = "cuda:0"
+    out = []
+    for D, N in ((6, 60), (8, 60), (8, 50), (8, 48)):
+        shape = synth.scaled(synth.LLAMA8B, depth=D, n_nodes=N)
+        rnd = Round(shape, dev)
+        for _ in range(3):
+            rnd.step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            rnd.step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        n_ver = int(rnd.draft_out["n_nodes"].sum().item()) - rnd.B
+        d, F, V = shape.d, shape.F, shape.V
+        nqkv = (shape.Hq + 2 * shape.Hkv) * shape.Dh
+        wbytes = 2 * (3 * d * d + D * (2 * d * nqkv + shape.Hq * shape.Dh * d + 3 * d * F + V * d))
+        e = _entry("draft + verify round", f"llama8b_bf16 D={D} K=10 W=10 N={N}", "whole round", ms * 1e3,
+                   "hbm", bytes_=wbytes, verified_tokens_per_s=round(n_ver / (ms / 1e3), 1),
+                   verified_nodes=n_ver)
+        out.append(dict(key="tree_budgets", **e))
+        del rnd
+        torch.cuda.empty_cache()
+    return out
+
+
 def op_rooflines(reps=20, keys=OP_KEYS):
     import numpy as np
     import torch
@@ -486,6 +520,8 @@ def op_rooflines(reps=20, keys=OP_KEYS):
         ops += catchup_ops(capi, synth, reps)
     if "commit" in keys:
         ops += commit_ops(capi, synth, reps)
+    if "tree_budgets" in keys:
+        ops += tree_budget_ops()
     torch.cuda.empty_cache()
     for o in ops:
         if o["key"] in OP_PROFILES:

@@ -102,7 +102,7 @@ typedef struct eagle3_drafter {
  * expansion; [P2] 二、EAGLE-2动态草稿树: top-K children per expanded node).
  * depth D >= 1 evaluation steps, topk K >= 1 children per evaluated node, width W >= 1
  * nodes evaluated per depth, n_nodes N >= 1 draft nodes kept (the root is extra).
- * Limits: K <= 16, 1 + (D-1)*W <= 64, N <= 255. */
+ * Limits: K <= 16, 1 + (D-1)*W <= 256, N <= 255. */
 typedef struct eagle3_tree_cfg {
   int32_t depth;
   int32_t topk;

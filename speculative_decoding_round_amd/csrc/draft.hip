@@ -15,15 +15,16 @@ namespace {
 typedef int intx4 __attribute__((ext_vector_type(4)));
 
 constexpr int KMAX = 16;     // largest top-K
-constexpr int SMAX = 64;     // largest slot count (one mask word)
+constexpr int SMAX = 256;    // largest slot count (four mask words)
 
 struct SlotState {
   int32_t* tok;      // [B*S]
   int32_t* parent;   // [B*S]  -1 root, -2 unused
   int32_t* valid;    // [B*S]
   float* score;      // [B*S]
-  uint64_t* mask;    // [B*S]  ancestors-or-self over slots
+  uint64_t* mask;    // [B*S, mw]  ancestors-or-self over slots, bit s of word s / 64
   int32_t* cand;     // [B*S]  candidate index of the slot's node (-1 root)
+  int mw;            // mask words per slot: ceil(S / 64)
 };
 struct CandState {
   int32_t* tok;      // [B*PMAX]
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(256) void k_init(int B, int S, int d, int V, const 
     st.parent[i] = s == 0 ? -1 : -2;
     st.valid[i] = s == 0;
     st.score[i] = 0.f;
-    st.mask[i] = s == 0 ? 1ull : 0ull;
+    for (int q = 0; q < st.mw; ++q) st.mask[(size_t)i * st.mw + q] = (s == 0 && q == 0) ? 1ull : 0ull;
     st.cand[i] = -1;
     if (dbg_tok) dbg_tok[i] = st.tok[i];
     if (dbg_par) dbg_par[i] = st.parent[i];
@@ -136,7 +137,8 @@ __global__ __launch_bounds__(1024) void k_prep(int R, int sb, int S, int d, int 
   store8<T>(ur + k0, o1);
   store8<T>(ur + d + k0, o2);
   store8<float>(f_rows + (size_t)r * d + k0, fv);
-  if (threadIdx.x == 0) row_mask[r] = valid ? st.mask[si] : 0ull;
+  if (threadIdx.x < st.mw)
+    row_mask[(size_t)r * st.mw + threadIdx.x] = valid ? st.mask[(size_t)si * st.mw + threadIdx.x] : 0ull;
 }
 
 // Residual + RMSNorm over a projection's split-K partials:
@@ -509,7 +511,7 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
   __shared__ int lab_of[1024];
   __shared__ int s_valid[SEL_MAXR];
   __shared__ float s_score[SEL_MAXR];
-  __shared__ uint64_t s_mask[SEL_MAXR];
+  __shared__ uint64_t s_mask[SEL_MAXR][SMAX / 64];
   __shared__ int s_cand[SEL_MAXR];
   __shared__ int fr_e[SEL_MAXR];
   __shared__ int s_rank[SEL_MAXNEW + SEL_MAXTOP + SEL_MAXNEW];   // frontier ranks, then list ranks
@@ -537,8 +539,8 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
     const int sidx = b * S + sb + w;
     const int valid = st.valid[sidx];
     const float score0 = st.score[sidx];
-    const uint64_t mk = st.mask[sidx];
     const int cand0 = st.cand[sidx];
+    if (lane < st.mw) s_mask[w][lane] = st.mask[(size_t)sidx * st.mw + lane];
     const bool ok = lane < n_chunks;
     const float cm = ok ? cmax[(size_t)m * n_chunks + lane] : kNegInf;
     const float cs_ = ok ? csum[(size_t)m * n_chunks + lane] : 0.f;
@@ -548,7 +550,6 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
     if (lane == 0) {
       s_valid[w] = valid;
       s_score[w] = score0;
-      s_mask[w] = mk;
       s_cand[w] = cand0;
     }
     if (valid) {
@@ -649,7 +650,8 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
       st.valid[i] = 1;
       st.score[i] = nsc[e];
       st.cand[i] = n_before + e;
-      st.mask[i] = s_mask[ps - sb] | (1ull << slot);
+      for (int q = 0; q < st.mw; ++q)
+        st.mask[(size_t)i * st.mw + q] = s_mask[ps - sb][q] | (q == (slot >> 6) ? 1ull << (slot & 63) : 0ull);
       if (dbg_tok) dbg_tok[i] = ntok[e];
       if (dbg_par) dbg_par[i] = ps;
     }
@@ -772,7 +774,8 @@ Plan make_plan(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, int max
   p.st.parent = c.take<int32_t>(BS);
   p.st.valid = c.take<int32_t>(BS);
   p.st.score = c.take<float>(BS);
-  p.st.mask = c.take<uint64_t>(BS);
+  p.st.mw = (p.S + 63) / 64;
+  p.st.mask = c.take<uint64_t>(BS * p.st.mw);
   p.st.cand = c.take<int32_t>(BS);
   p.cs.tok = c.take<int32_t>(BP);
   p.cs.pslot = c.take<int32_t>(BP);
@@ -787,7 +790,7 @@ Plan make_plan(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, int max
   p.kslot = c.take<char>(BS * p.Hkv * p.Dh * es);
   p.vslot = c.take<char>(BS * p.Hkv * p.Dh * es);
   const size_t M = p.Mmax;
-  p.row_mask = c.take<uint64_t>(M);
+  p.row_mask = c.take<uint64_t>(M * p.st.mw);
   p.f_rows = c.take<float>(M * p.d);
   p.u = c.take<char>(M * 2 * p.d * es);
   p.q_rows = c.take<char>(M * p.Hq * p.Dh * es);
@@ -875,7 +878,7 @@ int run_draft(const eagle3_drafter* w, const Plan& p, const void* h_low, const v
       a.kt_stride = p.S;
       a.kt_count = sb + R;
       a.mask = p.row_mask;
-      a.W64 = 1;
+      a.W64 = p.st.mw;
       a.kp = kpre;
       a.vp = vpre;
       a.p_cu = cu_prefix;

@@ -144,7 +144,14 @@ SMALL_BF16 = synth.scaled(synth.LLAMA8B, d=512, Hq=8, Hkv=2, Dh=128, F=1536, V=8
     (synth.scaled(SMALL_BF16, dtype="f32", B=2, Dh=64, Hq=8, Hkv=8), [77, 513]),
     (synth.scaled(SMALL_BF16, B=1, depth=1, topk=16, width=1, n_nodes=16), [64]),
     (synth.scaled(SMALL_BF16, B=2, depth=6, topk=10, width=10, n_nodes=60, V=4096), [2048, 5]),
-], ids=["bf16_ragged", "fp32_mha", "bf16_depth1_k16", "bf16_llama_budget"])
+    # EAGLE-3's depth 8 at the 60 / 50 / 48-node budgets: 71 evaluation slots (two mask words)
+    (synth.scaled(SMALL_BF16, B=2, depth=8, topk=10, width=10, n_nodes=60, V=4096), [1500, 40]),
+    (synth.scaled(SMALL_BF16, B=1, depth=8, topk=10, width=10, n_nodes=50, V=4096), [700]),
+    (synth.scaled(SMALL_BF16, B=1, depth=8, topk=10, width=10, n_nodes=48, V=4096), [33]),
+    # 177 slots (three mask words), a 200-node tree
+    (synth.scaled(SMALL_BF16, B=1, depth=12, topk=5, width=16, n_nodes=200, V=4096), [256]),
+], ids=["bf16_ragged", "fp32_mha", "bf16_depth1_k16", "bf16_llama_budget", "bf16_depth8_n60",
+        "bf16_depth8_n50", "bf16_depth8_n48", "bf16_177_slots"])
 def test_draft_small_full_protocol(shape, prefix):
     need_gpu()
     B = shape.B
