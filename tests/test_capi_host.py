@@ -91,7 +91,9 @@ def test_draft_validation_and_workspace(lib):
     t = Eagle3TreeCfg(depth=6, topk=10, width=10, n_nodes=60)
     ws = lib.eagle3_draft_expand_workspace_size(ctypes.byref(w), ctypes.byref(t), 1, 2048)
     assert 0 < ws < 512 << 20
-    t_bad = Eagle3TreeCfg(depth=8, topk=10, width=10, n_nodes=60)   # 71 slots > 64
+    t8 = Eagle3TreeCfg(depth=8, topk=10, width=10, n_nodes=60)       # 71 slots: two mask words
+    assert lib.eagle3_draft_expand_workspace_size(ctypes.byref(w), ctypes.byref(t8), 1, 2048) > ws
+    t_bad = Eagle3TreeCfg(depth=18, topk=1, width=16, n_nodes=60)    # 273 slots > 256
     assert lib.eagle3_draft_expand_workspace_size(ctypes.byref(w), ctypes.byref(t_bad), 1, 2048) == 0
     st = lib.eagle3_draft_expand(ctypes.byref(w), ctypes.byref(t_bad), 1, 256, 256, 256, 256, 256, 256,
                                  256, 2048, 256, 256, 256, 256, 256, None, 256, 1 << 30, None)
