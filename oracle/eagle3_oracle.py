@@ -703,3 +703,88 @@ def accept(cu_nodes, tokens, parents, logits, temperature: float, seed: int, rnd
             outt[b, s] = int(tokens[n0 + j])
         outt[b, best_len] = y[best]
     return acc, path, outt, bonus
+
+
+# =======================================================================================
+# Speculative-budget controller ([P5] 执行控制器): a host-side policy that adjusts the draft
+# tree budget from observed acceptance and latency, never the target decoding itself
+# =======================================================================================
+
+
+class BudgetController:
+    """[P5] 执行控制器.  The page lists what the controller watches (proposed, accepted and
+    committed tokens, mean accepted length, drafter and verify latency) and a simplified
+    policy: lower the tree budget when recent accepted length is low or drafting is
+    expensive; raise it cautiously when acceptance is stable and verification has spare
+    capacity; every adjustment bounded, with a cooldown and a fallback baseline so that
+    short-term noise does not make it oscillate.  The quality rule (deadline-driven thinking
+    allowance) changes answers and is a product decision, not part of this controller.
+
+    Reading taken (the page gives no numbers): budgets are a ladder of tree configurations in
+    increasing size; statistics are the last `window` rounds at the current level (cleared on
+    every change); with c = tokens committed per round (accept_len + 1), D the level's depth:
+      frac = mean(c) / (D + 1), cv = std(c) / mean(c) (population std),
+      draft share = mean(draft_ms) / mean(draft_ms + verify_ms),
+      goodput = mean(c) / mean(draft_ms + verify_ms).
+    A decision is taken only when the window is full and `cooldown` rounds have passed since
+    the last change, in this order:
+      1. after a raise, the first full window is compared with the goodput measured before
+         it; a drop of more than `revert_drop` (a fraction) steps back down (the fallback)
+         and blocks raises for 4 * cooldown rounds;
+      2. frac < low_frac or draft share > draft_share_max: one level down (not below 0);
+      3. frac >= high_frac and cv <= max_cv and mean(verify_ms) < verify_ms_max, raises not
+         blocked: one level up (not above the top).
+    Every change resets the round counter and the window.  All statistics in float64, sums
+    in round order."""
+
+    def __init__(self, n_levels, depths, start, cooldown, window, low_frac, high_frac, max_cv,
+                 draft_share_max, verify_ms_max, revert_drop):
+        self.n, self.depths = int(n_levels), [int(x) for x in depths]
+        self.level = int(start)
+        self.cooldown, self.window = int(cooldown), int(window)
+        self.low_frac, self.high_frac, self.max_cv = float(low_frac), float(high_frac), float(max_cv)
+        self.draft_share_max, self.verify_ms_max = float(draft_share_max), float(verify_ms_max)
+        self.revert_drop = float(revert_drop)
+        self.hist = []
+        self.since = 0
+        self.block = 0            # rounds during which raises are blocked
+        self.check = False        # the last change was a raise, goodput to be compared
+        self.g_before = 0.0
+
+    def _change(self, new_level):
+        self.level = new_level
+        self.since = 0
+        self.hist = []
+
+    def update(self, accept_len, draft_ms, verify_ms) -> int:
+        self.hist.append((float(accept_len) + 1.0, float(draft_ms), float(verify_ms)))
+        if len(self.hist) > self.window:
+            self.hist.pop(0)
+        self.since += 1
+        if self.block > 0:
+            self.block -= 1
+        if len(self.hist) < self.window or self.since < self.cooldown:
+            return self.level
+        n = float(len(self.hist))
+        mc = sum(h[0] for h in self.hist) / n
+        var = sum((h[0] - mc) ** 2 for h in self.hist) / n
+        cv = math.sqrt(var) / mc
+        md = sum(h[1] for h in self.hist) / n
+        mv = sum(h[2] for h in self.hist) / n
+        mr = sum(h[1] + h[2] for h in self.hist) / n
+        frac = mc / (self.depths[self.level] + 1)
+        good = mc / mr
+        if self.check:
+            self.check = False
+            if good < self.g_before * (1.0 - self.revert_drop) and self.level > 0:
+                self.block = 4 * self.cooldown
+                self._change(self.level - 1)
+                return self.level
+        if (frac < self.low_frac or md / mr > self.draft_share_max) and self.level > 0:
+            self._change(self.level - 1)
+        elif (frac >= self.high_frac and cv <= self.max_cv and mv < self.verify_ms_max
+              and self.block == 0 and self.level < self.n - 1):
+            self.g_before = good
+            self.check = True
+            self._change(self.level + 1)
+        return self.level
