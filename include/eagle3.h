@@ -328,6 +328,65 @@ EAGLE3_API int eagle3_linear(int M, int N, int K, int dtype, const void* X, int 
                              float* Y, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * Speculative-budget controller (host code; no device memory, no stream).  [P5] 执行控制器:
+ * adjust the draft-tree budget from what the rounds show -- committed tokens, drafter and
+ * verify latency -- without touching the target's decoding: lower the budget when recent
+ * accepted length is low or drafting is expensive, raise it cautiously when acceptance is
+ * stable and verification has room, always bounded, cooled down and falling back rather
+ * than oscillating.  The page gives the policy in words only; the thresholds are parameters.
+ *
+ * Per round the caller reports accept_len (committed tokens = accept_len + 1) and the
+ * measured draft and verify times; the controller keeps the last `window` rounds at the
+ * current level (cleared on every change) and, once the window is full and `cooldown` rounds
+ * have passed since the last change, with c the committed tokens per round and D the
+ * level's depth, frac = mean(c) / (D + 1), cv = std(c) / mean(c), goodput = mean(c) /
+ * mean(draft + verify):
+ *   1. the first full window after a raise whose goodput fell below (1 - revert_drop) of the
+ *      goodput before the raise steps back down and blocks raises for 4 * cooldown rounds;
+ *   2. frac < low_frac or mean(draft) / mean(draft + verify) > draft_share_max: one level down;
+ *   3. frac >= high_frac, cv <= max_cv, mean(verify) < verify_ms_max, raises not blocked:
+ *      one level up.
+ * Statistics in double precision, sums in round order (decisions are reproducible).
+ *  levels: tree budgets in increasing size (1 .. EAGLE3_BUDGET_MAX_LEVELS); start_level the
+ *  baseline; cooldown >= 1; window 1 .. EAGLE3_BUDGET_MAX_WINDOW.
+ * eagle3_budget_update returns the level to use for the next round (its tree in *next when
+ * next != NULL) or a negative status.  The state is caller-owned; one per request stream.
+ * ------------------------------------------------------------------------------------ */
+#define EAGLE3_BUDGET_MAX_LEVELS 16
+#define EAGLE3_BUDGET_MAX_WINDOW 256
+typedef struct eagle3_budget_params {
+  int32_t n_levels;
+  eagle3_tree_cfg levels[EAGLE3_BUDGET_MAX_LEVELS];
+  int32_t start_level;
+  int32_t cooldown;
+  int32_t window;
+  float low_frac;
+  float high_frac;
+  float max_cv;
+  float draft_share_max;
+  float verify_ms_max;
+  float revert_drop;
+} eagle3_budget_params;
+
+typedef struct eagle3_budget_state {
+  int32_t level;       /* current level                                           */
+  int32_t since;       /* rounds since the last change                            */
+  int32_t block;       /* rounds during which raises stay blocked                 */
+  int32_t check;       /* the last change was a raise: compare goodput next       */
+  int32_t count;       /* rounds in the window                                    */
+  int32_t head;        /* ring position of the oldest round                       */
+  double g_before;     /* goodput measured before the last raise                  */
+  double committed[EAGLE3_BUDGET_MAX_WINDOW];
+  double draft_ms[EAGLE3_BUDGET_MAX_WINDOW];
+  double verify_ms[EAGLE3_BUDGET_MAX_WINDOW];
+} eagle3_budget_state;
+
+EAGLE3_API int eagle3_budget_init(const eagle3_budget_params* p, eagle3_budget_state* s);
+EAGLE3_API int eagle3_budget_update(const eagle3_budget_params* p, eagle3_budget_state* s,
+                                    int32_t accept_len, float draft_ms, float verify_ms,
+                                    eagle3_tree_cfg* next);
+
+/* ------------------------------------------------------------------------------------
  * Launch timing.  While enabled, the library records a HIP event pair on the launch stream
  * around every kernel it enqueues whose name equals `only_kernel` (every kernel when
  * `only_kernel` is NULL).  eagle3_profile_read waits for the recorded events and reports

@@ -45,6 +45,21 @@ class Eagle3DraftDebug(ctypes.Structure):
                 ("slot_lse", c_void_p), ("slot_logits", c_void_p)]
 
 
+class Eagle3BudgetParams(ctypes.Structure):
+    _fields_ = [("n_levels", ctypes.c_int32), ("levels", Eagle3TreeCfg * 16),
+                ("start_level", ctypes.c_int32), ("cooldown", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("low_frac", c_float), ("high_frac", c_float),
+                ("max_cv", c_float), ("draft_share_max", c_float), ("verify_ms_max", c_float),
+                ("revert_drop", c_float)]
+
+
+class Eagle3BudgetState(ctypes.Structure):
+    _fields_ = [("level", ctypes.c_int32), ("since", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("check", ctypes.c_int32), ("count", ctypes.c_int32), ("head", ctypes.c_int32),
+                ("g_before", c_double), ("committed", c_double * 256), ("draft_ms", c_double * 256),
+                ("verify_ms", c_double * 256)]
+
+
 EXPORTS = {
     "eagle3_abi_version": (c_int, []),
     "eagle3_status_string": (c_char_p, [c_int]),
@@ -80,6 +95,8 @@ EXPORTS = {
                               c_void_p, c_int, c_int, c_float, c_uint64, c_uint64, c_int,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                               c_void_p]),
+    "eagle3_budget_init": (c_int, [c_void_p, c_void_p]),
+    "eagle3_budget_update": (c_int, [c_void_p, c_void_p, ctypes.c_int32, c_float, c_float, c_void_p]),
     "eagle3_profile_enable": (c_int, [c_int, c_char_p]),
     "eagle3_profile_reset": (c_int, []),
     "eagle3_profile_read": (c_int, [c_char_p, ctypes.POINTER(c_double), ctypes.POINTER(c_int)]),
@@ -439,6 +456,37 @@ def eagle3_linear(x, w, out: Optional[torch.Tensor] = None, workspace: Optional[
                              _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream))
     _check("eagle3_linear", st)
     return out
+
+
+# ---------------------------------------------------------------------------------------
+# Speculative-budget controller (host)
+# ---------------------------------------------------------------------------------------
+
+
+class BudgetController:
+    """Host-side budget controller over the library's state machine (eagle3_budget_*).
+    levels: sequence of (depth, topk, width, n_nodes) in increasing size."""
+
+    def __init__(self, levels, start: int, cooldown: int, window: int, low_frac: float,
+                 high_frac: float, max_cv: float, draft_share_max: float, verify_ms_max: float,
+                 revert_drop: float):
+        p = Eagle3BudgetParams(n_levels=len(levels), start_level=start, cooldown=cooldown,
+                               window=window, low_frac=low_frac, high_frac=high_frac, max_cv=max_cv,
+                               draft_share_max=draft_share_max, verify_ms_max=verify_ms_max,
+                               revert_drop=revert_drop)
+        for i, (d, k, w, n) in enumerate(levels):
+            p.levels[i] = Eagle3TreeCfg(depth=d, topk=k, width=w, n_nodes=n)
+        self.params = p
+        self.state = Eagle3BudgetState()
+        _check("eagle3_budget_init", lib().eagle3_budget_init(ctypes.byref(p), ctypes.byref(self.state)))
+
+    def update(self, accept_len: int, draft_ms: float, verify_ms: float):
+        """Report one round; returns (level, Eagle3TreeCfg) for the next round."""
+        t = Eagle3TreeCfg()
+        lv = lib().eagle3_budget_update(ctypes.byref(self.params), ctypes.byref(self.state), int(accept_len),
+                                        float(draft_ms), float(verify_ms), ctypes.byref(t))
+        _check("eagle3_budget_update", min(lv, 0))
+        return lv, t
 
 
 # ---------------------------------------------------------------------------------------
