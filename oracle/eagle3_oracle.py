@@ -504,6 +504,49 @@ def tree_attention(q, k_tree, v_tree, cu_nodes, mask, kpre, vpre, cu_prefix, sca
 
 
 # =======================================================================================
+# The training form of the long-context shape ([P4] USP 核心设计：三步走): every position
+# of the sequence is a query.  Step 1: causal attention over the main sequence (Out_main,
+# LSE_main); Step 2: each position's own TTT branch keys, the at most seven keys that the
+# unrolled draft steps produced at that position (Out_branch, LSE_branch); Step 3: the
+# streaming-softmax fusion, which is lse_merge below.
+# =======================================================================================
+
+
+def causal_attention(q, k, v, scale: float, rows=None):
+    """Step 1: position t, query head h (KV head h // (Hq/Hkv)) attends to the main keys
+    0 .. t.  q [L, Hq, Dh], k, v [L, Hkv, Dh].  Returns (O [L, Hq, Dh], LSE [L, Hq]) in
+    float64; with `rows` (positions), only those rows are computed (the others are left 0 /
+    -inf)."""
+    q, k, v = f64(q), f64(k), f64(v)
+    L, Hq, Dh = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    O = np.zeros((L, Hq, Dh))
+    LSE = np.full((L, Hq), NEG_INF)
+    for t in (range(L) if rows is None else rows):
+        for h in range(Hq):
+            O[t, h], LSE[t, h] = attend(q[t, h], k[:t + 1, h // G], v[:t + 1, h // G], scale)
+    return O, LSE
+
+
+def branch_attention(q, kb, vb, scale: float):
+    """Step 2: position t, query head h attends to its own branch keys kb[0 .. s-1, t]
+    (the unrolled steps' keys at position t, KV head h // (Hq/Hkv)), computed as per-position
+    dot products.  q [L, Hq, Dh], kb, vb [s, L, Hkv, Dh].  Returns (O [L, Hq, Dh],
+    LSE [L, Hq])."""
+    q, kb, vb = f64(q), f64(kb), f64(vb)
+    L, Hq, Dh = q.shape
+    Hkv = kb.shape[2]
+    G = Hq // Hkv
+    O = np.zeros((L, Hq, Dh))
+    LSE = np.full((L, Hq), NEG_INF)
+    for t in range(L):
+        for h in range(Hq):
+            O[t, h], LSE[t, h] = attend(q[t, h], kb[:, t, h // G], vb[:, t, h // G], scale)
+    return O, LSE
+
+
+# =======================================================================================
 # O6: log-sum-exp merge of partials ([P4] USP 核心设计 Step 3: streaming-softmax fusion of
 #     Out_branch/LSE_branch into Out_main/LSE_main with one consistent normalisation)
 # =======================================================================================
