@@ -308,7 +308,7 @@ def attention_op(capi, synth, shape, trees, prefix, bound, reps=20, seed=500):
 
 
 OP_KEYS = ("attn_longctx", "attn_batch16", "attn_70b", "attn_8b", "merge", "accept_greedy", "accept_t07",
-           "gemm_sweep", "catchup", "commit", "tree_budgets")
+           "gemm_sweep", "catchup", "commit", "tree_budgets", "usp")
 
 
 def gemm_sweep(capi, synth, reps):
@@ -445,6 +445,34 @@ def tree_budget_ops(steps=10):
     return out
 
 
+def usp_ops(capi, synth, reps):
+    """The long-context shape's training form at 65536 positions, 32 query / 8 KV heads of
+    128, bf16: the causal main attention (4 * Dh flops per (row, visible key): 35.2 TFLOP,
+    matrix-core bound) and the 7-step per-position branch (reads q and the branch K/V,
+    writes the fp32 output: HBM-bound).  The fusion is the `merge` op at the same scale."""
+    import torch
+    dev = "cuda:0"
+    L, Hq, Hkv, Dh, steps = 65536, 32, 8, 128, 7
+    q = synth.normal((L, Hq, Dh), 1.0, 1, torch.bfloat16, dev)
+    k = synth.normal((L, Hkv, Dh), 1.0, 2, torch.bfloat16, dev)
+    v = synth.normal((L, Hkv, Dh), 1.0, 3, torch.bfloat16, dev)
+    o = torch.empty((L, Hq, Dh), dtype=torch.float32, device=dev)
+    lse = torch.empty((L, Hq), dtype=torch.float32, device=dev)
+    sc = Dh ** -0.5
+    us = _time_b2b(lambda i: capi.eagle3_causal_attention(q, k, v, sc, o=o, lse=lse), max(2, reps // 5))
+    flops = 4 * Dh * Hq * L * (L + 1) // 2
+    out = [dict(key="usp", **_entry("causal attention (main)", f"L={L}, {Hq}/{Hkv} heads x {Dh}, bf16",
+                                    "k_tree_attn_dma (causal)", us, "mfma", flops=flops))]
+    del k, v
+    kb = synth.normal((steps, L, Hkv, Dh), 1.0, 4, torch.bfloat16, dev)
+    vb = synth.normal((steps, L, Hkv, Dh), 1.0, 5, torch.bfloat16, dev)
+    us = _time_b2b(lambda i: capi.eagle3_branch_attention(q, kb, vb, sc, o=o, lse=lse), reps)
+    byts = L * Hq * Dh * 2 + 2 * steps * L * Hkv * Dh * 2 + L * Hq * (Dh + 1) * 4
+    out.append(dict(key="usp", **_entry("branch attention", f"L={L}, {steps} steps, {Hq}/{Hkv} heads x {Dh}",
+                                        "k_branch_attn", us, "hbm", bytes_=byts)))
+    return out
+
+
 def op_rooflines(reps=20, keys=OP_KEYS):
     import numpy as np
     import torch
@@ -522,6 +550,8 @@ def op_rooflines(reps=20, keys=OP_KEYS):
         ops += commit_ops(capi, synth, reps)
     if "tree_budgets" in keys:
         ops += tree_budget_ops()
+    if "usp" in keys:
+        ops += usp_ops(capi, synth, reps)
     torch.cuda.empty_cache()
     for o in ops:
         if o["key"] in OP_PROFILES:

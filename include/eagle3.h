@@ -228,6 +228,28 @@ EAGLE3_API int eagle3_lse_merge(int S, int rows, int Dh, const float* o_part, co
                      int out_dtype, void* o, float* lse, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * The training form of the long-context shape: [P4] USP 核心设计：三步走.  Every position of
+ * a sequence is a query.
+ * eagle3_causal_attention -- Step 1 (main): position t, query head h attends to keys
+ *   0 .. t of its KV head h / (Hq/Hkv): Out_main and LSE_main.  bf16, head_dim 64 or 128.
+ * eagle3_branch_attention -- Step 2 (branch): position t, query head h attends to its own
+ *   TTT branch keys kb[j][t], j < n_steps (the unrolled draft steps' keys at position t),
+ *   as per-position dot products: Out_branch and LSE_branch.  bf16 or fp32, head_dim 128,
+ *   1 <= n_steps <= 16.
+ * Step 3 (fusion) is eagle3_lse_merge with S = 2 over rows = L * Hq: place Out_main and
+ * Out_branch as partials 0 and 1 of one [2, L*Hq, Dh] buffer (and the LSEs likewise).
+ *
+ *  q [L, Hq, Dh]; k, v [L, Hkv, Dh]; kb, vb [n_steps, L, Hkv, Dh] (dtype); scale > 0
+ *  o [L, Hq, Dh] fp32 (normalised), lse [L, Hq] fp32 natural log.
+ * ------------------------------------------------------------------------------------ */
+EAGLE3_API int eagle3_causal_attention(int L, int Hq, int Hkv, int Dh, int dtype, const void* q,
+                                       const void* k, const void* v, float scale, float* o,
+                                       float* lse, void* stream);
+EAGLE3_API int eagle3_branch_attention(int L, int n_steps, int Hq, int Hkv, int Dh, int dtype,
+                                       const void* q, const void* kb, const void* vb, float scale,
+                                       float* o, float* lse, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * eagle3_accept -- accept the longest draft path.  [P1] 论文位置 (accept the longest
  * correct prefix; the standard speculative-sampling rule keeps the target distribution);
  * [P2] 二、EAGLE-2动态草稿树 (accept the longest coherent path, roll back to its last node);

@@ -80,6 +80,10 @@ EXPORTS = {
                                       c_size_t, c_void_p]),
     "eagle3_lse_merge": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_int, c_void_p,
                                  c_void_p, c_void_p]),
+    "eagle3_causal_attention": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                        c_float, c_void_p, c_void_p, c_void_p]),
+    "eagle3_branch_attention": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p,
+                                        c_void_p, c_float, c_void_p, c_void_p, c_void_p]),
     "eagle3_linear_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int]),
     "eagle3_linear": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p, c_void_p,
                               c_size_t, c_void_p]),
@@ -428,6 +432,53 @@ def eagle3_drafter_catchup(drafter: Eagle3Drafter, tokens, pos, h_low, h_mid, h_
                                       workspace.data_ptr(), workspace.numel(), _stream(stream))
     _check("eagle3_drafter_catchup", st)
     return g_out
+
+
+# ---------------------------------------------------------------------------------------
+# Training form of the long-context shape (every position a query)
+# ---------------------------------------------------------------------------------------
+
+
+def eagle3_causal_attention(q, k, v, scale: float, o: Optional[torch.Tensor] = None,
+                            lse: Optional[torch.Tensor] = None, stream=None):
+    """Main causal attention of every position: q [L, Hq, Dh], k, v [L, Hkv, Dh] (bf16).
+    Returns (o [L, Hq, Dh] fp32, lse [L, Hq] fp32)."""
+    dt = q.dtype
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, n, dt)
+    L, Hq, Dh = q.shape
+    Hkv = k.shape[1]
+    if o is None:
+        o = torch.empty((L, Hq, Dh), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((L, Hq), dtype=torch.float32, device=q.device)
+    _dev(o, "o", torch.float32)
+    _dev(lse, "lse", torch.float32)
+    st = lib().eagle3_causal_attention(L, Hq, Hkv, Dh, dtype_code(dt), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                       float(scale), o.data_ptr(), lse.data_ptr(), _stream(stream))
+    _check("eagle3_causal_attention", st)
+    return o, lse
+
+
+def eagle3_branch_attention(q, kb, vb, scale: float, o: Optional[torch.Tensor] = None,
+                            lse: Optional[torch.Tensor] = None, stream=None):
+    """Per-position branch attention: q [L, Hq, Dh], kb, vb [n_steps, L, Hkv, Dh].
+    Returns (o [L, Hq, Dh] fp32, lse [L, Hq] fp32)."""
+    dt = q.dtype
+    for n, t in (("q", q), ("kb", kb), ("vb", vb)):
+        _dev(t, n, dt)
+    L, Hq, Dh = q.shape
+    n_steps, _, Hkv, _ = kb.shape
+    if o is None:
+        o = torch.empty((L, Hq, Dh), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((L, Hq), dtype=torch.float32, device=q.device)
+    _dev(o, "o", torch.float32)
+    _dev(lse, "lse", torch.float32)
+    st = lib().eagle3_branch_attention(L, n_steps, Hq, Hkv, Dh, dtype_code(dt), q.data_ptr(), kb.data_ptr(),
+                                       vb.data_ptr(), float(scale), o.data_ptr(), lse.data_ptr(), _stream(stream))
+    _check("eagle3_branch_attention", st)
+    return o, lse
 
 
 # ---------------------------------------------------------------------------------------

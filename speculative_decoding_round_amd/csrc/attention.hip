@@ -50,6 +50,7 @@ struct DevArgs {
   float scale_log2;
   int S;
   int n_rb;   // row blocks per (request, KV head) (bf16 kernel)
+  int causal_len;   // causal mode: sequence length (request b = positions b * q_stride ..)
   float* o_part;
   float* lse_part;
 };
@@ -296,6 +297,13 @@ __device__ __forceinline__ void dma16_nt_s(const void* sbase, uint32_t voff, uin
                "s"(lds_base)
                : "memory", "m0");
 }
+// The same with the cache policy left at its default: for streams that other workgroups
+// re-read through L2.
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(lds_base)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 template <int CPR>
@@ -335,7 +343,14 @@ struct DmaCfg {
 // than 2^8 above its reference, so p <= 2^8 and the accumulator is rarely touched.
 constexpr float kRescaleLog2 = 8.f;
 
-template <int DH, int QT, int WK, int KTW, int NST>
+// CAUSAL: every position of a sequence is a query row ([P4] USP step 1, the main causal
+// attention).  Request b is the block of q_stride positions from b * q_stride; its rows see
+// the keys 0 .. position (the sequence itself, from key 0), so a row block streams the keys
+// up to its last position and masks the tiles that reach past a row's position; there is
+// no tree split, and the output is split 0 = (Out_main, LSE_main).  Blocks are taken
+// largest first (the work grows with the position), and K/V are read with the default
+// cache policy: every block of a KV head re-reads the same keys.
+template <int DH, int QT, int WK, int KTW, int NST, bool CAUSAL = false>
 __global__ __launch_bounds__(256) void k_tree_attn_dma(DevArgs a) {
   using C = DmaCfg<DH, QT, WK, KTW, NST>;
   constexpr int CPR = C::CPR, WR = C::WR, NDT = DH / 16, NDC = DH / 32, NST16 = KTW / 16;
@@ -345,26 +360,31 @@ __global__ __launch_bounds__(256) void k_tree_attn_dma(DevArgs a) {
   // Workgroups that share K/V (the row blocks of one request, KV head and split) are
   // numbered so that they fall on the same XCD (workgroups go to XCDs round-robin), where
   // they share that XCD's L2.
-  const int n_groups = a.B * a.Hkv * (a.S + 1);
+  const int n_groups = a.B * a.Hkv * (CAUSAL ? 1 : a.S + 1);
   const int id = blockIdx.x, xcd = id % 8, t = id / 8;
   const int rbk = t % a.n_rb;
   const int grp = (t / a.n_rb) * 8 + xcd;
   if (grp >= n_groups) return;
-  const int split = grp % (a.S + 1);
-  const int bc = grp / (a.S + 1);
-  const int b = bc / a.Hkv;
+  const int split = CAUSAL ? 0 : grp % (a.S + 1);
+  const int bc = CAUSAL ? grp : grp / (a.S + 1);
+  const int b = CAUSAL ? a.B - 1 - bc / a.Hkv : bc / a.Hkv;
   const int c = bc % a.Hkv;
   const int q0 = a.q_cu ? a.q_cu[b] : b * a.q_stride;
-  const int nq = a.q_cu ? a.q_cu[b + 1] - q0 : a.q_stride;
+  const int nq = a.q_cu ? a.q_cu[b + 1] - q0 : (CAUSAL ? min(a.q_stride, a.causal_len - q0) : a.q_stride);
   const int R = nq * a.G;
   const int rb0 = rbk * C::ROWS;
   if (rb0 >= R) return;
 
-  const bool tree = split == a.S;
+  const bool tree = !CAUSAL && split == a.S;
   int k_lo = 0, k_hi = 0;
   const bf16* kbase;
   const bf16* vbase;
-  if (!tree) {
+  if (CAUSAL) {
+    // keys 0 .. the row block's last position
+    k_hi = q0 + min(nq, (rb0 + C::ROWS - 1) / a.G + 1);
+    kbase = reinterpret_cast<const bf16*>(a.kp) + (size_t)c * DH;
+    vbase = reinterpret_cast<const bf16*>(a.vp) + (size_t)c * DH;
+  } else if (!tree) {
     const int p0 = a.p_cu ? a.p_cu[b] : 0;
     const int P = a.p_cu ? a.p_cu[b + 1] - p0 : 0;
     const int chunk = split_keys(P, a.S);
@@ -439,7 +459,8 @@ __global__ __launch_bounds__(256) void k_tree_attn_dma(DevArgs a) {
     for (int u = 0; u < C::PER; ++u) {
       uint32_t off = voff[u];
       if (!whole) off = (uint32_t)min(relk[u], k_hi - 1 - t0) * (uint32_t)kstride * 2u + vpos[u];
-      dma16_nt_s(isv[u] ? vb : kb, off, st + (u * 4 + wu) * 1024);
+      if constexpr (CAUSAL) dma16_s(isv[u] ? vb : kb, off, st + (u * 4 + wu) * 1024);
+      else dma16_nt_s(isv[u] ? vb : kb, off, st + (u * 4 + wu) * 1024);
     }
   };
 
@@ -507,16 +528,20 @@ __global__ __launch_bounds__(256) void k_tree_attn_dma(DevArgs a) {
     // keys past the range end or outside the row's ancestor set -> -inf; whole prefix
     // tiles need no mask
     const int lim = k_hi - kbase_it;
-    if (tree || lim < KTW) {
+    // causal: tiles reaching past the wave's first row position
+    const bool cmask = CAUSAL && kbase_it + KTW - 1 > q0 + (rb0 + wr * QT * 16) / a.G;
+    if (tree || lim < KTW || cmask) {
       const int word = (kbase_it >> 6) & 3, sh = kbase_it & 63;  // a sub-tile lies in one word
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         const uint64_t bits = tree ? (smask[w][qt][r16][word] >> sh) >> (4 * g) : ~0ull;
+        // keys visible to this lane's row: relative key < rlim (causal: key <= position)
+        const int rlim = CAUSAL ? min(lim, q0 + max(rowid[qt], 0) / a.G + 1 - kbase_it) : lim;
 #pragma unroll
         for (int st = 0; st < NST16; ++st)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const bool vis = st * 16 + 4 * g + i < lim && ((bits >> (st * 16 + i)) & 1ull);
+            const bool vis = st * 16 + 4 * g + i < rlim && ((bits >> (st * 16 + i)) & 1ull);
             if (!vis) s[qt][st][i] = kNegInf;
           }
       }
@@ -838,9 +863,112 @@ int launch_attn_t(const e3h::AttnArgs& h, hipStream_t s) {
   return e3h::launch_status();
 }
 
+// [P4] USP step 2, the TTT branch: position t, query head h attends to its own branch keys
+// kb[j][t] (j < n_steps), computed as per-position dot products.  One workgroup per
+// (position, KV head): G query heads x DH/8 lanes, each lane 8 dimensions; a score is
+// reduced over the 16-lane row of its head.
+template <typename T, int DH>
+__global__ __launch_bounds__(1024) void k_branch_attn(int L, int n_steps, int Hq, int Hkv, const T* __restrict__ q,
+                                                      const T* __restrict__ kb, const T* __restrict__ vb,
+                                                      float scale_log2, float* __restrict__ o,
+                                                      float* __restrict__ lse) {
+  constexpr int LPH = DH / 8;   // lanes per head
+  const int t = blockIdx.x, c = blockIdx.y;
+  const int G = Hq / Hkv;
+  const int hg = threadIdx.x / LPH, d8 = threadIdx.x % LPH;
+  const int h = c * G + hg;
+  float qv[8];
+  load8<T>(q + ((size_t)t * Hq + h) * DH + d8 * 8, qv);
+  float sc[16];
+  float m = kNegInf;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    sc[j] = kNegInf;
+    if (j < n_steps) {
+      float kv[8];
+      load8<T>(kb + (((size_t)j * L + t) * Hkv + c) * DH + d8 * 8, kv);
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = __builtin_fmaf(qv[e], kv[e], d);
+      d = row16_reduce(d, OpAdd()) * scale_log2;   // a head's 16 lanes (DH = 128)
+      sc[j] = d;
+      m = fmaxf(m, d);
+    }
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j < n_steps) {
+      const float p = __builtin_amdgcn_exp2f(sc[j] - m);
+      tot += p;
+      float vv[8];
+      load8<T>(vb + (((size_t)j * L + t) * Hkv + c) * DH + d8 * 8, vv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(p, vv[e], acc[e]);
+    }
+  }
+  const float inv = 1.f / tot;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] *= inv;
+  store8<float>(o + ((size_t)t * Hq + h) * DH + d8 * 8, acc);
+  if (d8 == 0) lse[(size_t)t * Hq + h] = (m + log2f(tot)) * kLn2;
+}
+
 }  // namespace
 
 namespace e3h {
+
+// [P4] USP step 1: causal attention of every position over the sequence, bf16, positions in
+// blocks of 128 (rows = 128 x G per block, 128 rows per workgroup).
+int launch_causal_attention(int L, int Hq, int Hkv, int Dh, const void* q, const void* k, const void* v,
+                            float scale, float* o, float* lse, hipStream_t s) {
+  constexpr int CB = 128;
+  DevArgs a{};
+  a.B = (L + CB - 1) / CB;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.q = q;
+  a.q_cu = nullptr;
+  a.q_stride = CB;
+  a.q_rows_total = L;
+  a.kp = k;
+  a.vp = v;
+  a.p_cu = nullptr;
+  a.mask = nullptr;
+  a.W64 = 1;
+  a.S = 0;
+  a.causal_len = L;
+  a.scale_log2 = scale * kLog2e;
+  a.o_part = o;
+  a.lse_part = lse;
+  ProfScope ps("causal_attention", s);
+  auto go = [&](auto kern, int rows_wg) {
+    a.n_rb = (CB * a.G + rows_wg - 1) / rows_wg;
+    const long groups = (long)a.B * Hkv;
+    const long n = (groups + 7) / 8 * 8 * a.n_rb;
+    hipLaunchKernelGGL(kern, dim3((unsigned)n), dim3(256), 0, s, a);
+  };
+  if (Dh == 128) go(k_tree_attn_dma<128, 2, 1, 32, 4, true>, DmaCfg<128, 2, 1, 32, 4>::ROWS);
+  else if (Dh == 64) go(k_tree_attn_dma<64, 2, 1, 32, 4, true>, DmaCfg<64, 2, 1, 32, 4>::ROWS);
+  else return EAGLE3_EUNSUPPORTED;
+  return launch_status();
+}
+
+int launch_branch_attention(int L, int n_steps, int Hq, int Hkv, int Dh, int dtype, const void* q,
+                            const void* kb, const void* vb, float scale, float* o, float* lse, hipStream_t s) {
+  if (Dh != 128) return EAGLE3_EUNSUPPORTED;
+  ProfScope ps("branch_attention", s);
+  const dim3 grid(L, Hkv), block((Hq / Hkv) * (Dh / 8));
+  if (dtype == EAGLE3_BF16)
+    hipLaunchKernelGGL((k_branch_attn<bf16, 128>), grid, block, 0, s, L, n_steps, Hq, Hkv, (const bf16*)q,
+                       (const bf16*)kb, (const bf16*)vb, scale * kLog2e, o, lse);
+  else
+    hipLaunchKernelGGL((k_branch_attn<float, 128>), grid, block, 0, s, L, n_steps, Hq, Hkv, (const float*)q,
+                       (const float*)kb, (const float*)vb, scale * kLog2e, o, lse);
+  return launch_status();
+}
 
 // Prefix splits: enough workgroups for the launch target of the workgroup shape, but every
 // split keeps at least one iteration of keys and at least three times as many keys as its

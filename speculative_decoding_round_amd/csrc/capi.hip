@@ -281,6 +281,25 @@ int eagle3_drafter_catchup(const eagle3_drafter* w, int n, const int32_t* tokens
                         g_out, dev_status, workspace, (hipStream_t)stream);
 }
 
+int eagle3_causal_attention(int L, int Hq, int Hkv, int Dh, int dtype, const void* q, const void* k,
+                            const void* v, float scale, float* o, float* lse, void* stream) {
+  if (L <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || !(scale > 0.f)) return EAGLE3_EINVAL;
+  if (!dtype_ok(dtype) || !q || !k || !v || !o || !lse) return EAGLE3_EINVAL;
+  if ((uintptr_t)q % 16 || (uintptr_t)k % 16 || (uintptr_t)v % 16 || (uintptr_t)o % 16) return EAGLE3_EINVAL;
+  if (dtype != EAGLE3_BF16 || (Dh != 64 && Dh != 128)) return EAGLE3_EUNSUPPORTED;
+  if ((long)L * Hkv * Dh * 2 > 0xFFFFFFFFL) return EAGLE3_EUNSUPPORTED;   // 32-bit stream offsets
+  return launch_causal_attention(L, Hq, Hkv, Dh, q, k, v, scale, o, lse, (hipStream_t)stream);
+}
+
+int eagle3_branch_attention(int L, int n_steps, int Hq, int Hkv, int Dh, int dtype, const void* q,
+                            const void* kb, const void* vb, float scale, float* o, float* lse, void* stream) {
+  if (L <= 0 || n_steps <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || !(scale > 0.f)) return EAGLE3_EINVAL;
+  if (!dtype_ok(dtype) || !q || !kb || !vb || !o || !lse) return EAGLE3_EINVAL;
+  if ((uintptr_t)q % 16 || (uintptr_t)kb % 16 || (uintptr_t)vb % 16 || (uintptr_t)o % 16) return EAGLE3_EINVAL;
+  if (Dh != 128 || n_steps > 16 || (Hq / Hkv) * (Dh / 8) > 1024 || Hkv > 65535) return EAGLE3_EUNSUPPORTED;
+  return launch_branch_attention(L, n_steps, Hq, Hkv, Dh, dtype, q, kb, vb, scale, o, lse, (hipStream_t)stream);
+}
+
 size_t eagle3_accept_workspace_size(int T, int V) {
   if (T < 0 || V <= 0) return 0;
   return accept_workspace(T, V);

@@ -127,6 +127,15 @@ __device__ __forceinline__ float wave_reduce(float v, Op op) {
   return op(__uint_as_float(a), __uint_as_float(b));
 }
 
+// Reduction within each 16-lane row (lanes 16r .. 16r+15); every lane of the row gets it.
+template <typename Op>
+__device__ __forceinline__ float row16_reduce(float v, Op op) {
+  v = op(v, __uint_as_float(dpp_u<kDppXor1>(__float_as_uint(v))));
+  v = op(v, __uint_as_float(dpp_u<kDppXor2>(__float_as_uint(v))));
+  v = op(v, __uint_as_float(dpp_u<kDppHalfMirror>(__float_as_uint(v))));
+  return op(v, __uint_as_float(dpp_u<kDppMirror>(__float_as_uint(v))));
+}
+
 // Reduction across the four 16-lane rows only (lanes l, l^16, l^32, l^48).
 template <typename Op>
 __device__ __forceinline__ float row_reduce(float v, Op op) {

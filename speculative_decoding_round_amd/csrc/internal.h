@@ -32,6 +32,10 @@ int launch_tree_attention(const AttnArgs& a, hipStream_t s, const char* tag);
 int launch_lse_merge(int S, int rows, int Dh, const float* o_part, const float* lse_part,
                      int out_dtype, void* o, float* lse, hipStream_t s, const char* tag);
 int attention_splits(int B, int Hkv, int rows_per_kv, int max_prefix, int n_splits);
+int launch_causal_attention(int L, int Hq, int Hkv, int Dh, const void* q, const void* k, const void* v,
+                            float scale, float* o, float* lse, hipStream_t s);
+int launch_branch_attention(int L, int n_steps, int Hq, int Hkv, int Dh, int dtype, const void* q,
+                            const void* kb, const void* vb, float scale, float* o, float* lse, hipStream_t s);
 
 // ---- verify ----------------------------------------------------------------------------
 int launch_build_mask(int B, int T, const int32_t* cu_nodes, const int32_t* parents,
