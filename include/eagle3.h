@@ -235,7 +235,7 @@ EAGLE3_API int eagle3_lse_merge(int S, int rows, int Dh, const float* o_part, co
  * eagle3_branch_attention -- Step 2 (branch): position t, query head h attends to its own
  *   TTT branch keys kb[j][t], j < n_steps (the unrolled draft steps' keys at position t),
  *   as per-position dot products: Out_branch and LSE_branch.  bf16 or fp32, head_dim 128,
- *   1 <= n_steps <= 16.
+ *   1 <= n_steps <= 8.
  * Step 3 (fusion) is eagle3_lse_merge with S = 2 over rows = L * Hq: place Out_main and
  * Out_branch as partials 0 and 1 of one [2, L*Hq, Dh] buffer (and the LSEs likewise).
  *

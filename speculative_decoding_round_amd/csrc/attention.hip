@@ -864,32 +864,43 @@ int launch_attn_t(const e3h::AttnArgs& h, hipStream_t s) {
 }
 
 // [P4] USP step 2, the TTT branch: position t, query head h attends to its own branch keys
-// kb[j][t] (j < n_steps), computed as per-position dot products.  One workgroup per
-// (position, KV head): G query heads x DH/8 lanes, each lane 8 dimensions; a score is
-// reduced over the 16-lane row of its head.
+// kb[j][t] (j < n_steps), computed as per-position dot products.  A workgroup takes
+// positions of one KV head, G * DH/8 lanes each (16 lanes of 8 dimensions per query head);
+// every key and value load is issued before the arithmetic, and a score is reduced over the
+// 16 lanes of its head.
 template <typename T, int DH>
 __global__ __launch_bounds__(1024) void k_branch_attn(int L, int n_steps, int Hq, int Hkv, const T* __restrict__ q,
                                                       const T* __restrict__ kb, const T* __restrict__ vb,
                                                       float scale_log2, float* __restrict__ o,
                                                       float* __restrict__ lse) {
   constexpr int LPH = DH / 8;   // lanes per head
-  const int t = blockIdx.x, c = blockIdx.y;
+  constexpr int MAXS = 8;       // steps held in registers (host: n_steps <= MAXS)
   const int G = Hq / Hkv;
-  const int hg = threadIdx.x / LPH, d8 = threadIdx.x % LPH;
+  const int per = G * LPH;      // lanes per position
+  const int t = blockIdx.x * (blockDim.x / per) + threadIdx.x / per;
+  const int c = blockIdx.y;
+  if (t >= L) return;           // whole position groups only: a head's 16 lanes stay together
+  const int li = threadIdx.x % per;
+  const int hg = li / LPH, d8 = li % LPH;
   const int h = c * G + hg;
   float qv[8];
   load8<T>(q + ((size_t)t * Hq + h) * DH + d8 * 8, qv);
-  float sc[16];
+  float kv[MAXS][8], vv[MAXS][8];
+#pragma unroll
+  for (int j = 0; j < MAXS; ++j)
+    if (j < n_steps) {
+      load8<T>(kb + (((size_t)j * L + t) * Hkv + c) * DH + d8 * 8, kv[j]);
+      load8<T>(vb + (((size_t)j * L + t) * Hkv + c) * DH + d8 * 8, vv[j]);
+    }
+  float sc[MAXS];
   float m = kNegInf;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < MAXS; ++j) {
     sc[j] = kNegInf;
     if (j < n_steps) {
-      float kv[8];
-      load8<T>(kb + (((size_t)j * L + t) * Hkv + c) * DH + d8 * 8, kv);
       float d = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) d = __builtin_fmaf(qv[e], kv[e], d);
+      for (int e = 0; e < 8; ++e) d = __builtin_fmaf(qv[e], kv[j][e], d);
       d = row16_reduce(d, OpAdd()) * scale_log2;   // a head's 16 lanes (DH = 128)
       sc[j] = d;
       m = fmaxf(m, d);
@@ -898,16 +909,13 @@ __global__ __launch_bounds__(1024) void k_branch_attn(int L, int n_steps, int Hq
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float tot = 0.f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < MAXS; ++j)
     if (j < n_steps) {
       const float p = __builtin_amdgcn_exp2f(sc[j] - m);
       tot += p;
-      float vv[8];
-      load8<T>(vb + (((size_t)j * L + t) * Hkv + c) * DH + d8 * 8, vv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(p, vv[e], acc[e]);
+      for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(p, vv[j][e], acc[e]);
     }
-  }
   const float inv = 1.f / tot;
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] *= inv;
@@ -960,7 +968,9 @@ int launch_branch_attention(int L, int n_steps, int Hq, int Hkv, int Dh, int dty
                             const void* kb, const void* vb, float scale, float* o, float* lse, hipStream_t s) {
   if (Dh != 128) return EAGLE3_EUNSUPPORTED;
   ProfScope ps("branch_attention", s);
-  const dim3 grid(L, Hkv), block((Hq / Hkv) * (Dh / 8));
+  const int per = (Hq / Hkv) * (Dh / 8);        // lanes per position
+  const int ppw = per >= 256 ? 1 : 256 / per;   // positions per workgroup
+  const dim3 grid((L + ppw - 1) / ppw, Hkv), block(per * ppw);
   if (dtype == EAGLE3_BF16)
     hipLaunchKernelGGL((k_branch_attn<bf16, 128>), grid, block, 0, s, L, n_steps, Hq, Hkv, (const bf16*)q,
                        (const bf16*)kb, (const bf16*)vb, scale * kLog2e, o, lse);

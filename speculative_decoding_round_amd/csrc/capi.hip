@@ -296,7 +296,7 @@ int eagle3_branch_attention(int L, int n_steps, int Hq, int Hkv, int Dh, int dty
   if (L <= 0 || n_steps <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || !(scale > 0.f)) return EAGLE3_EINVAL;
   if (!dtype_ok(dtype) || !q || !kb || !vb || !o || !lse) return EAGLE3_EINVAL;
   if ((uintptr_t)q % 16 || (uintptr_t)kb % 16 || (uintptr_t)vb % 16 || (uintptr_t)o % 16) return EAGLE3_EINVAL;
-  if (Dh != 128 || n_steps > 16 || (Hq / Hkv) * (Dh / 8) > 1024 || Hkv > 65535) return EAGLE3_EUNSUPPORTED;
+  if (Dh != 128 || n_steps > 8 || (Hq / Hkv) * (Dh / 8) > 1024 || Hkv > 65535) return EAGLE3_EUNSUPPORTED;
   return launch_branch_attention(L, n_steps, Hq, Hkv, Dh, dtype, q, kb, vb, scale, o, lse, (hipStream_t)stream);
 }
 
