@@ -34,7 +34,10 @@ Llama-style drafter layer (RMSNorm eps 1e-5, no biases, half-split RoPE with
 theta 500000, final RMSNorm before the LM head); embedding and feature concatenated into
 a 2d-wide QKV input; tree expansion by per-depth top-W of cumulative log-probability; the
 stochastic acceptance rule in its deterministic-candidate form (Gumbel-max draw of the
-target token at every node, descend while the draw equals a child token).
+target token at every node, descend while the draw equals a child token); in its
+sampled-candidate form, siblings drawn without replacement and tested in the order drawn,
+each rejection taking its token out of q and replacing p by the normalised positive part
+of p - q (the probabilities of that form in float64).
 """
 from __future__ import annotations
 
@@ -745,6 +748,126 @@ def accept(cu_nodes, tokens, parents, logits, temperature: float, seed: int, rnd
         for s, j in enumerate(chain[1:]):
             outt[b, s] = int(tokens[n0 + j])
         outt[b, best_len] = y[best]
+    return acc, path, outt, bonus
+
+
+# =======================================================================================
+# O8: sampled candidates ([P2] 四 DFlash: every drafted token is kept with probability
+#     min(1, p_target / p_draft), the dice are thrown left to right and the first rejection
+#     ends the kept prefix; [P3] 先看 checkpoint 最终要参与什么计算: the continuous prefix is
+#     kept, the rejection point is corrected, and the output then follows the target model
+#     alone).  Tree form (a reading: the pages give the one-candidate rule): the children of
+#     a node are draws without replacement from the drafter's distribution q at that node,
+#     tested in the order drawn; after a rejection the target side becomes the normalised
+#     positive part of (p - q) and the rejected token is taken out of q (q renormalised).
+#     When every child is rejected, or the node has none, the next token is drawn from the
+#     target side as it then stands.
+# =======================================================================================
+
+ACCEPT_UNIFORM_C0 = 0x40000000   # counter word 0 of the acceptance uniforms (t >> 2 never reaches it)
+
+
+def softmax64(z_row, temperature: float) -> np.ndarray:
+    """softmax(z / T) in float64: a_t = z_t / T (z upcast exactly, T the float32 value),
+    p_t = exp(a_t - A) with A = max a + ln sum exp(a - max a)."""
+    a = np.asarray(z_row, dtype=np.float64) / float(np.float32(temperature))
+    m = a.max()
+    A = m + math.log(float(np.exp(a - m).sum()))
+    return np.exp(a - A)
+
+
+def rrs_node(p: np.ndarray, q: np.ndarray, cand: Sequence[int], u: Sequence[float]):
+    """The rejection chain at one node.  cand: the children's tokens in the order drawn,
+    u: one uniform in (0, 1) per child.  Candidate x (not already rejected here, inside the
+    vocabulary) is kept when u < p(x) / q(x) for the current p and q (q(x) = 0 keeps it
+    whenever p(x) > 0); otherwise p <- max(p - q, 0) / sum, q(x) <- 0, q <- q / sum.
+    Returns (index of the kept child or -1, the target side p after the chain, the list of
+    thresholds p(x)/q(x) met by each tested child, None for a skipped child)."""
+    p = np.array(p, dtype=np.float64)
+    q = np.array(q, dtype=np.float64)
+    V = p.shape[0]
+    tried, thr = set(), []
+    for k, x in enumerate(cand):
+        x = int(x)
+        if x < 0 or x >= V or x in tried:
+            thr.append(None)
+            continue
+        tried.add(x)
+        t = math.inf if q[x] == 0.0 else p[x] / q[x]
+        thr.append(t)
+        if float(u[k]) < t:
+            return k, p, thr
+        r = np.maximum(p - q, 0.0)
+        s = r.sum()
+        if s > 0.0:                 # a rejection leaves s > 0 unless p and q agree to rounding
+            p = r / s
+        q[x] = 0.0
+        sq = q.sum()
+        if sq <= 0.0:               # the drafter's mass is used up: nothing more to test
+            break
+        q = q / sq
+    return -1, p, thr
+
+
+def residual_draw(p: np.ndarray, g: np.ndarray) -> int:
+    """Gumbel-max draw from p: argmax over p_t > 0 of ln p_t + g_t (float64; g the float32
+    Gumbel noise upcast), lowest token id on ties."""
+    with np.errstate(divide="ignore"):
+        v = np.where(p > 0.0, np.log(p) + np.asarray(g, dtype=np.float64), -np.inf)
+    return int(np.argmax(v))
+
+
+def accept_uniform(seed: int, rnd: int, b: int, j: int) -> float:
+    """The uniform met by child node j of request b: Philox4x32-10 with counter
+    (ACCEPT_UNIFORM_C0, j, b, round), key (seed lo, seed hi), word 0, mapped as uniform23."""
+    w = philox4x32_10(ACCEPT_UNIFORM_C0, j, b, rnd & MASK32, seed & MASK32, (seed >> 32) & MASK32)
+    return float(uniform23(w[0]))
+
+
+def accept_sampled(cu_nodes, tokens, parents, logits, draft_logits, draft_row,
+                   temperature: float, seed: int, rnd: int, max_depth: int):
+    """Sampled-candidate acceptance.  Per request, from the root: at node i the target side
+    is p = softmax(z_i / T) and the draft side q = softmax(draft_logits[draft_row[i]] / T);
+    its children (nodes whose parent is i, in increasing node index) go through rrs_node
+    with their uniforms; a kept child becomes the next node; otherwise the bonus token is
+    residual_draw of the resulting target side with the Gumbel noise of node i (the noise
+    of the deterministic form).  A node whose draft row is outside draft_logits draws from
+    p directly.  Returns (accept_len, path, out_tokens, bonus) laid out as by `accept`."""
+    B = len(cu_nodes) - 1
+    acc = np.zeros(B, dtype=np.int32)
+    path = np.full((B, max_depth + 1), -1, dtype=np.int32)
+    outt = np.full((B, max_depth + 1), -1, dtype=np.int32)
+    bonus = np.zeros(B, dtype=np.int32)
+    lg = np.asarray(logits.float().numpy() if hasattr(logits, "float") else logits, dtype=np.float32)
+    dl = np.asarray(draft_logits.float().numpy() if hasattr(draft_logits, "float") else draft_logits,
+                    dtype=np.float32)
+    V, R = lg.shape[1], dl.shape[0]
+    for b in range(B):
+        n0, n1 = int(cu_nodes[b]), int(cu_nodes[b + 1])
+        kids: Dict[int, List[int]] = {}
+        for j in range(1, n1 - n0):
+            kids.setdefault(int(parents[n0 + j]), []).append(j)
+        i, chain = 0, [0]
+        while True:
+            p = softmax64(lg[n0 + i], temperature)
+            ch = kids.get(i, [])
+            r = int(draft_row[n0 + i])
+            if ch and 0 <= r < R:
+                q = softmax64(dl[r], temperature)
+                k, p, _ = rrs_node(p, q, [int(tokens[n0 + j]) for j in ch],
+                                   [accept_uniform(seed, rnd, b, j) for j in ch])
+                if k >= 0:
+                    i = ch[k]
+                    chain.append(i)
+                    continue
+            y = residual_draw(p, gumbel(seed, rnd, b, i, np.arange(V)))
+            break
+        L = len(chain) - 1
+        acc[b], bonus[b] = L, y
+        path[b, :L + 1] = chain
+        for s, j in enumerate(chain[1:]):
+            outt[b, s] = int(tokens[n0 + j])
+        outt[b, L] = y
     return acc, path, outt, bonus
 
 
