@@ -277,6 +277,45 @@ EAGLE3_API int eagle3_accept(int B, int T, const int32_t* cu_nodes, const int32_
                   int32_t* bonus, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * eagle3_accept_sampled -- acceptance of sampled candidates.  [P2] 四 DFlash (each drafted
+ * token is kept with probability min(1, p_target / p_draft), dice thrown left to right, the
+ * first rejection ends the kept prefix); [P3] 先看 checkpoint 最终要参与什么计算 (keep the
+ * continuous prefix, correct at the rejection; the output then follows the target alone).
+ * For a tree (the children of a node drawn without replacement from the drafter's
+ * distribution at that node, in node-index order) the children are tested in that order:
+ * child x is kept when u < p(x) / q(x); otherwise p becomes max(p - q, 0) normalised, x
+ * leaves q and q is renormalised.  A kept child is the next node; when all are rejected (or
+ * the node has none) the bonus token is a Gumbel-max draw from p as it then stands.
+ *
+ * At node i, p = softmax(logits_i / T) and q = softmax(draft_logits[draft_row[i]] / T), in
+ * float64.  The uniform of child node j of request b is Philox4x32-10 with counter
+ * (0x40000000, j, b, round mod 2^32), key (seed lo, seed hi), word 0, u = ((x>>9)+0.5)*2^-23;
+ * the draw at node i uses the Gumbel noise of eagle3_accept at node i (token t: counter
+ * (t>>2, i, b, round), word t & 3) and takes argmax_t ln p_t + G_t.  Children whose token is
+ * outside [0, V) or repeats an earlier sibling's are skipped; only the first max_children
+ * children of a node are tested (1 <= max_children <= 64, else EAGLE3_EUNSUPPORTED).
+ *
+ *  cu_nodes [B+1], tokens [T], parents [T] (request-local, parent < node; at most 256 nodes per
+ *  request), logits [T, V] dtype (target logits at every node), draft_logits [n_draft_rows, V]
+ *  draft_dtype (the drafter's logits; NULL when n_draft_rows == 0), draft_row [T] int32 (row of
+ *  draft_logits at node i; outside [0, n_draft_rows) for a node without children).
+ *  temperature > 0.  Outputs as for eagle3_accept (max_depth >= the deepest node).
+ *  dev_status: EAGLE3_DEV_BAD_ROW (a node with children has no draft row: it draws from p),
+ *  EAGLE3_DEV_BAD_TOKEN (a child token outside the vocabulary), EAGLE3_DEV_BAD_PATH (a request
+ *  with more than 256 nodes: the later nodes are ignored).
+ *  workspace: eagle3_accept_sampled_workspace_size(T, V, max_children) bytes.
+ * ------------------------------------------------------------------------------------ */
+EAGLE3_API size_t eagle3_accept_sampled_workspace_size(int T, int V, int max_children);
+EAGLE3_API int eagle3_accept_sampled(int B, int T, const int32_t* cu_nodes, const int32_t* tokens,
+                                     const int32_t* parents, const void* logits, int V, int dtype,
+                                     const void* draft_logits, int draft_dtype, int n_draft_rows,
+                                     const int32_t* draft_row, int max_children, float temperature,
+                                     uint64_t seed, uint64_t round, int max_depth,
+                                     int32_t* accept_len, int32_t* path, int32_t* out_tokens,
+                                     int32_t* bonus, int32_t* dev_status, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * eagle3_commit_kv -- commit the accepted path's KV.  [P5] 一棵候选树怎样被验证, step 5
  * (commit only the KV on the accepted path, release the other branches); [P2]
  * 二、EAGLE-2动态草稿树 (fall back to the last accepted node, where the next round starts).

@@ -825,11 +825,12 @@ def accept_uniform(seed: int, rnd: int, b: int, j: int) -> float:
 
 
 def accept_sampled(cu_nodes, tokens, parents, logits, draft_logits, draft_row,
-                   temperature: float, seed: int, rnd: int, max_depth: int):
+                   temperature: float, seed: int, rnd: int, max_depth: int,
+                   max_children: int = 1 << 30):
     """Sampled-candidate acceptance.  Per request, from the root: at node i the target side
     is p = softmax(z_i / T) and the draft side q = softmax(draft_logits[draft_row[i]] / T);
-    its children (nodes whose parent is i, in increasing node index) go through rrs_node
-    with their uniforms; a kept child becomes the next node; otherwise the bonus token is
+    its first max_children children (nodes whose parent is i, in increasing node index) go
+    through rrs_node with their uniforms; a kept child becomes the next node; otherwise the bonus token is
     residual_draw of the resulting target side with the Gumbel noise of node i (the noise
     of the deterministic form).  A node whose draft row is outside draft_logits draws from
     p directly.  Returns (accept_len, path, out_tokens, bonus) laid out as by `accept`."""
@@ -844,13 +845,18 @@ def accept_sampled(cu_nodes, tokens, parents, logits, draft_logits, draft_row,
     V, R = lg.shape[1], dl.shape[0]
     for b in range(B):
         n0, n1 = int(cu_nodes[b]), int(cu_nodes[b + 1])
+        if n1 <= n0:                         # empty request: nothing accepted, no bonus
+            bonus[b] = -1
+            continue
         kids: Dict[int, List[int]] = {}
         for j in range(1, n1 - n0):
-            kids.setdefault(int(parents[n0 + j]), []).append(j)
+            pj = int(parents[n0 + j])
+            if 0 <= pj < j:                  # a parent outside [0, j) makes j nobody's child
+                kids.setdefault(pj, []).append(j)
         i, chain = 0, [0]
         while True:
             p = softmax64(lg[n0 + i], temperature)
-            ch = kids.get(i, [])
+            ch = kids.get(i, [])[:max_children]
             r = int(draft_row[n0 + i])
             if ch and 0 <= r < R:
                 q = softmax64(dl[r], temperature)

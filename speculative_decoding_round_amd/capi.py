@@ -99,6 +99,11 @@ EXPORTS = {
                               c_void_p, c_int, c_int, c_float, c_uint64, c_uint64, c_int,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                               c_void_p]),
+    "eagle3_accept_sampled_workspace_size": (c_size_t, [c_int, c_int, c_int]),
+    "eagle3_accept_sampled": (c_int, [c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                                      c_int, c_void_p, c_int, c_int, c_void_p, c_int, c_float,
+                                      c_uint64, c_uint64, c_int, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "eagle3_budget_init": (c_int, [c_void_p, c_void_p]),
     "eagle3_budget_update": (c_int, [c_void_p, c_void_p, ctypes.c_int32, c_float, c_float, c_void_p]),
     "eagle3_profile_enable": (c_int, [c_int, c_char_p]),
@@ -376,6 +381,46 @@ def eagle3_accept(cu_nodes, tokens, parents, mask, logits, temperature: float, s
                              out["out_tokens"].data_ptr(), out["bonus"].data_ptr(),
                              workspace.data_ptr(), workspace.numel(), _stream(stream))
     _check("eagle3_accept", st)
+    return out
+
+
+def eagle3_accept_sampled(cu_nodes, tokens, parents, logits, draft_logits, draft_row,
+                          temperature: float, seed: int, round: int, max_depth: int,
+                          max_children: int, dev_status: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None,
+                          stream=None) -> dict:
+    """Acceptance of sampled candidates: draft_logits [R, V] holds the drafter's logits, and
+    draft_row[i] names the row of node i (-1 for a node without children)."""
+    _dev(cu_nodes, "cu_nodes", torch.int32)
+    _dev(tokens, "tokens", torch.int32)
+    _dev(parents, "parents", torch.int32)
+    _dev(draft_row, "draft_row", torch.int32)
+    _dev(logits, "logits")
+    B = cu_nodes.numel() - 1
+    T, V = logits.shape
+    dev = logits.device
+    R = 0 if draft_logits is None else draft_logits.shape[0]
+    if draft_logits is not None:
+        _dev(draft_logits, "draft_logits")
+        if draft_logits.shape[1] != V:
+            raise ValueError("draft_logits must have the target's vocabulary")
+    if out is None:
+        out = {"accept_len": torch.empty((B,), dtype=torch.int32, device=dev),
+               "path": torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev),
+               "out_tokens": torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev),
+               "bonus": torch.empty((B,), dtype=torch.int32, device=dev)}
+    if workspace is None:
+        workspace = _workspace(lib().eagle3_accept_sampled_workspace_size(T, V, int(max_children)), dev)
+    st = lib().eagle3_accept_sampled(
+        B, T, cu_nodes.data_ptr(), tokens.data_ptr(), parents.data_ptr(), logits.data_ptr(), V,
+        dtype_code(logits.dtype), None if draft_logits is None else draft_logits.data_ptr(),
+        dtype_code(logits.dtype if draft_logits is None else draft_logits.dtype), R,
+        draft_row.data_ptr(), int(max_children), float(temperature), int(seed) & (2**64 - 1),
+        int(round) & (2**64 - 1), int(max_depth), out["accept_len"].data_ptr(), out["path"].data_ptr(),
+        out["out_tokens"].data_ptr(), out["bonus"].data_ptr(),
+        None if dev_status is None else dev_status.data_ptr(), workspace.data_ptr(), workspace.numel(),
+        _stream(stream))
+    _check("eagle3_accept_sampled", st)
     return out
 
 

@@ -328,6 +328,34 @@ int eagle3_accept(int B, int T, const int32_t* cu_nodes, const int32_t* tokens,
                        (hipStream_t)stream);
 }
 
+size_t eagle3_accept_sampled_workspace_size(int T, int V, int max_children) {
+  if (T < 1 || V <= 0 || max_children < 1 || max_children > accept_sampled_max_children()) return 0;
+  return accept_sampled_workspace(T, V, max_children);
+}
+
+int eagle3_accept_sampled(int B, int T, const int32_t* cu_nodes, const int32_t* tokens,
+                          const int32_t* parents, const void* logits, int V, int dtype,
+                          const void* draft_logits, int draft_dtype, int n_draft_rows,
+                          const int32_t* draft_row, int max_children, float temperature,
+                          uint64_t seed, uint64_t round, int max_depth, int32_t* accept_len,
+                          int32_t* path, int32_t* out_tokens, int32_t* bonus, int32_t* dev_status,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (B <= 0 || T < B || V <= 0 || max_depth < 0 || n_draft_rows < 0) return EAGLE3_EINVAL;
+  if (!dtype_ok(dtype) || (n_draft_rows > 0 && !dtype_ok(draft_dtype))) return EAGLE3_EINVAL;
+  if (!(temperature > 0.f) || temperature == __builtin_huge_valf()) return EAGLE3_EINVAL;
+  if (!cu_nodes || !tokens || !parents || !logits || !draft_row || !accept_len || !path ||
+      !out_tokens || !bonus || (n_draft_rows > 0 && !draft_logits))
+    return EAGLE3_EINVAL;
+  if (max_children < 1 || max_children > accept_sampled_max_children()) return EAGLE3_EUNSUPPORTED;
+  const size_t need = accept_sampled_workspace(T, V, max_children);
+  if (!workspace || workspace_bytes < need) return EAGLE3_EWORKSPACE;
+  return launch_accept_sampled(B, T, cu_nodes, tokens, parents, logits, V, dtype,
+                               n_draft_rows > 0 ? draft_logits : nullptr, draft_dtype, n_draft_rows,
+                               draft_row, max_children, temperature, seed, round, max_depth,
+                               accept_len, path, out_tokens, bonus, dev_status, workspace,
+                               (hipStream_t)stream);
+}
+
 // ---- timing ---------------------------------------------------------------------------
 int eagle3_profile_enable(int on, const char* only_kernel) {
   std::lock_guard<std::mutex> lk(e3h::g_mu);

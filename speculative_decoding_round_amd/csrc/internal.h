@@ -47,6 +47,15 @@ int launch_accept(int B, int T, const int32_t* cu_nodes, const int32_t* tokens,
                   int max_depth, int32_t* accept_len, int32_t* path, int32_t* out_tokens,
                   int32_t* bonus, float* part_v, int* part_i, hipStream_t s);
 size_t accept_workspace(int T, int V);
+size_t accept_sampled_workspace(int T, int V, int max_children);
+int accept_sampled_max_children();
+int launch_accept_sampled(int B, int T, const int32_t* cu_nodes, const int32_t* tokens,
+                          const int32_t* parents, const void* logits, int V, int dtype,
+                          const void* draft_logits, int draft_dtype, int n_draft_rows,
+                          const int32_t* draft_row, int max_children, float temperature,
+                          uint64_t seed, uint64_t round, int max_depth, int32_t* accept_len,
+                          int32_t* path, int32_t* out_tokens, int32_t* bonus, int32_t* dev_status,
+                          void* workspace, hipStream_t s);
 int accept_chunks(int V);
 
 // ---- GEMM ------------------------------------------------------------------------------

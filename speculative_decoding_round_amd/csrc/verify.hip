@@ -54,71 +54,6 @@ __global__ __launch_bounds__(256) void k_build_mask(const int32_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------------------
-// Philox4x32-10 (Salmon et al., SC'11) and the fixed float32 natural log used for Gumbel
-// noise.  Contraction is disabled so every multiply and add rounds on its own, as in the
-// definition of the generator's output map.
-// ---------------------------------------------------------------------------------------
-__device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    if (r > 0) {
-      k0 += 0x9E3779B9u;
-      k1 += 0xBB67AE85u;
-    }
-    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
-    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
-    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
-    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
-    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
-    c[0] = n0;
-    c[1] = lo1;
-    c[2] = n2;
-    c[3] = lo0;
-  }
-}
-
-// ln v for positive normal v: v = 2^e m, m in [sqrt(1/2), sqrt(2)); s = (m-1)/(m+1);
-// ln v = e*ln2_hi + (e*ln2_lo + 2*(s + s^3 (1/3 + s^2 (1/5 + s^2 (1/7 + s^2/9))))).
-__device__ __forceinline__ float ln_fixed(float v) {
-#pragma clang fp contract(off)
-  const uint32_t bits = __float_as_uint(v);
-  int e = (int)((bits >> 23) & 0xffu) - 127;
-  float m = __uint_as_float((bits & 0x7fffffu) | 0x3f800000u);
-  if (m >= __uint_as_float(0x3fb504f3u)) {
-    m = m * 0.5f;
-    e += 1;
-  }
-  const float ef = (float)e;
-  const float s = (m - 1.0f) / (m + 1.0f);
-  const float t = s * s;
-  float p = __uint_as_float(0x3de38e39u);           // 1/9
-  p = p * t + __uint_as_float(0x3e124925u);         // 1/7
-  p = p * t + __uint_as_float(0x3e4ccccdu);         // 1/5
-  p = p * t + __uint_as_float(0x3eaaaaabu);         // 1/3
-  const float r = s + (s * t) * p;
-  return ef * __uint_as_float(0x3f317200u) + (ef * __uint_as_float(0x35bfbe8eu) + 2.0f * r);
-}
-
-__device__ __forceinline__ float gumbel_from_word(uint32_t x) {
-#pragma clang fp contract(off)
-  const float u = ((float)(x >> 9) + 0.5f) * 1.1920928955078125e-07f;  // 2^-23
-  const float inner = -ln_fixed(u);
-  return -ln_fixed(inner);
-}
-
-__device__ __forceinline__ int find_request(const int32_t* cu, int B, int node) {
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (cu[mid] <= node)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  return lo;
-}
-
-// ---------------------------------------------------------------------------------------
 // Acceptance pass 1: per (node, chunk of 4096 tokens) the best (value, token) of greedy z
 // or z*invT + Gumbel.  Thread t takes 16 consecutive tokens (vector loads issued together
 // when the row is 16-byte aligned); one Philox call yields the noise of four tokens.

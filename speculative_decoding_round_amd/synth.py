@@ -221,6 +221,57 @@ def verify_inputs(shape: Shape, trees: List[List[int]], prefix: List[int], seed:
     return out
 
 
+def sampled_tree_inputs(trees: List[List[int]], V: int, seed: int, dtype=torch.bfloat16,
+                        device="cpu", n_hot: int = 16, hot_boost: float = 6.0,
+                        target_noise: float = 0.5) -> dict:
+    """Inputs of one acceptance round over sampled candidates.  Every node with children gets
+    a draft logit row: N(0, 1) plus `hot_boost` on `n_hot` random tokens; its children carry
+    distinct tokens of that hot set (uniform without replacement; beyond n_hot children the
+    rest are distinct uniform tokens).  A node's target logits are its draft row plus
+    N(0, target_noise^2); a node without children gets a fresh hot-boosted row and draft row
+    -1.  Returns cu_nodes, tokens, parents, logits [T, V], draft_logits [R, V], draft_row [T]."""
+    g = _gen(seed)
+    parents = [p for t in trees for p in t]
+    T = len(parents)
+    tokens = torch.zeros(T, dtype=torch.int32)
+    draft_row = torch.full((T,), -1, dtype=torch.int32)
+    zq_rows, z = [], torch.empty((T, V), dtype=torch.float32)
+
+    def hot_row():
+        row = torch.randn(V, generator=g)
+        hot = torch.randperm(V, generator=g)[:n_hot]
+        row[hot] += hot_boost
+        return row, hot
+
+    n0 = 0
+    for t in trees:
+        kids = {}
+        for j in range(1, len(t)):
+            kids.setdefault(t[j], []).append(j)
+        for i in range(len(t)):
+            row, hot = hot_row()
+            ch = kids.get(i, [])
+            if ch:
+                draft_row[n0 + i] = len(zq_rows)
+                zq_rows.append(row)
+                pick = hot[torch.randperm(len(hot), generator=g)].tolist()
+                while len(pick) < len(ch):
+                    x = int(torch.randint(0, V, (1,), generator=g))
+                    if x not in pick:
+                        pick.append(x)
+                for c, x in zip(ch, pick):
+                    tokens[n0 + c] = x
+                z[n0 + i] = row + target_noise * torch.randn(V, generator=g)
+            else:
+                z[n0 + i] = row
+        n0 += len(t)
+    zq = torch.stack(zq_rows) if zq_rows else torch.zeros((1, V))
+    return {"cu_nodes": cu_from_lengths([len(t) for t in trees]).to(device),
+            "tokens": tokens.to(device), "parents": torch.tensor(parents, dtype=torch.int32, device=device),
+            "logits": z.to(dtype).to(device), "draft_logits": zq.to(dtype).to(device),
+            "draft_row": draft_row.to(device), "T": T}
+
+
 def plant_path(logits: torch.Tensor, tokens: torch.Tensor, parents: List[int], node0: int,
                end_node: int, bump: float = 1.0) -> None:
     """Make the root->end_node path of one request the target's greedy choice: for every

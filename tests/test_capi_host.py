@@ -171,3 +171,36 @@ def test_commit_and_catchup_validation(lib):
     assert lib.eagle3_drafter_catchup_workspace_size(None, 4) == 0
     assert lib.eagle3_drafter_catchup(None, 4, P, P, P, P, P, P, 10, P, P, None, None, P, 1 << 20,
                                       None) == -1
+
+
+def test_accept_sampled_validation(lib):
+    """Host-side checks of eagle3_accept_sampled, before anything is launched."""
+    P = 1 << 12
+    # B, T, cu, tokens, parents, logits, V, dtype, draft_logits, draft_dtype, R, draft_row,
+    # max_children, temperature, seed, round, max_depth, accept_len, path, out_tokens, bonus,
+    # dev_status, workspace, workspace_bytes, stream
+    ws = lib.eagle3_accept_sampled_workspace_size(60, 128256, 10)
+    assert ws > 0
+    assert lib.eagle3_accept_sampled_workspace_size(60, 128256, 65) == 0     # max_children > 64
+    assert lib.eagle3_accept_sampled_workspace_size(60, 128256, 16) > ws
+    args = [1, 60, P, P, P, P, 128256, 1, P, 1, 30, P, 10, 0.8, 1, 2, 6, P, P, P, P, None, P, ws, None]
+
+    def call(**kw):
+        a = list(args)
+        names = {"B": 0, "T": 1, "dtype": 7, "R": 10, "draft": 8, "maxc": 12, "temp": 13, "depth": 16,
+                 "ws": 22, "wsb": 23}
+        for k, v in kw.items():
+            a[names[k]] = v
+        return lib.eagle3_accept_sampled(*a)
+
+    assert call(B=0) == -1
+    assert call(dtype=3) == -1
+    assert call(temp=0.0) == -1                  # sampled acceptance needs T > 0
+    assert call(temp=float("inf")) == -1
+    assert call(depth=-1) == -1
+    assert call(R=-1) == -1
+    assert call(draft=None) == -1                # rows declared but no pointer
+    assert call(maxc=0) == -2
+    assert call(maxc=65) == -2
+    assert call(ws=None) == -3
+    assert call(wsb=ws - 1) == -3

@@ -1,0 +1,169 @@
+"""GPU parity of eagle3_accept_sampled (acceptance of sampled candidates) against the oracle's
+accept_sampled: accepted lengths, paths, output tokens and bonus tokens must be equal (integer
+results; both sides take every decision in float64), over many rounds (fresh uniforms and
+Gumbel noise), trees from chains to wide stars and random trees, ragged and full
+vocabularies, bf16 and fp32 logits, and the edge cases (empty request, a node without a draft
+row, repeated and out-of-vocabulary children, more children than max_children, every token the
+drafter can propose rejected, a child the drafter gives probability zero)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import eagle3_oracle as O
+from speculative_decoding_round_amd import capi, synth
+from tests.gpu_util import need_gpu
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+KEYS = ("accept_len", "path", "out_tokens", "bonus")
+
+
+def max_kids(trees):
+    m = 1
+    for t in trees:
+        cnt = {}
+        for p in t[1:]:
+            cnt[p] = cnt.get(p, 0) + 1
+        m = max([m] + list(cnt.values()))
+    return m
+
+
+def tree_depth(trees):
+    best = 0
+    for t in trees:
+        d = [0] * len(t)
+        for j in range(1, len(t)):
+            d[j] = d[t[j]] + 1
+        best = max(best, max(d))
+    return best
+
+
+def gpu_run(d, temp, seed, rnd, max_depth, maxc, status=None):
+    out = capi.eagle3_accept_sampled(d["cu_nodes"], d["tokens"], d["parents"], d["logits"],
+                                     d["draft_logits"], d["draft_row"], temp, seed, rnd, max_depth,
+                                     maxc, dev_status=status)
+    torch.cuda.synchronize()
+    return [out[k].cpu().numpy() for k in KEYS]
+
+
+def oracle_run(d, temp, seed, rnd, max_depth, maxc):
+    c = lambda k: d[k].cpu().numpy()
+    return O.accept_sampled(c("cu_nodes"), c("tokens"), c("parents"), d["logits"].float().cpu(),
+                            d["draft_logits"].float().cpu(), c("draft_row"), temp, seed, rnd,
+                            max_depth, max_children=maxc)
+
+
+def compare(d, temp, seed, rounds, max_depth, maxc, status=None):
+    lens = []
+    for rnd in rounds:
+        print(f"round {rnd}", flush=True)
+        got = gpu_run(d, temp, seed, rnd, max_depth, maxc, status)
+        ref = oracle_run(d, temp, seed, rnd, max_depth, maxc)
+        for k, g, r in zip(KEYS, got, ref):
+            assert np.array_equal(g, r), (k, rnd, g, r)
+        lens += list(got[0])
+    return np.array(lens)
+
+
+SMALL = [synth.full_tree(3, 3), synth.chain_tree(5), synth.star_tree(12)]
+
+
+@pytest.mark.parametrize("V,dt,noise,temp", [
+    (1003, torch.float32, 3.0, 0.7),       # one ragged chunk, scalar loads, many rejections
+    (9000, torch.bfloat16, 1.0, 1.0),      # three chunks, the last ragged
+    (9000, torch.float32, 0.3, 1.3),       # mostly kept
+], ids=["v1003_f32_noisy", "v9000_bf16", "v9000_f32_close"])
+def test_small_trees_match_oracle(V, dt, noise, temp):
+    need_gpu()
+    d = synth.sampled_tree_inputs(SMALL, V, seed=11, dtype=dt, device=DEV, target_noise=noise)
+    lens = compare(d, temp, 1234, range(10), tree_depth(SMALL), max_kids(SMALL))
+    assert lens.min() < lens.max()          # the rounds reach different depths
+
+
+def test_random_trees_full_vocabulary():
+    """Random 60-node trees of depth 6 over the Llama-3 vocabulary (128256), bf16."""
+    need_gpu()
+    trees = [synth.random_tree(60, 6, seed=s) for s in (3, 4)]
+    d = synth.sampled_tree_inputs(trees, 128256, seed=21, device=DEV, target_noise=2.0)
+    compare(d, 1.0, 77, range(4), tree_depth(trees), max_kids(trees))
+
+
+def test_batch16_full_vocabulary():
+    """Sixteen 48-node trees (the batched serving shape) at V = 128256, bf16."""
+    need_gpu()
+    trees = [synth.random_tree(48, 6, seed=100 + s) for s in range(16)]
+    d = synth.sampled_tree_inputs(trees, 128256, seed=31, device=DEV, target_noise=1.0)
+    compare(d, 0.8, 5, range(2), tree_depth(trees), max_kids(trees))
+
+
+def test_equal_distributions_keep_every_first_child():
+    """Target logits equal to the draft logits: p / q = 1 at every candidate, so each node
+    keeps its first child and the path is the first-child chain."""
+    need_gpu()
+    trees = [synth.full_tree(3, 3), synth.random_tree(30, 5, seed=9)]
+    d = synth.sampled_tree_inputs(trees, 5000, seed=41, dtype=torch.float32, device=DEV, target_noise=0.0)
+    for rnd in range(3):
+        acc, path, _, _ = gpu_run(d, 1.0, 3, rnd, tree_depth(trees), max_kids(trees))
+        for b, t in enumerate(trees):
+            i, chain = 0, [0]
+            while i in t[1:]:
+                i = t.index(i, 1)
+                chain.append(i)
+            assert acc[b] == len(chain) - 1
+            assert list(path[b, :len(chain)]) == chain
+
+
+def test_edge_cases_match_oracle():
+    """An empty request; a node with children but no draft row (flagged, draws from p); repeated
+    and out-of-vocabulary children (flagged, skipped); a star tested with max_children = 2."""
+    need_gpu()
+    trees = [synth.star_tree(6), synth.full_tree(2, 2), synth.star_tree(9)]
+    d = synth.sampled_tree_inputs(trees, 3000, seed=51, dtype=torch.float32, device=DEV, target_noise=3.0)
+    cu = d["cu_nodes"].cpu().tolist()
+    # insert an empty request after the first
+    d["cu_nodes"] = torch.tensor([cu[0], cu[1], cu[1], cu[2], cu[3]], dtype=torch.int32, device=DEV)
+    tok = d["tokens"].cpu()
+    tok[2] = tok[1]                   # star 0: children 1 and 2 share a token
+    tok[4] = 3000 + 5                 # star 0: child 4 outside the vocabulary
+    d["tokens"] = tok.to(DEV)
+    row = d["draft_row"].cpu()
+    row[cu[1] + 1] = -1               # full tree: node 1 has children but no draft row
+    d["draft_row"] = row.to(DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for maxc in (8, 2):
+        compare(d, 0.9, 8, range(6), 2, maxc, status)
+    st = int(status.item())
+    assert st & 16 and st & 4
+
+
+def test_every_proposable_token_rejected():
+    """A node whose drafter gives probability zero to all but three tokens, with children
+    [three positive tokens, then zero-probability ones], and a target concentrated elsewhere:
+    once the three are rejected nothing is left to test and the token is drawn from the
+    residual.  A second request's first child has draft probability zero: it is kept."""
+    need_gpu()
+    V = 8
+    trees = [[-1, 0, 0, 0, 0, 0], [-1, 0]]
+    T = 8
+    neg = float("-inf")
+    zq = torch.tensor([[0.0, 0.2, 0.4, neg, neg, neg, neg, neg],
+                       [0.0, 0.0, neg, 1.0, 1.0, 1.0, 1.0, 1.0]])
+    z = torch.full((T, V), -2.0)
+    z[0, 5:] = 3.0                                   # target mass on tokens 5..7
+    z[6] = torch.linspace(0, 1, V)
+    d = {"cu_nodes": torch.tensor([0, 6, 8], dtype=torch.int32),
+         "tokens": torch.tensor([0, 0, 1, 2, 3, 4, 0, 2], dtype=torch.int32),
+         "parents": torch.tensor([p for t in trees for p in t], dtype=torch.int32),
+         "logits": z, "draft_logits": zq,
+         "draft_row": torch.tensor([0, -1, -1, -1, -1, -1, 1, -1], dtype=torch.int32)}
+    # request 1's only child has token 2, where its drafter's probability is zero
+    d = {k: v.to(DEV) for k, v in d.items()}
+    draws = set()
+    for rnd in range(12):
+        got = gpu_run(d, 1.0, 2, rnd, 1, 8)
+        ref = oracle_run(d, 1.0, 2, rnd, 1, 8)
+        for k, g, r in zip(KEYS, got, ref):
+            assert np.array_equal(g, r), (k, rnd, g, r)
+        assert got[0][1] == 1 and got[2][1][0] == 2  # the zero-probability child is kept
+        draws.add(int(got[3][0]))
+    assert draws & {5, 6, 7}
