@@ -308,7 +308,51 @@ def attention_op(capi, synth, shape, trees, prefix, bound, reps=20, seed=500):
 
 
 OP_KEYS = ("attn_longctx", "attn_batch16", "attn_70b", "attn_8b", "merge", "accept_greedy", "accept_t07",
-           "gemm_sweep", "catchup", "commit", "tree_budgets", "usp")
+           "accept_sampled", "gemm_sweep", "catchup", "commit", "tree_budgets", "usp")
+
+
+def sampled_accept_ops(capi, synth, reps):
+    """Acceptance of sampled candidates (eagle3_accept_sampled) at the 8B shape (one random
+    61-node tree of depth 6) and the 70B shape (four), V = 128256 bf16 target and draft logits,
+    at most 10 children tested per node, T = 1.  Draft rows are hot-boosted N(0, 1) rows whose
+    children are hot tokens; target rows are the draft rows plus N(0, 1) (about half the
+    candidates kept).  Algorithmic bytes: every target row and every draft row read once."""
+    import numpy as np
+    import torch
+    dev = "cuda:0"
+    out = []
+    for key, sh, B in (("accept_sampled_8b", synth.LLAMA8B, 1), ("accept_sampled_70b", synth.LLAMA70B, 4)):
+        trees = [synth.random_tree(61, sh.depth, 4400 + i) for i in range(B)]
+        d = synth.sampled_tree_inputs(trees, sh.V, seed=970, device=dev, target_noise=1.0)
+        T, V, R = d["T"], sh.V, d["draft_logits"].shape[0]
+        nbytes = (T + R) * V * 2
+        ncopy = _copies(nbytes)
+        zs = [d["logits"]] + [d["logits"] + synth.normal((T, V), 0.05, 980 + c, torch.bfloat16, dev)
+                              for c in range(ncopy - 1)]
+        qs = [d["draft_logits"]] + [d["draft_logits"] + synth.normal((R, V), 0.05, 990 + c, torch.bfloat16, dev)
+                                    for c in range(ncopy - 1)]
+        maxc = 10
+        ws = torch.empty(capi.lib().eagle3_accept_sampled_workspace_size(T, V, maxc), dtype=torch.uint8, device=dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        ao = {"accept_len": torch.empty((B,), **i32), "path": torch.empty((B, sh.depth + 1), **i32),
+              "out_tokens": torch.empty((B, sh.depth + 1), **i32), "bonus": torch.empty((B,), **i32)}
+
+        def run(i, d=d, zs=zs, qs=qs, ws=ws, ao=ao, sh=sh):
+            capi.eagle3_accept_sampled(d["cu_nodes"], d["tokens"], d["parents"], zs[i % len(zs)],
+                                       qs[i % len(qs)], d["draft_row"], 1.0, 7, i, sh.depth, maxc,
+                                       workspace=ws, out=ao)
+        us = _time_b2b(run, reps)
+        lens = []
+        for i in range(16):
+            run(i)
+            lens += ao["accept_len"].cpu().tolist()
+        out.append(dict(key=key, **_entry("accept (sampled candidates, T=1)",
+                                          f"{sh.name}: {T} nodes ({R} with children) x {V} logits",
+                                          "k_samp_clear + k_samp_stats + k_samp_npass x 9 + k_samp_draw + k_samp_walk",
+                                          us, "hbm", bytes_=nbytes, rotating_copies=ncopy,
+                                          mean_accept_len=round(float(np.mean(lens)), 2))))
+        del zs, qs
+    return out
 
 
 def gemm_sweep(capi, synth, reps):
@@ -542,6 +586,8 @@ def op_rooflines(reps=20, keys=OP_KEYS):
                                           rotating_copies=ncopy,
                                           logits_per_s=round(T * V / (us * 1e-6) / 1e9, 2))))
         del logits
+    if "accept_sampled" in keys:
+        ops += sampled_accept_ops(capi, synth, reps)
     if "gemm_sweep" in keys:
         ops += gemm_sweep(capi, synth, reps)
     if "catchup" in keys:

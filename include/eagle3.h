@@ -64,6 +64,7 @@ extern "C" {
 #define EAGLE3_DEV_BAD_TOKEN 4   /* a token id outside [0, vocab)                       */
 #define EAGLE3_DEV_BAD_PATH 8    /* accept_len or a path node outside its request       */
 #define EAGLE3_DEV_BAD_ROW 16    /* a destination row outside the cache                 */
+#define EAGLE3_DEV_SYNC 32       /* a partial of another workgroup was not seen in time */
 
 EAGLE3_API int eagle3_abi_version(void);
 EAGLE3_API const char* eagle3_status_string(int status);
@@ -302,7 +303,9 @@ EAGLE3_API int eagle3_accept(int B, int T, const int32_t* cu_nodes, const int32_
  *  temperature > 0.  Outputs as for eagle3_accept (max_depth >= the deepest node).
  *  dev_status: EAGLE3_DEV_BAD_ROW (a node with children has no draft row: it draws from p),
  *  EAGLE3_DEV_BAD_TOKEN (a child token outside the vocabulary), EAGLE3_DEV_BAD_PATH (a request
- *  with more than 256 nodes: the later nodes are ignored).
+ *  with more than 256 nodes: the later nodes are ignored), EAGLE3_DEV_SYNC (a partial result
+ *  handed between workgroups was not visible within a bounded wait: the outputs of that call
+ *  are not to be trusted).
  *  workspace: eagle3_accept_sampled_workspace_size(T, V, max_children) bytes.
  * ------------------------------------------------------------------------------------ */
 EAGLE3_API size_t eagle3_accept_sampled_workspace_size(int T, int V, int max_children);

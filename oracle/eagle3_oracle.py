@@ -768,9 +768,10 @@ ACCEPT_UNIFORM_C0 = 0x40000000   # counter word 0 of the acceptance uniforms (t 
 
 
 def softmax64(z_row, temperature: float) -> np.ndarray:
-    """softmax(z / T) in float64: a_t = z_t / T (z upcast exactly, T the float32 value),
-    p_t = exp(a_t - A) with A = max a + ln sum exp(a - max a)."""
-    a = np.asarray(z_row, dtype=np.float64) / float(np.float32(temperature))
+    """softmax(z / T) in float64: a_t = z_t * (1 / T) (z upcast exactly, 1 / T the float64
+    reciprocal of the float32 temperature, rounded once), p_t = exp(a_t - A) with
+    A = max a + ln sum exp(a - max a)."""
+    a = np.asarray(z_row, dtype=np.float64) * (1.0 / float(np.float32(temperature)))
     m = a.max()
     A = m + math.log(float(np.exp(a - m).sum()))
     return np.exp(a - A)

@@ -2,19 +2,25 @@
 // drafter's distribution (not taken as its top-K).
 //
 // At node i the target side is p = softmax(z_i / T) and the draft side q = softmax(zq_i / T),
-// both in float64.  The children are tested in node-index order.  After r rejections the
-// target side is p_r(t) = max(p_t - lam q_t, 0) / N and the draft side q_r(t) = q_t / c for
-// the tokens not yet rejected, with c = 1 - (q of the rejected tokens): rejecting x moves lam
-// to lam + N / c and c to c - q_x, and the new N is sum_t max(p_t - lam q_t, 0).  (Induction:
-// max(p_r - q_r, 0) = max(p - (lam + N / c) q, 0) / N on every token not yet rejected, and a
-// rejected token x had p_r(x) < q_r(x), so p - lam' q is negative there from then on.)  Each
-// rejection therefore costs one reduction over the vocabulary, the only sequential part.
+// both in float64 (z / T formed as z * (1 / T)).  The children are tested in node-index order.
+// After r rejections the target side is p_r(t) = max(p_t - lam q_t, 0) / N and the draft side
+// q_r(t) = q_t / c for the tokens not yet rejected, with c = 1 - (q of the rejected tokens):
+// rejecting x moves lam to lam + N / c and c to c - q_x, and the new N is
+// sum_t max(p_t - lam q_t, 0).  (Induction: max(p_r - q_r, 0) = max(p - (lam + N / c) q, 0) / N
+// on every token not yet rejected, and a rejected token x had p_r(x) < q_r(x), so p - lam' q is
+// negative there from then on.)  Each rejection therefore costs one reduction over the
+// vocabulary, the only sequential part.
 //
-// Every pass runs over (node, chunk of 4096 tokens) items.  The workgroup that finishes a
-// node's last chunk (a per-node counter) combines the node's partials in one fixed order and
-// advances its chain: the node is either decided (a child kept, or a draw from the residual
-// target side) or queued on the list of the next pass.  The lists keep the grids of later
-// passes to the nodes still undecided.
+// Launches: clear; stats (log-sum-exps of p and q at every node with a draft row, then the test
+// of its first child); one pass per further child (N at the node's lam, then the test) over a
+// device-side list of the nodes still undecided; the walk from each root through the kept
+// children; the draw of the bonus token at each request's end node only.
+//
+// Within a pass, the workgroup that finishes a node's last chunk (a per-node counter) combines
+// the node's partials in one fixed order.  Partials travel through agent-scope relaxed atomic
+// stores and loads into per-pass slots preset to a sentinel: the reader waits (bounded) only
+// for a store that its writer has issued but that is not visible yet, and no workgroup has to
+// write back or invalidate the L2.
 #include "common.h"
 #include "internal.h"
 
@@ -27,8 +33,9 @@ constexpr int kMaxNodes = 256;    // nodes per request
 constexpr int kMaxKids = 64;      // children tested per node
 constexpr uint32_t kUniformC0 = 0x40000000u;   // counter word 0 of the acceptance uniforms
 constexpr double kNegInfD = -__builtin_huge_val();
-// p_t - lam q_t is exactly <= 0 in float64 when ln(p_t / (lam q_t)) is below this margin
-constexpr double kSkipMargin = -1e-9;
+constexpr uint64_t kEmpty = 0x7FF4DEADBEEF0001ull;   // sentinel of an unwritten double slot
+constexpr int kEmptyI = (int)0x80000000u;             // sentinel of an unwritten int slot
+constexpr int kSpinMax = 1 << 16;
 
 enum : int { ST_NEED = 0, ST_KEPT = 1, ST_DRAW = 2 };
 
@@ -47,18 +54,67 @@ struct SArgs {
   const void* logits;
   const void* dlogits;
   int B, T, V, nch, R, maxc, max_depth, az, aq;
-  double temp;
+  double invT;
   uint32_t seed_lo, seed_hi, rnd;
-  NodeSt* st;       // [T]
-  int* cnt;         // [T] chunks finished in the current pass
-  int* lists;       // [maxc + 1][T]: list m (2 .. maxc) waits for pass m; list 0 draws
-  int* list_n;      // [maxc + 1]
-  double* part;     // [T][nch][4]
-  int* part_i;      // [T][nch]
-  int* ydraw;       // [T] residual draw of a node
+  NodeSt* st;         // [T]
+  int* cnt;           // [T] chunks finished in the current pass
+  int* lists;         // [maxc + 1][T]: list m (2 .. maxc) waits for pass m; list 0: end nodes to draw
+  int* list_n;        // [maxc + 1]
+  uint64_t* p_stats;  // [T][nch][4]        (max a, sum, max b, sum)
+  uint64_t* p_n;      // [maxc - 1][T][nch] N partial of pass m
+  int* p_pos;         // [T][nch]           tokens with q > 0 (pass 2)
+  uint64_t* p_dv;     // [T][nch]           draw: best value
+  int* p_di;          // [T][nch]           draw: its token
+  int32_t* accept_len;
+  int32_t* path;
+  int32_t* out_tokens;
+  int32_t* bonus;
   int32_t* dev_status;
 };
 
+// ---- cross-workgroup slots -------------------------------------------------------------
+__device__ __forceinline__ void put_d(uint64_t* p, double v) {
+  __hip_atomic_store(p, (uint64_t)__double_as_longlong(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void put_i(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// A slot whose writer has already counted its chunk as finished: the store is issued, so it
+// becomes visible; the wait is bounded all the same and a miss is flagged.
+__device__ __forceinline__ double get_d(uint64_t* p, int32_t* dev_status) {
+  uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int it = 0; v == kEmpty && it < kSpinMax; ++it) {
+    __builtin_amdgcn_s_sleep(1);
+    v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (v == kEmpty) {
+    if (dev_status) atomicOr(dev_status, EAGLE3_DEV_SYNC);
+    return 0.0;
+  }
+  return __longlong_as_double((long long)v);
+}
+__device__ __forceinline__ int get_i(int* p, int32_t* dev_status) {
+  int v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int it = 0; v == kEmptyI && it < kSpinMax; ++it) {
+    __builtin_amdgcn_s_sleep(1);
+    v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (v == kEmptyI) {
+    if (dev_status) atomicOr(dev_status, EAGLE3_DEV_SYNC);
+    return 0;
+  }
+  return v;
+}
+
+// Count one finished chunk of node g; true (in every thread) in the workgroup that finished the
+// node's last chunk.  Thread 0 has issued the chunk's partial store before this call.
+__device__ __forceinline__ bool finish_chunk(const SArgs& a, int g, int* s_last) {
+  if (threadIdx.x == 0) *s_last = atomicAdd(&a.cnt[g], 1) == a.nch - 1;
+  __syncthreads();
+  return *s_last != 0;
+}
+
+// ---- loads and reductions --------------------------------------------------------------
 template <typename T>
 __device__ __forceinline__ void load_chunk(const T* row, int tb, int V, int aligned, float* z) {
   constexpr int EPC = Vec<T>::N;
@@ -108,6 +164,65 @@ __device__ __forceinline__ int wave_sum_i(int x) {
   return x;
 }
 
+// Block-wide max / sum of two values (256 threads); every thread receives both results.
+__device__ __forceinline__ void block_max2(double& x, double& y, double* sm) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    x = fmax(x, __shfl_xor(x, off));
+    y = fmax(y, __shfl_xor(y, off));
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sm[w] = x;
+    sm[4 + w] = y;
+  }
+  __syncthreads();
+  x = fmax(fmax(sm[0], sm[1]), fmax(sm[2], sm[3]));
+  y = fmax(fmax(sm[4], sm[5]), fmax(sm[6], sm[7]));
+  __syncthreads();
+}
+
+__device__ __forceinline__ void block_sum2(double& x, double& y, double* sm) {
+#pragma clang fp contract(off)
+  x = wave_sum_d(x);
+  y = wave_sum_d(y);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sm[w] = x;
+    sm[4 + w] = y;
+  }
+  __syncthreads();
+  x = (sm[0] + sm[1]) + (sm[2] + sm[3]);
+  y = (sm[4] + sm[5]) + (sm[6] + sm[7]);
+  __syncthreads();
+}
+
+// exp(x), x <= 0, by Tang's table-driven method (ACM TOMS 15(2), 1989): x = (64 k + j) ln2/64 + r
+// with |r| <= ln2/128, exp(x) = 2^k * 2^(j/64) * exp(r), exp(r) by its degree-5 Taylor polynomial
+// (truncation below 4e-17 relative on that interval).  ln2/64 is split in a float64 head and
+// tail (from the series of ln 2) so that r is formed to within rounding; tab[j] = 2^(j/64) is
+// filled per workgroup by exp2_table.  Below -1000 the result is 0.
+constexpr double kExpInvStep = 0x1.71547652b82fep+6;   // 64 / ln 2
+constexpr double kExpStepHi = 0x1.62e42fefa39efp-7;    // ln 2 / 64, head
+constexpr double kExpStepLo = 0x1.abc9e3b39803fp-62;   // ln 2 / 64 - head
+__device__ __forceinline__ void exp2_table(double* tab) {
+  if (threadIdx.x < 64) tab[threadIdx.x] = exp2((double)threadIdx.x * 0.015625);
+  __syncthreads();
+}
+__device__ __forceinline__ double exp_tab(double x, const double* tab) {
+  const double xc = fmax(x, -1000.0);
+  const double nd = __builtin_rint(xc * kExpInvStep);
+  const int n = (int)nd;
+  double r = __builtin_fma(-nd, kExpStepHi, xc);
+  r = __builtin_fma(-nd, kExpStepLo, r);
+  double p = __builtin_fma(r, 1.0 / 120.0, 1.0 / 24.0);
+  p = __builtin_fma(p, r, 1.0 / 6.0);
+  p = __builtin_fma(p, r, 0.5);
+  p = __builtin_fma(p, r, 1.0);
+  p = __builtin_fma(p, r, 1.0);
+  return __builtin_ldexp(tab[n & 63] * p, n >> 6);
+}
+
 __device__ __forceinline__ bool better_d(double va, int ia, double vb, int ib) {
   return (va > vb) | ((va == vb) & (ia < ib));
 }
@@ -131,6 +246,7 @@ __device__ __forceinline__ double accept_uniform(const SArgs& a, int b, int j) {
   return (double)(((float)(ctr[0] >> 9) + 0.5f) * 1.1920928955078125e-07f);  // 2^-23
 }
 
+// ---- the chain at one node -------------------------------------------------------------
 // Children of request-local node i (nodes j > i with parent i, in index order, at most maxc)
 // and their tokens, into LDS.  Whole block of 256 threads (one per possible node).
 __device__ __forceinline__ int node_children(const SArgs& a, int n0, int n, int i, int* s_kids,
@@ -185,8 +301,8 @@ __device__ void chain_step(const SArgs& a, NodeSt& s, const int* s_kids, const i
   }
   const int j = s_kids[s.k];
   const int x = s_tok[s.k];
-  const double px = exp((double)to_f32(zrow[x]) / a.temp - s.A);
-  const double qx = exp((double)to_f32(qrow[x]) / a.temp - s.Bq);
+  const double px = exp((double)to_f32(zrow[x]) * a.invT - s.A);
+  const double qx = exp((double)to_f32(qrow[x]) * a.invT - s.Bq);
   bool keep = qx == 0.0;
   if (!keep) {
     const double pr = px - s.lam * qx;
@@ -212,40 +328,34 @@ __device__ void chain_step(const SArgs& a, NodeSt& s, const int* s_kids, const i
   s.status = ST_NEED;
 }
 
-__device__ __forceinline__ void enqueue(const SArgs& a, const NodeSt& s, int g) {
+__device__ __forceinline__ void enqueue_need(const SArgs& a, const NodeSt& s, int g) {
   if (s.status == ST_NEED) {
     const int at = atomicAdd(&a.list_n[s.m], 1);
     a.lists[(size_t)s.m * a.T + at] = g;
-  } else if (s.status == ST_DRAW) {
-    const int at = atomicAdd(&a.list_n[0], 1);
-    a.lists[at] = g;
   }
 }
 
-// Count one finished chunk of node g; true in the workgroup that finished the last one.
-__device__ __forceinline__ bool finish_chunk(const SArgs& a, int g, int* s_last) {
-  if (threadIdx.x == 0) {
-    __threadfence();
-    const int old = atomicAdd(&a.cnt[g], 1);
-    *s_last = old == a.nch - 1;
-  }
-  __syncthreads();
-  const bool last = *s_last != 0;
-  if (last) __threadfence();
-  return last;
-}
-
-__global__ void k_samp_clear(int* cnt, int T, int* list_n, int nl) {
+// ---- kernels ---------------------------------------------------------------------------
+__global__ void k_samp_clear(SArgs a, int n_stats, int n_n, int n_one) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t < T) cnt[t] = 0;
-  if (t < nl) list_n[t] = 0;
+  if (t < a.T) a.cnt[t] = 0;
+  if (t <= a.maxc) a.list_n[t] = 0;
+  if (t < n_stats) a.p_stats[t] = kEmpty;
+  if (t < n_n) a.p_n[t] = kEmpty;
+  if (t < n_one) {
+    a.p_pos[t] = kEmptyI;
+    a.p_dv[t] = kEmpty;
+    a.p_di[t] = kEmptyI;
+  }
 }
 
-// Pass 1: both log-sum-exps of every node; the last chunk starts the node's chain.
+// Stats: log-sum-exps of p and q at every node with a draft row (the chunk's maximum first, so
+// every element costs one exp); the last chunk tests the node's first child.  A node without a
+// draft row is decided here (it draws from p) by its chunk-0 workgroup.
 template <typename TZ, typename TQ>
 __global__ __launch_bounds__(256) void k_samp_stats(SArgs a) {
 #pragma clang fp contract(off)
-  __shared__ double sm[4][4];
+  __shared__ double sm[8];
   __shared__ int s_kids[kMaxKids], s_tok[kMaxKids], s_cnt[4], s_last;
   const int g = blockIdx.x / a.nch, c = blockIdx.x % a.nch;
   const int b = find_request(a.cu_nodes, a.B, g);
@@ -257,73 +367,75 @@ __global__ __launch_bounds__(256) void k_samp_stats(SArgs a) {
     return;
   }
   const int r = a.draft_row[g];
-  const bool has_q = r >= 0 && r < a.R;
+  if (r < 0 || r >= a.R) {
+    if (c != 0) return;
+    const int nk = node_children(a, n0, n, i, s_kids, s_tok, s_cnt);
+    if (threadIdx.x != 0) return;
+    if (nk > 0 && a.dev_status) atomicOr(a.dev_status, EAGLE3_DEV_BAD_ROW);
+    NodeSt s = {};
+    s.status = ST_DRAW;
+    s.kept = -1;
+    a.st[g] = s;
+    return;
+  }
+  __shared__ double s_exp[64];
+  exp2_table(s_exp);
   const TZ* zrow = (const TZ*)a.logits + (size_t)g * a.V;
-  const TQ* qrow = (const TQ*)a.dlogits + (size_t)(has_q ? r : 0) * a.V;
+  const TQ* qrow = (const TQ*)a.dlogits + (size_t)r * a.V;
   const int tb = c * SC + 16 * threadIdx.x;
-  double ma = kNegInfD, sa = 0.0, mb = kNegInfD, sb = 0.0;
-  if (tb < a.V) {
-    const int ne = min(16, a.V - tb);
+  const int ne = min(16, a.V - tb);      // <= 0 past the vocabulary
+  double va[16], vb[16];
+  {
     float z[16];
-    double v[16];
     load_chunk(zrow, tb, a.V, a.az, z);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      v[e] = (double)z[e] / a.temp;
-      if (e < ne && v[e] > ma) ma = v[e];
-    }
-    sa = 0.0;
+    for (int e = 0; e < 16; ++e) va[e] = e < ne ? (double)z[e] * a.invT : kNegInfD;
+    load_chunk(qrow, tb, a.V, a.aq, z);
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      if (e < ne) sa = sa + exp(v[e] - ma);
-    if (has_q) {
-      load_chunk(qrow, tb, a.V, a.aq, z);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        v[e] = (double)z[e] / a.temp;
-        if (e < ne && v[e] > mb) mb = v[e];
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (e < ne) sb = sb + exp(v[e] - mb);
-    }
+    for (int e = 0; e < 16; ++e) vb[e] = e < ne ? (double)z[e] * a.invT : kNegInfD;
   }
-  wave_lse(ma, sa);
-  wave_lse(mb, sb);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if (lane == 0) {
-    sm[w][0] = ma;
-    sm[w][1] = sa;
-    sm[w][2] = mb;
-    sm[w][3] = sb;
+  double ma = kNegInfD, mb = kNegInfD;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    ma = fmax(ma, va[e]);
+    mb = fmax(mb, vb[e]);
   }
-  __syncthreads();
+  block_max2(ma, mb, sm);
+  double sa = 0.0, sb = 0.0;
+  if (ma != kNegInfD) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sa = sa + exp_tab(va[e] - ma, s_exp);
+  }
+  if (mb != kNegInfD) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sb = sb + exp_tab(vb[e] - mb, s_exp);
+  }
+  block_sum2(sa, sb, sm);
   if (threadIdx.x == 0) {
-    for (int q = 1; q < 4; ++q) {
-      lse_add(ma, sa, sm[q][0], sm[q][1]);
-      lse_add(mb, sb, sm[q][2], sm[q][3]);
-    }
-    double* p = a.part + ((size_t)g * a.nch + c) * 4;
-    p[0] = ma;
-    p[1] = sa;
-    p[2] = mb;
-    p[3] = sb;
+    uint64_t* p = a.p_stats + ((size_t)g * a.nch + c) * 4;
+    put_d(p + 0, ma);
+    put_d(p + 1, sa);
+    put_d(p + 2, mb);
+    put_d(p + 3, sb);
   }
   if (!finish_chunk(a, g, &s_last)) return;
   const int nk = node_children(a, n0, n, i, s_kids, s_tok, s_cnt);
   if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
   double MA = kNegInfD, SA = 0.0, MB = kNegInfD, SB = 0.0;
   for (int cc = lane; cc < a.nch; cc += 64) {
-    const double* p = a.part + ((size_t)g * a.nch + cc) * 4;
-    lse_add(MA, SA, p[0], p[1]);
-    lse_add(MB, SB, p[2], p[3]);
+    uint64_t* p = a.p_stats + ((size_t)g * a.nch + cc) * 4;
+    const double m0 = get_d(p + 0, a.dev_status), s0 = get_d(p + 1, a.dev_status);
+    const double m1 = get_d(p + 2, a.dev_status), s1 = get_d(p + 3, a.dev_status);
+    lse_add(MA, SA, m0, s0);
+    lse_add(MB, SB, m1, s1);
   }
   wave_lse(MA, SA);
   wave_lse(MB, SB);
   if (lane != 0) return;
   NodeSt s;
   s.A = MA + log(SA);
-  s.Bq = has_q ? MB + log(SB) : 0.0;
+  s.Bq = MB + log(SB);
   s.lam = 0.0;
   s.lam_prev = 0.0;
   s.N = 1.0;
@@ -336,10 +448,9 @@ __global__ __launch_bounds__(256) void k_samp_stats(SArgs a) {
   s.nk = nk;
   s.pad = 0;
   s.status = ST_DRAW;
-  if (nk > 0 && !has_q && a.dev_status) atomicOr(a.dev_status, EAGLE3_DEV_BAD_ROW);
   for (int k = 0; k < nk; ++k)
     if ((s_tok[k] < 0 || s_tok[k] >= a.V) && a.dev_status) atomicOr(a.dev_status, EAGLE3_DEV_BAD_TOKEN);
-  const int k0 = has_q ? next_valid(s_tok, nk, a.V, 0) : -1;
+  const int k0 = next_valid(s_tok, nk, a.V, 0);
   if (k0 >= 0) {
     s.k = k0;
     s.m = 1;
@@ -347,7 +458,7 @@ __global__ __launch_bounds__(256) void k_samp_stats(SArgs a) {
   }
   a.st[g] = s;
   a.cnt[g] = 0;
-  enqueue(a, s, g);
+  enqueue_need(a, s, g);
 }
 
 // Pass m (2 .. maxc): N at the node's current lam, for the nodes on list m; the last chunk
@@ -355,11 +466,14 @@ __global__ __launch_bounds__(256) void k_samp_stats(SArgs a) {
 template <typename TZ, typename TQ>
 __global__ __launch_bounds__(256) void k_samp_npass(SArgs a, int m) {
 #pragma clang fp contract(off)
-  __shared__ double sd[4];
-  __shared__ int si[4];
+  __shared__ double sm[8];
   __shared__ int s_kids[kMaxKids], s_tok[kMaxKids], s_cnt[4], s_last;
+  __shared__ double s_exp[64];
   const int items = a.list_n[m] * a.nch;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if ((int)blockIdx.x >= items) return;
+  exp2_table(s_exp);
+  const int lane = threadIdx.x & 63;
+  uint64_t* pn = a.p_n + (size_t)(m - 2) * a.T * a.nch;
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
     const int g = a.lists[(size_t)m * a.T + it / a.nch];
     const int c = it % a.nch;
@@ -367,45 +481,26 @@ __global__ __launch_bounds__(256) void k_samp_npass(SArgs a, int m) {
     const int r = a.draft_row[g];
     const TZ* zrow = (const TZ*)a.logits + (size_t)g * a.V;
     const TQ* qrow = (const TQ*)a.dlogits + (size_t)r * a.V;
-    const double ln_lam = log(s0.lam);
     const int tb = c * SC + 16 * threadIdx.x;
-    double acc = 0.0;
-    int pos = 0;
-    if (tb < a.V) {
-      const int ne = min(16, a.V - tb);
+    const int ne = min(16, a.V - tb);
+    double acc = 0.0, pos = 0.0;
+    {
       float z[16], zq[16];
       load_chunk(zrow, tb, a.V, a.az, z);
       load_chunk(qrow, tb, a.V, a.aq, zq);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        if (e >= ne) continue;
-        const double la = (double)z[e] / a.temp - s0.A;
-        const double lb = (double)zq[e] / a.temp - s0.Bq;
-        const bool skip = la - lb - ln_lam < kSkipMargin;
-        if (skip && m != 2) continue;
-        const double eb = exp(lb);
-        pos += eb > 0.0;
-        if (skip) continue;
-        const double d = exp(la) - s0.lam * eb;
-        if (d > 0.0) acc = acc + d;
+        const double pe = e < ne ? exp_tab((double)z[e] * a.invT - s0.A, s_exp) : 0.0;
+        const double qe = e < ne ? exp_tab((double)zq[e] * a.invT - s0.Bq, s_exp) : 0.0;
+        const double d = pe - s0.lam * qe;
+        acc = acc + (d > 0.0 ? d : 0.0);
+        pos = pos + (qe > 0.0 ? 1.0 : 0.0);
       }
     }
-    acc = wave_sum_d(acc);
-    pos = wave_sum_i(pos);
-    if (lane == 0) {
-      sd[w] = acc;
-      si[w] = pos;
-    }
-    __syncthreads();
+    block_sum2(acc, pos, sm);
     if (threadIdx.x == 0) {
-      double t = sd[0];
-      int pt = si[0];
-      for (int q = 1; q < 4; ++q) {
-        t = t + sd[q];
-        pt += si[q];
-      }
-      a.part[((size_t)g * a.nch + c) * 4] = t;
-      a.part_i[(size_t)g * a.nch + c] = pt;
+      put_d(pn + (size_t)g * a.nch + c, acc);
+      if (m == 2) put_i(a.p_pos + (size_t)g * a.nch + c, (int)pos);
     }
     if (finish_chunk(a, g, &s_last)) {
       const int b = find_request(a.cu_nodes, a.B, g);
@@ -416,8 +511,8 @@ __global__ __launch_bounds__(256) void k_samp_npass(SArgs a, int m) {
         double N = 0.0;
         int np = 0;
         for (int cc = lane; cc < a.nch; cc += 64) {
-          N = N + a.part[((size_t)g * a.nch + cc) * 4];
-          np += a.part_i[(size_t)g * a.nch + cc];
+          N = N + get_d(pn + (size_t)g * a.nch + cc, a.dev_status);
+          if (m == 2) np += get_i(a.p_pos + (size_t)g * a.nch + cc, a.dev_status);
         }
         N = wave_sum_d(N);
         np = wave_sum_i(np);
@@ -426,7 +521,7 @@ __global__ __launch_bounds__(256) void k_samp_npass(SArgs a, int m) {
           chain_step(a, s, s_kids, s_tok, b, zrow, qrow, true, N, np);
           a.st[g] = s;
           a.cnt[g] = 0;
-          enqueue(a, s, g);
+          enqueue_need(a, s, g);
         }
       }
     }
@@ -434,15 +529,61 @@ __global__ __launch_bounds__(256) void k_samp_npass(SArgs a, int m) {
   }
 }
 
-// Residual draw for the nodes on list 0: argmax over t of ln max(p_t - lam q_t, 0) + G_t
-// (for lam = 0: ln p_t = z_t / T - A), G the node's Gumbel noise.
+// Walk each request from its root through the kept children; its end node either ends on a
+// kept child at max_depth (that child's token is the bonus) or is queued for the draw.
+__global__ __launch_bounds__(64) void k_samp_walk(SArgs a) {
+  if (threadIdx.x != 0) return;
+  const int b = blockIdx.x;
+  const int P = a.max_depth + 1;
+  const int n0 = clampi(a.cu_nodes[b], 0, a.T);
+  const int n1 = clampi(a.cu_nodes[b + 1], n0, a.T);
+  int32_t* pth = a.path + (size_t)b * P;
+  int32_t* out = a.out_tokens + (size_t)b * P;
+  int s = 0;
+  if (n1 > n0) {
+    int i = 0;
+    pth[0] = 0;
+    for (;;) {
+      const NodeSt st = a.st[n0 + i];
+      if (st.status == ST_KEPT) {
+        const int j = st.kept;
+        if (s == a.max_depth) {     // deeper than the caller's bound: the kept child is the bonus
+          out[s] = a.tokens[n0 + j];
+          a.bonus[b] = a.tokens[n0 + j];
+          break;
+        }
+        ++s;
+        pth[s] = j;
+        out[s - 1] = a.tokens[n0 + j];
+        i = j;
+        continue;
+      }
+      const int at = atomicAdd(&a.list_n[0], 1);
+      a.lists[at] = n0 + i;
+      break;
+    }
+  } else {
+    a.bonus[b] = -1;
+  }
+  for (int k = n1 > n0 ? s + 1 : 0; k < P; ++k) {
+    pth[k] = -1;
+    out[k] = -1;
+  }
+  a.accept_len[b] = s;
+}
+
+// Draw at the end nodes: argmax over t of ln max(p_t - lam q_t, 0) + G_t, G the node's Gumbel
+// noise; with no rejection (lam = 0) the argmax of z_t / T + G_t (ln p_t up to a constant).
 template <typename TZ, typename TQ>
 __global__ __launch_bounds__(256) void k_samp_draw(SArgs a) {
 #pragma clang fp contract(off)
   __shared__ double sv[4];
   __shared__ int sx[4];
   __shared__ int s_last;
+  __shared__ double s_exp[64];
   const int items = a.list_n[0] * a.nch;
+  if ((int)blockIdx.x >= items) return;
+  exp2_table(s_exp);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
     const int g = a.lists[it / a.nch];
@@ -454,7 +595,6 @@ __global__ __launch_bounds__(256) void k_samp_draw(SArgs a) {
     const int r = plain ? 0 : a.draft_row[g];
     const TZ* zrow = (const TZ*)a.logits + (size_t)g * a.V;
     const TQ* qrow = (const TQ*)a.dlogits + (size_t)r * a.V;
-    const double ln_lam = plain ? 0.0 : log(s0.lam);
     const int tb = c * SC + 16 * threadIdx.x;
     double best = kNegInfD;
     int bi = 0x7fffffff;
@@ -470,16 +610,13 @@ __global__ __launch_bounds__(256) void k_samp_draw(SArgs a) {
         for (int u = 0; u < 4; ++u) {
           const int e = 4 * q + u, t = tb + e;
           if (t >= a.V) continue;
-          const double la = (double)z[e] / a.temp - s0.A;
           double v;
           if (plain) {
-            v = la;
+            v = (double)z[e] * a.invT;
           } else {
-            const double lb = (double)zq[e] / a.temp - s0.Bq;
-            if (la - lb - ln_lam < kSkipMargin) continue;
-            const double d = exp(la) - s0.lam * exp(lb);
-            if (!(d > 0.0)) continue;
-            v = log(d);
+            const double d = exp_tab((double)z[e] * a.invT - s0.A, s_exp) -
+                             s0.lam * exp_tab((double)zq[e] * a.invT - s0.Bq, s_exp);
+            v = d > 0.0 ? log(d) : kNegInfD;
           }
           v = v + (double)gumbel_from_word(ctr[u]);
           if (better_d(v, t, best, bi)) {
@@ -501,15 +638,15 @@ __global__ __launch_bounds__(256) void k_samp_draw(SArgs a) {
           best = sv[q];
           bi = sx[q];
         }
-      a.part[((size_t)g * a.nch + c) * 4] = best;
-      a.part_i[(size_t)g * a.nch + c] = bi;
+      put_d(a.p_dv + (size_t)g * a.nch + c, best);
+      put_i(a.p_di + (size_t)g * a.nch + c, bi);
     }
     if (finish_chunk(a, g, &s_last) && threadIdx.x < 64) {
       double bv = kNegInfD;
       int bx = 0x7fffffff;
       for (int cc = lane; cc < a.nch; cc += 64) {
-        const double v = a.part[((size_t)g * a.nch + cc) * 4];
-        const int x = a.part_i[(size_t)g * a.nch + cc];
+        const double v = get_d(a.p_dv + (size_t)g * a.nch + cc, a.dev_status);
+        const int x = get_i(a.p_di + (size_t)g * a.nch + cc, a.dev_status);
         if (better_d(v, x, bv, bx)) {
           bv = v;
           bx = x;
@@ -517,7 +654,10 @@ __global__ __launch_bounds__(256) void k_samp_draw(SArgs a) {
       }
       wave_argmax_d(bv, bx);
       if (lane == 0) {
-        a.ydraw[g] = bx < a.V ? bx : 0;
+        const int y = bx < a.V ? bx : 0;
+        const int L = a.accept_len[b];
+        a.out_tokens[(size_t)b * (a.max_depth + 1) + L] = y;
+        a.bonus[b] = y;
         a.cnt[g] = 0;
       }
     }
@@ -525,47 +665,11 @@ __global__ __launch_bounds__(256) void k_samp_draw(SArgs a) {
   }
 }
 
-// Walk each request from its root through the kept children.
-__global__ __launch_bounds__(64) void k_samp_walk(SArgs a, int32_t* accept_len, int32_t* path,
-                                                  int32_t* out_tokens, int32_t* bonus) {
-  if (threadIdx.x != 0) return;
-  const int b = blockIdx.x;
-  const int P = a.max_depth + 1;
-  const int n0 = clampi(a.cu_nodes[b], 0, a.T);
-  const int n1 = clampi(a.cu_nodes[b + 1], n0, a.T);
-  int32_t* pth = path + (size_t)b * P;
-  int32_t* out = out_tokens + (size_t)b * P;
-  int s = 0, y = -1;
-  if (n1 > n0) {
-    int i = 0;
-    pth[0] = 0;
-    for (;;) {
-      const NodeSt st = a.st[n0 + i];
-      if (st.status == ST_KEPT && s < a.max_depth) {
-        const int j = st.kept;
-        ++s;
-        pth[s] = j;
-        out[s - 1] = a.tokens[n0 + j];
-        i = j;
-        continue;
-      }
-      y = st.status == ST_KEPT ? a.tokens[n0 + st.kept] : a.ydraw[n0 + i];
-      break;
-    }
-    out[s] = y;
-  }
-  for (int k = n1 > n0 ? s + 1 : 0; k < P; ++k) {
-    pth[k] = -1;
-    out[k] = -1;
-  }
-  accept_len[b] = s;
-  bonus[b] = y;
-}
-
 struct SampLayout {
   NodeSt* st;
-  int *cnt, *lists, *list_n, *part_i, *ydraw;
-  double* part;
+  int *cnt, *lists, *list_n, *p_pos, *p_di;
+  uint64_t *p_stats, *p_n, *p_dv;
+  size_t bytes;
 };
 
 SampLayout carve_sampled(void* ws, int T, int nch, int maxc) {
@@ -575,16 +679,18 @@ SampLayout carve_sampled(void* ws, int T, int nch, int maxc) {
   L.cnt = c.take<int>((size_t)T);
   L.lists = c.take<int>((size_t)(maxc + 1) * T);
   L.list_n = c.take<int>((size_t)(maxc + 1));
-  L.part = c.take<double>((size_t)T * nch * 4);
-  L.part_i = c.take<int>((size_t)T * nch);
-  L.ydraw = c.take<int>((size_t)T);
+  L.p_stats = c.take<uint64_t>((size_t)T * nch * 4);
+  L.p_n = c.take<uint64_t>((size_t)(maxc > 1 ? maxc - 1 : 1) * T * nch);
+  L.p_pos = c.take<int>((size_t)T * nch);
+  L.p_dv = c.take<uint64_t>((size_t)T * nch);
+  L.p_di = c.take<int>((size_t)T * nch);
+  L.bytes = c.size();
   return L;
 }
 
 template <typename TZ, typename TQ>
-void launch_typed(const SArgs& a, int32_t* accept_len, int32_t* path, int32_t* out_tokens,
-                  int32_t* bonus, hipStream_t s) {
-  const int grid = (int)std::min<long>((long)a.T * a.nch, 2048);
+void launch_typed(const SArgs& a, hipStream_t s) {
+  const int grid = (int)std::min<long>((long)a.T * a.nch, 512);
   {
     e3h::ProfScope ps("sampled_stats", s);
     hipLaunchKernelGGL((k_samp_stats<TZ, TQ>), dim3((unsigned)((long)a.T * a.nch)), dim3(256), 0, s, a);
@@ -594,11 +700,12 @@ void launch_typed(const SArgs& a, int32_t* accept_len, int32_t* path, int32_t* o
     hipLaunchKernelGGL((k_samp_npass<TZ, TQ>), dim3(grid), dim3(256), 0, s, a, m);
   }
   {
-    e3h::ProfScope ps("sampled_draw", s);
-    hipLaunchKernelGGL((k_samp_draw<TZ, TQ>), dim3(grid), dim3(256), 0, s, a);
+    e3h::ProfScope ps("sampled_walk", s);
+    hipLaunchKernelGGL(k_samp_walk, dim3(a.B), dim3(64), 0, s, a);
   }
-  e3h::ProfScope ps("sampled_walk", s);
-  hipLaunchKernelGGL(k_samp_walk, dim3(a.B), dim3(64), 0, s, a, accept_len, path, out_tokens, bonus);
+  e3h::ProfScope ps("sampled_draw", s);
+  hipLaunchKernelGGL((k_samp_draw<TZ, TQ>), dim3((unsigned)std::min<long>((long)a.B * a.nch, 1024)), dim3(256),
+                     0, s, a);
 }
 
 }  // namespace
@@ -606,16 +713,7 @@ void launch_typed(const SArgs& a, int32_t* accept_len, int32_t* path, int32_t* o
 namespace e3h {
 
 size_t accept_sampled_workspace(int T, int V, int max_children) {
-  const int nch = (V + SC - 1) / SC;
-  Carve c(nullptr);
-  c.take<NodeSt>((size_t)T);
-  c.take<int>((size_t)T);
-  c.take<int>((size_t)(max_children + 1) * T);
-  c.take<int>((size_t)(max_children + 1));
-  c.take<double>((size_t)T * nch * 4);
-  c.take<int>((size_t)T * nch);
-  c.take<int>((size_t)T);
-  return c.size();
+  return carve_sampled(nullptr, T, (V + SC - 1) / SC, max_children).bytes;
 }
 
 int accept_sampled_max_children() { return kMaxKids; }
@@ -646,7 +744,7 @@ int launch_accept_sampled(int B, int T, const int32_t* cu_nodes, const int32_t* 
   a.max_depth = max_depth;
   a.az = ((size_t)V * elem_size(dtype)) % 16 == 0 && (uintptr_t)logits % 16 == 0;
   a.aq = draft_logits && ((size_t)V * elem_size(draft_dtype)) % 16 == 0 && (uintptr_t)draft_logits % 16 == 0;
-  a.temp = (double)temperature;
+  a.invT = 1.0 / (double)temperature;
   a.seed_lo = (uint32_t)seed;
   a.seed_hi = (uint32_t)(seed >> 32);
   a.rnd = (uint32_t)round;
@@ -654,28 +752,36 @@ int launch_accept_sampled(int B, int T, const int32_t* cu_nodes, const int32_t* 
   a.cnt = L.cnt;
   a.lists = L.lists;
   a.list_n = L.list_n;
-  a.part = L.part;
-  a.part_i = L.part_i;
-  a.ydraw = L.ydraw;
+  a.p_stats = L.p_stats;
+  a.p_n = L.p_n;
+  a.p_pos = L.p_pos;
+  a.p_dv = L.p_dv;
+  a.p_di = L.p_di;
+  a.accept_len = accept_len;
+  a.path = path;
+  a.out_tokens = out_tokens;
+  a.bonus = bonus;
   a.dev_status = dev_status;
   {
     e3h::ProfScope ps("sampled_clear", s);
-    const int nthreads = std::max(T, max_children + 1);
-    hipLaunchKernelGGL(k_samp_clear, dim3((nthreads + 255) / 256), dim3(256), 0, s, L.cnt, T, L.list_n,
-                       max_children + 1);
+    const int n_stats = T * nch * 4;
+    const int n_n = (max_children > 1 ? max_children - 1 : 1) * T * nch;
+    const int n_one = T * nch;
+    const int nthreads = std::max({T, max_children + 1, n_stats, n_n, n_one});
+    hipLaunchKernelGGL(k_samp_clear, dim3((nthreads + 255) / 256), dim3(256), 0, s, a, n_stats, n_n, n_one);
   }
   int st = launch_status();
   if (st) return st;
   const bool zb = dtype == EAGLE3_BF16;
   const bool qb = (draft_logits ? draft_dtype : dtype) == EAGLE3_BF16;
   if (zb && qb)
-    launch_typed<bf16, bf16>(a, accept_len, path, out_tokens, bonus, s);
+    launch_typed<bf16, bf16>(a, s);
   else if (zb)
-    launch_typed<bf16, float>(a, accept_len, path, out_tokens, bonus, s);
+    launch_typed<bf16, float>(a, s);
   else if (qb)
-    launch_typed<float, bf16>(a, accept_len, path, out_tokens, bonus, s);
+    launch_typed<float, bf16>(a, s);
   else
-    launch_typed<float, float>(a, accept_len, path, out_tokens, bonus, s);
+    launch_typed<float, float>(a, s);
   return launch_status();
 }
 

@@ -38,11 +38,17 @@ def tree_depth(trees):
     return best
 
 
+SYNC = 32      # a partial handed between workgroups was not seen within the bounded wait
+
+
 def gpu_run(d, temp, seed, rnd, max_depth, maxc, status=None):
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
     out = capi.eagle3_accept_sampled(d["cu_nodes"], d["tokens"], d["parents"], d["logits"],
                                      d["draft_logits"], d["draft_row"], temp, seed, rnd, max_depth,
                                      maxc, dev_status=status)
     torch.cuda.synchronize()
+    assert not int(status.item()) & SYNC
     return [out[k].cpu().numpy() for k in KEYS]
 
 
