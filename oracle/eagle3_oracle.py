@@ -276,9 +276,15 @@ def expand_tree(D: int, K: int, W: int, N: int, root_token: int,
         new = []
         for v in frontier:
             r = results[v["slot"]]
+            run = None
             for rank in range(K):
+                # a child never scores above a sibling created before it (for a top-K list, whose
+                # values fall with the rank, this changes nothing; for sampled children it keeps
+                # every kept sibling set a prefix of the draw order)
+                sc = child_score(v["score"], r["topk_vals"][rank], r["lse"])
+                run = sc if run is None else min(run, sc)
                 c = {"token": int(r["topk_ids"][rank]), "parent_slot": v["slot"],
-                     "depth": t, "score": child_score(v["score"], r["topk_vals"][rank], r["lse"]),
+                     "depth": t, "score": _f32(run),
                      "creation": len(cands), "slot": -1}
                 cands.append(c)
                 new.append(c)
@@ -823,6 +829,35 @@ def accept_uniform(seed: int, rnd: int, b: int, j: int) -> float:
     (ACCEPT_UNIFORM_C0, j, b, round), key (seed lo, seed hi), word 0, mapped as uniform23."""
     w = philox4x32_10(ACCEPT_UNIFORM_C0, j, b, rnd & MASK32, seed & MASK32, (seed >> 32) & MASK32)
     return float(uniform23(w[0]))
+
+
+DRAFT_NOISE_C1 = 0x80000000      # counter word 1 of the drafter's noise: above every node index
+
+
+def draft_gumbel(seed: int, rnd: int, b: int, slot: int, t: np.ndarray) -> np.ndarray:
+    """The drafter's Gumbel noise at evaluation slot `slot` of request b: as `gumbel`, with
+    counter word 1 = DRAFT_NOISE_C1 | slot (a stream apart from the verifier's)."""
+    t = np.asarray(t, dtype=np.uint64)
+    n = t.shape[0]
+    w = philox4x32_10(t >> np.uint64(2), np.full(n, DRAFT_NOISE_C1 | slot), np.full(n, b),
+                      np.full(n, rnd & MASK32), np.full(n, seed & MASK32),
+                      np.full(n, (seed >> 32) & MASK32))
+    x = np.choose((t & np.uint64(3)).astype(np.int64), w)
+    u = uniform23(x)
+    return (-ln_spec(-ln_spec(u))).astype(np.float32)
+
+
+def sample_children(z_row, temperature: float, K: int, seed: int, rnd: int, b: int, slot: int):
+    """K children drawn without replacement from softmax(z / T) by the Gumbel-top-K rule: the K
+    best tokens by zs_t + G_t (zs = z * invT, invT = 1/T, each rounded to float32, then the sum
+    rounded; ties to the lowest id), best first, which is the order they are drawn in.
+    Returns (ids, zs at the ids) -- the scaled logits without noise, which the scores use."""
+    z = np.asarray(z_row, dtype=np.float32)
+    invT = np.float32(1.0) / np.float32(temperature)
+    zs = (z * invT).astype(np.float32)
+    v = (zs + draft_gumbel(seed, rnd, b, slot, np.arange(z.shape[0]))).astype(np.float32)
+    ids = np.lexsort((np.arange(z.shape[0]), -v.astype(np.float64)))[:K]
+    return ids.astype(np.int64), zs[ids]
 
 
 def accept_sampled(cu_nodes, tokens, parents, logits, draft_logits, draft_row,

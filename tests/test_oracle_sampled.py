@@ -185,3 +185,66 @@ def test_walk_is_lossless_chi_square():
     assert dof >= 10
     from scipy.stats import chi2 as C
     assert C.sf(chi2, dof) > 1e-3, (chi2, dof)
+
+
+# ---- the drafter's side: children drawn without replacement ----------------------------
+
+
+def test_sample_children_is_drawing_without_replacement():
+    """Ordered pairs drawn by the Gumbel-top-2 rule over many rounds follow
+    q(x1) q(x2) / (1 - q(x1)), q = softmax(z / T) (chi-square over all 20 ordered pairs)."""
+    V, T, n = 5, 0.8, 12000
+    z = np.array([0.3, -1.0, 1.2, 0.0, 0.7], dtype=np.float32)
+    q = O.softmax64(z, T)
+    cnt = np.zeros((V, V))
+    for rnd in range(n):
+        ids, _ = O.sample_children(z, T, 2, 5, rnd, 1, 3)
+        cnt[ids[0], ids[1]] += 1
+    exp = np.array([[q[a] * q[b] / (1 - q[a]) if a != b else 0 for b in range(V)] for a in range(V)]) * n
+    m = exp > 0
+    chi = ((cnt[m] - exp[m]) ** 2 / exp[m]).sum()
+    from scipy.stats import chi2 as C
+    assert C.sf(chi, m.sum() - 1) > 1e-3, chi
+    assert np.all(cnt[~m] == 0)
+
+
+def test_sample_children_values_and_order():
+    rng = np.random.default_rng(2)
+    z = rng.normal(size=300).astype(np.float32) * 3
+    ids, zs = O.sample_children(z, 0.7, 8, 11, 4, 0, 17)
+    assert len(set(ids.tolist())) == 8
+    invT = np.float32(1) / np.float32(0.7)
+    np.testing.assert_array_equal(zs, (z[ids] * invT).astype(np.float32))
+    g = O.draft_gumbel(11, 4, 0, 17, np.arange(300))
+    v = ((z * invT).astype(np.float32) + g).astype(np.float32)
+    assert np.all(np.diff(v[ids].astype(np.float64)) <= 0)          # drawn best first
+    assert v[ids[-1]] >= np.sort(v)[-8]                              # and they are the 8 best
+    # the drafter's stream is not the verifier's
+    assert not np.array_equal(g, O.gumbel(11, 4, 0, 17, np.arange(300)))
+
+
+def test_expand_tree_scores_keep_sibling_prefixes():
+    """With children listed in draw order (values not sorted), a child's score never exceeds
+    an earlier sibling's; with a sorted top-K list the scores are the plain cumulative ones."""
+    vals = {0: [-0.5, -0.1, -2.0, -0.3], 1: [-1.0, -3.0, -0.2, -0.4]}
+
+    def evaluate(t, nodes):
+        out = []
+        for nd in nodes:
+            v = np.array(vals[min(t, 1)], dtype=np.float32)
+            out.append({"topk_ids": np.arange(4) + 10 * t, "topk_vals": v, "lse": np.float32(0.0)})
+        return out
+    tr = O.expand_tree(3, 4, 2, 12, 7, evaluate)
+    by_parent = {}
+    for c in tr["cands"]:
+        by_parent.setdefault((c["parent_slot"], c["depth"]), []).append(float(c["score"]))
+    for sc in by_parent.values():
+        assert all(b <= a for a, b in zip(sc, sc[1:]))
+    root_kids = by_parent[(0, 1)]
+    assert root_kids == [-0.5, -0.5, -2.0, -2.0]
+
+    def evaluate_sorted(t, nodes):
+        return [{"topk_ids": np.arange(4), "topk_vals": np.array([-0.1, -0.3, -0.5, -2.0], np.float32),
+                 "lse": np.float32(0.0)} for _ in nodes]
+    tr = O.expand_tree(2, 4, 2, 8, 7, evaluate_sorted)
+    assert [float(c["score"]) for c in tr["cands"][:4]] == [float(np.float32(x)) for x in (-0.1, -0.3, -0.5, -2.0)]
