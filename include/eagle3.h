@@ -160,6 +160,36 @@ EAGLE3_API int eagle3_draft_expand(const eagle3_drafter* w, const eagle3_tree_cf
                         void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * eagle3_draft_expand_sampled -- the draft-tree round with sampled candidates.  [P1] 推理流程
+ * and [P2] 三、EAGLE-3 (the draft head outputs a distribution over the vocabulary and the next
+ * token is drawn from it); [P2] 四 DFlash (drafted tokens are later kept with probability
+ * min(1, p_target / p_draft), which needs the drafter's distribution at every node).
+ *
+ * As eagle3_draft_expand, except that every evaluated node's children are K draws without
+ * replacement from softmax(z / T) (the K best of z * invT + G, invT = 1/T in fp32, G Gumbel
+ * noise from Philox4x32-10 with counter (t>>2, 0x80000000 | slot, b, round mod 2^32), key
+ * (seed lo, seed hi), word t & 3; u and G as in eagle3_accept), listed in draw order; the
+ * log-sum-exp is that of z * invT; a child's score is s_v + (z[t] * invT - lse), lowered to
+ * the score of any sibling drawn before it (so the siblings a budget keeps are always the
+ * first ones drawn, as eagle3_accept_sampled requires).
+ *
+ *  slot_logits : [B * S, V] fp32 (16-byte aligned)  every evaluated slot's logits (raw z)
+ *  draft_row   : [B, N+1] int32  row of slot_logits holding node i's logits (the drafter's
+ *                distribution at that node), -1 for a node that was not evaluated (it has no
+ *                children); pass it, flattened like the tree, to eagle3_accept_sampled
+ *  temperature > 0; other arguments, limits and the workspace as for eagle3_draft_expand.
+ * ------------------------------------------------------------------------------------ */
+EAGLE3_API int eagle3_draft_expand_sampled(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B,
+                                           float temperature, uint64_t seed, uint64_t round,
+                                           const void* h_low, const void* h_mid, const void* h_high,
+                                           const int32_t* root_tok, const void* kpre, const void* vpre,
+                                           const int32_t* cu_prefix, int max_prefix, int32_t* tokens,
+                                           int32_t* parents, int32_t* depth, float* score,
+                                           int32_t* n_nodes, float* slot_logits, int32_t* draft_row,
+                                           const eagle3_draft_debug* dbg, void* workspace,
+                                           size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * eagle3_build_tree_mask -- pack flattened trees: ancestor bitmask, depth and position.
  * [P2] 二、EAGLE-2动态草稿树 (flatten the tree, add positions, build the 0/1 tree attention
  * mask so a node sees only itself and its ancestors); [P5] 一棵候选树怎样被验证 (assign each

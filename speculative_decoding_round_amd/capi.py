@@ -68,6 +68,11 @@ EXPORTS = {
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                     c_size_t, c_void_p]),
+    "eagle3_draft_expand_sampled": (c_int, [c_void_p, c_void_p, c_int, c_float, c_uint64, c_uint64,
+                                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                            c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                            c_void_p]),
     "eagle3_build_tree_mask": (c_int, [c_int, c_int, c_void_p, c_void_p, c_void_p, c_int,
                                        c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
     "eagle3_tree_attention_num_splits": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int]),
@@ -258,6 +263,63 @@ def eagle3_draft_expand(drafter: Eagle3Drafter, tree: Eagle3TreeCfg, h_low, h_mi
         ctypes.byref(dbg_struct) if dbg_struct is not None else None,
         workspace.data_ptr(), workspace.numel(), _stream(stream))
     _check("eagle3_draft_expand", st)
+    return out
+
+
+def eagle3_draft_expand_sampled(drafter: Eagle3Drafter, tree: Eagle3TreeCfg, temperature: float,
+                                seed: int, round: int, h_low, h_mid, h_high, root_tok, kpre, vpre,
+                                cu_prefix, max_prefix: int, debug: bool = False,
+                                workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None,
+                                stream=None) -> dict:
+    """The draft-tree round with sampled candidates.  Returns dict(tokens, parents, depth, score,
+    n_nodes, slot_logits [B, S, V] fp32, draft_row [B, N+1] (row of slot_logits viewed as
+    [B*S, V] at each node, -1 when the node was not evaluated)[, debug])."""
+    B = h_low.shape[0]
+    dev = h_low.device
+    dt = h_low.dtype
+    for n, t in (("h_low", h_low), ("h_mid", h_mid), ("h_high", h_high), ("kpre", kpre),
+                 ("vpre", vpre)):
+        _dev(t, n, dt)
+    _dev(root_tok, "root_tok", torch.int32)
+    _dev(cu_prefix, "cu_prefix", torch.int32)
+    N1 = tree.n_nodes + 1
+    S = 1 + (tree.depth - 1) * tree.width
+    if out is None:
+        out = {
+            "tokens": torch.empty((B, N1), dtype=torch.int32, device=dev),
+            "parents": torch.empty((B, N1), dtype=torch.int32, device=dev),
+            "depth": torch.empty((B, N1), dtype=torch.int32, device=dev),
+            "score": torch.empty((B, N1), dtype=torch.float32, device=dev),
+            "n_nodes": torch.empty((B,), dtype=torch.int32, device=dev),
+            "slot_logits": torch.zeros((B, S, drafter.vocab), dtype=torch.float32, device=dev),
+            "draft_row": torch.empty((B, N1), dtype=torch.int32, device=dev),
+        }
+    dbg_struct = None
+    if debug:
+        K, d = tree.topk, drafter.d
+        dbg = {
+            "g": torch.empty((B, d), dtype=torch.float32, device=dev),
+            "slot_token": torch.empty((B, S), dtype=torch.int32, device=dev),
+            "slot_parent": torch.empty((B, S), dtype=torch.int32, device=dev),
+            "slot_a": torch.zeros((B, S, d), dtype=torch.float32, device=dev),
+            "slot_topk_id": torch.full((B, S, K), -1, dtype=torch.int32, device=dev),
+            "slot_topk_val": torch.zeros((B, S, K), dtype=torch.float32, device=dev),
+            "slot_lse": torch.zeros((B, S), dtype=torch.float32, device=dev),
+        }
+        dbg_struct = Eagle3DraftDebug(**{k: v.data_ptr() for k, v in dbg.items()})
+        dbg["slot_logits"] = out["slot_logits"]
+        out["debug"] = dbg
+    if workspace is None:
+        workspace = _workspace(eagle3_draft_expand_workspace_size(drafter, tree, B, max_prefix), dev)
+    st = lib().eagle3_draft_expand_sampled(
+        ctypes.byref(drafter), ctypes.byref(tree), B, float(temperature), int(seed) & (2**64 - 1),
+        int(round) & (2**64 - 1), h_low.data_ptr(), h_mid.data_ptr(), h_high.data_ptr(),
+        root_tok.data_ptr(), kpre.data_ptr(), vpre.data_ptr(), cu_prefix.data_ptr(), int(max_prefix),
+        out["tokens"].data_ptr(), out["parents"].data_ptr(), out["depth"].data_ptr(),
+        out["score"].data_ptr(), out["n_nodes"].data_ptr(), out["slot_logits"].data_ptr(),
+        out["draft_row"].data_ptr(), ctypes.byref(dbg_struct) if dbg_struct is not None else None,
+        workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _check("eagle3_draft_expand_sampled", st)
     return out
 
 

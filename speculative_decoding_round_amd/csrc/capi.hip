@@ -16,6 +16,13 @@ int draft_expand(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, const
                  const void* vpre, const int32_t* cu_prefix, int max_prefix, int32_t* tokens,
                  int32_t* parents, int32_t* depth, float* score, int32_t* n_nodes,
                  const eagle3_draft_debug* dbg, void* ws, size_t ws_bytes, hipStream_t s);
+int draft_expand_sampled(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, float temperature,
+                         uint64_t seed, uint64_t round, const void* h_low, const void* h_mid,
+                         const void* h_high, const int32_t* root_tok, const void* kpre, const void* vpre,
+                         const int32_t* cu_prefix, int max_prefix, int32_t* tokens, int32_t* parents,
+                         int32_t* depth, float* score, int32_t* n_nodes, float* slot_logits,
+                         int32_t* draft_row, const eagle3_draft_debug* dbg, void* ws, size_t ws_bytes,
+                         hipStream_t s);
 
 // ---------------------------------------------------------------------------------------
 // Launch timing registry
@@ -100,6 +107,19 @@ int eagle3_draft_expand(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B
   return draft_expand(w, t, B, h_low, h_mid, h_high, root_tok, kpre, vpre, cu_prefix, max_prefix,
                       tokens, parents, depth, score, n_nodes, dbg, workspace, workspace_bytes,
                       (hipStream_t)stream);
+}
+
+int eagle3_draft_expand_sampled(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B,
+                                float temperature, uint64_t seed, uint64_t round, const void* h_low,
+                                const void* h_mid, const void* h_high, const int32_t* root_tok,
+                                const void* kpre, const void* vpre, const int32_t* cu_prefix,
+                                int max_prefix, int32_t* tokens, int32_t* parents, int32_t* depth,
+                                float* score, int32_t* n_nodes, float* slot_logits, int32_t* draft_row,
+                                const eagle3_draft_debug* dbg, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return draft_expand_sampled(w, t, B, temperature, seed, round, h_low, h_mid, h_high, root_tok, kpre,
+                              vpre, cu_prefix, max_prefix, tokens, parents, depth, score, n_nodes,
+                              slot_logits, draft_row, dbg, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 // ---- tree mask ------------------------------------------------------------------------

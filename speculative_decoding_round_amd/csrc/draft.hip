@@ -37,6 +37,19 @@ struct CandState {
   int32_t* ntop;     // [B]
 };
 
+// Sampled drafting: children are drawn without replacement from softmax(z / T) by ranking
+// z * invT plus Gumbel noise (counter (t>>2, 0x80000000 | slot, b, round), word t & 3), the
+// log-sum-exp is that of z * invT, and every evaluated slot's logits are kept for the
+// verifier, with the node -> slot row map of the final tree.
+struct SampCfg {
+  int on;
+  float invT;
+  uint32_t seed_lo, seed_hi, rnd;
+  int V;
+  float* slot_logits;     // [B * S, V] fp32
+  int32_t* draft_row;     // [B, N + 1]
+};
+
 // ---------------------------------------------------------------------------------------
 // init: slot 0 = root, every other slot unused; concatenated fusion input.
 // ---------------------------------------------------------------------------------------
@@ -351,7 +364,7 @@ __global__ __launch_bounds__(256) void k_topk_chunk(const float* __restrict__ pa
                                                     float* __restrict__ cv, int* __restrict__ ci,
                                                     float* __restrict__ cmax, float* __restrict__ csum,
                                                     float* __restrict__ dbg_logits, int R, int sb, int S,
-                                                    SlotState st) {
+                                                    SlotState st, SampCfg sc) {
   __shared__ __attribute__((aligned(16))) float sv[4][TK_CAP];
   __shared__ __attribute__((aligned(16))) int si[4][TK_CAP];
   __shared__ float wv[4 * KMAX];
@@ -361,10 +374,11 @@ __global__ __launch_bounds__(256) void k_topk_chunk(const float* __restrict__ pa
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t0 = c * TK_CHUNK + w * 1024;
   float* dl = nullptr;
-  if (dbg_logits) {
-    const int b = m / R, j = m % R;
-    const int sidx = b * S + sb + j;
-    if (st.valid[sidx]) dl = dbg_logits + (size_t)sidx * V;
+  const int rb = m / R, rj = m % R;
+  float* lout = sc.on ? sc.slot_logits : dbg_logits;
+  if (lout) {
+    const int sidx = rb * S + sb + rj;
+    if (st.valid[sidx]) dl = lout + (size_t)sidx * V;
   }
   // the four float4 loads of a split are issued together, splits summed in order
   float v[16];
@@ -390,7 +404,7 @@ __global__ __launch_bounds__(256) void k_topk_chunk(const float* __restrict__ pa
     const int t = t0 + 4 * (lane + 64 * q);
     if (dl && t < V) *reinterpret_cast<floatx4*>(dl + t) = z[q];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[4 * q + e] = t + e < V ? z[q][e] : kNegInf;
+    for (int e = 0; e < 4; ++e) v[4 * q + e] = t + e < V ? (sc.on ? __fmul_rn(z[q][e], sc.invT) : z[q][e]) : kNegInf;
   }
   float lm = kNegInf;
 #pragma unroll
@@ -401,6 +415,17 @@ __global__ __launch_bounds__(256) void k_topk_chunk(const float* __restrict__ pa
 #pragma unroll
     for (int i = 0; i < 16; ++i) ls += __builtin_amdgcn_exp2f((v[i] - bm) * kLog2e);
   const float tot = wave_sum(ls);
+  if (sc.on) {   // the ranking values of sampled drafting: z * invT + Gumbel noise
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t = t0 + 4 * (lane + 64 * q);
+      if (t >= V) continue;
+      uint32_t ctr[4] = {(uint32_t)(t >> 2), 0x80000000u | (uint32_t)(sb + rj), (uint32_t)rb, sc.rnd};
+      philox4x32_10(ctr, sc.seed_lo, sc.seed_hi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * q + e] = __fadd_rn(v[4 * q + e], gumbel_from_word(ctr[e]));
+    }
+  }
   if (lane < K) {
     wv[w * K + lane] = kNegInf;   // a wave with fewer than K finite logits leaves padding
     wi[w * K + lane] = 0x7fffffff;
@@ -494,7 +519,7 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
                                                  int32_t* __restrict__ out_dep, float* __restrict__ out_score,
                                                  int32_t* __restrict__ out_n, int32_t* dbg_tok,
                                                  int32_t* dbg_par, int32_t* dbg_id, float* dbg_val,
-                                                 float* dbg_lse) {
+                                                 float* dbg_lse, SampCfg sc) {
 #pragma clang fp contract(off)
   __shared__ float s_val[SEL_MAXR][KMAX];
   __shared__ int s_id[SEL_MAXR][KMAX];
@@ -557,6 +582,9 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
       const float tot = wave_sum(cm != kNegInf ? cs_ * expf(cm - mx) : 0.f);
       const float row_lse = mx + logf(tot);
       wave_topk<16>(v, [&](int e) { return id[e]; }, K, s_cv[w], s_ci[w], [&](int r, float val, int idv) {
+        // sampled drafting ranks by noisy values; the scores use the child's z * invT
+        if (sc.on)
+          val = (idv >= 0 && idv < sc.V) ? __fmul_rn(sc.slot_logits[(size_t)sidx * sc.V + idv], sc.invT) : kNegInf;
         s_val[w][r] = val;
         s_id[w][r] = idv;
         if (dbg_id) dbg_id[(size_t)sidx * K + r] = idv;
@@ -579,7 +607,10 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
   const int m_total = ntop + n_new;
   for (int e = threadIdx.x; e < n_new; e += blockDim.x) {
     const int j = e / K, rk = e % K;
-    const float sc = s_score[j] + (s_val[j][rk] - s_lse[j]);
+    // a child never scores above a sibling created before it: no change for a top-K list
+    // (values fall with the rank); keeps sampled siblings a prefix of the draw order
+    float sc = s_score[j] + (s_val[j][rk] - s_lse[j]);
+    for (int r2 = 0; r2 < rk; ++r2) sc = fminf(sc, s_score[j] + (s_val[j][r2] - s_lse[j]));
     const int tk = s_id[j][rk];
     nsc[e] = sc;
     ntok[e] = tk;
@@ -675,6 +706,19 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
   }
   __syncthreads();
   const size_t ob = (size_t)b * (N + 1);
+  if (sc.draft_row) {   // node -> row of its evaluation slot's logits, -1 for a node never evaluated
+    int32_t* dr = sc.draft_row + ob;
+    for (int l = threadIdx.x; l <= N; l += blockDim.x) dr[l] = -1;
+    __syncthreads();
+    if (threadIdx.x == 0) dr[0] = b * S;
+    for (int sl = 1 + threadIdx.x; sl < sb + R; sl += blockDim.x) {
+      const int i = b * S + sl;
+      if (!st.valid[i]) continue;
+      const int c = st.cand[i];
+      const int lab = (c >= 0 && c < n_total) ? lab_of[c] : -1;
+      if (lab > 0) dr[lab] = i;
+    }
+  }
   for (int i = threadIdx.x; i < n_keep; i += blockDim.x) {
     const int idx = ktop[i];
     const int lab = lab_of[idx];
@@ -819,7 +863,8 @@ template <typename T>
 int run_draft(const eagle3_drafter* w, const Plan& p, const void* h_low, const void* h_mid,
               const void* h_high, const int32_t* root_tok, const void* kpre, const void* vpre,
               const int32_t* cu_prefix, int32_t* tokens, int32_t* parents, int32_t* depth,
-              float* score, int32_t* n_nodes, const eagle3_draft_debug* dbg, hipStream_t s) {
+              float* score, int32_t* n_nodes, const eagle3_draft_debug* dbg, const SampCfg& sc,
+              hipStream_t s) {
   using namespace e3h;
   const int B = p.B, d = p.d;
   const int dt = w->dtype;
@@ -922,14 +967,15 @@ int run_draft(const eagle3_drafter* w, const Plan& p, const void* h_low, const v
         ProfScope ps("topk_chunk", s);
         hipLaunchKernelGGL(k_topk_chunk, dim3(p.lm_nchunk, M), dim3(256), 0, s, p.gpart,
                            gp.splits, M, p.V, p.K, p.lm_nchunk, p.cv, p.ci, p.cmax, p.csum,
-                           dbg ? dbg->slot_logits : (float*)nullptr, R, sb, p.S, p.st);
+                           dbg ? dbg->slot_logits : (float*)nullptr, R, sb, p.S, p.st, sc);
         if ((st = launch_status())) return st;
       }
       ProfScope ps("draft_select", s);
       hipLaunchKernelGGL(k_select, dim3(B), dim3(1024), 0, s, step, p.D, p.K, p.W, p.N, p.S, p.PMAX, R,
                          p.lm_nchunk, p.cv, p.ci, p.cmax, p.csum, p.st, p.cs, tokens, parents, depth,
                          score, n_nodes, dbg_tok, dbg_par, dbg ? dbg->slot_topk_id : (int32_t*)nullptr,
-                         dbg ? dbg->slot_topk_val : (float*)nullptr, dbg ? dbg->slot_lse : (float*)nullptr);
+                         dbg ? dbg->slot_topk_val : (float*)nullptr, dbg ? dbg->slot_lse : (float*)nullptr,
+                         sc);
       if ((st = launch_status())) return st;
     }
   }
@@ -974,11 +1020,12 @@ size_t draft_workspace(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B,
   return make_plan(w, t, B, max_prefix, nullptr).bytes;
 }
 
-int draft_expand(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, const void* h_low,
-                 const void* h_mid, const void* h_high, const int32_t* root_tok, const void* kpre,
-                 const void* vpre, const int32_t* cu_prefix, int max_prefix, int32_t* tokens,
-                 int32_t* parents, int32_t* depth, float* score, int32_t* n_nodes,
-                 const eagle3_draft_debug* dbg, void* ws, size_t ws_bytes, hipStream_t s) {
+static int draft_common(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, const void* h_low,
+                        const void* h_mid, const void* h_high, const int32_t* root_tok, const void* kpre,
+                        const void* vpre, const int32_t* cu_prefix, int max_prefix, int32_t* tokens,
+                        int32_t* parents, int32_t* depth, float* score, int32_t* n_nodes,
+                        const eagle3_draft_debug* dbg, const SampCfg& sc, void* ws, size_t ws_bytes,
+                        hipStream_t s) {
   int st = draft_check(w, t, B, max_prefix);
   if (st) return st;
   if (!h_low || !h_mid || !h_high || !root_tok || !cu_prefix || !tokens || !parents || !depth ||
@@ -993,9 +1040,42 @@ int draft_expand(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, const
   p = make_plan(w, t, B, max_prefix, ws);
   if (w->dtype == EAGLE3_BF16)
     return run_draft<bf16>(w, p, h_low, h_mid, h_high, root_tok, kpre, vpre, cu_prefix, tokens, parents,
-                           depth, score, n_nodes, dbg, s);
+                           depth, score, n_nodes, dbg, sc, s);
   return run_draft<float>(w, p, h_low, h_mid, h_high, root_tok, kpre, vpre, cu_prefix, tokens, parents,
-                          depth, score, n_nodes, dbg, s);
+                          depth, score, n_nodes, dbg, sc, s);
+}
+
+int draft_expand(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, const void* h_low,
+                 const void* h_mid, const void* h_high, const int32_t* root_tok, const void* kpre,
+                 const void* vpre, const int32_t* cu_prefix, int max_prefix, int32_t* tokens,
+                 int32_t* parents, int32_t* depth, float* score, int32_t* n_nodes,
+                 const eagle3_draft_debug* dbg, void* ws, size_t ws_bytes, hipStream_t s) {
+  SampCfg sc = {};
+  return draft_common(w, t, B, h_low, h_mid, h_high, root_tok, kpre, vpre, cu_prefix, max_prefix, tokens,
+                      parents, depth, score, n_nodes, dbg, sc, ws, ws_bytes, s);
+}
+
+int draft_expand_sampled(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, float temperature,
+                         uint64_t seed, uint64_t round, const void* h_low, const void* h_mid,
+                         const void* h_high, const int32_t* root_tok, const void* kpre, const void* vpre,
+                         const int32_t* cu_prefix, int max_prefix, int32_t* tokens, int32_t* parents,
+                         int32_t* depth, float* score, int32_t* n_nodes, float* slot_logits,
+                         int32_t* draft_row, const eagle3_draft_debug* dbg, void* ws, size_t ws_bytes,
+                         hipStream_t s) {
+  if (!(temperature > 0.f) || temperature == __builtin_huge_valf()) return EAGLE3_EINVAL;
+  if (!slot_logits || !draft_row || (uintptr_t)slot_logits % 16) return EAGLE3_EINVAL;
+  if (!w) return EAGLE3_EINVAL;
+  SampCfg sc;
+  sc.on = 1;
+  sc.invT = 1.0f / temperature;
+  sc.seed_lo = (uint32_t)seed;
+  sc.seed_hi = (uint32_t)(seed >> 32);
+  sc.rnd = (uint32_t)round;
+  sc.V = w->vocab;
+  sc.slot_logits = slot_logits;
+  sc.draft_row = draft_row;
+  return draft_common(w, t, B, h_low, h_mid, h_high, root_tok, kpre, vpre, cu_prefix, max_prefix, tokens,
+                      parents, depth, score, n_nodes, dbg, sc, ws, ws_bytes, s);
 }
 
 }  // namespace e3h
