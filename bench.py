@@ -308,7 +308,7 @@ def attention_op(capi, synth, shape, trees, prefix, bound, reps=20, seed=500):
 
 
 OP_KEYS = ("attn_longctx", "attn_batch16", "attn_70b", "attn_8b", "merge", "accept_greedy", "accept_t07",
-           "accept_sampled", "gemm_sweep", "catchup", "commit", "tree_budgets", "usp")
+           "accept_sampled", "draft_sampled", "gemm_sweep", "catchup", "commit", "tree_budgets", "usp")
 
 
 def sampled_accept_ops(capi, synth, reps):
@@ -348,10 +348,48 @@ def sampled_accept_ops(capi, synth, reps):
             lens += ao["accept_len"].cpu().tolist()
         out.append(dict(key=key, **_entry("accept (sampled candidates, T=1)",
                                           f"{sh.name}: {T} nodes ({R} with children) x {V} logits",
-                                          "k_samp_clear + k_samp_stats + k_samp_npass x 9 + k_samp_draw + k_samp_walk",
+                                          "k_samp_clear + k_samp_stats + k_samp_npass x 9 + k_samp_walk + k_samp_draw",
                                           us, "hbm", bytes_=nbytes, rotating_copies=ncopy,
                                           mean_accept_len=round(float(np.mean(lens)), 2))))
         del zs, qs
+    return out
+
+
+def sampled_draft_ops(steps=10):
+    """The draft-tree round at the 8B shape (D = 6, K = W = 10, N = 60) with top-K children and
+    with sampled children (eagle3_draft_expand_sampled, T = 1: Gumbel noise on every logit of
+    the LM head, and every slot's logits kept for the verifier).  Both stream the fusion weights
+    once and the layer and LM-head weights at every depth step (HBM-bound)."""
+    import torch
+    from speculative_decoding_round_amd import capi, synth
+    dev = "cuda:0"
+    shape = synth.LLAMA8B
+    rnd = Round(shape, dev)
+    di = rnd.di
+    S = 1 + (shape.depth - 1) * shape.width
+    so = dict(rnd.draft_out)
+    so["slot_logits"] = torch.empty((rnd.B, S, shape.V), dtype=torch.float32, device=dev)
+    so["draft_row"] = torch.empty((rnd.B, rnd.n1), dtype=torch.int32, device=dev)
+
+    def det(i):
+        capi.eagle3_draft_expand(rnd.drafter, rnd.tree, di["h_low"], di["h_mid"], di["h_high"], di["root_tok"],
+                                 di["kpre"], di["vpre"], di["cu_prefix"], rnd.max_prefix, workspace=rnd.ws_draft,
+                                 out=rnd.draft_out)
+
+    def smp(i):
+        capi.eagle3_draft_expand_sampled(rnd.drafter, rnd.tree, 1.0, 7, i, di["h_low"], di["h_mid"], di["h_high"],
+                                         di["root_tok"], di["kpre"], di["vpre"], di["cu_prefix"], rnd.max_prefix,
+                                         workspace=rnd.ws_draft, out=so)
+    d, F, V, D = shape.d, shape.F, shape.V, shape.depth
+    nqkv = (shape.Hq + 2 * shape.Hkv) * shape.Dh
+    wbytes = 2 * (3 * d * d + D * (2 * d * nqkv + shape.Hq * shape.Dh * d + 3 * d * F + V * d))
+    out = []
+    for name, fn in (("draft round (top-K children)", det), ("draft round (sampled children, T=1)", smp)):
+        us = _time_b2b(fn, steps)
+        out.append(dict(key="draft_sampled", **_entry(name, "llama8b_bf16 D=6 K=10 W=10 N=60", "whole draft round",
+                                                      us, "hbm", bytes_=wbytes)))
+    del rnd, so
+    torch.cuda.empty_cache()
     return out
 
 
@@ -588,6 +626,8 @@ def op_rooflines(reps=20, keys=OP_KEYS):
         del logits
     if "accept_sampled" in keys:
         ops += sampled_accept_ops(capi, synth, reps)
+    if "draft_sampled" in keys:
+        ops += sampled_draft_ops()
     if "gemm_sweep" in keys:
         ops += gemm_sweep(capi, synth, reps)
     if "catchup" in keys:
