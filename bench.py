@@ -349,7 +349,7 @@ def sampled_accept_ops(capi, synth, reps):
         out.append(dict(key=key, **_entry("accept (sampled candidates, T=1)",
                                           f"{sh.name}: {T} nodes ({R} with children) x {V} logits",
                                           "k_samp_clear + k_samp_stats + k_samp_npass x 9 + k_samp_walk + k_samp_draw",
-                                          us, "hbm", bytes_=nbytes, rotating_copies=ncopy,
+                                          us, "latency", bytes_=nbytes, rotating_copies=ncopy, launches=13,
                                           mean_accept_len=round(float(np.mean(lens)), 2))))
         del zs, qs
     return out

@@ -29,6 +29,7 @@ using namespace e3;
 namespace {
 
 constexpr int SC = 4096;          // tokens per chunk, 16 per thread
+constexpr int DC = 1024;          // tokens per chunk of the end-node draw, 4 per thread
 constexpr int kMaxNodes = 256;    // nodes per request
 constexpr int kMaxKids = 64;      // children tested per node
 constexpr uint32_t kUniformC0 = 0x40000000u;   // counter word 0 of the acceptance uniforms
@@ -53,7 +54,7 @@ struct SArgs {
   const int32_t* draft_row;
   const void* logits;
   const void* dlogits;
-  int B, T, V, nch, R, maxc, max_depth, az, aq;
+  int B, T, V, nch, ndc, R, maxc, max_depth, az, aq;
   double invT;
   uint32_t seed_lo, seed_hi, rnd;
   NodeSt* st;         // [T]
@@ -63,8 +64,10 @@ struct SArgs {
   uint64_t* p_stats;  // [T][nch][4]        (max a, sum, max b, sum)
   uint64_t* p_n;      // [maxc - 1][T][nch] N partial of pass m
   int* p_pos;         // [T][nch]           tokens with q > 0 (pass 2)
-  uint64_t* p_dv;     // [T][nch]           draw: best value
-  int* p_di;          // [T][nch]           draw: its token
+  uint64_t* p_dv;     // [T][ndc]           draw: best value
+  int* p_di;          // [T][ndc]           draw: its token
+  int* kids_g;        // [T][maxc]          children of a node (written by the stats pass)
+  int* toks_g;        // [T][maxc]          their tokens
   int32_t* accept_len;
   int32_t* path;
   int32_t* out_tokens;
@@ -108,8 +111,8 @@ __device__ __forceinline__ int get_i(int* p, int32_t* dev_status) {
 
 // Count one finished chunk of node g; true (in every thread) in the workgroup that finished the
 // node's last chunk.  Thread 0 has issued the chunk's partial store before this call.
-__device__ __forceinline__ bool finish_chunk(const SArgs& a, int g, int* s_last) {
-  if (threadIdx.x == 0) *s_last = atomicAdd(&a.cnt[g], 1) == a.nch - 1;
+__device__ __forceinline__ bool finish_chunk(const SArgs& a, int g, int* s_last, int n_chunks = -1) {
+  if (threadIdx.x == 0) *s_last = atomicAdd(&a.cnt[g], 1) == (n_chunks < 0 ? a.nch : n_chunks) - 1;
   __syncthreads();
   return *s_last != 0;
 }
@@ -286,7 +289,7 @@ __device__ __forceinline__ int next_valid(const int* s_tok, int nk, int V, int k
 template <typename TZ, typename TQ>
 __device__ void chain_step(const SArgs& a, NodeSt& s, const int* s_kids, const int* s_tok, int b,
                            const TZ* zrow, const TQ* qrow, bool from_pass, double N_new,
-                           int npos_new) {
+                           int npos_new, const float* pre = nullptr) {
 #pragma clang fp contract(off)
   if (from_pass) {
     if (s.m == 2) s.npos = npos_new;
@@ -301,8 +304,10 @@ __device__ void chain_step(const SArgs& a, NodeSt& s, const int* s_kids, const i
   }
   const int j = s_kids[s.k];
   const int x = s_tok[s.k];
-  const double px = exp((double)to_f32(zrow[x]) * a.invT - s.A);
-  const double qx = exp((double)to_f32(qrow[x]) * a.invT - s.Bq);
+  const float zx = pre ? pre[0] : to_f32(zrow[x]);
+  const float qz = pre ? pre[1] : to_f32(qrow[x]);
+  const double px = exp((double)zx * a.invT - s.A);
+  const double qx = exp((double)qz * a.invT - s.Bq);
   bool keep = qx == 0.0;
   if (!keep) {
     const double pr = px - s.lam * qx;
@@ -336,14 +341,14 @@ __device__ __forceinline__ void enqueue_need(const SArgs& a, const NodeSt& s, in
 }
 
 // ---- kernels ---------------------------------------------------------------------------
-__global__ void k_samp_clear(SArgs a, int n_stats, int n_n, int n_one) {
+__global__ void k_samp_clear(SArgs a, int n_stats, int n_n, int n_one, int n_draw) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t < a.T) a.cnt[t] = 0;
   if (t <= a.maxc) a.list_n[t] = 0;
   if (t < n_stats) a.p_stats[t] = kEmpty;
   if (t < n_n) a.p_n[t] = kEmpty;
-  if (t < n_one) {
-    a.p_pos[t] = kEmptyI;
+  if (t < n_one) a.p_pos[t] = kEmptyI;
+  if (t < n_draw) {
     a.p_dv[t] = kEmpty;
     a.p_di[t] = kEmptyI;
   }
@@ -420,6 +425,10 @@ __global__ __launch_bounds__(256) void k_samp_stats(SArgs a) {
   }
   if (!finish_chunk(a, g, &s_last)) return;
   const int nk = node_children(a, n0, n, i, s_kids, s_tok, s_cnt);
+  if ((int)threadIdx.x < nk) {   // kept for the later passes of this node
+    a.kids_g[(size_t)g * a.maxc + threadIdx.x] = s_kids[threadIdx.x];
+    a.toks_g[(size_t)g * a.maxc + threadIdx.x] = s_tok[threadIdx.x];
+  }
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
   double MA = kNegInfD, SA = 0.0, MB = kNegInfD, SB = 0.0;
@@ -467,7 +476,8 @@ template <typename TZ, typename TQ>
 __global__ __launch_bounds__(256) void k_samp_npass(SArgs a, int m) {
 #pragma clang fp contract(off)
   __shared__ double sm[8];
-  __shared__ int s_kids[kMaxKids], s_tok[kMaxKids], s_cnt[4], s_last;
+  __shared__ int s_kids[kMaxKids], s_tok[kMaxKids], s_last;
+  __shared__ float s_pre[2];
   __shared__ double s_exp[64];
   const int items = a.list_n[m] * a.nch;
   if ((int)blockIdx.x >= items) return;
@@ -483,6 +493,12 @@ __global__ __launch_bounds__(256) void k_samp_npass(SArgs a, int m) {
     const TQ* qrow = (const TQ*)a.dlogits + (size_t)r * a.V;
     const int tb = c * SC + 16 * threadIdx.x;
     const int ne = min(16, a.V - tb);
+    float pz = 0.f, pq = 0.f;
+    if (threadIdx.x == 0) {   // the waiting candidate's logits, in case this chunk is the node's last
+      const int x = a.toks_g[(size_t)g * a.maxc + s0.k];
+      pz = to_f32(zrow[x]);
+      pq = to_f32(qrow[x]);
+    }
     double acc = 0.0, pos = 0.0;
     {
       float z[16], zq[16];
@@ -501,12 +517,16 @@ __global__ __launch_bounds__(256) void k_samp_npass(SArgs a, int m) {
     if (threadIdx.x == 0) {
       put_d(pn + (size_t)g * a.nch + c, acc);
       if (m == 2) put_i(a.p_pos + (size_t)g * a.nch + c, (int)pos);
+      s_pre[0] = pz;
+      s_pre[1] = pq;
     }
     if (finish_chunk(a, g, &s_last)) {
       const int b = find_request(a.cu_nodes, a.B, g);
-      const int n0 = a.cu_nodes[b];
-      const int n = min(a.cu_nodes[b + 1] - n0, kMaxNodes);
-      node_children(a, n0, n, g - n0, s_kids, s_tok, s_cnt);
+      if ((int)threadIdx.x < s0.nk) {
+        s_kids[threadIdx.x] = a.kids_g[(size_t)g * a.maxc + threadIdx.x];
+        s_tok[threadIdx.x] = a.toks_g[(size_t)g * a.maxc + threadIdx.x];
+      }
+      __syncthreads();
       if (threadIdx.x < 64) {
         double N = 0.0;
         int np = 0;
@@ -518,7 +538,7 @@ __global__ __launch_bounds__(256) void k_samp_npass(SArgs a, int m) {
         np = wave_sum_i(np);
         if (lane == 0) {
           NodeSt s = s0;
-          chain_step(a, s, s_kids, s_tok, b, zrow, qrow, true, N, np);
+          chain_step(a, s, s_kids, s_tok, b, zrow, qrow, true, N, np, s_pre);
           a.st[g] = s;
           a.cnt[g] = 0;
           enqueue_need(a, s, g);
@@ -581,13 +601,13 @@ __global__ __launch_bounds__(256) void k_samp_draw(SArgs a) {
   __shared__ int sx[4];
   __shared__ int s_last;
   __shared__ double s_exp[64];
-  const int items = a.list_n[0] * a.nch;
+  const int items = a.list_n[0] * a.ndc;
   if ((int)blockIdx.x >= items) return;
   exp2_table(s_exp);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
-    const int g = a.lists[it / a.nch];
-    const int c = it % a.nch;
+    const int g = a.lists[it / a.ndc];
+    const int c = it % a.ndc;
     const NodeSt s0 = a.st[g];
     const int b = find_request(a.cu_nodes, a.B, g);
     const uint32_t i_local = (uint32_t)(g - a.cu_nodes[b]);
@@ -595,16 +615,19 @@ __global__ __launch_bounds__(256) void k_samp_draw(SArgs a) {
     const int r = plain ? 0 : a.draft_row[g];
     const TZ* zrow = (const TZ*)a.logits + (size_t)g * a.V;
     const TQ* qrow = (const TQ*)a.dlogits + (size_t)r * a.V;
-    const int tb = c * SC + 16 * threadIdx.x;
+    const int tb = c * DC + 4 * threadIdx.x;
     double best = kNegInfD;
     int bi = 0x7fffffff;
     if (tb < a.V) {
-      float z[16], zq[16];
-      load_chunk(zrow, tb, a.V, a.az, z);
-      if (!plain) load_chunk(qrow, tb, a.V, a.aq, zq);
+      float z[4], zq[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t ctr[4] = {(uint32_t)((tb >> 2) + q), i_local, (uint32_t)b, a.rnd};
+      for (int e = 0; e < 4; ++e) {
+        z[e] = tb + e < a.V ? to_f32(zrow[tb + e]) : 0.f;
+        zq[e] = (!plain && tb + e < a.V) ? to_f32(qrow[tb + e]) : 0.f;
+      }
+      {
+        const int q = 0;
+        uint32_t ctr[4] = {(uint32_t)(tb >> 2), i_local, (uint32_t)b, a.rnd};
         philox4x32_10(ctr, a.seed_lo, a.seed_hi);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -638,15 +661,15 @@ __global__ __launch_bounds__(256) void k_samp_draw(SArgs a) {
           best = sv[q];
           bi = sx[q];
         }
-      put_d(a.p_dv + (size_t)g * a.nch + c, best);
-      put_i(a.p_di + (size_t)g * a.nch + c, bi);
+      put_d(a.p_dv + (size_t)g * a.ndc + c, best);
+      put_i(a.p_di + (size_t)g * a.ndc + c, bi);
     }
-    if (finish_chunk(a, g, &s_last) && threadIdx.x < 64) {
+    if (finish_chunk(a, g, &s_last, a.ndc) && threadIdx.x < 64) {
       double bv = kNegInfD;
       int bx = 0x7fffffff;
-      for (int cc = lane; cc < a.nch; cc += 64) {
-        const double v = get_d(a.p_dv + (size_t)g * a.nch + cc, a.dev_status);
-        const int x = get_i(a.p_di + (size_t)g * a.nch + cc, a.dev_status);
+      for (int cc = lane; cc < a.ndc; cc += 64) {
+        const double v = get_d(a.p_dv + (size_t)g * a.ndc + cc, a.dev_status);
+        const int x = get_i(a.p_di + (size_t)g * a.ndc + cc, a.dev_status);
         if (better_d(v, x, bv, bx)) {
           bv = v;
           bx = x;
@@ -667,12 +690,12 @@ __global__ __launch_bounds__(256) void k_samp_draw(SArgs a) {
 
 struct SampLayout {
   NodeSt* st;
-  int *cnt, *lists, *list_n, *p_pos, *p_di;
+  int *cnt, *lists, *list_n, *p_pos, *p_di, *kids_g, *toks_g;
   uint64_t *p_stats, *p_n, *p_dv;
   size_t bytes;
 };
 
-SampLayout carve_sampled(void* ws, int T, int nch, int maxc) {
+SampLayout carve_sampled(void* ws, int T, int nch, int ndc, int maxc) {
   e3h::Carve c(ws);
   SampLayout L;
   L.st = c.take<NodeSt>((size_t)T);
@@ -682,15 +705,17 @@ SampLayout carve_sampled(void* ws, int T, int nch, int maxc) {
   L.p_stats = c.take<uint64_t>((size_t)T * nch * 4);
   L.p_n = c.take<uint64_t>((size_t)(maxc > 1 ? maxc - 1 : 1) * T * nch);
   L.p_pos = c.take<int>((size_t)T * nch);
-  L.p_dv = c.take<uint64_t>((size_t)T * nch);
-  L.p_di = c.take<int>((size_t)T * nch);
+  L.p_dv = c.take<uint64_t>((size_t)T * ndc);
+  L.p_di = c.take<int>((size_t)T * ndc);
+  L.kids_g = c.take<int>((size_t)T * maxc);
+  L.toks_g = c.take<int>((size_t)T * maxc);
   L.bytes = c.size();
   return L;
 }
 
 template <typename TZ, typename TQ>
 void launch_typed(const SArgs& a, hipStream_t s) {
-  const int grid = (int)std::min<long>((long)a.T * a.nch, 512);
+  const int grid = (int)std::min<long>((long)a.T * a.nch, 4096);
   {
     e3h::ProfScope ps("sampled_stats", s);
     hipLaunchKernelGGL((k_samp_stats<TZ, TQ>), dim3((unsigned)((long)a.T * a.nch)), dim3(256), 0, s, a);
@@ -704,7 +729,7 @@ void launch_typed(const SArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_samp_walk, dim3(a.B), dim3(64), 0, s, a);
   }
   e3h::ProfScope ps("sampled_draw", s);
-  hipLaunchKernelGGL((k_samp_draw<TZ, TQ>), dim3((unsigned)std::min<long>((long)a.B * a.nch, 1024)), dim3(256),
+  hipLaunchKernelGGL((k_samp_draw<TZ, TQ>), dim3((unsigned)std::min<long>((long)a.B * a.ndc, 4096)), dim3(256),
                      0, s, a);
 }
 
@@ -713,7 +738,7 @@ void launch_typed(const SArgs& a, hipStream_t s) {
 namespace e3h {
 
 size_t accept_sampled_workspace(int T, int V, int max_children) {
-  return carve_sampled(nullptr, T, (V + SC - 1) / SC, max_children).bytes;
+  return carve_sampled(nullptr, T, (V + SC - 1) / SC, (V + DC - 1) / DC, max_children).bytes;
 }
 
 int accept_sampled_max_children() { return kMaxKids; }
@@ -726,8 +751,8 @@ int launch_accept_sampled(int B, int T, const int32_t* cu_nodes, const int32_t* 
                           int32_t* path, int32_t* out_tokens, int32_t* bonus, int32_t* dev_status,
                           void* workspace, hipStream_t s) {
   if (max_children < 1 || max_children > kMaxKids) return EAGLE3_EUNSUPPORTED;
-  const int nch = (V + SC - 1) / SC;
-  const SampLayout L = carve_sampled(workspace, T, nch, max_children);
+  const int nch = (V + SC - 1) / SC, ndc = (V + DC - 1) / DC;
+  const SampLayout L = carve_sampled(workspace, T, nch, ndc, max_children);
   SArgs a;
   a.cu_nodes = cu_nodes;
   a.tokens = tokens;
@@ -739,6 +764,7 @@ int launch_accept_sampled(int B, int T, const int32_t* cu_nodes, const int32_t* 
   a.T = T;
   a.V = V;
   a.nch = nch;
+  a.ndc = ndc;
   a.R = draft_logits ? n_draft_rows : 0;
   a.maxc = max_children;
   a.max_depth = max_depth;
@@ -757,6 +783,8 @@ int launch_accept_sampled(int B, int T, const int32_t* cu_nodes, const int32_t* 
   a.p_pos = L.p_pos;
   a.p_dv = L.p_dv;
   a.p_di = L.p_di;
+  a.kids_g = L.kids_g;
+  a.toks_g = L.toks_g;
   a.accept_len = accept_len;
   a.path = path;
   a.out_tokens = out_tokens;
@@ -766,9 +794,10 @@ int launch_accept_sampled(int B, int T, const int32_t* cu_nodes, const int32_t* 
     e3h::ProfScope ps("sampled_clear", s);
     const int n_stats = T * nch * 4;
     const int n_n = (max_children > 1 ? max_children - 1 : 1) * T * nch;
-    const int n_one = T * nch;
-    const int nthreads = std::max({T, max_children + 1, n_stats, n_n, n_one});
-    hipLaunchKernelGGL(k_samp_clear, dim3((nthreads + 255) / 256), dim3(256), 0, s, a, n_stats, n_n, n_one);
+    const int n_one = T * nch, n_draw = T * ndc;
+    const int nthreads = std::max({T, max_children + 1, n_stats, n_n, n_one, n_draw});
+    hipLaunchKernelGGL(k_samp_clear, dim3((nthreads + 255) / 256), dim3(256), 0, s, a, n_stats, n_n, n_one,
+                       n_draw);
   }
   int st = launch_status();
   if (st) return st;
