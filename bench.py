@@ -393,6 +393,47 @@ def sampled_draft_ops(steps=10):
     return out
 
 
+def round_distribution(rnd: "Round", n: int) -> dict:
+    """Per-round device times over n more rounds (an event between consecutive rounds on the
+    launch stream): median, p10, p90 in ms."""
+    import numpy as np
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(n):
+        rnd.step()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    t = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(n)])
+    return {"rounds": n, "median": round(float(np.median(t)), 4), "p10": round(float(np.percentile(t, 10)), 4),
+            "p90": round(float(np.percentile(t, 90)), 4)}
+
+
+def measured_ceilings() -> dict:
+    """What this part reaches outside the library, for scale: a 1 GiB device-to-device copy
+    (torch's copy kernel; read + write bytes over time) and an 8192^3 bf16 matrix product
+    (torch.matmul, i.e. the vendor GEMM library) against the published peaks."""
+    import torch
+    dev = "cuda:0"
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    us_copy = _time_b2b(lambda i: dst.copy_(src), 10)
+    del src, dst
+    m = 8192
+    a = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
+    b = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
+    c = torch.empty((m, m), dtype=torch.bfloat16, device=dev)
+    us_mm = _time_b2b(lambda i: torch.matmul(a, b, out=c), 10)
+    del a, b, c
+    torch.cuda.empty_cache()
+    copy_gbs = 2 * n / (us_copy * 1e-6) / 1e9
+    tflops = 2 * m ** 3 / (us_mm * 1e-6) / 1e12
+    return {"copy_1gib_gbs": round(copy_gbs, 1), "copy_frac": round(copy_gbs / HBM_PEAK_GBS, 4),
+            "gemm_bf16_8192_tflops": round(tflops, 1), "gemm_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def gemm_sweep(capi, synth, reps):
     """The drafter projections' GEMM (eagle3_linear) over the number of rows: at the QKV
     shape (N = 6144, K = 8192) for M = 1 .. 8192, and at M = 2048 (a prompt's worth of rows)
@@ -772,6 +813,8 @@ def main():
     }
     if not args.no_ops:
         line["gemms"] = gemm_rooflines(rnd, args.steps)
+        line["round_ms"] = round_distribution(rnd, 100)
+        line["ceilings"] = measured_ceilings()
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev)
