@@ -168,37 +168,48 @@ def cpu_baseline(rnd: Round):
     di = {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in rnd.di.items()}
     drafter = O.Drafter(w, s.Hq, s.Hkv, s.Dh)                 # fp64 upcast: not timed
     vi = {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in rnd.vi.items()}
-    t0 = time.perf_counter()
-    res = O.draft_round(drafter, s.depth, s.topk, s.width, s.n_nodes, di["h_low"], di["h_mid"],
-                        di["h_high"], di["root_tok"], di["kpre"], di["vpre"], rnd.prefix)
-    parents, tokens, cu = [], [], [0]
-    for r in res:
-        n = len(r["parents"])
-        parents += r["parents"] + [0] * (rnd.n1 - n)
-        tokens += r["tokens"] + [0] * (rnd.n1 - n)
-        cu.append(cu[-1] + rnd.n1)
-    cup = vi["cu_prefix"].tolist()
-    mask, _, _, _ = O.build_tree_mask(parents, cu, cup)
-    S = rnd.S
-    o_parts, l_parts = [], []
-    for sp in range(S + 1):
-        def filt(b, P, sp=sp):
-            keep = np.zeros(P, dtype=bool)
-            if sp < S:
-                ch = (-(-P // S) + 127) // 128 * 128
-                keep[min(P, sp * ch):min(P, sp * ch + ch)] = True
-            return keep, np.full(rnd.n1, sp == S)
-        o, l = O.tree_attention(vi["q"], vi["k_tree"], vi["v_tree"], cu, mask, vi["kpre"],
-                                vi["vpre"], cup, rnd.scale, key_filter=filt)
-        o_parts.append(o.reshape(-1, s.Dh))
-        l_parts.append(l.reshape(-1))
-    O.lse_merge(np.stack(o_parts), np.stack(l_parts))
-    O.accept(cu, tokens, parents, vi["logits"], s.temperature, 20260101, 0, s.depth)
-    dt = time.perf_counter() - t0
-    verified = sum(len(r["tokens"]) - 1 for r in res)
-    return {"value": verified / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one full draft+verify round of the same workload ({verified} verified "
-                      f"tree tokens) in {dt:.2f} s, float64 numpy oracle"}
+
+    def one_round():
+        t0 = time.perf_counter()
+        res = O.draft_round(drafter, s.depth, s.topk, s.width, s.n_nodes, di["h_low"], di["h_mid"],
+                            di["h_high"], di["root_tok"], di["kpre"], di["vpre"], rnd.prefix)
+        parents, tokens, cu = [], [], [0]
+        for r in res:
+            n = len(r["parents"])
+            parents += r["parents"] + [0] * (rnd.n1 - n)
+            tokens += r["tokens"] + [0] * (rnd.n1 - n)
+            cu.append(cu[-1] + rnd.n1)
+        cup = vi["cu_prefix"].tolist()
+        mask, _, _, _ = O.build_tree_mask(parents, cu, cup)
+        S = rnd.S
+        o_parts, l_parts = [], []
+        for sp in range(S + 1):
+            def filt(b, P, sp=sp):
+                keep = np.zeros(P, dtype=bool)
+                if sp < S:
+                    ch = (-(-P // S) + 127) // 128 * 128
+                    keep[min(P, sp * ch):min(P, sp * ch + ch)] = True
+                return keep, np.full(rnd.n1, sp == S)
+            o, l = O.tree_attention(vi["q"], vi["k_tree"], vi["v_tree"], cu, mask, vi["kpre"],
+                                    vi["vpre"], cup, rnd.scale, key_filter=filt)
+            o_parts.append(o.reshape(-1, s.Dh))
+            l_parts.append(l.reshape(-1))
+        O.lse_merge(np.stack(o_parts), np.stack(l_parts))
+        O.accept(cu, tokens, parents, vi["logits"], s.temperature, 20260101, 0, s.depth)
+        return time.perf_counter() - t0, sum(len(r["tokens"]) - 1 for r in res)
+
+    dt, verified = one_round()
+    out = {"value": verified / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"one full draft+verify round of the same workload ({verified} verified "
+                     f"tree tokens) in {dt:.2f} s, float64 numpy oracle"}
+    try:   # the same round again on one core
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            dt1, v1 = one_round()
+        out["single_core"] = {"value": v1 / dt1, "seconds": round(dt1, 2)}
+    except Exception:  # pragma: no cover
+        pass
+    return out
 
 
 # ---------------------------------------------------------------------------------------
