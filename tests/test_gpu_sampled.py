@@ -173,3 +173,15 @@ def test_every_proposable_token_rejected():
         assert got[0][1] == 1 and got[2][1][0] == 2  # the zero-probability child is kept
         draws.add(int(got[3][0]))
     assert draws & {5, 6, 7}
+
+
+@pytest.mark.parametrize("shape_name,B", [("llama8b", 1), ("llama70b", 4)])
+def test_bench_configurations(shape_name, B):
+    """The inputs the benchmark times (random 61-node trees of depth 6 at the 8B and 70B
+    shapes, V = 128256 bf16, T = 1, at most 10 children tested per node), through the same
+    entry point, equal to the oracle's walk over several rounds."""
+    need_gpu()
+    sh = synth.LLAMA8B if shape_name == "llama8b" else synth.LLAMA70B
+    trees = [synth.random_tree(61, sh.depth, 4400 + i) for i in range(B)]
+    d = synth.sampled_tree_inputs(trees, sh.V, seed=970, device=DEV, target_noise=1.0)
+    compare(d, 1.0, 7, range(3), sh.depth, 10)
