@@ -54,7 +54,7 @@ struct SampCfg {
 // init: slot 0 = root, every other slot unused; concatenated fusion input.
 // ---------------------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void k_init(int B, int S, int d, int V, const int32_t* __restrict__ root_tok,
+__global__ __launch_bounds__(256) void k_init(int /*B*/, int S, int d, int V, const int32_t* __restrict__ root_tok,
                                               SlotState st, CandState cs, const T* __restrict__ hl,
                                               const T* __restrict__ hm, const T* __restrict__ hh,
                                               T* __restrict__ xf, int32_t* dbg_tok, int32_t* dbg_par) {
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(1024) void k_prep(int R, int sb, int S, int d, int 
   store8<T>(ur + k0, o1);
   store8<T>(ur + d + k0, o2);
   store8<float>(f_rows + (size_t)r * d + k0, fv);
-  if (threadIdx.x < st.mw)
+  if ((int)threadIdx.x < st.mw)
     row_mask[(size_t)r * st.mw + threadIdx.x] = valid ? st.mask[(size_t)si * st.mw + threadIdx.x] : 0ull;
 }
 
@@ -213,7 +213,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_epi_qkv(const float* __restrict__ part, int splits, int M, int Hq,
                                                  int Hkv, int Dh, int R, int sb, int S, int step,
                                                  float theta, const int32_t* __restrict__ cu_prefix,
-                                                 SlotState st, T* __restrict__ q_rows,
+                                                 SlotState /*st*/, T* __restrict__ q_rows,
                                                  T* __restrict__ kslot, T* __restrict__ vslot) {
   const int half = Dh / 2;
   const int H = Hq + 2 * Hkv;
