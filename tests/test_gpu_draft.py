@@ -150,8 +150,11 @@ SMALL_BF16 = synth.scaled(synth.LLAMA8B, d=512, Hq=8, Hkv=2, Dh=128, F=1536, V=8
     (synth.scaled(SMALL_BF16, B=1, depth=8, topk=10, width=10, n_nodes=48, V=4096), [33]),
     # 177 slots (three mask words), a 200-node tree
     (synth.scaled(SMALL_BF16, B=1, depth=12, topk=5, width=16, n_nodes=200, V=4096), [256]),
+    # the largest vocabulary the drafter takes: 64 chunks of 4096 logits, one per lane of the
+    # selection's merge wave
+    (synth.scaled(SMALL_BF16, B=1, depth=3, topk=4, width=3, n_nodes=10, V=64 * 4096), [100]),
 ], ids=["bf16_ragged", "fp32_mha", "bf16_depth1_k16", "bf16_llama_budget", "bf16_depth8_n60",
-        "bf16_depth8_n50", "bf16_depth8_n48", "bf16_177_slots"])
+        "bf16_depth8_n50", "bf16_depth8_n48", "bf16_177_slots", "bf16_max_vocab"])
 def test_draft_small_full_protocol(shape, prefix):
     need_gpu()
     B = shape.B

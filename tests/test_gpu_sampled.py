@@ -185,3 +185,12 @@ def test_bench_configurations(shape_name, B):
     trees = [synth.random_tree(61, sh.depth, 4400 + i) for i in range(B)]
     d = synth.sampled_tree_inputs(trees, sh.V, seed=970, device=DEV, target_noise=1.0)
     compare(d, 1.0, 7, range(3), sh.depth, 10)
+
+
+def test_vocabulary_beyond_64_chunks():
+    """V = 300000 (74 chunks of 4096 per node, more than one wave of partials per node) with a
+    ragged last chunk: the per-node combines loop over the chunks."""
+    need_gpu()
+    trees = [synth.full_tree(2, 2), synth.star_tree(5)]
+    d = synth.sampled_tree_inputs(trees, 300000, seed=61, device=DEV, target_noise=2.0)
+    compare(d, 1.0, 13, range(3), tree_depth(trees), max_kids(trees))
