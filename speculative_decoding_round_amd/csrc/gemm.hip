@@ -692,6 +692,7 @@ GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu) {
         if ((long)p.n_blocks * ((p.chunks_total + c4 - 1) / c4) >= 192) p.waves = 4;
       }
       splits = (kRingTargetWgs + p.n_blocks * p.waves - 1) / (p.n_blocks * p.waves);
+      if (p.waves == 1) splits = 1;   // >= 512 n-blocks cover the CUs: no fp32 partials to re-read
     }
     int cps = (p.chunks_total + splits - 1) / splits;
     cps = (cps + 8 * p.waves - 1) / (8 * p.waves) * (8 * p.waves);
