@@ -27,7 +27,7 @@ import sys
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LM_HEAD_KERNEL = re.compile(r"k_gemm_ring<1, 8, 4, false, 1, 1>")   # the LM head (role 1), one row tile
+LM_HEAD_KERNEL = re.compile(r"k_gemm_ring<1, 8, \d+, false, 1, 1>")   # the LM head (role 1), one row tile
 
 
 def source_hash(files=("gemm.hip", "common.h")) -> str:
