@@ -552,11 +552,6 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
   float* csc = cs.score + (size_t)b * PMAX;
   int32_t* topn = cs.topn + (size_t)b * N;
   float* topsc = cs.topsc + (size_t)b * N;
-  for (int i = threadIdx.x; i < ntop; i += blockDim.x) {
-    msc[i] = topsc[i];
-    midx[i] = topn[i];
-  }
-
   // ---- phase 1: per-row top-K over the chunks' lists (lane l holds chunk l's list) and
   // log-sum-exp from the chunks' (max, sum), combined in lane order
   if (w < R) {
@@ -595,6 +590,12 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
         if (dbg_lse) dbg_lse[sidx] = row_lse;
       }
     }
+  }
+  // the running list into LDS, from the highest thread down: the top waves sit out phase 1
+  // when R < 16, so these loads overlap its loads instead of preceding them
+  for (int i = (int)(blockDim.x - 1 - threadIdx.x); i < ntop; i += blockDim.x) {
+    msc[i] = topsc[i];
+    midx[i] = topn[i];
   }
   __syncthreads();
 
