@@ -138,8 +138,8 @@ def test_sampler_consistent_with_vectorised_draws():
 def test_chi_square_lossless():
     """Speculative sampling must reproduce the target distribution: on the K=3 two-level
     tree with V=16 and T=1, the first emitted token follows softmax(z_root), and the
-    second token, conditioned on accepting child c, follows softmax(z_c); 3e5 draws,
-    chi-square p > 0.01."""
+    second token, conditioned on accepting child c, follows softmax(z_c); 1e6 draws,
+    chi-square p > 0.01.  The rounds are drawn in blocks to bound memory."""
     V, T = 16, 1.0
     rng = np.random.default_rng(5)
     par = synth.full_tree(3, 2)
@@ -147,9 +147,13 @@ def test_chi_square_lossless():
     tok = [0] + [int(x) for x in rng.choice(V, 3, replace=False)] + \
         [int(x) for x in rng.integers(0, V, 9)]
     z = (rng.standard_normal((n, V)) * 1.2).astype(np.float32)
-    rounds = np.arange(300_000, dtype=np.uint64)
+    rounds = np.arange(1_000_000, dtype=np.uint64)
     seed = 20260601
-    y_root = O.draws_over_rounds(z[0], T, seed, rounds, 0, 0)
+
+    def draws(row, sel, i):
+        return np.concatenate([O.draws_over_rounds(row, T, seed, sel[a:a + 250_000], 0, i)
+                               for a in range(0, len(sel), 250_000)] or [np.zeros(0, np.int64)])
+    y_root = draws(z[0], rounds, 0)
 
     def probs(row):
         p = np.exp(row.astype(np.float64) - row.max())
@@ -161,7 +165,7 @@ def test_chi_square_lossless():
     # second token given the accepted depth-1 child c
     for c in (1, 2, 3):
         sel = rounds[y_root == tok[c]]
-        y_c = O.draws_over_rounds(z[c], T, seed, sel, 0, c)
+        y_c = draws(z[c], sel, c)
         obs = np.bincount(y_c, minlength=V)
         pc = probs(z[c] / T)
         keep = pc * obs.sum() >= 5

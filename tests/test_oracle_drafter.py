@@ -219,3 +219,48 @@ def test_child_score_never_exceeds_parent():
         sp = np.float32(rng.uniform(-30, 0))
         for v in z[:3]:
             assert O.child_score(sp, v, max(lse, z.max())) <= sp
+
+
+def _root_path(slots, s):
+    by = {x["slot"]: x for x in slots}
+    path = []
+    while s >= 0:
+        path.append(s)
+        s = by[s]["parent_slot"]
+    return path[::-1]
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_branching_tree_slots_match_textbook_paths(seed):
+    """On a branching tree (W > 1, so every depth evaluates several siblings and cousins),
+    every evaluated node must equal the textbook layer run along its own root-to-node path
+    alone: a drafted node sees the prefix and its ancestors, never a sibling, a cousin or a
+    node of another branch ([P3] 从序列到动态草稿树; [P2] 二、EAGLE-2动态草稿树, where a
+    second-level node attends to its parent and the root only).  The reference keys are
+    built independently for each slot (textbook layer over [prefix; root..slot])."""
+    D, K, W, N = 3, 3, 3, 9
+    w, dr = small_drafter(40 + seed)
+    P = 6
+    di = synth.draft_inputs(SMALL, seed=50 + seed, prefix=[P])
+    g = O.fuse_features(O.f64(di["h_low"]), O.f64(di["h_mid"]), O.f64(di["h_high"]), dr.w_fuse)[0]
+    res = O.draft_round(dr, D, K, W, N, di["h_low"], di["h_mid"], di["h_high"], di["root_tok"],
+                        di["kpre"], di["vpre"], [P])[0]
+    slots = res["slots"]
+    assert len(slots) == 1 + (D - 1) * W
+    # the tree branches: some depth holds evaluated nodes with different parents, and some
+    # node has an evaluated sibling
+    par = [x["parent_slot"] for x in slots if x["depth"] == 2]
+    assert len(par) == W
+    checked = 0
+    for x in slots:
+        path = _root_path(slots, x["slot"])
+        by = {y["slot"]: y for y in slots}
+        toks = [by[s]["token"] for s in path]
+        ref = textbook_layer(w, SMALL, toks, lambda t, f: torch.tensor(g) if t == 0 else f, P,
+                             di["kpre"], di["vpre"])[-1]
+        st = res["store"][x["slot"]]
+        np.testing.assert_allclose(st["a"], ref[0], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(st["z"], ref[1], rtol=1e-10, atol=1e-12)
+        assert abs(st["lse"] - ref[2]) < 1e-10
+        checked += 1
+    assert checked == len(slots)
