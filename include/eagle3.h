@@ -71,8 +71,8 @@ EAGLE3_API const char* eagle3_status_string(int status);
 
 /* ====================================================================================
  * Drafter description.
- * A single Llama-style decoder layer ([P1] 训练细节: "A single Transformer decoder
- * layer"; [P3] 多层特征融合到底融合了什么: a_{t+1} = D(e(x_t), g_t)) plus the feature-fusion
+ * One Llama-style decoder layer (the drafter is one decoder layer, [P1] 训练细节;
+ * [P3] 多层特征融合到底融合了什么: a_{t+1} = D(e(x_t), g_t)) plus the feature-fusion
  * projection and the LM head.  Every projection is stored [out_features, in_features]
  * row-major; all tensors have element type `dtype`.
  * ==================================================================================== */
@@ -360,7 +360,9 @@ EAGLE3_API int eagle3_accept_sampled(int B, int T, const int32_t* cu_nodes, cons
  *  Hkv, Dh >= 1 with Hkv * Dh * element size a multiple of 16 bytes; path_stride >= 1
  *  cu_nodes [B+1], path [B, path_stride], accept_len [B], dst_row [B]: int32 (device)
  *  k_tree, v_tree [T, Hkv, Dh] dtype; k_cache, v_cache [cache_rows, Hkv, Dh] dtype, written
- *  in place (they must not overlap the tree rows).
+ *  in place (they must not overlap the tree rows).  Both caches must hold cache_rows rows
+ *  of the tree's (Hkv, Dh): the kernel trusts cache_rows for its bounds, so a shorter cache
+ *  is an out-of-bounds write (the Python binding refuses mismatched shapes).
  *  dev_status: EAGLE3_DEV_BAD_PATH (accept_len outside [0, path_stride) or a node outside
  *  its request: those rows are skipped), EAGLE3_DEV_BAD_ROW (destination outside
  *  [0, cache_rows): skipped).
@@ -385,7 +387,9 @@ EAGLE3_API int eagle3_commit_kv(int B, int Hkv, int Dh, int dtype, int path_stri
  *
  *  w: the drafter, as for eagle3_draft_expand; n >= 1
  *  tokens, pos, dst_row [n] int32 (device); h_low, h_mid, h_high [n, d] dtype
- *  k_cache, v_cache [cache_rows, Hkv, Dh] dtype (the drafter prefix KV), written in place
+ *  k_cache, v_cache [cache_rows, Hkv, Dh] dtype (the drafter prefix KV), written in place;
+ *  both must hold cache_rows rows of the drafter's (Hkv, Dh) (the kernel trusts cache_rows
+ *  for its bounds; the Python binding refuses mismatched shapes)
  *  g_out [n, d] fp32, may be NULL
  *  dev_status: EAGLE3_DEV_BAD_TOKEN (token clamped into the vocabulary),
  *  EAGLE3_DEV_BAD_ROW (destination outside [0, cache_rows): row skipped)

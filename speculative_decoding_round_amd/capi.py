@@ -491,6 +491,17 @@ def eagle3_accept_sampled(cu_nodes, tokens, parents, logits, draft_logits, draft
 # ---------------------------------------------------------------------------------------
 
 
+def _cache_pair(k_cache, v_cache, row_shape) -> None:
+    """The kernels bound their writes by k_cache's row count alone: both caches must be
+    [rows, Hkv, Dh] with the same rows and the (Hkv, Dh) of what is written into them."""
+    if k_cache.dim() != 3 or tuple(k_cache.shape[1:]) != tuple(row_shape):
+        raise ValueError(f"k_cache shape {tuple(k_cache.shape)} is not [rows, {row_shape[0]}, {row_shape[1]}]")
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError(f"v_cache shape {tuple(v_cache.shape)} differs from k_cache {tuple(k_cache.shape)}")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("k_cache and v_cache must be contiguous")
+
+
 def eagle3_commit_kv(cu_nodes, path, accept_len, k_tree, v_tree, dst_row, k_cache, v_cache,
                      dev_status: Optional[torch.Tensor] = None, stream=None) -> None:
     """Copy the accepted path's tree K/V rows (path [B, path_stride] from eagle3_accept) into
@@ -503,6 +514,9 @@ def eagle3_commit_kv(cu_nodes, path, accept_len, k_tree, v_tree, dst_row, k_cach
         _dev(t, n, dt)
     B = cu_nodes.numel() - 1
     _, Hkv, Dh = k_tree.shape
+    if tuple(v_tree.shape) != tuple(k_tree.shape):
+        raise ValueError(f"v_tree shape {tuple(v_tree.shape)} differs from k_tree {tuple(k_tree.shape)}")
+    _cache_pair(k_cache, v_cache, (Hkv, Dh))
     st = lib().eagle3_commit_kv(B, Hkv, Dh, dtype_code(dt), path.shape[1], cu_nodes.data_ptr(),
                                 path.data_ptr(), accept_len.data_ptr(), k_tree.data_ptr(),
                                 v_tree.data_ptr(), dst_row.data_ptr(), k_cache.shape[0],
@@ -527,6 +541,7 @@ def eagle3_drafter_catchup(drafter: Eagle3Drafter, tokens, pos, h_low, h_mid, h_
                  ("v_cache", v_cache)):
         _dev(t, n, dt)
     n_rows = tokens.numel()
+    _cache_pair(k_cache, v_cache, (drafter.n_heads_kv, drafter.head_dim))
     if g_out is None:
         g_out = torch.empty((n_rows, drafter.d), dtype=torch.float32, device=h_low.device)
     _dev(g_out, "g_out", torch.float32)

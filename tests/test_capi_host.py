@@ -225,3 +225,22 @@ def test_draft_sampled_validation(lib):
     assert call(logits=P + 4) == -1            # slot logits must be 16-byte aligned
     assert call(rows=None) == -1
     assert call(ws_bytes=16) == -3
+
+
+def test_binding_refuses_mismatched_caches():
+    """The commit and catch-up kernels bound their writes by k_cache's row count: the binding
+    refuses caches whose row shape differs from what is written, or whose V cache has a
+    different shape from the K cache (either would be an out-of-bounds device write)."""
+    import torch
+    k = torch.empty((10, 8, 128))
+    capi._cache_pair(k, torch.empty((10, 8, 128)), (8, 128))
+    with pytest.raises(ValueError):
+        capi._cache_pair(k, torch.empty((9, 8, 128)), (8, 128))     # shorter V cache
+    with pytest.raises(ValueError):
+        capi._cache_pair(k, torch.empty((10, 8, 64)), (8, 128))     # V row of another shape
+    with pytest.raises(ValueError):
+        capi._cache_pair(torch.empty((10, 4, 128)), torch.empty((10, 4, 128)), (8, 128))
+    with pytest.raises(ValueError):
+        capi._cache_pair(torch.empty((10, 1024)), torch.empty((10, 1024)), (8, 128))
+    with pytest.raises(ValueError):
+        capi._cache_pair(torch.empty((10, 8, 256))[:, :, :128], torch.empty((10, 8, 128)), (8, 128))

@@ -9,7 +9,7 @@ import torch
 
 from oracle import eagle3_oracle as O
 from speculative_decoding_round_amd import capi, synth
-from tests.gpu_util import TOL, lse_err, need_gpu, np32, rel_err
+from tests.gpu_util import TOL, lse_err, need_gpu, np32, rel_err, rel_err_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -35,6 +35,7 @@ def test_causal_matches_oracle(L, Hq, Hkv, Dh):
     torch.cuda.synchronize()
     ro, rl = O.causal_attention(q.cpu(), k.cpu(), v.cpu(), sc)
     assert rel_err(np32(o), ro) <= TOL[BF]
+    assert rel_err_rows(np32(o), ro, Dh) <= TOL[BF]     # row 0 sees one key, the last row all
     assert lse_err(np32(lse), rl) <= TOL[BF]
 
 
@@ -51,6 +52,7 @@ def test_causal_full_size_sampled():
                   set(np.random.default_rng(3).integers(0, L, 8).tolist()))
     ro, rl = O.causal_attention(q.cpu(), k.cpu(), v.cpu(), sc, rows=rows)
     assert rel_err(np32(o[rows]), ro[rows]) <= TOL[BF]
+    assert rel_err_rows(np32(o[rows]), ro[rows], Dh) <= TOL[BF]
     assert lse_err(np32(lse[rows]), rl[rows]) <= TOL[BF]
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
 
@@ -65,6 +67,7 @@ def test_branch_matches_oracle(dt, steps):
     torch.cuda.synchronize()
     ro, rl = O.branch_attention(q.cpu(), kb.cpu(), vb.cpu(), sc)
     assert rel_err(np32(o), ro) <= TOL[dt]
+    assert rel_err_rows(np32(o), ro, Dh) <= TOL[dt]
     assert lse_err(np32(lse), rl) <= TOL[dt]
 
 

@@ -11,7 +11,7 @@ import torch
 
 from oracle import eagle3_oracle as O
 from speculative_decoding_round_amd import capi, synth
-from tests.gpu_util import TOL, lse_err, need_gpu, np32, rel_err, u64
+from tests.gpu_util import TOL, lse_err, need_gpu, np32, rel_err, rel_err_rows, u64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -105,6 +105,9 @@ ATTN_CASES = [
     ("fp32_dh128_many_splits", torch.float32, 4, 2, 128, [7, 64], [65, 1000], 9),
     ("bf16_dh64_no_prefix", torch.bfloat16, 8, 8, 64, [40, 2], [0, 0], 0),
     ("gqa8_bf16", torch.bfloat16, 64, 8, 128, [61], [515], 0),
+    # prefix lengths 0 and 8192 in one call: a lone root's output is its own value (large),
+    # a long prefix's output is an average of 8192 values (small); per-row tolerance
+    ("bf16_prefix_0_and_8192", torch.bfloat16, 32, 8, 128, [1, 61, 5], [0, 8192, 8192], 0),
 ]
 
 
@@ -123,6 +126,7 @@ def test_tree_attention_matches_oracle(name, dt, Hq, Hkv, Dh, sizes, prefix, spl
     mask_np = u64(mk["mask"])
     Oref, Lref = oracle_attention(vi, mask_np, scale)
     assert rel_err(np32(out["o"]), Oref) <= TOL[dt]
+    assert rel_err_rows(np32(out["o"]), Oref, Dh) <= TOL[dt]
     assert lse_err(np32(out["lse"]), Lref) <= TOL[dt]
     # each partial equals the oracle restricted to that split's keys
     S = out["splits"]
@@ -138,6 +142,7 @@ def test_tree_attention_matches_oracle(name, dt, Hq, Hkv, Dh, sizes, prefix, spl
                                     vi["cu_nodes"].tolist(), mask_np, vi["kpre"].cpu(), vi["vpre"].cpu(),
                                     cp, scale, key_filter=filt)
         assert rel_err(np32(out["o_part"][s]), o_s) <= max(TOL[dt], 1e-4) or np.all(o_s == 0)
+        assert rel_err_rows(np32(out["o_part"][s]), o_s, Dh) <= max(TOL[dt], 1e-4)
         assert lse_err(np32(out["lse_part"][s]), l_s) <= TOL[dt]
 
 
