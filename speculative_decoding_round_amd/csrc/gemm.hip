@@ -8,6 +8,7 @@
 // A workgroup is WK waves that split its k-range (summed in LDS in wave order, so results
 // are deterministic); workgroups tile (n-block, k-split).
 #include <cstring>
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -331,6 +332,190 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_ring(const bf16* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------------------
+// bf16 weight streaming for 32 < M <= 192 rows (a batch of requests times the frontier).
+// Past two row tiles a wave can no longer keep its X rows for a k-block in registers beside
+// the accumulators of eight W tiles, and X re-read per wave would cost more load traffic
+// than W itself.  So the four waves of a workgroup split the rows instead of the k-range:
+// wave w owns row tiles w, w + 4, w + 8 (MT tiles of 16 rows in all), and every W tile is
+// fetched once per workgroup into one shared LDS ring (two LDS-DMA instructions per wave,
+// whole 512-byte row segments, non-temporal) and read by all four waves against their own
+// rows.  The block's X (MT tiles x 8 chunks) has an LDS buffer of its own; each wave copies
+// its rows into registers at the block's first W tile, and the next block's X is fetched
+// right after the barrier of the second W tile, when every wave has its copy.
+// One barrier per W tile orders the ring: past it the tile's DMA has landed for every wave
+// (each waited for its own two instructions by vmcnt), and every wave has finished reading
+// the slot that the DMA issued next overwrites.  The vmcnt waits count the DMA instructions
+// issued after the awaited ones, including the next block's X when it lies between them.
+// Needs K % 32 == 0; MT <= 12; NT >= NS.
+// ---------------------------------------------------------------------------------------
+template <int I, int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+  if constexpr (I < N) {
+    fn(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(fn);
+  }
+}
+
+template <int MT, int NT, int NS, bool SILU, int ROLE>
+__global__ __launch_bounds__(256) void k_gemm_wide(const bf16* __restrict__ X, int M, int ldx,
+                                                   const bf16* __restrict__ W, int N, int K,
+                                                   float* __restrict__ Y, int n_blocks,
+                                                   int chunks_total, int chunks_per_split,
+                                                   void* __restrict__ act, int F) {
+  constexpr int MTW = (MT + 3) / 4;   // row tiles per wave (at most)
+  static_assert(MT >= 1 && MT <= 12, "row tiles");
+  static_assert(NS >= 3 && NT >= NS, "the next block's X is issued after W stage NS of a block");
+  static_assert(2 * (NS - 1) <= 63 && 2 * (NS - 2) + 2 * MT <= 63, "outstanding DMA must fit the vmcnt counter");
+  static_assert((MT + NS) * RING_TILE <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(16))) char lds[(MT + NS) * RING_TILE];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int nb = blockIdx.x % n_blocks, ks = blockIdx.x / n_blocks;
+  const int cs0 = ks * chunks_per_split;
+  const int cs1 = min(chunks_total, cs0 + chunks_per_split);
+  const int n_kb = cs1 > cs0 ? (cs1 - cs0 + 7) / 8 : 0;
+  const int total = n_kb * NT;                     // W stages
+  const uint32_t xbuf0 = lds_u32(lds);
+  const uint32_t wring0 = xbuf0 + MT * RING_TILE;
+  const char* wring = lds + MT * RING_TILE;
+
+  // this wave's two DMA instructions of a 16-row tile: rows 4 wv .. 4 wv + 3
+  auto dma_tile = [&](const bf16* base, int ld, int row0, int rmax, int c0, int lastp, uint32_t slot) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = 2 * wv + h;
+      const int rt = 2 * i + (lane >> 5);
+      const int row = min(row0 + rt, rmax);
+      const int pc = min((lane & 31) ^ rt, lastp);
+      ring_dma(base + (size_t)row * ld + c0 * 32 + pc * 8, slot + i * 1024);
+    }
+  };
+  auto issue_w = [&](int s) {      // stage s: k-block s / NT, W tile s % NT of this n-block
+    const int j = s / NT, t = s - j * NT;
+    const int c0 = cs0 + j * 8;
+    dma_tile(W, K, tile_row0<NT, SILU>(nb, t, F), N - 1, c0, min(8, cs1 - c0) * 4 - 1,
+             wring0 + (uint32_t)(s % NS) * RING_TILE);
+  };
+  auto issue_x = [&](int j) {      // the MT row tiles of X for k-block j
+    const int c0 = cs0 + j * 8;
+    const int lastp = min(8, cs1 - c0) * 4 - 1;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) dma_tile(X, ldx, t * 16, M - 1, c0, lastp, xbuf0 + t * RING_TILE);
+  };
+  auto opoff = [&](int u) { return (uint32_t)(r16 * 512 + (((4 * u + g) ^ r16) * 16)); };
+
+  floatx4 acc[NT][MTW];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int mw = 0; mw < MTW; ++mw) acc[nt][mw] = floatx4{0.f, 0.f, 0.f, 0.f};
+  u32x4 xv[8][MTW];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+#pragma unroll
+    for (int mw = 0; mw < MTW; ++mw) xv[u][mw] = u32x4{0, 0, 0, 0};
+
+  // this wave's X rows of block jb into registers; rows of tiles it does not own (past MT)
+  // read tile 0 and are zeroed, so every wave runs MTW row tiles without a branch
+  auto read_x = [&](int jb) {
+    const int nvalid = min(8, cs1 - (cs0 + jb * 8));
+#pragma unroll
+    for (int mw = 0; mw < MTW; ++mw) {
+      const bool own = mw * 4 + 3 < MT || mw * 4 + wv < MT;
+      const char* xt = lds + (own ? mw * 4 + wv : 0) * RING_TILE;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xt + opoff(u));
+        xv[u][mw] = (own && u < nvalid) ? v : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  u32x4 wf[2][8];
+  auto read_w = [&](int st, u32x4 (&f)[8]) {
+    const char* slot = wring + (st % NS) * RING_TILE;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) f[u] = *reinterpret_cast<const u32x4*>(slot + opoff(u));
+  };
+
+  // Pipeline.  The ring holds NS W stages (stage s in slot s % NS).  Iteration s: wait for
+  // W(s+1) and pass the barrier; refill the slot of W(s), whose reads every wave finished
+  // before the barrier, with W(s+NS); read W(s+1)'s operands; then run stage s's MFMAs, so
+  // the operand reads of the next stage overlap this stage's matrix work.  The next block's
+  // X goes into the X buffer after the barrier of a block's first stage (every wave read
+  // the block's X before it) and is read into registers after the block's last MFMAs.
+  if (n_kb > 0) issue_x(0);
+#pragma unroll
+  for (int s0 = 0; s0 < NS; ++s0)
+    if (s0 < total) issue_w(s0);
+  if (total > 0) {
+    if (NS - 1 < total) ring_wait_vm<2 * (NS - 1)>();
+    else ring_wait_vm<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    read_x(0);
+    read_w(0, wf[0]);
+  }
+
+  int s = 0;
+  for (int j = 0; j < n_kb; ++j) {
+    const bool next_x = j + 1 < n_kb;
+    static_for<0, NT>([&](auto ntc) {
+      constexpr int nt = decltype(ntc)::value;
+      constexpr int cur = nt & 1;          // NT is even: stage parity is nt's
+      // lgkmcnt(0) through the builtin, on every path, so that the compiler's own wait
+      // tracking knows this stage's operand reads (issued one iteration earlier) are
+      // complete and adds no waits on the next stage's reads before the MFMAs
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      if (s + 1 < total) {
+        // own DMA of W(s+1) has landed.  Issued after it so far: W(s+2 .. s+NS-1), and the
+        // next block's X when it follows W(s+1) (it was issued right after W(j NT + NS), at
+        // this block's first stage).  At a block's last stage the next block's X must have
+        // landed too: it precedes W(s+1), or (NT == NS) follows it directly, and the
+        // 2 (NS - 2) instructions left in flight are W(s+2 ..).
+        if (s + NS - 1 < total) {
+          if constexpr (nt == NT - 1) {
+            ring_wait_vm<2 * (NS - 2)>();
+          } else if constexpr (nt >= 1 && nt <= NS - 1) {
+            if (next_x) ring_wait_vm<2 * (NS - 2) + 2 * MT>();
+            else ring_wait_vm<2 * (NS - 2)>();
+          } else {
+            ring_wait_vm<2 * (NS - 2)>();
+          }
+        } else {
+          ring_wait_vm<0>();
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (s + NS < total) issue_w(s + NS);
+        if constexpr (nt == 0) {
+          if (next_x) issue_x(j + 1);
+        }
+        read_w(s + 1, wf[cur ^ 1]);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int mw = 0; mw < MTW; ++mw) acc[nt][mw] = Mfma<bf16>::run(wf[cur][u], xv[u][mw], acc[nt][mw]);
+      if constexpr (nt == NT - 1) {
+        if (next_x) read_x(j + 1);
+      }
+      ++s;
+    });
+  }
+
+  float* Ys = Y + (size_t)ks * M * N;
+  constexpr int NOUT = SILU ? NT / 2 : NT;
+#pragma unroll
+  for (int nt = 0; nt < NOUT; ++nt)
+#pragma unroll
+    for (int mw = 0; mw < MTW; ++mw)
+      if (mw * 4 + wv < MT) {
+        const int m = (mw * 4 + wv) * 16 + r16;
+        const int n = tile_row0<NT, SILU>(nb, nt, F) + 4 * g;
+        store_out<bf16, SILU>(Ys, act, M, N, F, m, n, acc[nt][mw], acc[SILU ? nt + NOUT : nt][mw]);
+      }
+}
+
+// ---------------------------------------------------------------------------------------
 // bf16 GEMM for many rows (M >= 256), bound by the matrix cores:
 //   Y[m][n] = sum_k X[m][k] W[n][k], fp32 out.
 // A workgroup owns a 256 (n) x 256 (m) output tile; its four waves (one per SIMD) each hold
@@ -595,10 +780,54 @@ int launch_ring(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, f
   }
 }
 
+// Wide kernel shapes: 16 W tiles per k-block (256 output features, so X costs MT/16 of W's
+// DMA traffic), the ring as deep as the X buffer leaves room for in 160 KB of LDS.  The
+// SiLU gate/up (no k-split) takes 8 tiles (64 gate + 64 up features) when 16 would leave
+// CUs idle.
+constexpr int wide_ns(int mt, int nt) { return nt < 20 - mt ? nt : 20 - mt; }
+constexpr int kWideMTs[] = {3, 4, 6, 8, 10};
+
+template <int MT, int NT, int ROLE, bool SILU>
+int launch_wide_r(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y, void* act,
+                  hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm_wide<MT, NT, wide_ns(MT, NT), SILU, ROLE>), dim3(p.n_blocks * p.splits),
+                     dim3(256), 0, s, (const bf16*)X, p.M, ldx, (const bf16*)W, p.N, p.K, Y, p.n_blocks,
+                     p.chunks_total, p.chunks_per_split, act, p.N / 2);
+  return e3h::launch_status();
+}
+
+template <int MT>
+int launch_wide(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y, void* act,
+                hipStream_t s, int role) {
+  if (p.silu) {
+    return p.NT == 16 ? launch_wide_r<MT, 16, 6, true>(p, X, ldx, W, Y, act, s)
+                      : launch_wide_r<MT, 8, 6, true>(p, X, ldx, W, Y, act, s);
+  }
+  switch (role) {
+    case 1: return launch_wide_r<MT, 16, 1, false>(p, X, ldx, W, Y, act, s);
+    case 2: return launch_wide_r<MT, 16, 2, false>(p, X, ldx, W, Y, act, s);
+    case 3: return launch_wide_r<MT, 16, 3, false>(p, X, ldx, W, Y, act, s);
+    case 4: return launch_wide_r<MT, 16, 4, false>(p, X, ldx, W, Y, act, s);
+    case 5: return launch_wide_r<MT, 16, 5, false>(p, X, ldx, W, Y, act, s);
+    default: return launch_wide_r<MT, 16, 0, false>(p, X, ldx, W, Y, act, s);
+  }
+}
+
 template <typename T>
 int dispatch_gemm(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y,
                   void* act, hipStream_t s, const char* tag) {
   if constexpr (sizeof(T) == 2) {
+    if (p.wide) {
+      const int role = gemm_role(tag);
+      switch (p.MT) {
+        case 3: return launch_wide<3>(p, X, ldx, W, Y, act, s, role);
+        case 4: return launch_wide<4>(p, X, ldx, W, Y, act, s, role);
+        case 6: return launch_wide<6>(p, X, ldx, W, Y, act, s, role);
+        case 8: return launch_wide<8>(p, X, ldx, W, Y, act, s, role);
+        case 10: return launch_wide<10>(p, X, ldx, W, Y, act, s, role);
+        default: return EAGLE3_EUNSUPPORTED;
+      }
+    }
     if (p.ring) {
       const int role = gemm_role(tag);
       return p.MT == 1 ? launch_ring<1>(p, X, ldx, W, Y, act, s, role)
@@ -629,6 +858,7 @@ GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu) {
   p.silu = silu;
   p.ring = false;
   p.tile = false;
+  p.wide = false;
   p.M = M;
   p.N = N;
   p.K = K;
@@ -699,6 +929,51 @@ GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu) {
     p.chunks_per_split = cps;
     p.splits = (p.chunks_total + cps - 1) / cps;
     return p;
+  }
+  if (dtype == EAGLE3_BF16 && mt_need >= 3 && mt_need <= 10 && K % 32 == 0) {
+    // 33 .. 160 rows: the wide kernel (waves split the rows, one shared W ring per
+    // workgroup, one workgroup per CU).  A k-split in whole 8-chunk blocks brings the grid
+    // to about one workgroup per CU; its count minimises (rounds of workgroups over the CUs)
+    // x (blocks per workgroup) at ~25 GB/s per CU plus the fp32 partials' write and read.
+    int mt = 0;
+    for (int v : kWideMTs)
+      if (v >= mt_need) {
+        mt = v;
+        break;
+      }
+    // SiLU: 16 tiles when that still gives ~200 workgroups, else 8
+    const int nt = silu && (N / 2) / 128 < 200 ? 8 : 16;
+    if (!silu || (N / 2) % (16 * (nt / 2)) == 0) {
+      p.wide = true;
+      p.MT = mt;
+      p.NT = nt;
+      p.waves = 4;
+      p.chunks_total = K / 32;
+      const int n_kb = (p.chunks_total + 7) / 8;
+      if (silu) {
+        p.n_blocks = (N / 2) / (16 * (nt / 2));
+        p.chunks_per_split = n_kb * 8;
+        p.splits = 1;
+        return p;
+      }
+      p.n_blocks = ((N + 15) / 16 + nt - 1) / nt;
+      const double t_kb = nt * 8192.0 / 25e9;
+      double best = 0;
+      int best_kbps = n_kb;
+      for (int kbps = n_kb; kbps >= 1; --kbps) {
+        const int sp = (n_kb + kbps - 1) / kbps;
+        const long wgs = (long)p.n_blocks * sp;
+        const long rounds = (wgs + kTileCUs - 1) / kTileCUs;
+        const double t = (double)rounds * kbps * t_kb + (sp > 1 ? 2.0 * sp * (double)M * N * 4 / 6e12 : 0.0);
+        if (kbps == n_kb || t < best * 0.97) {
+          best = t;
+          best_kbps = kbps;
+        }
+      }
+      p.chunks_per_split = best_kbps * 8;
+      p.splits = (n_kb + best_kbps - 1) / best_kbps;
+      return p;
+    }
   }
   static const int mts[] = {1, 2, 3, 4, 6, 8, 10};
   p.MT = 0;

@@ -65,7 +65,8 @@ struct GemmPlan {
   int M, N, K, MT, NT, n_blocks, splits, chunks_total, chunks_per_split, waves;
   bool silu;
   bool ring;   // bf16 LDS-ring kernel (one wave per workgroup)
-  bool tile;   // bf16 tiled MFMA kernel for many rows (M >= 256)
+  bool tile;   // bf16 tiled MFMA kernel for many rows (M > 160)
+  bool wide;   // bf16 wide kernel (33 .. 160 rows: four waves split the rows, shared W ring)
 };
 GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu = false);
 int launch_gemm(const GemmPlan& p, int dtype, const void* X, int ldx, const void* W, float* Ypart,
