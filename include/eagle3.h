@@ -308,6 +308,24 @@ EAGLE3_API int eagle3_accept(int B, int T, const int32_t* cu_nodes, const int32_
                   int32_t* bonus, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * eagle3_accept_noalloc -- eagle3_accept for callers that cannot allocate device memory
+ * (code under stream capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, rule and outputs as eagle3_accept, without the workspace: its scratch
+ * (the per-(node, 4096-token chunk) winner list, 8 bytes per entry) is a fixed 1 MiB array
+ * inside the library, one per GPU, held until the process ends.  Calls whose
+ * T * ceil(V / 4096) exceeds eagle3_accept_noalloc_max_entries() (131008; e.g. T <= 4094 at
+ * V = 128256) return EAGLE3_EUNSUPPORTED before anything is enqueued.  Every call on a GPU
+ * shares that GPU's array, so calls that overlap on one GPU (other streams or host threads)
+ * race; serialise them.  Nothing is allocated or freed.
+ * ------------------------------------------------------------------------------------ */
+EAGLE3_API size_t eagle3_accept_noalloc_max_entries(void);
+EAGLE3_API int eagle3_accept_noalloc(int B, int T, const int32_t* cu_nodes, const int32_t* tokens,
+                                     const int32_t* parents, const uint64_t* mask, int W64,
+                                     const void* logits, int V, int dtype, float temperature,
+                                     uint64_t seed, uint64_t round, int max_depth, int32_t* accept_len,
+                                     int32_t* path, int32_t* out_tokens, int32_t* bonus, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * eagle3_accept_sampled -- acceptance of sampled candidates.  [P2] 四 DFlash (each drafted
  * token is kept with probability min(1, p_target / p_draft), dice thrown left to right, the
  * first rejection ends the kept prefix); [P3] 先看 checkpoint 最终要参与什么计算 (keep the

@@ -104,6 +104,10 @@ EXPORTS = {
                               c_void_p, c_int, c_int, c_float, c_uint64, c_uint64, c_int,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                               c_void_p]),
+    "eagle3_accept_noalloc_max_entries": (c_size_t, []),
+    "eagle3_accept_noalloc": (c_int, [c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                                      c_void_p, c_int, c_int, c_float, c_uint64, c_uint64, c_int,
+                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "eagle3_accept_sampled_workspace_size": (c_size_t, [c_int, c_int, c_int]),
     "eagle3_accept_sampled": (c_int, [c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
                                       c_int, c_void_p, c_int, c_int, c_void_p, c_int, c_float,
@@ -443,6 +447,33 @@ def eagle3_accept(cu_nodes, tokens, parents, mask, logits, temperature: float, s
                              out["out_tokens"].data_ptr(), out["bonus"].data_ptr(),
                              workspace.data_ptr(), workspace.numel(), _stream(stream))
     _check("eagle3_accept", st)
+    return out
+
+
+def eagle3_accept_noalloc(cu_nodes, tokens, parents, mask, logits, temperature: float, seed: int,
+                          round: int, max_depth: int, out: Optional[dict] = None, stream=None) -> dict:
+    """eagle3_accept without a workspace (the library's fixed per-GPU scratch array); for
+    callers that cannot allocate.  Pass `out` to allocate nothing here either."""
+    _dev(cu_nodes, "cu_nodes", torch.int32)
+    _dev(tokens, "tokens", torch.int32)
+    _dev(parents, "parents", torch.int32)
+    _dev(mask, "mask", torch.uint64)
+    _dev(logits, "logits")
+    B = cu_nodes.numel() - 1
+    T, V = logits.shape
+    W64 = mask.shape[1] if mask.dim() == 2 else 1
+    dev = logits.device
+    if out is None:
+        out = {"accept_len": torch.empty((B,), dtype=torch.int32, device=dev),
+               "path": torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev),
+               "out_tokens": torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev),
+               "bonus": torch.empty((B,), dtype=torch.int32, device=dev)}
+    st = lib().eagle3_accept_noalloc(B, T, cu_nodes.data_ptr(), tokens.data_ptr(), parents.data_ptr(),
+                                     mask.data_ptr(), W64, logits.data_ptr(), V, dtype_code(logits.dtype),
+                                     float(temperature), int(seed) & (2**64 - 1), int(round) & (2**64 - 1),
+                                     int(max_depth), out["accept_len"].data_ptr(), out["path"].data_ptr(),
+                                     out["out_tokens"].data_ptr(), out["bonus"].data_ptr(), _stream(stream))
+    _check("eagle3_accept_noalloc", st)
     return out
 
 

@@ -244,3 +244,26 @@ def test_binding_refuses_mismatched_caches():
         capi._cache_pair(torch.empty((10, 1024)), torch.empty((10, 1024)), (8, 128))
     with pytest.raises(ValueError):
         capi._cache_pair(torch.empty((10, 8, 256))[:, :, :128], torch.empty((10, 8, 128)), (8, 128))
+
+
+def test_accept_noalloc_host_validation(lib):
+    """eagle3_accept_noalloc rejects a winner list larger than its fixed scratch array (and
+    bad arguments) on the host, before any device call."""
+    P = 1 << 12
+    n_max = lib.eagle3_accept_noalloc_max_entries()
+    assert n_max == (1 << 20) // 8 - 64
+    V = 128256
+    T_ok = n_max // 32
+    T_big = T_ok + 1
+    # B, T, cu_nodes, tokens, parents, mask, W64, logits, V, dtype, temperature, seed, round,
+    # max_depth, accept_len, path, out_tokens, bonus, stream
+    args = [1, T_big, P, P, P, P, 1, P, V, 1, 0.0, 0, 0, 6, P, P, P, P, None]
+    assert lib.eagle3_accept_noalloc(*args) == -2                 # over the scratch array
+    bad = list(args); bad[1] = 0
+    assert lib.eagle3_accept_noalloc(*bad) == -1                  # T < B
+    bad = list(args); bad[6] = 5
+    assert lib.eagle3_accept_noalloc(*bad) == -2                  # W64 > 4
+    bad = list(args); bad[10] = -1.0
+    assert lib.eagle3_accept_noalloc(*bad) == -1                  # negative temperature
+    bad = list(args); bad[2] = None
+    assert lib.eagle3_accept_noalloc(*bad) == -1                  # null cu_nodes
