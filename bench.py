@@ -1,13 +1,17 @@
 """Benchmark: one EAGLE-3 draft-tree round + one tree-verification round per step.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama70b]
 
 A step runs the whole hot path on one stream through the C-ABI:
   eagle3_draft_expand -> eagle3_build_tree_mask -> eagle3_tree_attention (partials)
   -> eagle3_lse_merge -> eagle3_accept.
-Inputs are seeded synthetic tensors already resident in HBM (random-init drafter weights of
-the Llama-3.1-8B shape, Gaussian features and KV); the verify layer's Q/K/V and the target
-logits are given, untimed.  Prints one JSON line.
+The default workload is the largest one that fits one GPU: a Llama-3.1-70B-shaped drafter
+(d 8192, 64 / 8 heads of 128, FFN 28672, vocabulary 128256, fusion 24576 -> 8192), batch 4,
+8192-token prefixes, 60-node trees of depth 6 (K = W = 10), acceptance at T = 0.7.  Inputs
+are seeded synthetic tensors already resident in HBM (random-init weights, Gaussian features
+and KV); the verify layer's Q/K/V and the target logits (the drafter's own logits plus
+noise) are given, untimed.  The whole rounds of the 8B-shaped and batch-16 workloads are
+reported as extra fields.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -30,14 +34,17 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "batch16", "llama70b", "tiny"])
+    ap.add_argument("--workload", default="llama70b", choices=["llama8b", "batch16", "llama70b", "tiny"])
+    ap.add_argument("--no-other-rounds", action="store_true",
+                    help="skip the whole rounds of the other workloads (extra fields)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ops", action="store_true", help="skip the per-op roofline measurements")
     ap.add_argument("--only-ops", action="store_true",
                     help="measure only the per-op rooflines (no round, no CPU baseline)")
     ap.add_argument("--ops", default=",".join(OP_KEYS),
                     help="comma-separated per-op measurements to run")
-    ap.add_argument("--kernel", default="gemm_lm_head", help="kernel timed for the roofline")
+    ap.add_argument("--kernel", default="gemm_lm_head",
+                    help="kernel timed for the roofline (gemm_lm_head: the depth steps' LM head)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (for scaling HBM byte "
                          "counters against a kernel of known traffic)")
@@ -45,9 +52,21 @@ def parse():
 
 
 class Round:
-    """Preallocated buffers for one draft + verify round."""
+    """Preallocated buffers for one draft + verify round.
 
-    def __init__(self, shape, dev, seed=1234):
+    Per-round inputs (the drafter's prefix KV, the verify layer's Q/K/V and prefix KV, the
+    target logits) exist in `ncopy` identical copies at different addresses, and round r reads
+    copy r % ncopy, so that together they exceed the 256 MB Infinity Cache twice and every
+    round reads them from HBM, as a serving loop over fresh requests would.
+
+    Target logits (harness, untimed): one draft round is run with per-slot logits kept; at
+    every drafted node the drafter evaluated, Z_t = Z_d + N(0, noise^2) (the workloads'
+    "target logits correlated with the draft logits"); at a leaf the drafter never evaluated
+    (it only decides the bonus token) a fresh N(0, 1) row.  The batch-16 workload instead takes
+    N(0, 1) rows with one planted path per request (a uniform length 0..depth, a random node at
+    that depth, each edge's child token raised above its parent row's maximum)."""
+
+    def __init__(self, shape, dev, seed=1234, rotate=True, targets=True):
         import torch
         from speculative_decoding_round_amd import capi, synth
         self.shape = shape
@@ -55,7 +74,7 @@ class Round:
         self.B = shape.B
         self.prefix = synth.prefix_lengths(shape, seed)
         self.w = synth.drafter_weights(shape, seed=seed, device=dev)
-        self.di = synth.draft_inputs(shape, seed=seed + 1, device=dev, prefix=self.prefix)
+        di = synth.draft_inputs(shape, seed=seed + 1, device=dev, prefix=self.prefix)
         self.drafter = capi.make_drafter(self.w, shape.Hq, shape.Hkv, shape.Dh)
         self.tree = capi.Eagle3TreeCfg(depth=shape.depth, topk=shape.topk, width=shape.width,
                                        n_nodes=shape.n_nodes)
@@ -73,7 +92,7 @@ class Round:
                           "n_nodes": torch.empty((self.B,), **i32)}
         # verify layer: queries and tree K/V for every node, its own prefix KV, target logits
         trees = [[-1] + [0] * (n1 - 1)] * self.B        # shapes only; topology comes from the draft
-        self.vi = synth.verify_inputs(shape, trees, self.prefix, seed=seed + 2, device=dev)
+        vi = synth.verify_inputs(shape, trees, self.prefix, seed=seed + 2, device=dev)
         self.cu_nodes = torch.arange(0, self.T + 1, n1, **i32)
         self.mask_out = {"mask": torch.empty((self.T, 1), dtype=torch.uint64, device=dev),
                          "depth": torch.empty((self.T,), **i32), "pos": torch.empty((self.T,), **i32)}
@@ -93,9 +112,58 @@ class Round:
                         "bonus": torch.empty((self.B,), **i32)}
         self.scale = float(1.0 / math.sqrt(Dh))
         self.round = 0
+        self.di, self.vi = di, vi
+        if targets:
+            vi["logits"] = self.target_logits(seed + 3)
+        per_round = sum(t.numel() * t.element_size() for t in (di["kpre"], di["vpre"]))
+        per_round += sum(vi[k].numel() * vi[k].element_size()
+                         for k in ("q", "k_tree", "v_tree", "kpre", "vpre", "logits"))
+        self.per_round_input_bytes = per_round
+        self.ncopy = _copies(per_round) if rotate else 1
+        dk, vk = ("kpre", "vpre"), ("q", "k_tree", "v_tree", "kpre", "vpre", "logits")
+        self.di_c = [di] + [dict(di, **{k: di[k].clone() for k in dk}) for _ in range(self.ncopy - 1)]
+        self.vi_c = [vi] + [dict(vi, **{k: vi[k].clone() for k in vk}) for _ in range(self.ncopy - 1)]
+
+    def target_logits(self, seed):
+        """Target logits [T, V] for the drafted trees (see the class docstring)."""
+        import torch
+        from speculative_decoding_round_amd import synth
+        s, c, di = self.shape, self.capi, self.di
+        out = c.eagle3_draft_expand(self.drafter, self.tree, di["h_low"], di["h_mid"], di["h_high"],
+                                    di["root_tok"], di["kpre"], di["vpre"], di["cu_prefix"],
+                                    self.max_prefix, debug=True, debug_logits=True)
+        torch.cuda.synchronize()
+        tok, par = out["tokens"].cpu(), out["parents"].cpu()
+        dbg = out["debug"]
+        st, sp = dbg["slot_token"].cpu(), dbg["slot_parent"].cpu()
+        g = torch.Generator(device="cpu").manual_seed(seed)
+        rows = []
+        for b in range(self.B):
+            slot_of = {0: 0}
+            for i in range(1, self.n1):
+                ps = slot_of.get(int(par[b, i]), -1)
+                hit = ((sp[b] == ps) & (st[b] == tok[b, i])).nonzero() if ps >= 0 else []
+                slot_of[i] = int(hit[0]) if len(hit) else -1
+            for i in range(self.n1):
+                z = torch.randn(s.V, generator=g)
+                if s.verify_tree != "random" and slot_of[i] >= 0:
+                    z = dbg["slot_logits"][b, slot_of[i]].cpu() + s.noise * z
+                rows.append(z)
+        z = torch.stack(rows)
+        if s.verify_tree == "random":
+            dep = out["depth"].cpu()
+            for b in range(self.B):
+                L = int(torch.randint(0, s.depth + 1, (1,), generator=g))
+                cand = [i for i in range(self.n1) if int(dep[b, i]) == L] or [0]
+                end = cand[int(torch.randint(0, len(cand), (1,), generator=g))]
+                synth.plant_path(z, tok.view(-1), par[b].tolist(), b * self.n1, end)
+        self.draft_tokens = tok
+        self.draft_parents = par
+        return z.to(synth.torch_dtype(s)).to(self.di["kpre"].device)
 
     def step(self):
-        c, s, di, vi = self.capi, self.shape, self.di, self.vi
+        c, s = self.capi, self.shape
+        di, vi = self.di_c[self.round % self.ncopy], self.vi_c[self.round % self.ncopy]
         out = c.eagle3_draft_expand(self.drafter, self.tree, di["h_low"], di["h_mid"], di["h_high"],
                                     di["root_tok"], di["kpre"], di["vpre"], di["cu_prefix"],
                                     self.max_prefix, workspace=self.ws_draft, out=self.draft_out)
@@ -113,6 +181,16 @@ class Round:
                         seed=20260101, round=self.round, max_depth=s.depth, workspace=self.ws_acc,
                         out=self.acc_out)
         self.round += 1
+
+    def mean_accept_len(self, rounds=32):
+        """Mean accept length per request over `rounds` further rounds (each round draws its
+        own Gumbel noise at T > 0; greedy rounds repeat)."""
+        import torch
+        hist = torch.empty((rounds, self.B), dtype=torch.int32, device=self.acc_out["accept_len"].device)
+        for r in range(rounds):
+            self.step()
+            hist[r].copy_(self.acc_out["accept_len"])
+        return float(hist.float().mean().item())
 
 
 def recorded(name: str, field: str):
@@ -151,64 +229,75 @@ def lm_head_bytes(shape, M):
     return shape.V * shape.d * es + M * shape.d * es + M * shape.V * 4
 
 
-def cpu_baseline(rnd: Round):
-    """Time the oracle (as written, untuned) on a bounded sample: one full draft + verify
-    round of the same workload on the host cores."""
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(rnd: Round, repeats: int = 3):
+    """Time the oracle (as written, untuned) on a bounded sample of the same workload: the
+    whole draft + verify round of request 0 alone (its prefix, the same drafter shapes, tree
+    budget, verify splits and acceptance rule), median of `repeats` runs on the host cores,
+    then one run on one core.  Scaled to verified tree tokens per second."""
     import numpy as np
     import torch
     from oracle import eagle3_oracle as O
-    from speculative_decoding_round_amd import synth
+    from threadpoolctl import threadpool_info, threadpool_limits
     s = rnd.shape
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     w = {k: v.cpu() for k, v in rnd.w.items()}
     di = {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in rnd.di.items()}
     drafter = O.Drafter(w, s.Hq, s.Hkv, s.Dh)                 # fp64 upcast: not timed
-    vi = {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in rnd.vi.items()}
+    n1, P = rnd.n1, rnd.prefix[0]
+    vi = {k: rnd.vi[k][:n1].cpu() for k in ("q", "k_tree", "v_tree", "logits")}
+    vi["kpre"] = rnd.vi["kpre"][:P].cpu()
+    vi["vpre"] = rnd.vi["vpre"][:P].cpu()
+    S = rnd.S
 
     def one_round():
         t0 = time.perf_counter()
-        res = O.draft_round(drafter, s.depth, s.topk, s.width, s.n_nodes, di["h_low"], di["h_mid"],
-                            di["h_high"], di["root_tok"], di["kpre"], di["vpre"], rnd.prefix)
-        parents, tokens, cu = [], [], [0]
-        for r in res:
-            n = len(r["parents"])
-            parents += r["parents"] + [0] * (rnd.n1 - n)
-            tokens += r["tokens"] + [0] * (rnd.n1 - n)
-            cu.append(cu[-1] + rnd.n1)
-        cup = vi["cu_prefix"].tolist()
+        res = O.draft_round(drafter, s.depth, s.topk, s.width, s.n_nodes, di["h_low"][:1], di["h_mid"][:1],
+                            di["h_high"][:1], di["root_tok"][:1], di["kpre"][:P], di["vpre"][:P], [P])[0]
+        n = len(res["parents"])
+        parents = res["parents"] + [0] * (n1 - n)
+        tokens = res["tokens"] + [0] * (n1 - n)
+        cu, cup = [0, n1], [0, P]
         mask, _, _, _ = O.build_tree_mask(parents, cu, cup)
-        S = rnd.S
         o_parts, l_parts = [], []
         for sp in range(S + 1):
-            def filt(b, P, sp=sp):
-                keep = np.zeros(P, dtype=bool)
+            def filt(b, Pb, sp=sp):
+                keep = np.zeros(Pb, dtype=bool)
                 if sp < S:
-                    ch = (-(-P // S) + 127) // 128 * 128
-                    keep[min(P, sp * ch):min(P, sp * ch + ch)] = True
-                return keep, np.full(rnd.n1, sp == S)
-            o, l = O.tree_attention(vi["q"], vi["k_tree"], vi["v_tree"], cu, mask, vi["kpre"],
-                                    vi["vpre"], cup, rnd.scale, key_filter=filt)
+                    ch = (-(-Pb // S) + 127) // 128 * 128
+                    keep[min(Pb, sp * ch):min(Pb, sp * ch + ch)] = True
+                return keep, np.full(n1, sp == S)
+            o, l = O.tree_attention(vi["q"], vi["k_tree"], vi["v_tree"], cu, mask, vi["kpre"], vi["vpre"],
+                                    cup, rnd.scale, key_filter=filt)
             o_parts.append(o.reshape(-1, s.Dh))
             l_parts.append(l.reshape(-1))
         O.lse_merge(np.stack(o_parts), np.stack(l_parts))
         O.accept(cu, tokens, parents, vi["logits"], s.temperature, 20260101, 0, s.depth)
-        return time.perf_counter() - t0, sum(len(r["tokens"]) - 1 for r in res)
+        return time.perf_counter() - t0, n - 1
 
-    dt, verified = one_round()
-    out = {"value": verified / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-           "sample": f"one full draft+verify round of the same workload ({verified} verified "
-                     f"tree tokens) in {dt:.2f} s, float64 numpy oracle"}
-    try:   # the same round again on one core
-        from threadpoolctl import threadpool_limits
-        with threadpool_limits(limits=1):
-            dt1, v1 = one_round()
-        out["single_core"] = {"value": v1 / dt1, "seconds": round(dt1, 2)}
-    except Exception:  # pragma: no cover
-        pass
+    times = []
+    for _ in range(repeats):
+        dt, verified = one_round()
+        times.append(dt)
+    med = float(np.median(times))
+    out = {"value": verified / med, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"request 0 of the workload alone: one draft + verify round ({verified} verified tree "
+                     f"tokens, prefix {P}), float64 numpy oracle, median of {repeats} runs "
+                     f"({', '.join(f'{t:.2f}' for t in times)} s)",
+           "seconds_median": round(med, 3), "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(),
+           "affinity_cpus": len(os.sched_getaffinity(0))}
+    with threadpool_limits(limits=1):
+        dt1, v1 = one_round()
+    out["single_core"] = {"value": v1 / dt1, "seconds": round(dt1, 2), "cores": 1}
     return out
 
 
@@ -729,7 +818,8 @@ def gemm_rooflines(rnd: "Round", steps: int):
         "gemm_o": (d * s.Hq * s.Dh, avg_m, s.Hq * s.Dh, d, 4),
         "gemm_gate_up": (2 * F * d, avg_m, d, F, es),
         "gemm_down": (d * F, avg_m, F, d, 4),
-        "gemm_lm_head": (V * d, avg_m, d, V, 4),
+        "gemm_lm_head": (V * d, s.B * s.width, d, V, 4),       # depth steps: B * W rows
+        "gemm_lm_head_root": (V * d, s.B, d, V, 4),            # the root step: B rows
     }
     out = []
     for tag, (wn, m, kin, nout, oes) in spec.items():
@@ -741,6 +831,39 @@ def gemm_rooflines(rnd: "Round", steps: int):
         out.append(_entry(tag, s.name, "k_gemm", us, "hbm", bytes_=b, launches=n))
     capi.eagle3_profile_reset()
     return out
+
+
+def round_summary(shape, steps, warmup, dev):
+    """A whole round of another workload, as extra fields of the line: device time per round
+    over `steps` rounds (HIP events), verified tree tokens per second, mean accept length."""
+    import torch
+    rnd = Round(shape, dev)
+    for _ in range(warmup):
+        rnd.step()
+    torch.cuda.synchronize()
+    n_ver = int(rnd.draft_out["n_nodes"].sum().item()) - rnd.B
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        rnd.step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    out = {"workload": workload_name(rnd), "value": round(n_ver / (ms / 1e3), 2), "unit": "tokens/s",
+           "ms_per_step": round(ms, 4), "verified_nodes_per_round": n_ver, "steps": steps,
+           "mean_accept_len": round(rnd.mean_accept_len(), 3), "temperature": shape.temperature,
+           "rotating_input_copies": rnd.ncopy}
+    del rnd
+    torch.cuda.empty_cache()
+    return out
+
+
+def workload_name(rnd) -> str:
+    s = rnd.shape
+    pre = f"prefix {rnd.max_prefix}" if len(set(rnd.prefix)) == 1 else \
+        f"prefixes {min(rnd.prefix)}..{max(rnd.prefix)}"
+    return (f"{s.name}: batch {s.B}, draft tree D={s.depth} K={s.topk} W={s.width} N={s.n_nodes}, "
+            f"verify over {pre}, {'greedy' if s.temperature == 0 else f'T={s.temperature}'} acceptance")
 
 
 def main():
@@ -764,8 +887,9 @@ def main():
             out["copy_calibration_bytes"] = n
         print(json.dumps(out), flush=True)
         return
-    shape = {"llama8b": synth.LLAMA8B, "batch16": synth.BATCH16, "llama70b": synth.LLAMA70B,
-             "tiny": synth.TINY}[args.workload]
+    shapes = {"llama8b": synth.LLAMA8B, "batch16": synth.BATCH16, "llama70b": synth.LLAMA70B,
+              "tiny": synth.TINY}
+    shape = shapes[args.workload]
     rnd = Round(shape, dev)
     for _ in range(args.warmup):
         rnd.step()
@@ -800,28 +924,33 @@ def main():
     ms_ev, _, k_ms, k_n = timed(True)
 
     value = n_verified / (ms / 1e3)
-    # rows the LM head sees: B at the root step, B*W at every later step
-    rows = [shape.B] + [shape.B * shape.width] * (shape.depth - 1)
-    bytes_avg = sum(lm_head_bytes(shape, m) for m in rows) / len(rows)
+    # the LM head of the depth steps (B * W rows; the root step's launch is tagged apart)
+    lm_rows = shape.B * shape.width if args.kernel == "gemm_lm_head" else shape.B
+    bytes_lm = lm_head_bytes(shape, lm_rows)
     k_avg_ms = k_ms / max(k_n, 1)
-    achieved = bytes_avg / (k_avg_ms / 1e3) / 1e9
+    achieved = bytes_lm / (k_avg_ms / 1e3) / 1e9
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if shape.dtype == "bf16" else "f32", "data": "synthetic",
-        "config": {"workload": f"{shape.name}: draft tree D={shape.depth} K={shape.topk} "
-                               f"W={shape.width} N={shape.n_nodes}, verify over prefix {rnd.max_prefix}",
+        "dtype": "bf16" if shape.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded random-init drafter weights, Gaussian features and KV; target logits "
+                "= draft logits + noise at the drafted nodes)",
+        "config": {"workload": workload_name(rnd),
                    "batch": shape.B, "d": shape.d, "heads": [shape.Hq, shape.Hkv, shape.Dh],
                    "ffn": shape.F, "vocab": shape.V, "prefix": rnd.prefix if shape.B <= 4 else "ragged",
-                   "verified_nodes_per_round": n_verified, "temperature": shape.temperature},
-        "roofline": {"kernel": args.kernel, "bound": "hbm", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                   "verified_nodes_per_round": n_verified, "temperature": shape.temperature,
+                   "target_logit_noise": shape.noise, "rotating_input_copies": rnd.ncopy,
+                   "per_round_input_bytes": rnd.per_round_input_bytes},
+        "roofline": {"kernel": f"{args.kernel} ({lm_rows} rows per launch)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(args.workload), "avg_launch_us": round(k_avg_ms * 1e3, 2),
-                     "launches": k_n, "algorithmic_bytes_per_launch": int(bytes_avg)},
+                     "launches": k_n, "algorithmic_bytes_per_launch": int(bytes_lm)},
         "wall_s_timed": round(wall, 3),
         "ms_per_step_with_kernel_events": round(ms_ev, 4),
     }
+    line["mean_accept_len"] = round(rnd.mean_accept_len(), 3)
     if not args.no_ops:
         line["gemms"] = gemm_rooflines(rnd, args.steps)
         line["round_ms"] = round_distribution(rnd, 100)
@@ -836,9 +965,12 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(rnd)
+    del rnd
+    torch.cuda.empty_cache()
+    if not args.no_other_rounds:
+        line["other_rounds"] = [round_summary(shapes[w], args.steps, args.warmup, dev)
+                                for w in ("llama8b", "batch16", "llama70b") if w != args.workload]
     if not args.no_ops:
-        del rnd
-        torch.cuda.empty_cache()
         line["ops"] = op_rooflines(keys=keys)
     print(json.dumps(line), flush=True)
 

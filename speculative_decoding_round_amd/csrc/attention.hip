@@ -812,7 +812,15 @@ void launch_merge_rows(int S_rt, int rows, const float* o_part, const float* lse
 // Workgroups aimed for per launch: one per CU for shape 0; for shape 1 several rounds of
 // the two resident per CU, which evens out ragged requests; for shape 2 (hundreds of rows,
 // math-bound) one round.
-inline int attn_cfg(int rows) { return rows <= 32 ? 0 : rows <= 256 ? 1 : 2; }
+// Workgroup shape by query rows per KV head: <= 32 rows, keys split over the waves; 65 .. 128
+// rows (e.g. ten drafted nodes x 8 heads per KV head) in one 128-row block, so each K/V split
+// is streamed by one workgroup and the splits stay few; other rows up to 256 in 64-row blocks;
+// more in 128-row blocks.
+inline int attn_cfg(int rows) {
+  if (rows <= 32) return 0;
+  if (rows > 64 && rows <= 128) return 2;
+  return rows <= 256 ? 1 : 2;
+}
 inline int attn_cfg_rows(int cfg) { return cfg == 0 ? 32 : cfg == 1 ? 64 : 128; }
 inline int attn_cfg_keys(int cfg) { return cfg == 0 ? 128 : 32; }
 inline int attn_cfg_wgs(int cfg) { return cfg == 0 ? 256 : cfg == 1 ? 2048 : 512; }

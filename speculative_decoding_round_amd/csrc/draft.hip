@@ -963,7 +963,10 @@ int run_draft(const eagle3_drafter* w, const Plan& p, const void* h_low, const v
     // LM head, top-K and log-sum-exp, then the tree selection
     {
       GemmPlan gp = plan_gemm(M, p.V, d, dt);
-      if ((st = launch_gemm(gp, dt, p.xl, d, w->w_lm, p.gpart, s, "gemm_lm_head"))) return st;
+      // the root step's launch (B rows) carries its own tag, so timings of the depth steps'
+      // LM head (B * W rows) are not averaged with it
+      if ((st = launch_gemm(gp, dt, p.xl, d, w->w_lm, p.gpart, s, step == 0 ? "gemm_lm_head_root" : "gemm_lm_head")))
+        return st;
       {
         ProfScope ps("topk_chunk", s);
         hipLaunchKernelGGL(k_topk_chunk, dim3(p.lm_nchunk, M), dim3(256), 0, s, p.gpart,

@@ -750,6 +750,7 @@ int launch_ring_r(const e3h::GemmPlan& p, const void* X, int ldx, const void* W,
 
 inline int gemm_role(const char* tag) {
   static const char* names[] = {"gemm_lm_head", "gemm_qkv", "gemm_o", "gemm_down", "gemm_fuse", "gemm_gate_up"};
+  if (tag && strcmp(tag, "gemm_lm_head_root") == 0) return 1;
   for (int i = 0; i < 6; ++i)
     if (tag && strcmp(tag, names[i]) == 0) return i + 1;
   return 0;
@@ -780,12 +781,14 @@ int launch_ring(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, f
   }
 }
 
-// Wide kernel shapes: 16 W tiles per k-block (256 output features, so X costs MT/16 of W's
-// DMA traffic), the ring as deep as the X buffer leaves room for in 160 KB of LDS.  The
-// SiLU gate/up (no k-split) takes 8 tiles (64 gate + 64 up features) when 16 would leave
-// CUs idle.
+// Wide kernel shapes.  Row tiles MT in {3, 6, 10} (48, 96 or 160 rows).  NT W tiles per
+// k-block (16 NT output features; X costs MT/NT of W's DMA traffic) is chosen by the planner
+// from {8, 10, 12, 14, 16} so that the workgroups (one per CU) fill the 256 CUs; the ring is
+// as deep as the X buffer leaves room for in 160 KB of LDS.  The 16-tile kernels get one
+// symbol per projection (ROLE), the others share role 0 (6 for the SiLU gate/up).
 constexpr int wide_ns(int mt, int nt) { return nt < 20 - mt ? nt : 20 - mt; }
-constexpr int kWideMTs[] = {3, 4, 6, 8, 10};
+constexpr int kWideMTs[] = {3, 6, 10};
+constexpr int kWideNTs[] = {16, 14, 12, 10, 8};
 
 template <int MT, int NT, int ROLE, bool SILU>
 int launch_wide_r(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y, void* act,
@@ -800,8 +803,20 @@ template <int MT>
 int launch_wide(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y, void* act,
                 hipStream_t s, int role) {
   if (p.silu) {
-    return p.NT == 16 ? launch_wide_r<MT, 16, 6, true>(p, X, ldx, W, Y, act, s)
-                      : launch_wide_r<MT, 8, 6, true>(p, X, ldx, W, Y, act, s);
+    switch (p.NT) {
+      case 16: return launch_wide_r<MT, 16, 6, true>(p, X, ldx, W, Y, act, s);
+      case 14: return launch_wide_r<MT, 14, 6, true>(p, X, ldx, W, Y, act, s);
+      case 8: return launch_wide_r<MT, 8, 6, true>(p, X, ldx, W, Y, act, s);
+      default: return EAGLE3_EUNSUPPORTED;
+    }
+  }
+  switch (p.NT) {
+    case 14: return launch_wide_r<MT, 14, 0, false>(p, X, ldx, W, Y, act, s);
+    case 12: return launch_wide_r<MT, 12, 0, false>(p, X, ldx, W, Y, act, s);
+    case 10: return launch_wide_r<MT, 10, 0, false>(p, X, ldx, W, Y, act, s);
+    case 8: return launch_wide_r<MT, 8, 0, false>(p, X, ldx, W, Y, act, s);
+    case 16: break;
+    default: return EAGLE3_EUNSUPPORTED;
   }
   switch (role) {
     case 1: return launch_wide_r<MT, 16, 1, false>(p, X, ldx, W, Y, act, s);
@@ -821,9 +836,7 @@ int dispatch_gemm(const e3h::GemmPlan& p, const void* X, int ldx, const void* W,
       const int role = gemm_role(tag);
       switch (p.MT) {
         case 3: return launch_wide<3>(p, X, ldx, W, Y, act, s, role);
-        case 4: return launch_wide<4>(p, X, ldx, W, Y, act, s, role);
         case 6: return launch_wide<6>(p, X, ldx, W, Y, act, s, role);
-        case 8: return launch_wide<8>(p, X, ldx, W, Y, act, s, role);
         case 10: return launch_wide<10>(p, X, ldx, W, Y, act, s, role);
         default: return EAGLE3_EUNSUPPORTED;
       }
@@ -932,46 +945,44 @@ GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu) {
   }
   if (dtype == EAGLE3_BF16 && mt_need >= 3 && mt_need <= 10 && K % 32 == 0) {
     // 33 .. 160 rows: the wide kernel (waves split the rows, one shared W ring per
-    // workgroup, one workgroup per CU).  A k-split in whole 8-chunk blocks brings the grid
-    // to about one workgroup per CU; its count minimises (rounds of workgroups over the CUs)
-    // x (blocks per workgroup) at ~25 GB/s per CU plus the fp32 partials' write and read.
+    // workgroup, one workgroup per CU).  For each tile count NT, a k-split in whole 8-chunk
+    // blocks; the (NT, split) pair minimises (rounds of workgroups over the CUs) x (blocks per
+    // workgroup) x (time of one block: NT W tiles from HBM at ~25 GB/s per CU, plus the MT X
+    // tiles from L2 at ~2.5x that) plus the fp32 partials' write and read at ~6 TB/s.
     int mt = 0;
     for (int v : kWideMTs)
       if (v >= mt_need) {
         mt = v;
         break;
       }
-    // SiLU: 16 tiles when that still gives ~200 workgroups, else 8
-    const int nt = silu && (N / 2) / 128 < 200 ? 8 : 16;
-    if (!silu || (N / 2) % (16 * (nt / 2)) == 0) {
-      p.wide = true;
-      p.MT = mt;
-      p.NT = nt;
-      p.waves = 4;
-      p.chunks_total = K / 32;
-      const int n_kb = (p.chunks_total + 7) / 8;
-      if (silu) {
-        p.n_blocks = (N / 2) / (16 * (nt / 2));
-        p.chunks_per_split = n_kb * 8;
-        p.splits = 1;
-        return p;
-      }
-      p.n_blocks = ((N + 15) / 16 + nt - 1) / nt;
-      const double t_kb = nt * 8192.0 / 25e9;
-      double best = 0;
-      int best_kbps = n_kb;
+    const int n_kb = (K / 32 + 7) / 8;
+    double best = -1;
+    for (int nt : kWideNTs) {
+      if (silu && !(nt == 16 || nt == 14 || nt == 8)) continue;
+      if (silu && (N / 2) % (16 * (nt / 2))) continue;
+      const int nbk = silu ? (N / 2) / (16 * (nt / 2)) : ((N + 15) / 16 + nt - 1) / nt;
+      const double t_kb = (nt + 0.4 * mt) * 8192.0 / 25e9;
       for (int kbps = n_kb; kbps >= 1; --kbps) {
+        if (silu && kbps != n_kb) break;   // the SiLU product needs the whole k-range
         const int sp = (n_kb + kbps - 1) / kbps;
-        const long wgs = (long)p.n_blocks * sp;
+        if (sp > 1 && (n_kb + sp - 1) / sp != kbps) continue;   // the same split count, fewer blocks
+        const long wgs = (long)nbk * sp;
         const long rounds = (wgs + kTileCUs - 1) / kTileCUs;
         const double t = (double)rounds * kbps * t_kb + (sp > 1 ? 2.0 * sp * (double)M * N * 4 / 6e12 : 0.0);
-        if (kbps == n_kb || t < best * 0.97) {
+        if (best < 0 || t < best * 0.98) {
           best = t;
-          best_kbps = kbps;
+          p.wide = true;
+          p.MT = mt;
+          p.NT = nt;
+          p.n_blocks = nbk;
+          p.chunks_per_split = kbps * 8;
+          p.splits = sp;
         }
       }
-      p.chunks_per_split = best_kbps * 8;
-      p.splits = (n_kb + best_kbps - 1) / best_kbps;
+    }
+    if (p.wide) {
+      p.waves = 4;
+      p.chunks_total = K / 32;
       return p;
     }
   }

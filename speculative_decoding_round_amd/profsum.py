@@ -27,7 +27,8 @@ import sys
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LM_HEAD_KERNEL = re.compile(r"k_gemm_ring<1, 8, \d+, false, 1, 1>")   # the LM head (role 1), one row tile
+# the LM head (role 1): the LDS-ring kernel at one row tile, or the wide kernel (33 .. 160 rows)
+LM_HEAD_KERNEL = re.compile(r"k_gemm_ring<1, 8, \d+, false, 1, 1>|k_gemm_wide<\d+, 16, \d+, false, 1>")
 
 
 def source_hash(files=("gemm.hip", "common.h")) -> str:
@@ -43,7 +44,7 @@ def gemm_source_hash() -> str:
 
 
 # kernel name pattern -> the sources its code comes from (for staleness of stored counters)
-KERNEL_SOURCES = {"k_gemm_ring": ("gemm.hip", "common.h"),
+KERNEL_SOURCES = {"k_gemm_ring": ("gemm.hip", "common.h"), "k_gemm_wide": ("gemm.hip", "common.h"),
                   "k_tree_attn_dma": ("attention.hip", "common.h"),
                   "k_lse_merge": ("attention.hip", "common.h"),
                   "k_accept_scan": ("verify.hip", "common.h")}
@@ -69,6 +70,9 @@ def _role(name: str) -> str:
     m = re.search(r"k_gemm_ring<\d+, \d+, \d+, (?:false|true), (\d+), \d+>", name)
     if m and m.group(1) in RING_ROLES:
         return "  <- " + RING_ROLES[m.group(1)]
+    m = re.search(r"k_gemm_wide<\d+, \d+, \d+, (?:false|true), (\d+)>", name)
+    if m and m.group(1) in RING_ROLES:
+        return "  <- " + RING_ROLES[m.group(1)]
     if re.search(r"k_gemm<[^>]*true>", name):
         return "  <- MLP gate/up (SiLU)"
     return ""
@@ -83,7 +87,7 @@ def stats(csv_path, bench_json, out, cmd):
         mark = _role(r["Name"])
         lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
                      f"{float(r['Percentage']):8.2f}  {_short(r['Name'])}{mark}")
-    lm = [r for r in rows if LM_HEAD_KERNEL.search(r["Name"])]
+    lm = sorted([r for r in rows if LM_HEAD_KERNEL.search(r["Name"])], key=lambda r: -float(r["TotalDurationNs"]))
     if lm:
         lines += ["", f"LM-head GEMM average (rocprofv3): {float(lm[0]['AverageNs']) / 1e3:.2f} us",
                   f"LM-head GEMM average (bench.py HIP events, same run): "
