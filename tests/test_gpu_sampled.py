@@ -194,3 +194,69 @@ def test_vocabulary_beyond_64_chunks():
     trees = [synth.full_tree(2, 2), synth.star_tree(5)]
     d = synth.sampled_tree_inputs(trees, 300000, seed=61, device=DEV, target_noise=2.0)
     compare(d, 1.0, 13, range(3), tree_depth(trees), max_kids(trees))
+
+
+def test_accept_sampled_chi_square_on_gpu():
+    """Losslessness of the sampled-candidate rule on the GPU, 1e6 draws: two-level trees whose
+    root has 3 children drawn without replacement from its draft distribution q_root and each
+    child 2 of its own (fresh draws per request and call, Gumbel-top-k on the host); target and
+    draft logits depend on the token path.  The first output token must follow
+    p(. | root) = softmax(z_root / T), and the second, given that the first was the kept child
+    a, p(. | root, a) (chi-square p > 0.01 for each of the two tables)."""
+    need_gpu()
+    from scipy import stats
+    from tests.test_oracle_sampled import _path_logits
+    V, K1, K2, T, B, calls = 6, 3, 2, 0.8, 100_000, 10
+    zt_root, zq_root = _path_logits([], V, 7), _path_logits([], V, 8)
+    zt1 = np.stack([_path_logits([x], V, 7) for x in range(V)])          # target at child x
+    zq1 = np.stack([_path_logits([x], V, 8) for x in range(V)])          # draft at child x
+    zt2 = np.stack([[_path_logits([x, y], V, 7) for y in range(V)] for x in range(V)])
+    lq_root = np.log(O.softmax64(zq_root, T))
+    lq1 = np.log(np.stack([O.softmax64(zq1[x], T) for x in range(V)]))
+    n = 1 + K1 + K1 * K2
+    par = [-1] + [0] * K1 + [1 + a for a in range(K1) for _ in range(K2)]
+    rng = np.random.default_rng(2026)
+    first, pair = np.zeros(V), np.zeros((V, V))
+    for call in range(calls):
+        g = rng.gumbel(size=(B, V))
+        c1 = np.argsort(-(lq_root[None, :] + g), axis=1)[:, :K1]                        # [B, K1]
+        g2 = rng.gumbel(size=(B, K1, V))
+        c2 = np.argsort(-(lq1[c1] + g2), axis=2)[:, :, :K2]                              # [B, K1, K2]
+        tok = np.concatenate([np.zeros((B, 1), np.int64), c1, c2.reshape(B, -1)], axis=1)
+        tgt = np.concatenate([np.broadcast_to(zt_root, (B, 1, V)), zt1[c1],
+                              zt2[np.repeat(c1, K2, axis=1), c2.reshape(B, -1)]], axis=1)
+        drf = np.concatenate([np.broadcast_to(zq_root, (B, 1, V)), zq1[c1]], axis=1)      # [B, 4, V]
+        drow = np.full((B, n), -1, np.int64)
+        drow[:, :1 + K1] = np.arange(B)[:, None] * (1 + K1) + np.arange(1 + K1)[None, :]
+        d = {"cu_nodes": torch.arange(0, (B + 1) * n, n, dtype=torch.int32, device=DEV),
+             "tokens": torch.tensor(tok.reshape(-1), dtype=torch.int32, device=DEV),
+             "parents": torch.tensor(par * B, dtype=torch.int32, device=DEV),
+             "logits": torch.tensor(tgt.reshape(-1, V), dtype=torch.float32, device=DEV),
+             "draft_logits": torch.tensor(drf.reshape(-1, V), dtype=torch.float32, device=DEV),
+             "draft_row": torch.tensor(drow.reshape(-1), dtype=torch.int32, device=DEV)}
+        acc, path, outt, bonus = gpu_run(d, T, 4242, call, 2, K1)
+        first += np.bincount(outt[:, 0], minlength=V)
+        went = acc >= 1
+        np.add.at(pair, (outt[went, 0], outt[went, 1]), 1)
+        if call == 0:       # the GPU walk equals the oracle's on the first requests of this call
+            m = 3
+            o = O.accept_sampled(np.arange(0, (m + 1) * n, n), tok[:m].reshape(-1), np.array(par * m),
+                                 tgt[:m].reshape(-1, V), drf[:m].reshape(-1, V), drow[:m].reshape(-1),
+                                 T, 4242, call, 2, max_children=K1)
+            for got, ref in zip((acc, path, outt, bonus), o):
+                assert np.array_equal(got[:m], ref)
+    p1 = O.softmax64(zt_root, T)
+    assert first.sum() == B * calls
+    assert stats.chisquare(first, p1 * first.sum()).pvalue > 0.01
+    chi, dof = 0.0, 0
+    for a in range(V):
+        na = pair[a].sum()
+        if na < 1000:
+            continue
+        e = na * O.softmax64(zt1[a], T)
+        keep = e >= 5
+        o_, e_ = pair[a][keep], e[keep] / e[keep].sum() * pair[a][keep].sum()
+        chi += ((o_ - e_) ** 2 / e_).sum()
+        dof += int(keep.sum()) - 1
+    assert pair.sum() > 200_000 and dof >= 10
+    assert stats.chi2.sf(chi, dof) > 0.01, (chi, dof)

@@ -241,8 +241,9 @@ def test_accept_full_vocab_and_no_match():
 
 def test_accept_chi_square_on_gpu():
     """Losslessness on the GPU path: the first emitted token of the K=3 two-level tree with
-    V=16, T=1 follows softmax(z_root) over 1e6 draws (chi-square p > 0.01), and the GPU's
-    draws equal the oracle's for sampled rounds."""
+    V=16, T=1 follows softmax(z_root) over 1e6 draws (chi-square p > 0.01); the second token,
+    given the accepted depth-1 child c, follows softmax(z_c) (p > 0.01); and the GPU's draws
+    equal the oracle's for sampled rounds."""
     need_gpu()
     from scipy import stats
     V = 16
@@ -250,18 +251,23 @@ def test_accept_chi_square_on_gpu():
     par = synth.full_tree(3, 2)
     n = len(par)
     z = (rng.standard_normal((n, V)) * 1.2).astype(np.float32)
-    tok = [0] + [int(x) for x in rng.choice(V, 3, replace=False)] + [int(x) for x in rng.integers(0, V, 9)]
+    # the depth-1 children carry the root's three most likely tokens, so that about half of
+    # the 1e6 rounds go through a child and the conditional test below sees many draws
+    tok = [0] + [int(x) for x in np.argsort(-z[0])[:3]] + [int(x) for x in rng.integers(0, V, 9)]
     B = 100000
     cu = torch.arange(0, (B + 1) * n, n, dtype=torch.int32, device=DEV)
     par_t = torch.tensor(par * B, dtype=torch.int32, device=DEV)
     tok_t = torch.tensor(tok * B, dtype=torch.int32, device=DEV)
     lg = torch.tensor(np.tile(z, (B, 1)), dtype=torch.float32, device=DEV)
     mk = capi.eagle3_build_tree_mask(cu, par_t, None, max_nodes=n)
-    firsts = []
+    firsts, seconds, vias = [], [], []
     for rnd in range(10):
         out = capi.eagle3_accept(cu, tok_t, par_t, mk["mask"], lg, 1.0, seed=424242, round=rnd,
                                  max_depth=2)
         firsts.append(out["out_tokens"][:, 0].cpu().numpy())
+        went = out["accept_len"].cpu().numpy() >= 1
+        seconds.append(out["out_tokens"][:, 1].cpu().numpy()[went])
+        vias.append(out["path"][:, 1].cpu().numpy()[went])
         if rnd == 0:
             for b in (0, 1, 777, B - 1):
                 acc, path, outt, bonus = O.accept([0, n], tok, par, z, 1.0, 424242, 0, 2)
@@ -273,3 +279,83 @@ def test_accept_chi_square_on_gpu():
     p /= p.sum()
     obs = np.bincount(y, minlength=V)
     assert stats.chisquare(obs, p * obs.sum()).pvalue > 0.01
+    # the second token, given that the walk went through depth-1 child c (path[1] == c), is the
+    # draw at c: it follows softmax(z_c) (one chi-square over the three children's tables)
+    chi, dof = 0.0, 0
+    sec = np.concatenate(seconds)
+    via = np.concatenate(vias)
+    for c in (1, 2, 3):
+        yc = sec[via == c]
+        pc = np.exp(z[c].astype(np.float64) - z[c].max())
+        pc /= pc.sum()
+        e = pc * len(yc)
+        keep = e >= 5
+        o = np.bincount(yc, minlength=V)[keep]
+        e = e[keep] / e[keep].sum() * o.sum()
+        chi += ((o - e) ** 2 / e).sum()
+        dof += int(keep.sum()) - 1
+    assert len(sec) > 300000 and stats.chi2.sf(chi, dof) > 0.01, (chi, dof)
+
+
+def test_accept_duplicate_siblings_and_ties_on_gpu():
+    """Greedy acceptance with sibling nodes carrying the same token (possible in random-topology
+    trees): both are length-1 matches, the lower index wins; a deeper match under the
+    higher-index sibling wins by length; greedy ties inside a row go to the lowest token id.
+    Then random trees whose siblings repeat tokens, GPU against the oracle bit for bit."""
+    need_gpu()
+    par = [-1, 0, 0, 2]
+    tok = [9, 4, 4, 6]
+    z = np.zeros((4, 10), dtype=np.float32)
+    z[0, 4] = 1
+    z[1, 1] = 1
+    z[2, 7] = 1
+    z[3, 2] = 1
+    cu = torch.tensor([0, 4], dtype=torch.int32, device=DEV)
+    par_t = torch.tensor(par, dtype=torch.int32, device=DEV)
+    tok_t = torch.tensor(tok, dtype=torch.int32, device=DEV)
+    mk = capi.eagle3_build_tree_mask(cu, par_t, None, max_nodes=4)
+    out = capi.eagle3_accept(cu, tok_t, par_t, mk["mask"], torch.tensor(z, device=DEV), 0.0, seed=0,
+                             round=0, max_depth=2)
+    assert out["accept_len"].item() == 1 and out["path"][0, 1].item() == 1 and out["bonus"].item() == 1
+    z[2, 7] = 0
+    z[2, 6] = 1
+    out = capi.eagle3_accept(cu, tok_t, par_t, mk["mask"], torch.tensor(z, device=DEV), 0.0, seed=0,
+                             round=0, max_depth=2)
+    assert out["accept_len"].item() == 2 and out["path"][0].tolist() == [0, 2, 3] and out["bonus"].item() == 2
+    zt = np.zeros((1, 6), dtype=np.float32)
+    zt[0, [2, 4]] = 3.0
+    one = torch.tensor([0, 1], dtype=torch.int32, device=DEV)
+    root = torch.tensor([-1], dtype=torch.int32, device=DEV)
+    mk1 = capi.eagle3_build_tree_mask(one, root, None, max_nodes=1)
+    out = capi.eagle3_accept(one, torch.zeros(1, dtype=torch.int32, device=DEV), root, mk1["mask"],
+                             torch.tensor(zt, device=DEV), 0.0, seed=0, round=0, max_depth=0)
+    assert out["bonus"].item() == 2
+    # random trees, tokens drawn from a 3-token alphabet so siblings repeat; each parent row
+    # favours one of those tokens
+    rng = np.random.default_rng(17)
+    V, sizes = 64, [40, 61, 17, 2, 33]
+    trees = [synth.random_tree(n, 6, 900 + n) for n in sizes]
+    cuh = cu_of(trees)
+    parh = [p for t in trees for p in t]
+    tokh = rng.integers(0, 3, cuh[-1]).tolist()
+    zr = rng.standard_normal((cuh[-1], V)).astype(np.float32)
+    zr[np.arange(cuh[-1]), rng.integers(0, 3, cuh[-1])] += 4.0
+    for dt in (torch.float32, torch.bfloat16):
+        zd = torch.tensor(zr).to(dt)
+        cu_t = torch.tensor(cuh, dtype=torch.int32, device=DEV)
+        p_t = torch.tensor(parh, dtype=torch.int32, device=DEV)
+        mk = capi.eagle3_build_tree_mask(cu_t, p_t, None, max_nodes=max(sizes))
+        out = capi.eagle3_accept(cu_t, torch.tensor(tokh, dtype=torch.int32, device=DEV), p_t, mk["mask"],
+                                 zd.to(DEV), 0.0, seed=0, round=0, max_depth=6)
+        acc, path, outt, bonus = O.accept(cuh, tokh, parh, zd, 0.0, 0, 0, 6)
+        assert np.array_equal(out["accept_len"].cpu().numpy(), acc)
+        assert np.array_equal(out["path"].cpu().numpy(), path)
+        assert np.array_equal(out["out_tokens"].cpu().numpy(), outt)
+        assert np.array_equal(out["bonus"].cpu().numpy(), bonus)
+        assert acc.max() >= 1
+    # the random trees do hold siblings with equal tokens
+    kids = {}
+    for b, t in enumerate(trees):
+        for j in range(1, len(t)):
+            kids.setdefault((b, t[j]), []).append(tokh[cuh[b] + j])
+    assert any(len(v) != len(set(v)) for v in kids.values())
