@@ -4,6 +4,7 @@
     python -m speculative_decoding_round_amd.profsum opstats KERNEL_STATS_CSV OPS_JSON OUT.txt CMD
     python -m speculative_decoding_round_amd.profsum traffic FETCH_CSV WRITE_CSV OUT.txt CMD [KERNEL_RE [TITLE]]
     python -m speculative_decoding_round_amd.profsum counter CSV OUT.txt CMD KERNEL_RE COUNTER
+    python -m speculative_decoding_round_amd.profsum counters CSV OUT.txt CMD KERNEL_RE TITLE
 
 `stats` lists the kernels of a `rocprofv3 --kernel-trace --stats` run with their average
 duration, marks the LM-head GEMM and puts bench.py's own event-timed average beside it.
@@ -154,6 +155,36 @@ def counter(csv_path, out, cmd, kernel_re, name):
     open(out, "w").write("\n".join(lines) + "\n")
 
 
+def counters(csv_path, out, cmd, kernel_re, title, xcds=8, simds=1024):
+    """Several counters of one --pmc pass, per dispatch, for every kernel matching KERNEL_RE,
+    with the derived rates: MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x cycles,
+    GRBM_GUI_ACTIVE summed over the XCDs / XCDs), cycles per MFMA instruction, waiting share of
+    wave cycles, and LDS bank-conflict cycles per LDS-active cycle."""
+    pat = re.compile(kernel_re)
+    agg = defaultdict(lambda: defaultdict(list))
+    for r in csv.DictReader(open(csv_path)):
+        if pat.search(r["Kernel_Name"]):
+            agg[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    lines = [f"# {title} (rocprofv3 --pmc, per-dispatch averages)", f"command: {cmd}", ""]
+    for k, cs in agg.items():
+        avg = {c: sum(v) / len(v) for c, v in cs.items()}
+        n = len(next(iter(cs.values())))
+        lines.append(f"kernel: {_short(k)}  ({n} dispatches)")
+        lines.append("  " + ", ".join(f"{c} {v:.0f}" for c, v in sorted(avg.items())))
+        gui = avg.get("GRBM_GUI_ACTIVE", 0) / xcds
+        if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            lines.append(f"  mfma_busy_fraction: {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (simds * gui):.3f}")
+        if avg.get("SQ_INSTS_MFMA"):
+            lines.append(f"  cycles_per_mfma: {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / avg['SQ_INSTS_MFMA']:.1f}")
+        if avg.get("SQ_WAVE_CYCLES"):
+            lines.append(f"  wait_any_share: {avg.get('SQ_WAIT_ANY', 0) / avg['SQ_WAVE_CYCLES']:.3f}, "
+                         f"wait_lds_share: {avg.get('SQ_WAIT_INST_LDS', 0) / avg['SQ_WAVE_CYCLES']:.3f}")
+        if avg.get("SQ_LDS_IDX_ACTIVE"):
+            lines.append(f"  lds_bank_conflict_per_active: {avg.get('SQ_LDS_BANK_CONFLICT', 0) / avg['SQ_LDS_IDX_ACTIVE']:.3f}")
+        lines.append(f"  source_sha256_16: {source_hash(sources_for(_short(k)))}")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     mode = sys.argv[1]
     if mode == "stats":
@@ -164,5 +195,7 @@ if __name__ == "__main__":
         traffic(*sys.argv[2:8])
     elif mode == "counter":
         counter(*sys.argv[2:7])
+    elif mode == "counters":
+        counters(*sys.argv[2:7])
     else:
         raise SystemExit(__doc__)
