@@ -536,15 +536,21 @@ def measured_ceilings() -> dict:
 
 def gemm_sweep(capi, synth, reps):
     """The drafter projections' GEMM (eagle3_linear) over the number of rows: at the QKV
-    shape (N = 6144, K = 8192) for M = 1 .. 8192, and at M = 2048 (a prompt's worth of rows)
-    for the MLP-down and LM-head shapes.  Few rows are bound by streaming W (HBM), many by
-    the matrix cores (bf16 MFMA)."""
+    shape (N = 6144, K = 8192) for M = 1 .. 8192, at M = 2048 (a prompt's worth of rows) for
+    the MLP-down and LM-head shapes, and at the depth-step rows of the 70B-shaped (40) and
+    batch-16 (160) rounds.  Up to 160 rows are bound by streaming W (HBM), many rows by the
+    matrix cores (bf16 MFMA)."""
     import torch
     dev = "cuda:0"
     out = []
     cases = [(m, 6144, 8192, "QKV") for m in (1, 10, 160, 1024, 2048, 8192)]
     cases += [(2048, 4096, 12288, "feature fusion"), (2048, 4096, 14336, "MLP down"),
               (2048, 128256, 4096, "LM head")]
+    # the depth steps' rows of the 70B-shaped (4 x 10 = 40) and batch-16 (16 x 10 = 160)
+    # rounds at their projections' shapes (gate/up as a plain product of both halves)
+    cases += [(40, 10240, 16384, "70B QKV"), (40, 57344, 8192, "70B gate/up"), (40, 8192, 28672, "70B MLP down"),
+              (40, 8192, 8192, "70B O"), (40, 128256, 8192, "70B LM head"),
+              (160, 28672, 4096, "8B gate/up"), (160, 4096, 14336, "8B MLP down"), (160, 128256, 4096, "8B LM head")]
     for M, N, K, name in cases:
         wbytes = N * K * 2
         ncopy = _copies(wbytes) if M <= 160 else 1
@@ -559,7 +565,7 @@ def gemm_sweep(capi, synth, reps):
         us = _time_b2b(run, reps if M <= 2048 else max(4, reps // 4))
         bound = "hbm" if M <= 160 else "mfma"
         e = _entry(f"linear ({name})", f"M={M} N={N} K={K} bf16", "k_gemm_ring" if M <= 32 else
-                   ("k_gemm" if M <= 160 else "k_gemm_tile"), us, bound,
+                   ("k_gemm_wide" if M <= 160 else "k_gemm_tile"), us, bound,
                    bytes_=wbytes + M * K * 2 + M * N * 4, flops=2 * M * N * K)
         out.append(dict(key="gemm_sweep", **e))
         del ws, x, y, wk
