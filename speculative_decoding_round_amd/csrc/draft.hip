@@ -270,6 +270,33 @@ __global__ __launch_bounds__(256) void k_epi_qkv(const float* __restrict__ part,
 // ---------------------------------------------------------------------------------------
 constexpr int TK_CAP = 64;
 
+// Ranks the wave's compacted pairs sv/si[0 .. total), total <= TK_CAP, against each other
+// by (value desc, id asc) (ids distinct); the pair of rank r < K goes to out(r, ...).  The
+// list is padded to a multiple of four with (-inf, INT_MAX), which beats no entry, so each
+// pair is ranked against four entries per LDS read.
+template <typename Out>
+__device__ __forceinline__ void rank_compacted(float* sv, int* si, int total, int K, Out out) {
+  const int lane = threadIdx.x & 63;
+  const int total4 = (total + 3) & ~3;
+  if (lane >= total && lane < total4) {
+    sv[lane] = kNegInf;
+    si[lane] = 0x7fffffff;
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (lane < total) {
+    const float a = sv[lane];
+    const int ia = si[lane];
+    int r = 0;
+    for (int j = 0; j < total4; j += 4) {
+      const floatx4 bv = *reinterpret_cast<const floatx4*>(sv + j);
+      const intx4 bi = *reinterpret_cast<const intx4*>(si + j);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r += (int)((bv[q] > a) | ((bv[q] == a) & (bi[q] < ia)));
+    }
+    if (r < K) out(r, a, ia);
+  }
+}
+
 template <int NV, typename IdOf, typename Out>
 __device__ __forceinline__ void wave_topk(const float* v, IdOf id_of, int K, float* sv, int* si, Out out) {
   const int lane = threadIdx.x & 63;
@@ -300,26 +327,7 @@ __device__ __forceinline__ void wave_topk(const float* v, IdOf id_of, int K, flo
       }
       off += __popcll(bal[e]);
     }
-    // pad to a multiple of four with (-inf, INT_MAX), which beats no entry, and rank each
-    // compacted pair against four entries per LDS read
-    const int total4 = (total + 3) & ~3;
-    if (lane >= total && lane < total4) {
-      sv[lane] = kNegInf;
-      si[lane] = 0x7fffffff;
-    }
-    __builtin_amdgcn_wave_barrier();
-    if (lane < total) {
-      const float a = sv[lane];
-      const int ia = si[lane];
-      int r = 0;
-      for (int j = 0; j < total4; j += 4) {
-        const floatx4 bv = *reinterpret_cast<const floatx4*>(sv + j);
-        const intx4 bi = *reinterpret_cast<const intx4*>(si + j);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) r += (int)((bv[q] > a) | ((bv[q] == a) & (bi[q] < ia)));
-      }
-      if (r < K) out(r, a, ia);
-    }
+    rank_compacted(sv, si, total, K, out);
   } else {
     // a pair that won a round is taken out by its bit, so that when fewer than K finite
     // values exist the -inf padding is drawn in id order, each pair once
@@ -504,7 +512,180 @@ __device__ __forceinline__ int rank_idx(const float* sc, const int* ix, int lo, 
 }
 
 constexpr int SEL_MAXNEW = SEL_MAXR * KMAX;   // new candidates per step
+
+// The LM head's output when it ran with block statistics (stats != nullptr): the logits z
+// [M, V] and, per row and block of 128 columns, the best logit (value desc, column asc), its
+// column and the sum of e^(z - best) over the block (three planes of M x e3h::kLmStatsLd).
+struct LmBlocks {
+  const float* stats;
+  const float* z;
+  float* dbg_z;      // per-slot copy of the logits [B * S, V] (optional)
+  int M, nblk, V;    // nblk = ceil(V / 128)
+};
 constexpr int SEL_MAXTOP = 256;               // N <= 255
+
+// Row top-K (value desc, column asc) and log-sum-exp from the LM head's statistics per block
+// of 128 columns (one wave per row; an invalid row only issues its loads and returns 0).
+// Fast path: tau, the value of the K-th of K rounds of wave maxima over the lanes' two best
+// block bests (each lane holds 16 blocks), is at most the row's K-th best value (the rounds
+// take at least K distinct entries at or above it), so every entry of the top K lies in a
+// block whose best reaches tau; when at most 32 blocks do, their logits are scanned for the
+// entries >= tau, which are ranked against each other when at most TK_CAP pass.  Otherwise (ties, or logits bunched at the top) the
+// exact path: the K blocks with the best entries (a block whose best is not among them has K
+// distinct entries above all of its own) are scanned for the entries at or above theta, the
+// K-th of those block bests, and ranked, or (many ties at theta) K exact rounds over the K
+// blocks each take the best entry below the previous round's.  The log-sum-exp combines the
+// blocks' (best, sum) pairs.
+template <typename Out>
+__device__ __forceinline__ float row_topk_blocks(const LmBlocks& lb, int m, int K, bool valid, float* sv, int* si,
+                                                 float* sbv, int* sblk, Out out) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  constexpr int LD = e3h::kLmStatsLd;
+  const size_t plane = (size_t)lb.M * LD, row = (size_t)m * LD + 16 * lane;   // blocks 16 lane + i
+  float bv[16], bs[16];
+  int bi[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const floatx4 a = *reinterpret_cast<const floatx4*>(lb.stats + row + 4 * q);
+    const intx4 c = *reinterpret_cast<const intx4*>(reinterpret_cast<const int*>(lb.stats) + plane + row + 4 * q);
+    const floatx4 d = *reinterpret_cast<const floatx4*>(lb.stats + 2 * plane + row + 4 * q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool ok = 16 * lane + 4 * q + e < lb.nblk;
+      bv[4 * q + e] = ok ? a[e] : kNegInf;
+      bi[4 * q + e] = ok ? c[e] : 0x7fffffff;
+      bs[4 * q + e] = ok ? d[e] : 0.f;
+    }
+  }
+  if (!valid) return 0.f;
+  float lm = kNegInf;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) lm = fmaxf(lm, bv[i]);
+  const float mx = wave_max(lm);
+  float ls = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ls += bv[i] != kNegInf ? bs[i] * expf(bv[i] - mx) : 0.f;
+  const float lse = mx + logf(wave_sum(ls));
+  const float* zr = lb.z + (size_t)m * lb.V;
+
+  // ---- fast path
+  {
+    // tau: K rounds over the lanes' two best block bests (a round takes every lane's current
+    // head that equals the wave maximum), at most the K-th best value
+    float x = lm, x2 = kNegInf, tau = kNegInf;
+    bool seen = false;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool first = (bv[i] == lm) & !seen;
+      seen |= first;
+      x2 = first ? x2 : fmaxf(x2, bv[i]);
+    }
+    for (int k = 0; k < K; ++k) {
+      tau = wave_max(x);
+      if (x == tau) {
+        x = x2;
+        x2 = kNegInf;
+      }
+    }
+    int nb = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool in = bv[i] >= tau;
+      const uint64_t bal = __ballot(in);
+      const int pos = nb + __popcll(bal & below);
+      if (in & (pos < 2 * KMAX)) sblk[pos] = 16 * lane + i;
+      nb += __popcll(bal);
+    }
+    if (nb <= 2 * KMAX) {
+      __builtin_amdgcn_wave_barrier();
+      int total = 0;
+      for (int r0 = 0; r0 < nb; r0 += KMAX) {   // up to 16 blocks per pass, two columns per lane each
+        float z[2 * KMAX];
+        int n[2 * KMAX];
+#pragma unroll
+        for (int r = 0; r < KMAX; ++r) {
+          const int c = r0 + r < nb ? sblk[r0 + r] : -1;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int col = 128 * c + 64 * h + lane;
+            n[2 * r + h] = (c >= 0) & (col < lb.V) ? col : lb.V;
+            z[2 * r + h] = n[2 * r + h] < lb.V ? zr[n[2 * r + h]] : kNegInf;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 2 * KMAX; ++i) {
+          const bool keep = (n[i] < lb.V) & (z[i] >= tau);
+          const uint64_t bal = __ballot(keep);
+          if (bal) {
+            const int pos = total + __popcll(bal & below);
+            if (keep & (pos < TK_CAP)) {
+              sv[pos] = z[i];
+              si[pos] = n[i];
+            }
+            total += __popcll(bal);
+          }
+        }
+      }
+      if (total <= TK_CAP) {
+        rank_compacted(sv, si, total, K, out);
+        return lse;
+      }
+    }
+  }
+
+  // ---- exact path: the K best blocks (padding (-inf, INT_MAX) ranks last) and theta
+  wave_topk<16>(bv, [&](int e) { return bi[e]; }, K, sv, si, [&](int r, float val, int idv) {
+    sbv[r] = val;
+    sblk[r] = idv;
+  });
+  __builtin_amdgcn_wave_barrier();
+  const float tv = sbv[K - 1];
+  const int ti = sblk[K - 1];
+  int nsel = 0;
+  for (int r = 0; r < K; ++r) nsel += sblk[r] != 0x7fffffff ? 1 : 0;
+  const int tot = nsel * 128;   // the selected blocks' columns, block after block
+  auto col_of = [&](int q) { return ((sblk[q >> 7] >> 7) << 7) + (q & 127); };
+  int total = 0;
+  for (int q0 = 0; q0 < tot; q0 += 64) {
+    const int q = q0 + lane;
+    const int col = q < tot ? col_of(q) : lb.V;
+    const float zv = col < lb.V ? zr[col] : kNegInf;
+    const bool keep = (col < lb.V) & ((zv > tv) | ((zv == tv) & (col <= ti)));
+    const uint64_t bal = __ballot(keep);
+    const int pos = total + __popcll(bal & below);
+    if (keep & (pos < TK_CAP)) {
+      sv[pos] = zv;
+      si[pos] = col;
+    }
+    total += __popcll(bal);
+  }
+  if (total <= TK_CAP) {
+    rank_compacted(sv, si, total, K, out);
+  } else {
+    float pv = __builtin_huge_valf();
+    int pi = -1;
+    for (int k = 0; k < K; ++k) {
+      float v = kNegInf;
+      int id = 0x7fffffff;
+      for (int q = lane; q < tot; q += 64) {
+        const int col = col_of(q);
+        if (col < lb.V) {
+          const float zv = zr[col];
+          if (((zv < pv) | ((zv == pv) & (col > pi))) & better(zv, col, v, id)) {
+            v = zv;
+            id = col;
+          }
+        }
+      }
+      wave_argmax(v, id);
+      if (lane == 0) out(k, v, id);
+      pv = v;
+      pi = id;
+    }
+  }
+  return lse;
+}
 
 // Phase 2 keeps a running list of the N best candidates created so far: the N best of all
 // candidates are the N best of (the previous list and the new candidates), so each step ranks
@@ -519,9 +700,11 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
                                                  int32_t* __restrict__ out_dep, float* __restrict__ out_score,
                                                  int32_t* __restrict__ out_n, int32_t* dbg_tok,
                                                  int32_t* dbg_par, int32_t* dbg_id, float* dbg_val,
-                                                 float* dbg_lse, SampCfg sc) {
+                                                 float* dbg_lse, SampCfg sc, LmBlocks lb) {
 #pragma clang fp contract(off)
   __shared__ float s_val[SEL_MAXR][KMAX];
+  __shared__ float s_bv[SEL_MAXR][KMAX];
+  __shared__ int s_blk[SEL_MAXR][2 * KMAX];
   __shared__ int s_id[SEL_MAXR][KMAX];
   __shared__ float s_lse[SEL_MAXR];
   __shared__ __attribute__((aligned(16))) float s_cv[SEL_MAXR][TK_CAP];
@@ -552,8 +735,9 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
   float* csc = cs.score + (size_t)b * PMAX;
   int32_t* topn = cs.topn + (size_t)b * N;
   float* topsc = cs.topsc + (size_t)b * N;
-  // ---- phase 1: per-row top-K over the chunks' lists (lane l holds chunk l's list) and
-  // log-sum-exp from the chunks' (max, sum), combined in lane order
+  // ---- phase 1: each row's top-K and log-sum-exp, from the LM head's block statistics, or
+  // from the chunk lists of k_topk_chunk (lane l holds chunk l's list; the chunks' (max, sum)
+  // combined in lane order)
   if (w < R) {
     const int m = b * R + w;
     const int sidx = b * S + sb + w;
@@ -561,34 +745,45 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
     const float score0 = st.score[sidx];
     const int cand0 = st.cand[sidx];
     if (lane < st.mw) s_mask[w][lane] = st.mask[(size_t)sidx * st.mw + lane];
-    const bool ok = lane < n_chunks;
-    const float cm = ok ? cmax[(size_t)m * n_chunks + lane] : kNegInf;
-    const float cs_ = ok ? csum[(size_t)m * n_chunks + lane] : 0.f;
-    float v[16];
-    int id[16];
-    load_list(cv, ci, ((size_t)m * n_chunks + lane) * K, K, ok, v, id);
     if (lane == 0) {
       s_valid[w] = valid;
       s_score[w] = score0;
       s_cand[w] = cand0;
     }
-    if (valid) {
-      const float mx = wave_max(cm);
-      const float tot = wave_sum(cm != kNegInf ? cs_ * expf(cm - mx) : 0.f);
-      const float row_lse = mx + logf(tot);
-      wave_topk<16>(v, [&](int e) { return id[e]; }, K, s_cv[w], s_ci[w], [&](int r, float val, int idv) {
-        // sampled drafting ranks by noisy values; the scores use the child's z * invT
-        if (sc.on)
-          val = (idv >= 0 && idv < sc.V) ? __fmul_rn(sc.slot_logits[(size_t)sidx * sc.V + idv], sc.invT) : kNegInf;
-        s_val[w][r] = val;
-        s_id[w][r] = idv;
-        if (dbg_id) dbg_id[(size_t)sidx * K + r] = idv;
-        if (dbg_val) dbg_val[(size_t)sidx * K + r] = val;
-      });
-      if (lane == 0) {
-        s_lse[w] = row_lse;
-        if (dbg_lse) dbg_lse[sidx] = row_lse;
+    auto out = [&](int r, float val, int idv) {
+      // sampled drafting ranks by noisy values; the scores use the child's z * invT
+      if (sc.on)
+        val = (idv >= 0 && idv < sc.V) ? __fmul_rn(sc.slot_logits[(size_t)sidx * sc.V + idv], sc.invT) : kNegInf;
+      s_val[w][r] = val;
+      s_id[w][r] = idv;
+      if (dbg_id) dbg_id[(size_t)sidx * K + r] = idv;
+      if (dbg_val) dbg_val[(size_t)sidx * K + r] = val;
+    };
+    float row_lse = 0.f;
+    if (lb.stats) {
+      row_lse = row_topk_blocks(lb, m, K, valid != 0, s_cv[w], s_ci[w], s_bv[w], s_blk[w], out);
+      if (valid && lb.dbg_z) {
+        const floatx4* src = reinterpret_cast<const floatx4*>(lb.z + (size_t)m * lb.V);
+        floatx4* dst = reinterpret_cast<floatx4*>(lb.dbg_z + (size_t)sidx * lb.V);
+        for (int t = lane; t < lb.V / 4; t += 64) dst[t] = src[t];
       }
+    } else {
+      const bool ok = lane < n_chunks;
+      const float cm = ok ? cmax[(size_t)m * n_chunks + lane] : kNegInf;
+      const float cs_ = ok ? csum[(size_t)m * n_chunks + lane] : 0.f;
+      float v[16];
+      int id[16];
+      load_list(cv, ci, ((size_t)m * n_chunks + lane) * K, K, ok, v, id);
+      if (valid) {
+        const float mx = wave_max(cm);
+        const float tot = wave_sum(cm != kNegInf ? cs_ * expf(cm - mx) : 0.f);
+        row_lse = mx + logf(tot);
+        wave_topk<16>(v, [&](int e) { return id[e]; }, K, s_cv[w], s_ci[w], out);
+      }
+    }
+    if (valid && lane == 0) {
+      s_lse[w] = row_lse;
+      if (dbg_lse) dbg_lse[sidx] = row_lse;
     }
   }
   // the running list into LDS, from the highest thread down: the top waves sit out phase 1
@@ -771,7 +966,7 @@ struct Plan {
   // pointers (null when measuring)
   SlotState st;
   CandState cs;
-  float *gfuse, *slot_a, *f_rows, *h1, *a_rows, *gpart, *att_o, *att_lse, *cv, *cmax, *csum;
+  float *gfuse, *slot_a, *f_rows, *h1, *a_rows, *gpart, *att_o, *att_lse, *cv, *cmax, *csum, *lmst;
   int* ci;
   uint64_t* row_mask;
   void *xf, *u, *q_rows, *kslot, *vslot, *attn, *mn, *act, *xl;
@@ -856,6 +1051,7 @@ Plan make_plan(const eagle3_drafter* w, const eagle3_tree_cfg* t, int B, int max
   p.ci = c.take<int>(M * p.lm_nchunk * p.K);
   p.cmax = c.take<float>(M * p.lm_nchunk);
   p.csum = c.take<float>(M * p.lm_nchunk);
+  p.lmst = c.take<float>(3 * M * (size_t)e3h::kLmStatsLd);
   p.bytes = c.size();
   return p;
 }
@@ -960,14 +1156,29 @@ int run_draft(const eagle3_drafter* w, const Plan& p, const void* h_low, const v
                          dbg ? dbg->slot_a : (float*)nullptr);
       if ((st = launch_status())) return st;
     }
-    // LM head, top-K and log-sum-exp, then the tree selection
+    // LM head, top-K and log-sum-exp, then the tree selection.  Drafting by top-K in bf16: the
+    // LM head also emits per-block statistics, from which the selection takes each row's
+    // top-K and log-sum-exp directly.  Otherwise (sampled drafting, fp32, a plan without the
+    // statistics) k_topk_chunk first reduces chunks of 4096 logits to lists.
     {
-      GemmPlan gp = plan_gemm(M, p.V, d, dt);
+      GemmPlan gp = plan_gemm(M, p.V, d, dt, false, !sc.on);
+      const bool fused = !sc.on && gemm_block_stats_ok(gp) && (p.V + 127) / 128 <= kLmStatsLd;
+      if (!fused) gp = plan_gemm(M, p.V, d, dt);
+      LmBlocks lb{};
+      if (fused) {
+        lb.stats = p.lmst;
+        lb.z = p.gpart;
+        lb.dbg_z = dbg ? dbg->slot_logits : nullptr;
+        lb.M = M;
+        lb.nblk = (p.V + 127) / 128;
+        lb.V = p.V;
+      }
       // the root step's launch (B rows) carries its own tag, so timings of the depth steps'
       // LM head (B * W rows) are not averaged with it
-      if ((st = launch_gemm(gp, dt, p.xl, d, w->w_lm, p.gpart, s, step == 0 ? "gemm_lm_head_root" : "gemm_lm_head")))
+      if ((st = launch_gemm(gp, dt, p.xl, d, w->w_lm, p.gpart, s, step == 0 ? "gemm_lm_head_root" : "gemm_lm_head",
+                            nullptr, fused ? p.lmst : nullptr)))
         return st;
-      {
+      if (!fused) {
         ProfScope ps("topk_chunk", s);
         hipLaunchKernelGGL(k_topk_chunk, dim3(p.lm_nchunk, M), dim3(256), 0, s, p.gpart,
                            gp.splits, M, p.V, p.K, p.lm_nchunk, p.cv, p.ci, p.cmax, p.csum,
@@ -979,7 +1190,7 @@ int run_draft(const eagle3_drafter* w, const Plan& p, const void* h_low, const v
                          p.lm_nchunk, p.cv, p.ci, p.cmax, p.csum, p.st, p.cs, tokens, parents, depth,
                          score, n_nodes, dbg_tok, dbg_par, dbg ? dbg->slot_topk_id : (int32_t*)nullptr,
                          dbg ? dbg->slot_topk_val : (float*)nullptr, dbg ? dbg->slot_lse : (float*)nullptr,
-                         sc);
+                         sc, lb);
       if ((st = launch_status())) return st;
     }
   }

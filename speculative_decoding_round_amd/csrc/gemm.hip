@@ -158,6 +158,62 @@ __global__ __launch_bounds__(WK * 64) void k_gemm(const T* __restrict__ X, int M
   }
 }
 
+// LM-head statistics of one 16-row tile over 128 consecutive columns (eight 16-column tiles
+// t of the accumulators, from column col0): for each row, the best logit by (value desc,
+// column asc), its column, and the sum of e^(z - best) over the columns below N (the
+// selection forms each row's top-K and log-sum-exp from these).  Lanes r16, r16 + 16, r16 + 32
+// and r16 + 48 hold row r16 (4 columns of every tile each, ascending within a lane), so the
+// reductions cross the four 16-lane rows only; the lanes of the first row write.  Layout:
+// three planes of M x kLmStatsLd (best value fp32, its column int32, sum fp32), entry
+// col0 / 128 of row m.  Kept lean: it runs once per workgroup, after the weight stream.
+template <typename Tile>
+__device__ __forceinline__ void lm_block_stats(Tile tile, int m, int M, int N, int col0,
+                                               float* __restrict__ stats) {
+  if (col0 >= N) return;   // a block wholly past the vocabulary end (uniform)
+  const int g = (threadIdx.x & 63) >> 4;
+  float v[32];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const floatx4 x = tile(t);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[4 * t + e] = x[e];
+  }
+  if (col0 + 128 > N) {   // the vocabulary's last block: columns past N take no part
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      if (col0 + (i >> 2) * 16 + 4 * g + (i & 3) >= N) v[i] = kNegInf;
+  }
+  float mx = v[0];
+#pragma unroll
+  for (int i = 1; i + 1 < 32; i += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(v[i], v[i + 1]));
+  mx = __builtin_fmaxf(mx, v[31]);
+  mx = row_reduce(mx, OpMax());
+  // the first column holding the maximum (columns ascend within the lane), then the
+  // smallest over the row's four lanes
+  int bi = 0x7fffffff;
+#pragma unroll
+  for (int i = 31; i >= 0; --i)
+    if (v[i] == mx) bi = col0 + (i >> 2) * 16 + 4 * g + (i & 3);
+  uint32_t ia, ib;
+  swap16((uint32_t)bi, ia, ib);
+  bi = min((int)ia, (int)ib);
+  swap32((uint32_t)bi, ia, ib);
+  bi = min((int)ia, (int)ib);
+  float sum = 0.f;
+  if (mx != kNegInf) {
+    const float off = mx * kLog2e;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) sum += __builtin_amdgcn_exp2f(__builtin_fmaf(v[i], kLog2e, -off));
+  }
+  sum = row_reduce(sum, OpAdd());
+  if (g == 0 && m < M) {
+    const size_t plane = (size_t)M * e3h::kLmStatsLd, i = (size_t)m * e3h::kLmStatsLd + (col0 >> 7);
+    stats[i] = mx;
+    reinterpret_cast<int*>(stats)[plane + i] = bi;
+    stats[2 * plane + i] = sum;
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // bf16 weight streaming through an LDS ring (one wave per workgroup).
 //
@@ -206,7 +262,8 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_ring(const bf16* __restrict__ 
                                                        const bf16* __restrict__ W, int N, int K,
                                                        float* __restrict__ Y, int n_blocks,
                                                        int chunks_total, int chunks_per_split,
-                                                       void* __restrict__ act, int F) {
+                                                       void* __restrict__ act, int F,
+                                                       float* __restrict__ stats) {
   static_assert(MT >= 1 && MT <= 2, "X is held in registers for one k-block");
   static_assert(NST >= 2 && 8 * (NST - 2) <= 63, "outstanding DMA must fit the vmcnt counter");
   static_assert((WK - 1) * NTB * MT * 64 * 16 <= WK * NST * RING_TILE, "reduction fits the rings");
@@ -319,6 +376,12 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_ring(const bf16* __restrict__ 
         for (int mt = 0; mt < MT; ++mt) acc[nt][mt] += red[(((w - 1) * NTB + nt) * MT + mt) * 64 + lane];
   }
 
+  if constexpr (ROLE == 1 && !SILU && NTB == 8) {
+    if (stats)   // the LM head without a k-split: statistics per 128 columns of the logits
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        lm_block_stats([&](int t) { return acc[t][mt]; }, mt * 16 + r16, M, N, nb * NTB * 16, stats);
+  }
   float* Ys = Y + (size_t)ks * M * N;
   constexpr int NOUT = SILU ? NTB / 2 : NTB;
 #pragma unroll
@@ -361,7 +424,8 @@ __global__ __launch_bounds__(256) void k_gemm_wide(const bf16* __restrict__ X, i
                                                    const bf16* __restrict__ W, int N, int K,
                                                    float* __restrict__ Y, int n_blocks,
                                                    int chunks_total, int chunks_per_split,
-                                                   void* __restrict__ act, int F) {
+                                                   void* __restrict__ act, int F,
+                                                   float* __restrict__ stats) {
   constexpr int MTW = (MT + 3) / 4;   // row tiles per wave (at most)
   static_assert(MT >= 1 && MT <= 12, "row tiles");
   static_assert(NS >= 3 && NT >= NS, "the next block's X is issued after W stage NS of a block");
@@ -502,6 +566,16 @@ __global__ __launch_bounds__(256) void k_gemm_wide(const bf16* __restrict__ X, i
     });
   }
 
+  if constexpr (ROLE == 1 && !SILU && NT % 8 == 0) {
+    if (stats)   // the LM head without a k-split: statistics per 128 columns of the logits
+#pragma unroll
+      for (int mw = 0; mw < MTW; ++mw)
+        if (mw * 4 + wv < MT)
+#pragma unroll
+          for (int h = 0; h < NT / 8; ++h)   // 128 columns at a time
+            lm_block_stats([&](int t) { return acc[8 * h + t][mw]; }, (mw * 4 + wv) * 16 + r16, M, N,
+                           nb * NT * 16 + 128 * h, stats);
+  }
   float* Ys = Y + (size_t)ks * M * N;
   constexpr int NOUT = SILU ? NT / 2 : NT;
 #pragma unroll
@@ -741,10 +815,10 @@ int dispatch_mt(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, f
 
 template <int MT, int ROLE, int WK, bool SILU>
 int launch_ring_r(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y, void* act,
-                  hipStream_t s) {
+                  hipStream_t s, float* stats = nullptr) {
   hipLaunchKernelGGL((k_gemm_ring<MT, kRingNTB, kRingNST, SILU, ROLE, WK>), dim3(p.n_blocks * p.splits),
                      dim3(64 * WK), 0, s, (const bf16*)X, p.M, ldx, (const bf16*)W, p.N, p.K, Y, p.n_blocks,
-                     p.chunks_total, p.chunks_per_split, act, p.N / 2);
+                     p.chunks_total, p.chunks_per_split, act, p.N / 2, stats);
   return e3h::launch_status();
 }
 
@@ -756,15 +830,17 @@ inline int gemm_role(const char* tag) {
   return 0;
 }
 
-// Instantiated shapes: the LM head one wave per workgroup; the other projections two; the
-// SiLU gate/up four.
+// Instantiated shapes: the LM head one wave per workgroup (four when its vocabulary is too
+// small to fill the chip and the k-range stays whole for the block statistics); the other
+// projections two or four; the SiLU gate/up four.
 template <int MT>
 int launch_ring(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y, void* act,
-                hipStream_t s, int role) {
+                hipStream_t s, int role, float* stats) {
   if (p.silu) return launch_ring_r<MT, 6, 4, true>(p, X, ldx, W, Y, act, s);
-  if (p.waves == 1) return launch_ring_r<MT, 1, 1, false>(p, X, ldx, W, Y, act, s);
+  if (p.waves == 1) return launch_ring_r<MT, 1, 1, false>(p, X, ldx, W, Y, act, s, stats);
   if (p.waves == 4) {
     switch (role) {
+      case 1: return launch_ring_r<MT, 1, 4, false>(p, X, ldx, W, Y, act, s, stats);
       case 2: return launch_ring_r<MT, 2, 4, false>(p, X, ldx, W, Y, act, s);
       case 3: return launch_ring_r<MT, 3, 4, false>(p, X, ldx, W, Y, act, s);
       case 4: return launch_ring_r<MT, 4, 4, false>(p, X, ldx, W, Y, act, s);
@@ -792,16 +868,16 @@ constexpr int kWideNTs[] = {16, 14, 12, 10, 8};
 
 template <int MT, int NT, int ROLE, bool SILU>
 int launch_wide_r(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y, void* act,
-                  hipStream_t s) {
+                  hipStream_t s, float* stats = nullptr) {
   hipLaunchKernelGGL((k_gemm_wide<MT, NT, wide_ns(MT, NT), SILU, ROLE>), dim3(p.n_blocks * p.splits),
                      dim3(256), 0, s, (const bf16*)X, p.M, ldx, (const bf16*)W, p.N, p.K, Y, p.n_blocks,
-                     p.chunks_total, p.chunks_per_split, act, p.N / 2);
+                     p.chunks_total, p.chunks_per_split, act, p.N / 2, stats);
   return e3h::launch_status();
 }
 
 template <int MT>
 int launch_wide(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y, void* act,
-                hipStream_t s, int role) {
+                hipStream_t s, int role, float* stats) {
   if (p.silu) {
     switch (p.NT) {
       case 16: return launch_wide_r<MT, 16, 6, true>(p, X, ldx, W, Y, act, s);
@@ -819,7 +895,7 @@ int launch_wide(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, f
     default: return EAGLE3_EUNSUPPORTED;
   }
   switch (role) {
-    case 1: return launch_wide_r<MT, 16, 1, false>(p, X, ldx, W, Y, act, s);
+    case 1: return launch_wide_r<MT, 16, 1, false>(p, X, ldx, W, Y, act, s, stats);
     case 2: return launch_wide_r<MT, 16, 2, false>(p, X, ldx, W, Y, act, s);
     case 3: return launch_wide_r<MT, 16, 3, false>(p, X, ldx, W, Y, act, s);
     case 4: return launch_wide_r<MT, 16, 4, false>(p, X, ldx, W, Y, act, s);
@@ -830,21 +906,21 @@ int launch_wide(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, f
 
 template <typename T>
 int dispatch_gemm(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y,
-                  void* act, hipStream_t s, const char* tag) {
+                  void* act, hipStream_t s, const char* tag, float* stats) {
   if constexpr (sizeof(T) == 2) {
     if (p.wide) {
       const int role = gemm_role(tag);
       switch (p.MT) {
-        case 3: return launch_wide<3>(p, X, ldx, W, Y, act, s, role);
-        case 6: return launch_wide<6>(p, X, ldx, W, Y, act, s, role);
-        case 10: return launch_wide<10>(p, X, ldx, W, Y, act, s, role);
+        case 3: return launch_wide<3>(p, X, ldx, W, Y, act, s, role, stats);
+        case 6: return launch_wide<6>(p, X, ldx, W, Y, act, s, role, stats);
+        case 10: return launch_wide<10>(p, X, ldx, W, Y, act, s, role, stats);
         default: return EAGLE3_EUNSUPPORTED;
       }
     }
     if (p.ring) {
       const int role = gemm_role(tag);
-      return p.MT == 1 ? launch_ring<1>(p, X, ldx, W, Y, act, s, role)
-                       : launch_ring<2>(p, X, ldx, W, Y, act, s, role);
+      return p.MT == 1 ? launch_ring<1>(p, X, ldx, W, Y, act, s, role, stats)
+                       : launch_ring<2>(p, X, ldx, W, Y, act, s, role, stats);
     }
   }
   switch (p.MT) {
@@ -866,7 +942,7 @@ namespace e3h {
 // Plan: single-wave workgroups when the n-blocks alone fill the chip (the LM head);
 // otherwise four-wave workgroups and a k-split that brings the grid to about 256
 // workgroups, keeping at least one X block of chunks per wave.
-GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu) {
+GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu, bool whole_k) {
   GemmPlan p;
   p.silu = silu;
   p.ring = false;
@@ -923,6 +999,11 @@ GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu) {
     if (silu) {
       p.n_blocks = (N / 2) / (16 * (kRingNTB / 2));
       p.waves = 4;
+    } else if (whole_k) {
+      // no k-split (the LM head's block statistics need whole sums): four waves share a
+      // workgroup's k-range unless the n-blocks alone fill the chip
+      p.n_blocks = ((N + 15) / 16 + kRingNTB - 1) / kRingNTB;
+      p.waves = p.n_blocks >= 512 ? 1 : 4;
     } else {
       p.n_blocks = ((N + 15) / 16 + kRingNTB - 1) / kRingNTB;
       p.waves = p.n_blocks >= 512 ? 1 : 2;
@@ -959,11 +1040,12 @@ GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu) {
     double best = -1;
     for (int nt : kWideNTs) {
       if (silu && !(nt == 16 || nt == 14 || nt == 8)) continue;
+      if (whole_k && nt != 16) continue;   // the statistics epilogue is built for 16 tiles
       if (silu && (N / 2) % (16 * (nt / 2))) continue;
       const int nbk = silu ? (N / 2) / (16 * (nt / 2)) : ((N + 15) / 16 + nt - 1) / nt;
       const double t_kb = (nt + 0.4 * mt) * 8192.0 / 25e9;
       for (int kbps = n_kb; kbps >= 1; --kbps) {
-        if (silu && kbps != n_kb) break;   // the SiLU product needs the whole k-range
+        if ((silu || whole_k) && kbps != n_kb) break;   // the SiLU product needs the whole k-range
         const int sp = (n_kb + kbps - 1) / kbps;
         if (sp > 1 && (n_kb + sp - 1) / sp != kbps) continue;   // the same split count, fewer blocks
         const long wgs = (long)nbk * sp;
@@ -1022,7 +1104,11 @@ GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu) {
 }
 
 int launch_gemm(const GemmPlan& p, int dtype, const void* X, int ldx, const void* W, float* Ypart,
-                hipStream_t s, const char* tag, void* act) {
+                hipStream_t s, const char* tag, void* act, float* stats) {
+  // the block statistics come from the LM head's ring or wide kernel without a k-split
+  if (stats && (!gemm_block_stats_ok(p) || gemm_role(tag) != 1 || dtype != EAGLE3_BF16 ||
+                (p.N + 127) / 128 > kLmStatsLd))
+    return EAGLE3_EINVAL;
   if (p.tile) {
     if (dtype != EAGLE3_BF16) return EAGLE3_EUNSUPPORTED;
     // row offsets are 32-bit byte offsets from the operand base
@@ -1037,8 +1123,8 @@ int launch_gemm(const GemmPlan& p, int dtype, const void* X, int ldx, const void
   if (p.MT == 0) return EAGLE3_EUNSUPPORTED;
   if (p.silu && (!act || (p.N / 2) % (16 * (p.NT / 2)))) return EAGLE3_EUNSUPPORTED;
   ProfScope ps(tag, s);
-  if (dtype == EAGLE3_BF16) return dispatch_gemm<bf16>(p, X, ldx, W, Ypart, act, s, tag);
-  return dispatch_gemm<float>(p, X, ldx, W, Ypart, act, s, tag);
+  if (dtype == EAGLE3_BF16) return dispatch_gemm<bf16>(p, X, ldx, W, Ypart, act, s, tag, stats);
+  return dispatch_gemm<float>(p, X, ldx, W, Ypart, act, s, tag, nullptr);
 }
 
 int launch_epi_sum(const GemmPlan& p, const float* part, float* out, const float* resid,

@@ -68,9 +68,21 @@ struct GemmPlan {
   bool tile;   // bf16 tiled MFMA kernel for many rows (M > 160)
   bool wide;   // bf16 wide kernel (33 .. 160 rows: four waves split the rows, shared W ring)
 };
-GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu = false);
+// whole_k: no k-split, as the LM head's block statistics need (see launch_gemm).
+GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu = false, bool whole_k = false);
+// Whether a plan's kernel can emit the LM head's block statistics: the bf16 ring kernel, or
+// the wide kernel at 16 tiles per block, without a k-split.
+inline bool gemm_block_stats_ok(const GemmPlan& p) {
+  return !p.silu && p.splits == 1 && (p.ring || (p.wide && p.NT == 16));
+}
+// Row stride of the statistics planes: blocks of 128 columns, so N <= 131072.
+constexpr int kLmStatsLd = 1024;
+// stats (LM head only, tag "gemm_lm_head" or "gemm_lm_head_root", a plan with
+// gemm_block_stats_ok): besides the logits, per row and block of 128 columns the best logit
+// (value desc, column asc), its column and the sum of e^(z - best) over the block, in three
+// planes of M x kLmStatsLd (fp32, int32, fp32; entry n / 128 for the block of column n).
 int launch_gemm(const GemmPlan& p, int dtype, const void* X, int ldx, const void* W, float* Ypart,
-                hipStream_t s, const char* tag, void* act = nullptr);
+                hipStream_t s, const char* tag, void* act = nullptr, float* stats = nullptr);
 
 // out[m][n] = (resid ? resid[m][n] : 0) + sum_s part[s][m][n]  (split order)
 int launch_epi_sum(const GemmPlan& p, const float* part, float* out, const float* resid,

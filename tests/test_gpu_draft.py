@@ -243,6 +243,31 @@ def test_draft_batch16_full_size_sampled():
     check_teacher_forced(shape, w, di, out, shape.B, prefix, slots_per_request=chain)
 
 
+@pytest.mark.parametrize("kind,V", [("plain", 4104), ("periodic3", 8192), ("paired", 4104)])
+def test_draft_topk_wide_lm_head_statistics(kind, V):
+    """40 evaluated rows per step (4 requests x width 10): the LM head runs in the wide
+    kernel and emits statistics per 128 columns, from which the selection takes each row's
+    top-K and log-sum-exp.  Top-K ids stay exact with plain logits, with heavy ties (the
+    exact path), and when the vocabulary ends 8 columns into a block (V = 4104: the last
+    256-column workgroup has a half wholly past the end)."""
+    need_gpu()
+    shape = synth.scaled(SMALL_BF16, V=V, B=4, depth=3, topk=10, width=10, n_nodes=20)
+    prefix = [100, 257, 33, 1]
+    w = synth.drafter_weights(shape, seed=41, device=DEV)
+    _tied_lm_head(w, kind)
+    di = synth.draft_inputs(shape, seed=42, device=DEV, prefix=prefix)
+    dr = capi.make_drafter(w, shape.Hq, shape.Hkv, shape.Dh)
+    tree = capi.Eagle3TreeCfg(depth=shape.depth, topk=shape.topk, width=shape.width,
+                              n_nodes=shape.n_nodes)
+    out = capi.eagle3_draft_expand(dr, tree, di["h_low"], di["h_mid"], di["h_high"], di["root_tok"],
+                                   di["kpre"], di["vpre"], di["cu_prefix"], max(prefix), debug=True,
+                                   debug_logits=True)
+    torch.cuda.synchronize()
+    check_topk_on_gpu_logits(shape, out["debug"], shape.B)
+    check_selection_replay(shape, out, shape.B)
+    check_teacher_forced(shape, w, di, out, shape.B, prefix)
+
+
 def test_draft_ignores_stale_workspace_contents():
     """Unused evaluation slots sit inside the drafter's tree-key range (masked out); the
     round must not depend on what the workspace held before (here: all NaN bytes)."""
