@@ -57,8 +57,27 @@ __global__ __launch_bounds__(256) void k_build_mask(const int32_t* __restrict__ 
 // Acceptance pass 1: per (node, chunk of 4096 tokens) the best (value, token) of greedy z
 // or z*invT + Gumbel.  Thread t takes 16 consecutive tokens (vector loads issued together
 // when the row is 16-byte aligned); one Philox call yields the noise of four tokens.
+//
+// At T > 0 most of the Gumbel noise is never needed: G(u) = -ln(-ln u) rises with u, and a
+// word whose 23-bit cell index k = x >> 9 has L leading ones has 1 - u > 2^-(L+1), so
+// -ln u > 2^-(L+1) and G < (L+1) ln 2.  With a margin of 2^-10 over that (far above the
+// rounding of the two logarithms), U = z*invT + G_bound(L) bounds the token's value (the same
+// rounded addition, with a larger addend).  Each lane computes the exact value of its token
+// with the largest bound; every token whose bound lies below the wave's best exact value
+// cannot win the chunk (it stays strictly below a value the chunk attains), and the few
+// remaining tokens are compacted across the wave (through LDS) so that their logarithms are
+// evaluated by whole waves rather than by scattered lanes.  The winner is the same token as
+// with every value computed.
 // ---------------------------------------------------------------------------------------
 constexpr int ACC_CHUNK = 4096;
+constexpr int ACC_EXACT_CAP = 256;   // compacted tokens per wave; beyond, every token is evaluated
+
+// Upper bound of gumbel_from_word(x) from the leading ones of x's top 23 bits.
+__device__ __forceinline__ float gumbel_bound(uint32_t x) {
+#pragma clang fp contract(off)
+  const int ones = min(23, (int)__clz(~x));
+  return (float)(ones + 1) * 0.693147182f + 0.0009765625f;
+}
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_accept_scan(const T* __restrict__ logits, int V, int n_chunks,
@@ -71,6 +90,9 @@ __global__ __launch_bounds__(256) void k_accept_scan(const T* __restrict__ logit
   constexpr int EPC = Vec<T>::N;
   __shared__ float sv[8];
   __shared__ int si[8];
+  __shared__ float s_xa[4][ACC_EXACT_CAP];
+  __shared__ uint32_t s_xw[4][ACC_EXACT_CAP];
+  __shared__ int s_xt[4][ACC_EXACT_CAP];
   const int node = blockIdx.x / n_chunks;
   const int c = blockIdx.x % n_chunks;
   const int tb = c * ACC_CHUNK + 16 * threadIdx.x;
@@ -96,21 +118,80 @@ __global__ __launch_bounds__(256) void k_accept_scan(const T* __restrict__ logit
         best = z[e];
         bi = tb + e;
       }
-  } else if (tb < V) {
-    const int b = find_request(cu_nodes, B, node);
-    const uint32_t i_local = (uint32_t)(node - cu_nodes[b]);
+  } else {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    uint32_t wd[16] = {};
+    float a[16], ub[16];
+    if (tb < V) {
+      const int b = find_request(cu_nodes, B, node);
+      const uint32_t i_local = (uint32_t)(node - cu_nodes[b]);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t ctr[4] = {(uint32_t)((tb >> 2) + q), i_local, (uint32_t)b, rnd};
-      philox4x32_10(ctr, seed_lo, seed_hi);
+      for (int q = 0; q < 4; ++q) {
+        uint32_t ctr[4] = {(uint32_t)((tb >> 2) + q), i_local, (uint32_t)b, rnd};
+        philox4x32_10(ctr, seed_lo, seed_hi);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int t = tb + 4 * q + w;
-        if (t >= V) continue;
-        const float val = z[4 * q + w] * invT + gumbel_from_word(ctr[w]);
-        if (better(val, t, best, bi)) {
+        for (int w = 0; w < 4; ++w) wd[4 * q + w] = ctr[w];
+      }
+    }
+    // the bounds, and the exact value of the lane's token with the largest one
+    float utop = kNegInf, atop = 0.f;
+    uint32_t wtop = 0;
+    int etop = -1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const bool in = tb + e < V;
+      a[e] = z[e] * invT;
+      ub[e] = in ? a[e] + gumbel_bound(wd[e]) : kNegInf;
+      if (in & (etop < 0 || ub[e] > utop)) {
+        utop = ub[e];
+        atop = a[e];
+        wtop = wd[e];
+        etop = e;
+      }
+    }
+    if (etop >= 0) {
+      best = atop + gumbel_from_word(wtop);
+      bi = tb + etop;
+    }
+    const float th = wave_max(best);
+    // tokens that may still reach th, compacted over the wave
+    float* xa = s_xa[wv];
+    uint32_t* xw = s_xw[wv];
+    int* xt = s_xt[wv];
+    const uint64_t below = (1ull << lane) - 1ull;
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const bool need = (tb + e < V) & (e != etop) & (ub[e] >= th);
+      const uint64_t bal = __ballot(need);
+      if (bal) {
+        const int pos = cnt + __popcll(bal & below);
+        if (need & (pos < ACC_EXACT_CAP)) {
+          xa[pos] = a[e];
+          xw[pos] = wd[e];
+          xt[pos] = tb + e;
+        }
+        cnt += __popcll(bal);
+      }
+    }
+    if (cnt <= ACC_EXACT_CAP) {
+      __builtin_amdgcn_wave_barrier();
+      for (int j = lane; j < cnt; j += 64) {
+        const float val = xa[j] + gumbel_from_word(xw[j]);
+        if (better(val, xt[j], best, bi)) {
           best = val;
-          bi = t;
+          bi = xt[j];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        if ((tb + e < V) & (e != etop) & (ub[e] >= th)) {
+          const float val = a[e] + gumbel_from_word(wd[e]);
+          if (better(val, tb + e, best, bi)) {
+            best = val;
+            bi = tb + e;
+          }
         }
       }
     }

@@ -174,3 +174,27 @@ def test_chi_square_lossless():
     for r in range(0, 400):
         acc, path, outt, bonus = O.accept([0, n], tok, par, z, T, seed, r, 2)
         assert outt[0][0] == y_root[r]
+
+
+def test_gumbel_bound_of_the_scan_holds_for_every_word():
+    """The acceptance scan skips the logarithms of a token when z*invT + B(L) is below a value
+    the chunk attains, where L is the number of leading ones of the word's top 23 bits and
+    B(L) = (L+1) ln 2 + 2^-10 (float32).  Every one of the 2^23 cells must satisfy
+    G(u) <= B(L) with G the float32 noise of the oracle (the kernel's arithmetic), or the
+    skip could drop a winner.  Mathematically 1 - u > 2^-(L+1), so G < (L+1) ln 2."""
+    k = np.arange(1 << 23, dtype=np.uint64)
+    x = k << np.uint64(9)
+    g = -O.ln_spec(-O.ln_spec(O.uniform23(x)))
+    # leading ones of the 23-bit cell index
+    kk = k.astype(np.int64)
+    ones = np.zeros(kk.shape, dtype=np.int64)
+    run = np.ones(kk.shape, dtype=bool)
+    for bit in range(22, -1, -1):
+        run &= ((kk >> bit) & 1) == 1
+        ones += run
+    bound = (ones + 1).astype(np.float32) * np.float32(0.693147182) + np.float32(0.0009765625)
+    assert (g <= bound).all()
+    # and the bound is not loose where it matters (the top cells of each class)
+    for L in (0, 5, 12, 22, 23):
+        sel = ones == L
+        assert bound[sel].max() - g[sel].max() < 0.75
