@@ -806,7 +806,9 @@ void launch_merge_rows(int S_rt, int rows, const float* o_part, const float* lse
 }
 
 // Workgroup shape of the bf16 kernel by query rows per (request, KV head):
-// 0: <= 32 rows: 32 rows per workgroup, keys split over the 4 waves (one workgroup per CU);
+// 0: <= 32 rows: 32 rows per workgroup (one 16-row tile per wave), keys split over two wave
+//    pairs, four 32 KB stages (one workgroup per CU, three stages in flight: these launches
+//    only stream K/V, and a deeper ring beats the 64 KB stages of a four-way key split);
 // 1: <= 256 rows: 64 rows per workgroup, one 16-row tile per wave, keys shared;
 // 2: more: 128 rows per workgroup, two 16-row tiles per wave, keys shared.
 // Workgroups aimed for per launch: one per CU for shape 0; for shape 1 several rounds of
@@ -822,6 +824,8 @@ inline int attn_cfg(int rows) {
   return rows <= 256 ? 1 : 2;
 }
 inline int attn_cfg_rows(int cfg) { return cfg == 0 ? 32 : cfg == 1 ? 64 : 128; }
+// keys per iteration, for split sizing (shape 0 streams 64 per iteration, but its splits keep
+// at least 128 keys, two iterations)
 inline int attn_cfg_keys(int cfg) { return cfg == 0 ? 128 : 32; }
 inline int attn_cfg_wgs(int cfg) { return cfg == 0 ? 256 : cfg == 1 ? 2048 : 512; }
 
@@ -859,7 +863,7 @@ int launch_attn_t(const e3h::AttnArgs& h, hipStream_t s) {
       hipLaunchKernelGGL(kern, dim3((unsigned)n), dim3(256), 0, s, a);
     };
     switch (attn_cfg(rows)) {
-      case 0: go(k_tree_attn_dma<DH, 2, 4, 32, 2>, DmaCfg<DH, 2, 4, 32, 2>::ROWS); break;
+      case 0: go(k_tree_attn_dma<DH, 1, 2, 32, 4>, DmaCfg<DH, 1, 2, 32, 4>::ROWS); break;
       case 1: go(k_tree_attn_dma<DH, 1, 1, 32, 4>, DmaCfg<DH, 1, 1, 32, 4>::ROWS); break;
       default: go(k_tree_attn_dma<DH, 2, 1, 32, 4>, DmaCfg<DH, 2, 1, 32, 4>::ROWS); break;
     }
