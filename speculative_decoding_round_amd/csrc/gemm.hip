@@ -1017,6 +1017,14 @@ GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu, bool whole_k) {
       }
       splits = (kRingTargetWgs + p.n_blocks * p.waves - 1) / (p.n_blocks * p.waves);
       if (p.waves == 1) splits = 1;   // >= 512 n-blocks cover the CUs: no fp32 partials to re-read
+      // 65 .. 128 n-blocks (the 70B-shaped QKV of the root rows): two-wave workgroups over
+      // kRingTargetWgs / 2 splits land unevenly on the CUs (two or three per CU); one four-wave
+      // workgroup per CU over floor(256 / n_blocks) splits keeps the grid to one round
+      // (measured 63 -> 55 us for 4 x 10240 x 16384)
+      if (p.waves == 2 && p.n_blocks > 64 && p.n_blocks <= 128) {
+        p.waves = 4;
+        splits = 256 / p.n_blocks;
+      }
     }
     int cps = (p.chunks_total + splits - 1) / splits;
     cps = (cps + 8 * p.waves - 1) / (8 * p.waves) * (8 * p.waves);

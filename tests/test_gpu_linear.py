@@ -22,6 +22,7 @@ BF, F32 = torch.bfloat16, torch.float32
     (1, 6144, 8192, BF, None),      # ring, one row (QKV shape)
     (10, 4096, 4096, BF, None),     # ring, two waves, split-K partials summed
     (32, 2048, 1024, BF, None),     # ring, two row tiles
+    (4, 10240, 16384, BF, None),    # ring, 80 n-blocks: four-wave workgroups, three k-splits
     (40, 4096, 4096, BF, None),     # wide kernel, three row tiles (wave 3 holds none)
     (160, 1024, 4096, BF, None),    # wide kernel, ten row tiles
     (33, 1000, 1056, BF, None),     # wide: one row past two tiles, ragged n-block, 33 chunks
@@ -40,7 +41,7 @@ BF, F32 = torch.bfloat16, torch.float32
     (2048, 6144, 8192, BF, 64),     # tiled kernel at the QKV shape of a 2048-token prompt
     (1024, 6144, 8192, BF, 32),     # the same with 1024 rows: k split in two
     (1024, 4096, 14336, BF, 32),    # tiled kernel at the MLP-down shape
-], ids=["ring_m1", "ring_m10_split", "ring_m32", "wide_m40", "wide_m160", "wide_m33_ragged",
+], ids=["ring_m1", "ring_m10_split", "ring_m32", "ring_m4_80_nblocks", "wide_m40", "wide_m160", "wide_m33_ragged",
         "wide_m48_split", "wide_m64", "wide_m100", "wide_m128_down", "wide_qkv_70b", "wide_lm_70b",
         "wide_lm_batch16", "regs_m40_k1000", "fp32_m10", "tile_m256",
         "tile_m200", "tile_ragged", "tile_qkv_2048", "tile_qkv_1024_split", "tile_down_1024"])
