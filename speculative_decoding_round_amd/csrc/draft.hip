@@ -482,35 +482,6 @@ __global__ __launch_bounds__(256) void k_topk_chunk(const float* __restrict__ pa
 // ---------------------------------------------------------------------------------------
 constexpr int SEL_MAXR = 16;   // rows (W) per request handled by one workgroup
 
-// Number of entries f in [lo, hi) that beat (sa, e) by (score desc, index asc) where an
-// entry's index is its position; `sc` is LDS, 16-byte aligned at lo (a multiple of 4),
-// padded with -inf up to a multiple of 4.
-__device__ __forceinline__ int rank_of(const float* sc, int lo, int hi, float sa, int e) {
-  int rank = 0;
-#pragma unroll 4
-  for (int f = lo; f < hi; f += 4) {
-    const floatx4 v = *reinterpret_cast<const floatx4*>(sc + f);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) rank += (int)((v[q] > sa) | ((v[q] == sa) & (f + q < e)));
-  }
-  return rank;
-}
-
-// Number of entries of [lo, hi) that beat (sa, ia) by (score desc, index asc), the indices
-// given in `ix`; lo a multiple of 4; both LDS arrays 16-byte aligned, padded with
-// (-inf, INT_MAX) to a multiple of 4.
-__device__ __forceinline__ int rank_idx(const float* sc, const int* ix, int lo, int hi, float sa, int ia) {
-  int rank = 0;
-#pragma unroll 4
-  for (int f = lo; f < hi; f += 4) {
-    const floatx4 v = *reinterpret_cast<const floatx4*>(sc + f);
-    const intx4 i = *reinterpret_cast<const intx4*>(ix + f);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) rank += (int)((v[q] > sa) | ((v[q] == sa) & (i[q] < ia)));
-  }
-  return rank;
-}
-
 constexpr int SEL_MAXNEW = SEL_MAXR * KMAX;   // new candidates per step
 
 // The LM head's output when it ran with block statistics (stats != nullptr): the logits z
@@ -565,7 +536,7 @@ __device__ __forceinline__ float row_topk_blocks(const LmBlocks& lb, int m, int 
   const float mx = wave_max(lm);
   float ls = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) ls += bv[i] != kNegInf ? bs[i] * expf(bv[i] - mx) : 0.f;
+  for (int i = 0; i < 16; ++i) ls += bv[i] != kNegInf ? bs[i] * __builtin_amdgcn_exp2f((bv[i] - mx) * kLog2e) : 0.f;
   const float lse = mx + logf(wave_sum(ls));
   const float* zr = lb.z + (size_t)m * lb.V;
 
@@ -709,11 +680,11 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
   __shared__ float s_lse[SEL_MAXR];
   __shared__ __attribute__((aligned(16))) float s_cv[SEL_MAXR][TK_CAP];
   __shared__ __attribute__((aligned(16))) int s_ci[SEL_MAXR][TK_CAP];
-  __shared__ __attribute__((aligned(16))) float nsc[SEL_MAXNEW + 4];   // new candidates, creation order
+  __shared__ float nsc[SEL_MAXNEW];   // new candidates, creation order
   __shared__ int ntok[SEL_MAXNEW];
   __shared__ int nps[SEL_MAXNEW];
-  __shared__ __attribute__((aligned(16))) float msc[SEL_MAXTOP + SEL_MAXNEW + 4];   // list, then new
-  __shared__ __attribute__((aligned(16))) int midx[SEL_MAXTOP + SEL_MAXNEW + 4];
+  __shared__ float msc[SEL_MAXTOP];   // the running list: scores, candidate indices
+  __shared__ int midx[SEL_MAXTOP];
   __shared__ int ktop[SEL_MAXTOP];
   __shared__ float ktsc[SEL_MAXTOP];
   __shared__ int lab_of[1024];
@@ -722,7 +693,8 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
   __shared__ uint64_t s_mask[SEL_MAXR][SMAX / 64];
   __shared__ int s_cand[SEL_MAXR];
   __shared__ int fr_e[SEL_MAXR];
-  __shared__ int s_rank[SEL_MAXNEW + SEL_MAXTOP + SEL_MAXNEW];   // frontier ranks, then list ranks
+  __shared__ int s_rank[SEL_MAXNEW];   // ranks of the new candidates among themselves
+  __shared__ int nord[SEL_MAXNEW];     // the new candidates in rank order
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int sb = step == 0 ? 0 : 1 + (step - 1) * W;
@@ -811,48 +783,62 @@ __global__ __launch_bounds__(1024) void k_select(int step, int D, int K, int W, 
     nsc[e] = sc;
     ntok[e] = tk;
     nps[e] = sb + j;
-    msc[ntop + e] = sc;
-    midx[ntop + e] = n_before + e;
+    s_rank[e] = rk;
   }
-  if (threadIdx.x < 4) {
-    nsc[n_new + threadIdx.x] = kNegInf;
-    msc[m_total + threadIdx.x] = kNegInf;
-    midx[m_total + threadIdx.x] = 0x7fffffff;
-  }
-  for (int i = threadIdx.x; i < SEL_MAXNEW + m_total; i += blockDim.x) s_rank[i] = 0;
   for (int i = threadIdx.x; i < n_total; i += blockDim.x) lab_of[i] = -1;
   __syncthreads();
-  // Ranks by (score desc, creation asc): of the new candidates among themselves (the W best
-  // take the next step's slots) and of the running list with the new candidates (the N best
-  // are kept).  The whole workgroup works on (entry, 16-entry chunk) pairs; the integer
-  // partial counts are summed by LDS atomics, whose order does not matter.
-  {
-    constexpr int CH = 16;
-    const int cf = last ? 0 : (n_new + CH - 1) / CH;
-    const int cl = (m_total + CH - 1) / CH;
-    const int items_f = n_new * cf, items = items_f + m_total * cl;
-    for (int it = threadIdx.x; it < items; it += blockDim.x) {
-      if (it < items_f) {
-        const int e = it % n_new, lo = (it / n_new) * CH;
-        const int part = rank_of(nsc, lo, min(lo + CH, n_new), nsc[e], e);
-        if (part) atomicAdd(&s_rank[e], part);
-      } else {
-        const int jt = it - items_f;
-        const int i = jt % m_total, lo = (jt / m_total) * CH;
-        const int part = rank_idx(msc, midx, lo, min(lo + CH, m_total), msc[i], midx[i]);
-        if (part) atomicAdd(&s_rank[SEL_MAXNEW + i], part);
-      }
+  // Ranks by (score desc, creation asc), a strict order (creation indices are distinct).  Each
+  // evaluated row's children are sorted in it (scores fall with the child rank, creation
+  // rises), and so is the running list of the N best so far.  So a candidate's rank among the
+  // new ones is its child rank plus, for every other row, the length of that row's prefix that
+  // beats it (a binary search); and in the union with the running list it is its rank in its
+  // own sorted list plus the prefix of the other list that beats it.
+  for (int pr = threadIdx.x; pr < n_new * nE; pr += blockDim.x) {
+    const int e = pr / nE, j2 = pr - e * nE;
+    if (j2 == e / K) continue;
+    const float se = nsc[e];
+    int lo = 0, hi = K;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1, f = j2 * K + mid;
+      if ((nsc[f] > se) | ((nsc[f] == se) & (f < e))) lo = mid + 1;
+      else hi = mid;
     }
+    if (lo) atomicAdd(&s_rank[e], lo);
   }
   __syncthreads();
+  for (int e = threadIdx.x; e < n_new; e += blockDim.x) nord[s_rank[e]] = e;
+  __syncthreads();
   if (!last)
-    for (int e = threadIdx.x; e < n_new; e += blockDim.x)
-      if (s_rank[e] < W) fr_e[s_rank[e]] = e;   // slots written at the end (a barrier after global stores waits for them)
-  for (int i = threadIdx.x; i < m_total; i += blockDim.x) {
-    const int r = s_rank[SEL_MAXNEW + i];
+    for (int r = threadIdx.x; r < min(W, n_new); r += blockDim.x) fr_e[r] = nord[r];
+  for (int x = threadIdx.x; x < m_total; x += blockDim.x) {
+    float sx;
+    int ix, own, lo = 0, hi;
+    if (x < ntop) {   // a running-list entry against the new candidates in rank order
+      sx = msc[x];
+      ix = midx[x];
+      own = x;
+      hi = n_new;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1, f = nord[mid];
+        if ((nsc[f] > sx) | ((nsc[f] == sx) & (n_before + f < ix))) lo = mid + 1;
+        else hi = mid;
+      }
+    } else {          // the new candidate of rank x - ntop against the running list
+      own = x - ntop;
+      const int e = nord[own];
+      sx = nsc[e];
+      ix = n_before + e;
+      hi = ntop;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((msc[mid] > sx) | ((msc[mid] == sx) & (midx[mid] < ix))) lo = mid + 1;
+        else hi = mid;
+      }
+    }
+    const int r = own + lo;
     if (r < N) {
-      ktop[r] = midx[i];
-      ktsc[r] = msc[i];
+      ktop[r] = ix;
+      ktsc[r] = sx;
     }
   }
   __syncthreads();
