@@ -243,6 +243,38 @@ def test_draft_batch16_full_size_sampled():
     check_teacher_forced(shape, w, di, out, shape.B, prefix, slots_per_request=chain)
 
 
+def test_draft_topk_statistics_at_the_widest_vocabulary():
+    """The LM-head statistics path at its widest vocabulary (V = 131064: 1024 blocks of 128
+    columns, the last holding 120) with the largest top-K and width (16): every lane of the
+    selection holds 16 blocks, the candidate gather takes the most blocks, and top-K ids stay
+    exact against the GPU's own logits."""
+    need_gpu()
+    shape = synth.scaled(SMALL_BF16, V=131064, B=1, depth=3, topk=16, width=16, n_nodes=40)
+    prefix = [300]
+    w = synth.drafter_weights(shape, seed=51, device=DEV)
+    di = synth.draft_inputs(shape, seed=52, device=DEV, prefix=prefix)
+    dr = capi.make_drafter(w, shape.Hq, shape.Hkv, shape.Dh)
+    tree = capi.Eagle3TreeCfg(depth=shape.depth, topk=shape.topk, width=shape.width,
+                              n_nodes=shape.n_nodes)
+    out = capi.eagle3_draft_expand(dr, tree, di["h_low"], di["h_mid"], di["h_high"], di["root_tok"],
+                                   di["kpre"], di["vpre"], di["cu_prefix"], max(prefix), debug=True,
+                                   debug_logits=True)
+    torch.cuda.synchronize()
+    check_topk_on_gpu_logits(shape, out["debug"], shape.B)
+    check_selection_replay(shape, out, shape.B)
+    # the log-sum-exp formed from the blocks' (best, sum) pairs against float64 over the logits
+    dbg = out["debug"]
+    lg = dbg["slot_logits"].cpu().numpy().astype(np.float64)
+    lse = dbg["slot_lse"].cpu().numpy()
+    sp = dbg["slot_parent"].cpu().numpy()
+    for s_ in range(lg.shape[1]):
+        if sp[0, s_] == -2:
+            continue
+        z = lg[0, s_]
+        ref = z.max() + np.log(np.exp(z - z.max()).sum())
+        assert abs(lse[0, s_] - ref) <= 1e-5 * max(1.0, abs(ref)), (s_, lse[0, s_], ref)
+
+
 @pytest.mark.parametrize("kind,V", [("plain", 4104), ("periodic3", 8192), ("paired", 4104)])
 def test_draft_topk_wide_lm_head_statistics(kind, V):
     """40 evaluated rows per step (4 requests x width 10): the LM head runs in the wide
