@@ -59,8 +59,8 @@ __global__ __launch_bounds__(256) void k_build_mask(const int32_t* __restrict__ 
 // when the row is 16-byte aligned); one Philox call yields the noise of four tokens.
 //
 // At T > 0 most of the Gumbel noise is never needed: G(u) = -ln(-ln u) rises with u, and a
-// word whose 23-bit cell index k = x >> 9 has L leading ones has 1 - u > 2^-(L+1), so
-// -ln u > 2^-(L+1) and G < (L+1) ln 2.  With a margin of 2^-10 over that (far above the
+// word whose 23-bit cell index k = x >> 9 has L leading ones has 1 - u >= 2^-(L+1), so
+// -ln u > 1 - u >= 2^-(L+1) and G < (L+1) ln 2.  With a margin of 2^-10 over that (far above the
 // rounding of the two logarithms), U = z*invT + G_bound(L) bounds the token's value (the same
 // rounded addition, with a larger addend).  Each lane computes the exact value of its token
 // with the largest bound; every token whose bound lies below the wave's best exact value

@@ -181,7 +181,8 @@ def test_gumbel_bound_of_the_scan_holds_for_every_word():
     the chunk attains, where L is the number of leading ones of the word's top 23 bits and
     B(L) = (L+1) ln 2 + 2^-10 (float32).  Every one of the 2^23 cells must satisfy
     G(u) <= B(L) with G the float32 noise of the oracle (the kernel's arithmetic), or the
-    skip could drop a winner.  Mathematically 1 - u > 2^-(L+1), so G < (L+1) ln 2."""
+    skip could drop a winner.  Mathematically 1 - u >= 2^-(L+1) and -ln u > 1 - u, so
+    G < (L+1) ln 2."""
     k = np.arange(1 << 23, dtype=np.uint64)
     x = k << np.uint64(9)
     g = -O.ln_spec(-O.ln_spec(O.uniform23(x)))
