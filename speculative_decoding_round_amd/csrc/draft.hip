@@ -544,13 +544,11 @@ __device__ __forceinline__ float row_topk_blocks(const LmBlocks& lb, int m, int 
   {
     // tau: K rounds over the lanes' two best block bests (a round takes every lane's current
     // head that equals the wave maximum), at most the K-th best value
-    float x = lm, x2 = kNegInf, tau = kNegInf;
-    bool seen = false;
+    float x = bv[0], x2 = kNegInf, tau = kNegInf;   // the lane's best and second best
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const bool first = (bv[i] == lm) & !seen;
-      seen |= first;
-      x2 = first ? x2 : fmaxf(x2, bv[i]);
+    for (int i = 1; i < 16; ++i) {
+      x2 = fmaxf(x2, fminf(x, bv[i]));
+      x = fmaxf(x, bv[i]);
     }
     for (int k = 0; k < K; ++k) {
       tau = wave_max(x);
