@@ -861,10 +861,14 @@ int launch_ring(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, f
 // k-block (16 NT output features; X costs MT/NT of W's DMA traffic) is chosen by the planner
 // from {8, 10, 12, 14, 16} so that the workgroups (one per CU) fill the 256 CUs; the ring is
 // as deep as the X buffer leaves room for in 160 KB of LDS.  The 16-tile kernels get one
-// symbol per projection (ROLE), the others share role 0 (6 for the SiLU gate/up).
+// symbol per projection (ROLE), the others share role 0 (6 for the SiLU gate/up).  The LM
+// head with block statistics at three row tiles may also take 32 tiles per k-block (512
+// output features): its 128256 columns then fit one round of 251 workgroups instead of two
+// rounds of 501, and X is half as large a share of each workgroup's stream (70B-shaped
+// depth steps: 331.7 -> 315.7 us, 6.4 -> 6.7 TB/s).
 constexpr int wide_ns(int mt, int nt) { return nt < 20 - mt ? nt : 20 - mt; }
 constexpr int kWideMTs[] = {3, 6, 10};
-constexpr int kWideNTs[] = {16, 14, 12, 10, 8};
+constexpr int kWideNTs[] = {32, 16, 14, 12, 10, 8};
 
 template <int MT, int NT, int ROLE, bool SILU>
 int launch_wide_r(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, float* Y, void* act,
@@ -887,6 +891,9 @@ int launch_wide(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, f
     }
   }
   switch (p.NT) {
+    case 32:
+      if constexpr (MT == 3) return launch_wide_r<MT, 32, 1, false>(p, X, ldx, W, Y, act, s, stats);
+      return EAGLE3_EUNSUPPORTED;
     case 14: return launch_wide_r<MT, 14, 0, false>(p, X, ldx, W, Y, act, s);
     case 12: return launch_wide_r<MT, 12, 0, false>(p, X, ldx, W, Y, act, s);
     case 10: return launch_wide_r<MT, 10, 0, false>(p, X, ldx, W, Y, act, s);
@@ -1048,7 +1055,8 @@ GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu, bool whole_k) {
     double best = -1;
     for (int nt : kWideNTs) {
       if (silu && !(nt == 16 || nt == 14 || nt == 8)) continue;
-      if (whole_k && nt != 16) continue;   // the statistics epilogue is built for 16 tiles
+      if (whole_k && nt != 16 && nt != 32) continue;   // the statistics epilogue takes 16 or 32 tiles
+      if (nt == 32 && (mt != 3 || !whole_k)) continue;   // only the LM head at three row tiles
       if (silu && (N / 2) % (16 * (nt / 2))) continue;
       const int nbk = silu ? (N / 2) / (16 * (nt / 2)) : ((N + 15) / 16 + nt - 1) / nt;
       const double t_kb = (nt + 0.4 * mt) * 8192.0 / 25e9;

@@ -71,9 +71,9 @@ struct GemmPlan {
 // whole_k: no k-split, as the LM head's block statistics need (see launch_gemm).
 GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu = false, bool whole_k = false);
 // Whether a plan's kernel can emit the LM head's block statistics: the bf16 ring kernel, or
-// the wide kernel at 16 tiles per block, without a k-split.
+// the wide kernel at 16 or 32 tiles per block, without a k-split.
 inline bool gemm_block_stats_ok(const GemmPlan& p) {
-  return !p.silu && p.splits == 1 && (p.ring || (p.wide && p.NT == 16));
+  return !p.silu && p.splits == 1 && (p.ring || (p.wide && (p.NT == 16 || p.NT == 32)));
 }
 // Row stride of the statistics planes: blocks of 128 columns, so N <= 131072.
 constexpr int kLmStatsLd = 1024;

@@ -29,7 +29,7 @@ from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 # the LM head (role 1): the LDS-ring kernel at one row tile, or the wide kernel (33 .. 160 rows)
-LM_HEAD_KERNEL = re.compile(r"k_gemm_ring<1, 8, \d+, false, 1, 1>|k_gemm_wide<\d+, 16, \d+, false, 1>")
+LM_HEAD_KERNEL = re.compile(r"k_gemm_ring<1, 8, \d+, false, 1, 1>|k_gemm_wide<\d+, (?:16|32), \d+, false, 1>")
 
 
 def source_hash(files=("gemm.hip", "common.h")) -> str:

@@ -8,9 +8,10 @@ def test_lm_head_pattern_ignores_the_stage_count():
         assert profsum.LM_HEAD_KERNEL.search(f"k_gemm_ring<1, 8, {nst}, false, 1, 1>")
     assert not profsum.LM_HEAD_KERNEL.search("k_gemm_ring<1, 8, 3, false, 2, 4>")    # QKV
     assert not profsum.LM_HEAD_KERNEL.search("k_gemm_ring<1, 8, 3, true, 6, 4>")     # gate/up
-    # the wide kernel (33 .. 160 rows): the LM head is role 1 at 16 tiles per block
+    # the wide kernel (33 .. 160 rows): the LM head is role 1 at 16 or 32 tiles per block
     assert profsum.LM_HEAD_KERNEL.search("k_gemm_wide<3, 16, 16, false, 1>")
     assert profsum.LM_HEAD_KERNEL.search("k_gemm_wide<10, 16, 10, false, 1>")
+    assert profsum.LM_HEAD_KERNEL.search("k_gemm_wide<3, 32, 17, false, 1>")   # 32 tiles per block
     assert not profsum.LM_HEAD_KERNEL.search("k_gemm_wide<3, 14, 14, true, 6>")
     assert not profsum.LM_HEAD_KERNEL.search("k_gemm_wide<3, 10, 10, false, 0>")
 
