@@ -219,9 +219,10 @@ __device__ __forceinline__ void lm_block_stats(Tile tile, int m, int M, int N, i
 //
 // A tile is 16 rows x 8 chunks (a 512-byte row segment).  It moves from HBM to a slot of
 // this wave's LDS ring by eight LDS-DMA instructions, each taking two whole 512-byte row
-// segments (lanes 0-31 and 32-63), so every HBM line is fetched whole, non-temporally.  A
-// row's 16-byte pieces are stored XOR-swizzled (piece p at position p ^ row), which keeps
-// the MFMA operand reads (16 rows at one piece) free of bank conflicts.  Per 8-chunk k-block
+// segments (lanes 0-31 and 32-63), so every HBM line is fetched whole (W non-temporally;
+// X, which every workgroup re-reads, with the default policy).  A row's 16-byte pieces are
+// stored XOR-swizzled (piece p at position p ^ row), which keeps the MFMA operand reads (16
+// rows at one piece) free of bank conflicts.  Per 8-chunk k-block
 // the stream is MT tiles of X (the evaluated rows, kept in registers for the block) and then
 // NTB tiles of W; NST slots are in flight.  W feeds operand A (16 output features), X
 // operand B, accumulation in fp32.  Needs K % 32 == 0 and MT <= 2.
@@ -232,16 +233,23 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// 16 bytes per lane into LDS at lds_base + 16 * lane, non-temporal.  Issued as assembly so
-// that the compiler does not see an outstanding LDS write (it would drain every DMA before
-// each later LDS read); completion is ordered by the explicit vmcnt waits of the ring.
-// M0 is written by the asm and named as clobbered; the compiler does not preserve reserved
-// registers across asm (hence its warning), which is harmless: nothing else in these
-// kernels keeps a value in M0.
+// 16 bytes per lane into LDS at lds_base + 16 * lane, non-temporal (W: read once).  Issued
+// as assembly so that the compiler does not see an outstanding LDS write (it would drain
+// every DMA before each later LDS read); completion is ordered by the explicit vmcnt waits
+// of the ring.  M0 is written by the asm and named as clobbered; the compiler does not
+// preserve reserved registers across asm (hence its warning), which is harmless: nothing
+// else in these kernels keeps a value in M0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void ring_dma(const void* gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(gptr), "s"(lds_base)
+               : "memory", "m0");
+}
+// The same with the default cache policy, for X: every workgroup re-reads the same rows, which
+// then come from L2 (non-temporal, they were fetched again from further out: 70B-shaped round
+// 4.56 -> 4.50 ms, batch-16 round 3.46 -> 3.30 ms).
+__device__ __forceinline__ void ring_dma_x(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -310,7 +318,8 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_ring(const bf16* __restrict__ 
       const int rt = 2 * i + (lane >> 5);
       const int row = min(row0 + rt, rmax);
       const int pc = min((lane & 31) ^ rt, lastp);
-      ring_dma(base + (size_t)row * ld + c0 * 32 + pc * 8, slot + i * 1024);
+      if (r < MT) ring_dma_x(base + (size_t)row * ld + c0 * 32 + pc * 8, slot + i * 1024);
+      else ring_dma(base + (size_t)row * ld + c0 * 32 + pc * 8, slot + i * 1024);
     }
   };
 
@@ -402,7 +411,8 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_ring(const bf16* __restrict__ 
 // wave w owns row tiles w, w + 4, w + 8 (MT tiles of 16 rows in all), and every W tile is
 // fetched once per workgroup into one shared LDS ring (two LDS-DMA instructions per wave,
 // whole 512-byte row segments, non-temporal) and read by all four waves against their own
-// rows.  The block's X (MT tiles x 8 chunks) has an LDS buffer of its own; each wave copies
+// rows.  The block's X (MT tiles x 8 chunks, fetched with the default cache policy: every
+// workgroup reads the same rows, from L2) has an LDS buffer of its own; each wave copies
 // its rows into registers at the block's first W tile, and the next block's X is fetched
 // right after the barrier of the second W tile, when every wave has its copy.
 // One barrier per W tile orders the ring: past it the tile's DMA has landed for every wave
@@ -445,27 +455,29 @@ __global__ __launch_bounds__(256) void k_gemm_wide(const bf16* __restrict__ X, i
   const char* wring = lds + MT * RING_TILE;
 
   // this wave's two DMA instructions of a 16-row tile: rows 4 wv .. 4 wv + 3
-  auto dma_tile = [&](const bf16* base, int ld, int row0, int rmax, int c0, int lastp, uint32_t slot) {
+  auto dma_tile = [&](const bf16* base, int ld, int row0, int rmax, int c0, int lastp, uint32_t slot,
+                      auto is_x) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int i = 2 * wv + h;
       const int rt = 2 * i + (lane >> 5);
       const int row = min(row0 + rt, rmax);
       const int pc = min((lane & 31) ^ rt, lastp);
-      ring_dma(base + (size_t)row * ld + c0 * 32 + pc * 8, slot + i * 1024);
+      if constexpr (decltype(is_x)::value) ring_dma_x(base + (size_t)row * ld + c0 * 32 + pc * 8, slot + i * 1024);
+      else ring_dma(base + (size_t)row * ld + c0 * 32 + pc * 8, slot + i * 1024);
     }
   };
   auto issue_w = [&](int s) {      // stage s: k-block s / NT, W tile s % NT of this n-block
     const int j = s / NT, t = s - j * NT;
     const int c0 = cs0 + j * 8;
     dma_tile(W, K, tile_row0<NT, SILU>(nb, t, F), N - 1, c0, min(8, cs1 - c0) * 4 - 1,
-             wring0 + (uint32_t)(s % NS) * RING_TILE);
+             wring0 + (uint32_t)(s % NS) * RING_TILE, std::false_type{});
   };
   auto issue_x = [&](int j) {      // the MT row tiles of X for k-block j
     const int c0 = cs0 + j * 8;
     const int lastp = min(8, cs1 - c0) * 4 - 1;
 #pragma unroll
-    for (int t = 0; t < MT; ++t) dma_tile(X, ldx, t * 16, M - 1, c0, lastp, xbuf0 + t * RING_TILE);
+    for (int t = 0; t < MT; ++t) dma_tile(X, ldx, t * 16, M - 1, c0, lastp, xbuf0 + t * RING_TILE, std::true_type{});
   };
   auto opoff = [&](int u) { return (uint32_t)(r16 * 512 + (((4 * u + g) ^ r16) * 16)); };
 

@@ -275,18 +275,20 @@ def test_draft_topk_statistics_at_the_widest_vocabulary():
         assert abs(lse[0, s_] - ref) <= 1e-5 * max(1.0, abs(ref)), (s_, lse[0, s_], ref)
 
 
-@pytest.mark.parametrize("kind,V", [("plain", 4104), ("periodic3", 8192), ("paired", 4104),
-                                    ("plain", 65544)])
-def test_draft_topk_wide_lm_head_statistics(kind, V):
+@pytest.mark.parametrize("kind,V,B", [("plain", 4104, 4), ("periodic3", 8192, 4), ("paired", 4104, 4),
+                                      ("plain", 65544, 4), ("plain", 4104, 16), ("periodic3", 8192, 16)])
+def test_draft_topk_wide_lm_head_statistics(kind, V, B):
     """40 evaluated rows per step (4 requests x width 10): the LM head runs in the wide
     kernel and emits statistics per 128 columns, from which the selection takes each row's
     top-K and log-sum-exp.  Top-K ids stay exact with plain logits, with heavy ties (the
     exact path), and when the vocabulary ends 8 columns into a block (V = 4104: the last
     256-column workgroup has a half wholly past the end; V = 65544: 32 tiles per workgroup,
-    one round of 129 workgroups, the last with three 128-column quarters past the end)."""
+    one round of 129 workgroups, the last with three 128-column quarters past the end).
+    With 16 requests (160 rows) the wide kernel holds ten row tiles (waves 0 and 1 three
+    each, waves 2 and 3 two) at 16 tiles per workgroup."""
     need_gpu()
-    shape = synth.scaled(SMALL_BF16, V=V, B=4, depth=3, topk=10, width=10, n_nodes=20)
-    prefix = [100, 257, 33, 1]
+    shape = synth.scaled(SMALL_BF16, V=V, B=B, depth=3, topk=10, width=10, n_nodes=20)
+    prefix = [100, 257, 33, 1] * (B // 4)
     w = synth.drafter_weights(shape, seed=41, device=DEV)
     _tied_lm_head(w, kind)
     di = synth.draft_inputs(shape, seed=42, device=DEV, prefix=prefix)

@@ -1,8 +1,8 @@
 """GPU parity of eagle3_linear (the drafter projections' GEMM kernels) against the oracle's
 float64 projection, through the C-ABI: the LDS-ring kernel (M <= 32, with and without split-K
 partial sums), the wide kernel (33 .. 160 rows, four waves splitting the rows over a shared W
-ring; also whole and split k-ranges, a ragged last k-block and a ragged last n-block), the
-register-stationary kernel (K not a multiple of 32), and the tiled matrix-core kernel
+ring; also whole and split k-ranges, ragged rows, a ragged last k-block and a ragged last
+n-block), the register-stationary kernel (K not a multiple of 32), and the tiled matrix-core kernel
 (M > 160, including ragged M and N, whole and split k-ranges), at fp32 and bf16.  Full-size
 shapes are checked on sampled rows."""
 import numpy as np
@@ -25,6 +25,9 @@ BF, F32 = torch.bfloat16, torch.float32
     (4, 10240, 16384, BF, None),    # ring, 80 n-blocks: four-wave workgroups, three k-splits
     (40, 4096, 4096, BF, None),     # wide kernel, three row tiles (wave 3 holds none)
     (160, 1024, 4096, BF, None),    # wide kernel, ten row tiles
+    (96, 2048, 4096, BF, None),     # wide: six row tiles
+    (97, 1000, 1056, BF, None),     # wide: one row past six tiles, ragged n-block, 33 chunks
+    (150, 4104, 2080, BF, None),    # wide: ragged rows, n-block and last k-block (65 chunks)
     (33, 1000, 1056, BF, None),     # wide: one row past two tiles, ragged n-block, 33 chunks
     (48, 4096, 8192, BF, None),     # wide: three full row tiles, k split
     (64, 2048, 2304, BF, None),     # wide: four row tiles (one per wave)
@@ -41,7 +44,8 @@ BF, F32 = torch.bfloat16, torch.float32
     (2048, 6144, 8192, BF, 64),     # tiled kernel at the QKV shape of a 2048-token prompt
     (1024, 6144, 8192, BF, 32),     # the same with 1024 rows: k split in two
     (1024, 4096, 14336, BF, 32),    # tiled kernel at the MLP-down shape
-], ids=["ring_m1", "ring_m10_split", "ring_m32", "ring_m4_80_nblocks", "wide_m40", "wide_m160", "wide_m33_ragged",
+], ids=["ring_m1", "ring_m10_split", "ring_m32", "ring_m4_80_nblocks", "wide_m40", "wide_m160", "wide_m96",
+        "wide_m97_ragged", "wide_m150_ragged_split", "wide_m33_ragged",
         "wide_m48_split", "wide_m64", "wide_m100", "wide_m128_down", "wide_qkv_70b", "wide_lm_70b",
         "wide_lm_batch16", "regs_m40_k1000", "fp32_m10", "tile_m256",
         "tile_m200", "tile_ragged", "tile_qkv_2048", "tile_qkv_1024_split", "tile_down_1024"])
@@ -90,11 +94,12 @@ def test_linear_split_k_is_deterministic():
     assert torch.equal(a, b)
 
 
-def test_wide_split_k_is_deterministic():
-    """The wide kernel's k-split partial sums are added in split order: two calls agree bit
-    for bit (160 rows at the 8B QKV shape, whose plan splits the k-range)."""
+@pytest.mark.parametrize("M", [48, 160], ids=["three_tiles", "ten_tiles"])
+def test_wide_split_k_is_deterministic(M):
+    """The wide kernel's k-split partial sums are added in split order: two calls agree bit for
+    bit (48 and 160 rows at the 8B QKV shape, whose plans split the k-range)."""
     need_gpu()
-    M, N, K = 160, 6144, 8192
+    N, K = 6144, 8192
     assert capi.lib().eagle3_linear_workspace_size(M, N, K, capi.EAGLE3_BF16) > 0
     x = synth.normal((M, K), 1.0, 31, BF, DEV)
     w = synth.normal((N, K), K ** -0.5, 32, BF, DEV)
@@ -102,6 +107,6 @@ def test_wide_split_k_is_deterministic():
     b = capi.eagle3_linear(x, w)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
-    sel = np.array([0, 17, 80, 159])
+    sel = np.array([0, 17, 40, M - 1])
     ref = O.project(x[torch.as_tensor(sel, device=DEV)].cpu(), w.cpu())
     assert rel_err(np32(a)[sel], ref) <= TOL[BF]
