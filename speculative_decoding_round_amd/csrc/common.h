@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "eagle3.h"
 
 namespace e3 {
@@ -350,6 +352,16 @@ __device__ __forceinline__ int find_request(const int32_t* cu, int B, int node) 
       hi = mid - 1;
   }
   return lo;
+}
+
+// fn(std::integral_constant<int, i>{}) for i = I .. N - 1, unrolled at compile time (for
+// register arrays indexed by a loop counter).
+template <int I, int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+  if constexpr (I < N) {
+    fn(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(fn);
+  }
 }
 
 }  // namespace e3

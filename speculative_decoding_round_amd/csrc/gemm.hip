@@ -421,14 +421,6 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_ring(const bf16* __restrict__ 
 // issued after the awaited ones, including the next block's X when it lies between them.
 // Needs K % 32 == 0; MT <= 12; NT >= NS.
 // ---------------------------------------------------------------------------------------
-template <int I, int N, typename Fn>
-__device__ __forceinline__ void static_for(Fn&& fn) {
-  if constexpr (I < N) {
-    fn(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(fn);
-  }
-}
-
 template <int MT, int NT, int NS, bool SILU, int ROLE>
 __global__ __launch_bounds__(256) void k_gemm_wide(const bf16* __restrict__ X, int M, int ldx,
                                                    const bf16* __restrict__ W, int N, int K,
