@@ -1048,7 +1048,12 @@ GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu, bool whole_k) {
     // workgroup, one workgroup per CU).  For each tile count NT, a k-split in whole 8-chunk
     // blocks; the (NT, split) pair minimises (rounds of workgroups over the CUs) x (blocks per
     // workgroup) x (time of one block: NT W tiles from HBM at ~25 GB/s per CU, plus the MT X
-    // tiles from L2 at ~2.5x that) plus the fp32 partials' write and read at ~6 TB/s.
+    // tiles from L2) plus the fp32 partials' write and read.  Coefficients fitted to sweeps
+    // of (NT, split) on this part: at three row tiles an X tile costs ~5% of a W tile and the
+    // partials move at ~2.5 TB/s (eagle3_linear at the 70B-shaped O projection 34.3 -> 30.3 us
+    // and MLP down 85.8 -> 82.2 us at 8 tiles x 4 splits instead of 16 x 8, sum pass included;
+    // the drafter round, whose residual-norm launch reads the partials, measured the same); at
+    // six and ten row tiles an X tile costs ~40% of a W tile and the partials move at ~6 TB/s.
     int mt = 0;
     for (int v : kWideMTs)
       if (v >= mt_need) {
@@ -1063,14 +1068,15 @@ GemmPlan plan_gemm(int M, int N, int K, int dtype, bool silu, bool whole_k) {
       if (nt == 32 && (mt != 3 || !whole_k)) continue;   // only the LM head at three row tiles
       if (silu && (N / 2) % (16 * (nt / 2))) continue;
       const int nbk = silu ? (N / 2) / (16 * (nt / 2)) : ((N + 15) / 16 + nt - 1) / nt;
-      const double t_kb = (nt + 0.4 * mt) * 8192.0 / 25e9;
+      const double x_cost = mt == 3 ? 0.05 : 0.4, part_bw = mt == 3 ? 2.5e12 : 6e12;
+      const double t_kb = (nt + x_cost * mt) * 8192.0 / 25e9;
       for (int kbps = n_kb; kbps >= 1; --kbps) {
         if ((silu || whole_k) && kbps != n_kb) break;   // the SiLU product needs the whole k-range
         const int sp = (n_kb + kbps - 1) / kbps;
         if (sp > 1 && (n_kb + sp - 1) / sp != kbps) continue;   // the same split count, fewer blocks
         const long wgs = (long)nbk * sp;
         const long rounds = (wgs + kTileCUs - 1) / kTileCUs;
-        const double t = (double)rounds * kbps * t_kb + (sp > 1 ? 2.0 * sp * (double)M * N * 4 / 6e12 : 0.0);
+        const double t = (double)rounds * kbps * t_kb + (sp > 1 ? 2.0 * sp * (double)M * N * 4 / part_bw : 0.0);
         if (best < 0 || t < best * 0.98) {
           best = t;
           p.wide = true;
