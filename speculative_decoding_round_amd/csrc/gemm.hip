@@ -865,7 +865,8 @@ int launch_ring(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, f
 // k-block (16 NT output features; X costs MT/NT of W's DMA traffic) is chosen by the planner
 // from {8, 10, 12, 14, 16} so that the workgroups (one per CU) fill the 256 CUs; the ring is
 // as deep as the X buffer leaves room for in 160 KB of LDS.  The 16-tile kernels get one
-// symbol per projection (ROLE), the others share role 0 (6 for the SiLU gate/up).  The LM
+// symbol per projection (ROLE), the 8-tile ones one for the QKV, O and MLP-down projections,
+// the others share role 0 (6 for the SiLU gate/up).  The LM
 // head with block statistics at three row tiles may also take 32 tiles per k-block (512
 // output features): its 128256 columns then fit one round of 251 workgroups instead of two
 // rounds of 501, and X is half as large a share of each workgroup's stream (70B-shaped
@@ -901,7 +902,13 @@ int launch_wide(const e3h::GemmPlan& p, const void* X, int ldx, const void* W, f
     case 14: return launch_wide_r<MT, 14, 0, false>(p, X, ldx, W, Y, act, s);
     case 12: return launch_wide_r<MT, 12, 0, false>(p, X, ldx, W, Y, act, s);
     case 10: return launch_wide_r<MT, 10, 0, false>(p, X, ldx, W, Y, act, s);
-    case 8: return launch_wide_r<MT, 8, 0, false>(p, X, ldx, W, Y, act, s);
+    case 8:
+      switch (role) {
+        case 2: return launch_wide_r<MT, 8, 2, false>(p, X, ldx, W, Y, act, s);
+        case 3: return launch_wide_r<MT, 8, 3, false>(p, X, ldx, W, Y, act, s);
+        case 4: return launch_wide_r<MT, 8, 4, false>(p, X, ldx, W, Y, act, s);
+        default: return launch_wide_r<MT, 8, 0, false>(p, X, ldx, W, Y, act, s);
+      }
     case 16: break;
     default: return EAGLE3_EUNSUPPORTED;
   }
