@@ -827,6 +827,18 @@ def gemm_rooflines(rnd: "Round", steps: int):
         "gemm_lm_head": (V * d, s.B * s.width, d, V, 4),       # depth steps: B * W rows
         "gemm_lm_head_root": (V * d, s.B, d, V, 4),            # the root step: B rows
     }
+    def kernel_for(ms_rows):
+        """The bf16 weight-streaming kernels that run these row counts: the LDS ring up to 32
+        rows, the wide kernel up to 160."""
+        names = []
+        for r in ms_rows:
+            k = "k_gemm_ring" if r <= 32 else "k_gemm_wide"
+            if k not in names:
+                names.append(k)
+        return " / ".join(names)
+
+    root, deep = [s.B], [s.B * s.width]
+    launched = {"gemm_fuse": root, "gemm_lm_head": deep, "gemm_lm_head_root": root}
     out = []
     for tag, (wn, m, kin, nout, oes) in spec.items():
         ms, n = capi.eagle3_profile_read(tag)
@@ -834,7 +846,8 @@ def gemm_rooflines(rnd: "Round", steps: int):
             continue
         us = ms / n * 1e3
         b = wn * es + m * kin * es + m * nout * oes
-        out.append(_entry(tag, s.name, "k_gemm", us, "hbm", bytes_=b, launches=n))
+        out.append(_entry(tag, s.name, kernel_for(launched.get(tag, root + deep)), us, "hbm", bytes_=b,
+                          launches=n))
     capi.eagle3_profile_reset()
     return out
 
