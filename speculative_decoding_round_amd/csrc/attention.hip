@@ -549,13 +549,15 @@ __global__ __launch_bounds__(256) void k_tree_attn_dma(DevArgs a) {
     // online softmax against the reference max (scale > 0 is folded into the exponent)
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      float tmax = kNegInf;
+      float lmax = kNegInf;
 #pragma unroll
       for (int st = 0; st < NST16; ++st)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[qt][st][i]);
-      tmax = row_reduce(tmax, OpMax()) * sc;
-      if (__any(tmax > m_ref[qt] + kRescaleLog2)) {
+        for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, s[qt][st][i]);
+      // the lane's maximum decides whether its row passes the reference (scaling by sc > 0
+      // keeps the order), so the row maximum is reduced across lanes only when one does
+      if (__any(lmax * sc > m_ref[qt] + kRescaleLog2)) {
+        const float tmax = row_reduce(lmax, OpMax()) * sc;
         const float m_new = fmaxf(m_ref[qt], tmax);
         const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_ref[qt] - m_new);
         l_run[qt] *= alpha;
@@ -810,7 +812,9 @@ void launch_merge_rows(int S_rt, int rows, const float* o_part, const float* lse
 //    pairs, four 32 KB stages (one workgroup per CU, three stages in flight: these launches
 //    only stream K/V, and a deeper ring beats the 64 KB stages of a four-way key split);
 // 1: <= 256 rows: 64 rows per workgroup, one 16-row tile per wave, keys shared;
-// 2: more: 128 rows per workgroup, two 16-row tiles per wave, keys shared.
+// 2: more: 128 rows per workgroup, two 16-row tiles per wave, keys shared, 64 keys per
+//    iteration in two 32 KB stages (half the barriers and per-tile softmax steps per key of
+//    32-key tiles in four stages, at the same 64 KB of LDS; these launches are math-bound).
 // Workgroups aimed for per launch: one per CU for shape 0; for shape 1 several rounds of
 // the two resident per CU, which evens out ragged requests; for shape 2 (hundreds of rows,
 // math-bound) one round.
@@ -826,7 +830,7 @@ inline int attn_cfg(int rows) {
 inline int attn_cfg_rows(int cfg) { return cfg == 0 ? 32 : cfg == 1 ? 64 : 128; }
 // keys per iteration, for split sizing (shape 0 streams 64 per iteration, but its splits keep
 // at least 128 keys, two iterations)
-inline int attn_cfg_keys(int cfg) { return cfg == 0 ? 128 : 32; }
+inline int attn_cfg_keys(int cfg) { return cfg == 0 ? 128 : cfg == 1 ? 32 : 64; }
 inline int attn_cfg_wgs(int cfg) { return cfg == 0 ? 256 : cfg == 1 ? 2048 : 512; }
 
 template <typename T, int DH>
@@ -865,7 +869,7 @@ int launch_attn_t(const e3h::AttnArgs& h, hipStream_t s) {
     switch (attn_cfg(rows)) {
       case 0: go(k_tree_attn_dma<DH, 1, 2, 32, 4>, DmaCfg<DH, 1, 2, 32, 4>::ROWS); break;
       case 1: go(k_tree_attn_dma<DH, 1, 1, 32, 4>, DmaCfg<DH, 1, 1, 32, 4>::ROWS); break;
-      default: go(k_tree_attn_dma<DH, 2, 1, 32, 4>, DmaCfg<DH, 2, 1, 32, 4>::ROWS); break;
+      default: go(k_tree_attn_dma<DH, 2, 1, 64, 2>, DmaCfg<DH, 2, 1, 64, 2>::ROWS); break;
     }
   } else {
     const int rb = (rows + ROWS - 1) / ROWS;
@@ -940,7 +944,7 @@ __global__ __launch_bounds__(1024) void k_branch_attn(int L, int n_steps, int Hq
 namespace e3h {
 
 // [P4] USP step 1: causal attention of every position over the sequence, bf16, positions in
-// blocks of 128 (rows = 128 x G per block, 128 rows per workgroup).
+// blocks of 128 (rows = 128 x G per block, 128 rows per workgroup, 64 keys per iteration).
 int launch_causal_attention(int L, int Hq, int Hkv, int Dh, const void* q, const void* k, const void* v,
                             float scale, float* o, float* lse, hipStream_t s) {
   constexpr int CB = 128;
@@ -970,8 +974,8 @@ int launch_causal_attention(int L, int Hq, int Hkv, int Dh, const void* q, const
     const long n = (groups + 7) / 8 * 8 * a.n_rb;
     hipLaunchKernelGGL(kern, dim3((unsigned)n), dim3(256), 0, s, a);
   };
-  if (Dh == 128) go(k_tree_attn_dma<128, 2, 1, 32, 4, true>, DmaCfg<128, 2, 1, 32, 4>::ROWS);
-  else if (Dh == 64) go(k_tree_attn_dma<64, 2, 1, 32, 4, true>, DmaCfg<64, 2, 1, 32, 4>::ROWS);
+  if (Dh == 128) go(k_tree_attn_dma<128, 2, 1, 64, 2, true>, DmaCfg<128, 2, 1, 64, 2>::ROWS);
+  else if (Dh == 64) go(k_tree_attn_dma<64, 2, 1, 64, 2, true>, DmaCfg<64, 2, 1, 64, 2>::ROWS);
   else return EAGLE3_EUNSUPPORTED;
   return launch_status();
 }
