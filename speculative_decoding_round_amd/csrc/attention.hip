@@ -812,9 +812,10 @@ void launch_merge_rows(int S_rt, int rows, const float* o_part, const float* lse
 //    pairs, four 32 KB stages (one workgroup per CU, three stages in flight: these launches
 //    only stream K/V, and a deeper ring beats the 64 KB stages of a four-way key split);
 // 1: <= 256 rows: 64 rows per workgroup, one 16-row tile per wave, keys shared;
-// 2: more: 128 rows per workgroup, two 16-row tiles per wave, keys shared, 64 keys per
-//    iteration in two 32 KB stages (half the barriers and per-tile softmax steps per key of
-//    32-key tiles in four stages, at the same 64 KB of LDS; these launches are math-bound).
+// 2: more: 128 rows per workgroup, two 16-row tiles per wave, keys shared.
+// Shapes 1 and 2 take 64 keys per iteration in two 32 KB stages: half the barriers and
+// per-tile softmax steps per key of 32-key tiles in four 16 KB stages, at the same 64 KB of
+// LDS (their launches are bound by the math, not the stream).
 // Workgroups aimed for per launch: one per CU for shape 0; for shape 1 several rounds of
 // the two resident per CU, which evens out ragged requests; for shape 2 (hundreds of rows,
 // math-bound) one round.
@@ -830,7 +831,7 @@ inline int attn_cfg(int rows) {
 inline int attn_cfg_rows(int cfg) { return cfg == 0 ? 32 : cfg == 1 ? 64 : 128; }
 // keys per iteration, for split sizing (shape 0 streams 64 per iteration, but its splits keep
 // at least 128 keys, two iterations)
-inline int attn_cfg_keys(int cfg) { return cfg == 0 ? 128 : cfg == 1 ? 32 : 64; }
+inline int attn_cfg_keys(int cfg) { return cfg == 0 ? 128 : 64; }
 inline int attn_cfg_wgs(int cfg) { return cfg == 0 ? 256 : cfg == 1 ? 2048 : 512; }
 
 template <typename T, int DH>
@@ -868,7 +869,7 @@ int launch_attn_t(const e3h::AttnArgs& h, hipStream_t s) {
     };
     switch (attn_cfg(rows)) {
       case 0: go(k_tree_attn_dma<DH, 1, 2, 32, 4>, DmaCfg<DH, 1, 2, 32, 4>::ROWS); break;
-      case 1: go(k_tree_attn_dma<DH, 1, 1, 32, 4>, DmaCfg<DH, 1, 1, 32, 4>::ROWS); break;
+      case 1: go(k_tree_attn_dma<DH, 1, 1, 64, 2>, DmaCfg<DH, 1, 1, 64, 2>::ROWS); break;
       default: go(k_tree_attn_dma<DH, 2, 1, 64, 2>, DmaCfg<DH, 2, 1, 64, 2>::ROWS); break;
     }
   } else {
