@@ -465,11 +465,15 @@ __global__ __launch_bounds__(256) void k_tree_attn_dma(DevArgs a) {
   };
 
   floatx4 acc[QT][NDT];
-  float m_ref[QT], l_run[QT];
+  // l_acc: each row's sum of P, formed by one more MFMA per 32 keys with a block of ones in
+  // place of V^T (every element of the 16 x 16 result is the row's sum over those keys), so
+  // the sum costs no vector adds and uses the same bf16 P as the output
+  float m_ref[QT];
+  floatx4 l_acc[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     m_ref[qt] = kNegInf;
-    l_run[qt] = 0.f;
+    l_acc[qt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
@@ -560,22 +564,16 @@ __global__ __launch_bounds__(256) void k_tree_attn_dma(DevArgs a) {
         const float tmax = row_reduce(lmax, OpMax()) * sc;
         const float m_new = fmaxf(m_ref[qt], tmax);
         const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_ref[qt] - m_new);
-        l_run[qt] *= alpha;
+        l_acc[qt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] *= alpha;
         m_ref[qt] = m_new;
       }
       const float nm = m_ref[qt] == kNegInf ? 0.f : -m_ref[qt];
-      float psum = 0.f;
 #pragma unroll
       for (int st = 0; st < NST16; ++st)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][st][i], sc, nm));
-          s[qt][st][i] = p;
-          psum += p;
-        }
-      l_run[qt] += psum;
+        for (int i = 0; i < 4; ++i) s[qt][st][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][st][i], sc, nm));
     }
     // O^T += V^T P^T, 32 keys per step
 #pragma unroll
@@ -605,12 +603,15 @@ __global__ __launch_bounds__(256) void k_tree_attn_dma(DevArgs a) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) acc[qt][dt] = Mfma<bf16>::run(va, pb[qt], acc[qt][dt]);
       }
+      const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) l_acc[qt] = Mfma<bf16>::run(ones, pb[qt], l_acc[qt]);
     }
   }
 
   float l_tot[QT];
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) l_tot[qt] = row_reduce(l_run[qt], OpAdd());
+  for (int qt = 0; qt < QT; ++qt) l_tot[qt] = l_acc[qt][0];
 
   if constexpr (WK > 1) {
     // key groups 1.. hand their (m, l, O) to group 0 through LDS
