@@ -817,9 +817,11 @@ void launch_merge_rows(int S_rt, int rows, const float* o_part, const float* lse
 // Shapes 1 and 2 take 64 keys per iteration in two 32 KB stages: half the barriers and
 // per-tile softmax steps per key of 32-key tiles in four 16 KB stages, at the same 64 KB of
 // LDS (their launches are bound by the math, not the stream).
-// Workgroups aimed for per launch: one per CU for shape 0; for shape 1 several rounds of
-// the two resident per CU, which evens out ragged requests; for shape 2 (hundreds of rows,
-// math-bound) one round.
+// Workgroups aimed for per launch: one per CU for shape 0; for shape 1 four rounds of the two
+// resident per CU, which evens out ragged requests, or two when each (request, KV head) has
+// one row block (every workgroup then streams K/V no other one reads, and its fixed start and
+// end costs weigh more: batch-16 drafter steps 3.28 -> 3.23 ms per round); for shape 2
+// (hundreds of rows, math-bound) one round.
 // Workgroup shape by query rows per KV head: <= 32 rows, keys split over the waves; 65 .. 128
 // rows (e.g. ten drafted nodes x 8 heads per KV head) in one 128-row block, so each K/V split
 // is streamed by one workgroup and the splits stay few; other rows up to 256 in 64-row blocks;
@@ -833,7 +835,9 @@ inline int attn_cfg_rows(int cfg) { return cfg == 0 ? 32 : cfg == 1 ? 64 : 128; 
 // keys per iteration, for split sizing (shape 0 streams 64 per iteration, but its splits keep
 // at least 128 keys, two iterations)
 inline int attn_cfg_keys(int cfg) { return cfg == 0 ? 128 : 64; }
-inline int attn_cfg_wgs(int cfg) { return cfg == 0 ? 256 : cfg == 1 ? 2048 : 512; }
+inline int attn_cfg_wgs(int cfg, long row_blocks) {
+  return cfg == 0 ? 256 : cfg == 1 ? (row_blocks == 1 ? 1024 : 2048) : 512;
+}
 
 template <typename T, int DH>
 int launch_attn_t(const e3h::AttnArgs& h, hipStream_t s) {
@@ -1010,7 +1014,7 @@ int attention_splits(int B, int Hkv, int rows_per_kv, int max_prefix, int n_spli
   const int rows_wg = attn_cfg_rows(cfg), kiter = attn_cfg_keys(cfg);
   const long rb = (rows + rows_wg - 1) / rows_wg;
   const long base = (long)B * Hkv * rb;
-  long s = (attn_cfg_wgs(cfg) + base - 1) / base;
+  long s = (attn_cfg_wgs(cfg, rb) + base - 1) / base;
   const long min_keys = std::max<long>(kiter, 3L * std::min(rows, rows_wg));
   const long max_s = (max_prefix + min_keys - 1) / min_keys;
   if (s > max_s) s = max_s;
