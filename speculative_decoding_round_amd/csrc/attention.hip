@@ -820,8 +820,10 @@ void launch_merge_rows(int S_rt, int rows, const float* o_part, const float* lse
 // Workgroups aimed for per launch: one per CU for shape 0; for shape 1 four rounds of the two
 // resident per CU, which evens out ragged requests, or two when each (request, KV head) has
 // one row block (every workgroup then streams K/V no other one reads, and its fixed start and
-// end costs weigh more: batch-16 drafter steps 3.28 -> 3.23 ms per round); for shape 2
-// (hundreds of rows, math-bound) one round.
+// end costs weigh more: batch-16 drafter steps 3.28 -> 3.23 ms per round); for shape 2 one
+// round (hundreds of rows, math-bound), or, with one row block per (request, KV head), a
+// little under one round (the 70B-shaped drafter steps: 14 prefix splits and 480 workgroups
+// beat 16 and 544 by ~50 us per round, and 15 and 512 by ~30 us).
 // Workgroup shape by query rows per KV head: <= 32 rows, keys split over the waves; 65 .. 128
 // rows (e.g. ten drafted nodes x 8 heads per KV head) in one 128-row block, so each K/V split
 // is streamed by one workgroup and the splits stay few; other rows up to 256 in 64-row blocks;
@@ -836,7 +838,9 @@ inline int attn_cfg_rows(int cfg) { return cfg == 0 ? 32 : cfg == 1 ? 64 : 128; 
 // at least 128 keys, two iterations)
 inline int attn_cfg_keys(int cfg) { return cfg == 0 ? 128 : 64; }
 inline int attn_cfg_wgs(int cfg, long row_blocks) {
-  return cfg == 0 ? 256 : cfg == 1 ? (row_blocks == 1 ? 1024 : 2048) : 512;
+  if (cfg == 0) return 256;
+  if (cfg == 1) return row_blocks == 1 ? 1024 : 2048;
+  return row_blocks == 1 ? 448 : 512;
 }
 
 template <typename T, int DH>
