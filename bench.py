@@ -32,8 +32,8 @@ HBM_PEAK_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama70b", choices=["llama8b", "batch16", "llama70b", "tiny"])
     ap.add_argument("--no-other-rounds", action="store_true",
                     help="skip the whole rounds of the other workloads (extra fields)")
