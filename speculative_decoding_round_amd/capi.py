@@ -167,6 +167,32 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
     return t
 
 
+def _shape(t, name: str, *dims) -> None:
+    """Raise unless `t` has len(dims) dimensions matching `dims` (None matches any extent).
+    The library sees raw pointers only: a tensor smaller than the layout the arguments imply
+    would be read or written out of bounds on the device."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dim() != len(dims) or any(d is not None and t.shape[i] != d for i, d in enumerate(dims)):
+        want = ", ".join("*" if d is None else str(d) for d in dims)
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected [{want}]")
+
+
+def _out_shapes(out: Optional[dict], shapes: dict) -> None:
+    """Caller-provided outputs must have the shapes the call writes."""
+    if out is None:
+        return
+    for k, dims in shapes.items():
+        if out.get(k) is not None:
+            _shape(out[k], k, *dims)
+
+
+def _kv_pair(k, v, Hkv: int, Dh: int, kname: str, vname: str) -> None:
+    _shape(k, kname, None, Hkv, Dh)
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"{vname} shape {tuple(v.shape)} differs from {kname} {tuple(k.shape)}")
+
+
 def dtype_code(dt: torch.dtype) -> int:
     if dt == torch.float32:
         return EAGLE3_F32
@@ -201,15 +227,32 @@ def make_drafter(weights: dict, n_heads_q: int, n_heads_kv: int, head_dim: int,
     """Describe device-resident drafter weights (layouts as in include/eagle3.h).  The
     returned struct holds raw pointers: keep `weights` alive while it is used."""
     dt = weights["embed"].dtype
-    for k in WEIGHT_KEYS:
-        _dev(weights[k], k, dt)
     V, d = weights["embed"].shape
     F = weights["w_down"].shape[1]
+    if n_heads_kv <= 0 or n_heads_q % n_heads_kv:
+        raise ValueError("n_heads_q must be a positive multiple of n_heads_kv")
+    dims = {"embed": (V, d), "w_fuse": (d, 3 * d), "g_embed": (d,), "g_feat": (d,), "g_mlp": (d,),
+            "g_final": (d,), "w_qkv": ((n_heads_q + 2 * n_heads_kv) * head_dim, 2 * d),
+            "w_o": (d, n_heads_q * head_dim), "w_gate_up": (2 * F, d), "w_down": (d, F), "w_lm": (V, d)}
+    for k in WEIGHT_KEYS:
+        _shape(weights[k], k, *dims[k])
+    for k in WEIGHT_KEYS:
+        _dev(weights[k], k, dt)
     s = Eagle3Drafter(d=d, n_heads_q=n_heads_q, n_heads_kv=n_heads_kv, head_dim=head_dim, ffn=F,
                       vocab=V, dtype=dtype_code(dt), eps=eps, rope_theta=rope_theta)
     for k in WEIGHT_KEYS:
         setattr(s, k, weights[k].data_ptr())
     return s
+
+
+def _draft_inputs(drafter: Eagle3Drafter, h_low, h_mid, h_high, root_tok, kpre, vpre, cu_prefix) -> int:
+    B = h_low.shape[0] if isinstance(h_low, torch.Tensor) and h_low.dim() == 2 else -1
+    for n, t in (("h_low", h_low), ("h_mid", h_mid), ("h_high", h_high)):
+        _shape(t, n, B, drafter.d)
+    _shape(root_tok, "root_tok", B)
+    _shape(cu_prefix, "cu_prefix", B + 1)
+    _kv_pair(kpre, vpre, drafter.n_heads_kv, drafter.head_dim, "kpre", "vpre")
+    return B
 
 
 def eagle3_draft_expand_workspace_size(drafter: Eagle3Drafter, tree: Eagle3TreeCfg, B: int,
@@ -222,8 +265,9 @@ def eagle3_draft_expand(drafter: Eagle3Drafter, tree: Eagle3TreeCfg, h_low, h_mi
                         root_tok, kpre, vpre, cu_prefix, max_prefix: int, debug: bool = False,
                         debug_logits: bool = False, workspace: Optional[torch.Tensor] = None,
                         out: Optional[dict] = None, stream=None) -> dict:
-    """One draft-tree round.  Returns dict(tokens, parents, depth, score, n_nodes[, debug])."""
-    B = h_low.shape[0]
+    """One draft-tree round.  Returns dict(tokens, parents, depth, score, n_nodes[, debug]).
+    kpre, vpre [rows, Hkv, Dh] must hold every row that cu_prefix (device) names."""
+    B = _draft_inputs(drafter, h_low, h_mid, h_high, root_tok, kpre, vpre, cu_prefix)
     dev = h_low.device
     dt = h_low.dtype
     for n, t in (("h_low", h_low), ("h_mid", h_mid), ("h_high", h_high), ("kpre", kpre),
@@ -232,6 +276,8 @@ def eagle3_draft_expand(drafter: Eagle3Drafter, tree: Eagle3TreeCfg, h_low, h_mi
     _dev(root_tok, "root_tok", torch.int32)
     _dev(cu_prefix, "cu_prefix", torch.int32)
     N1 = tree.n_nodes + 1
+    _out_shapes(out, {"tokens": (B, N1), "parents": (B, N1), "depth": (B, N1), "score": (B, N1),
+                      "n_nodes": (B,)})
     if out is None:
         out = {
             "tokens": torch.empty((B, N1), dtype=torch.int32, device=dev),
@@ -278,7 +324,7 @@ def eagle3_draft_expand_sampled(drafter: Eagle3Drafter, tree: Eagle3TreeCfg, tem
     """The draft-tree round with sampled candidates.  Returns dict(tokens, parents, depth, score,
     n_nodes, slot_logits [B, S, V] fp32, draft_row [B, N+1] (row of slot_logits viewed as
     [B*S, V] at each node, -1 when the node was not evaluated)[, debug])."""
-    B = h_low.shape[0]
+    B = _draft_inputs(drafter, h_low, h_mid, h_high, root_tok, kpre, vpre, cu_prefix)
     dev = h_low.device
     dt = h_low.dtype
     for n, t in (("h_low", h_low), ("h_mid", h_mid), ("h_high", h_high), ("kpre", kpre),
@@ -288,6 +334,8 @@ def eagle3_draft_expand_sampled(drafter: Eagle3Drafter, tree: Eagle3TreeCfg, tem
     _dev(cu_prefix, "cu_prefix", torch.int32)
     N1 = tree.n_nodes + 1
     S = 1 + (tree.depth - 1) * tree.width
+    _out_shapes(out, {"tokens": (B, N1), "parents": (B, N1), "depth": (B, N1), "score": (B, N1),
+                      "n_nodes": (B,), "slot_logits": (B, S, drafter.vocab), "draft_row": (B, N1)})
     if out is None:
         out = {
             "tokens": torch.empty((B, N1), dtype=torch.int32, device=dev),
@@ -335,12 +383,19 @@ def eagle3_draft_expand_sampled(drafter: Eagle3Drafter, tree: Eagle3TreeCfg, tem
 def eagle3_build_tree_mask(cu_nodes, parents, cu_prefix, max_nodes: int, W64: int = 1,
                            T: Optional[int] = None, dev_status: Optional[torch.Tensor] = None,
                            out: Optional[dict] = None, stream=None) -> dict:
+    _shape(cu_nodes, "cu_nodes", None)
+    _shape(parents, "parents", None)
+    B = cu_nodes.numel() - 1
+    T = parents.numel() if T is None else T
+    if parents.numel() < T:
+        raise ValueError(f"parents has {parents.numel()} entries, fewer than T = {T}")
+    if cu_prefix is not None:
+        _shape(cu_prefix, "cu_prefix", B + 1)
+    _out_shapes(out, {"mask": (T, W64), "depth": (T,), "pos": (T,)})
     _dev(cu_nodes, "cu_nodes", torch.int32)
     _dev(parents, "parents", torch.int32)
     if cu_prefix is not None:
         _dev(cu_prefix, "cu_prefix", torch.int32)
-    B = cu_nodes.numel() - 1
-    T = parents.numel() if T is None else T
     dev = parents.device
     if out is None:
         out = {"mask": torch.empty((T, W64), dtype=torch.uint64, device=dev),
@@ -367,9 +422,21 @@ def eagle3_tree_attention(q, k_tree, v_tree, cu_nodes, max_nodes: int, mask, kpr
                           partials: bool = False, merged: bool = True,
                           workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None,
                           stream=None) -> dict:
-    """Tree attention.  partials=True returns o_part/lse_part; merged=True returns o/lse."""
+    """Tree attention.  partials=True returns o_part/lse_part; merged=True returns o/lse.
+    kpre, vpre [rows, Hkv, Dh] must hold every row that cu_prefix (device) names."""
+    _shape(q, "q", None, None, None)
     T, Hq, Dh = q.shape
-    Hkv = k_tree.shape[1]
+    Hkv = k_tree.shape[1] if isinstance(k_tree, torch.Tensor) and k_tree.dim() == 3 else -1
+    if Hkv <= 0 or Hq % Hkv:
+        raise ValueError("k_tree must be [T, Hkv, Dh] with Hq a multiple of Hkv")
+    _kv_pair(k_tree, v_tree, Hkv, Dh, "k_tree", "v_tree")
+    if k_tree.shape[0] != T:
+        raise ValueError(f"k_tree has {k_tree.shape[0]} rows, q has {T}")
+    if not isinstance(mask, torch.Tensor) or mask.dim() not in (1, 2) or mask.shape[0] != T:
+        raise ValueError(f"mask must be [T, W64] or [T] with T = {T} rows")
+    if max_prefix > 0:
+        _kv_pair(kpre, vpre, Hkv, Dh, "kpre", "vpre")
+        _shape(cu_prefix, "cu_prefix", cu_nodes.numel())
     dt = q.dtype
     for n, t in (("q", q), ("k_tree", k_tree), ("v_tree", v_tree)):
         _dev(t, n, dt)
@@ -383,6 +450,8 @@ def eagle3_tree_attention(q, k_tree, v_tree, cu_nodes, max_nodes: int, mask, kpr
     W64 = mask.shape[1] if mask.dim() == 2 else 1
     S = eagle3_tree_attention_num_splits(B, Hq, Hkv, max_nodes, max_prefix, n_splits)
     dev = q.device
+    _out_shapes(out, {"o_part": (S + 1, T, Hq, Dh), "lse_part": (S + 1, T, Hq), "o": (T, Hq, Dh),
+                      "lse": (T, Hq)})
     if out is None:
         out = {}
         if partials:
@@ -408,9 +477,12 @@ def eagle3_tree_attention(q, k_tree, v_tree, cu_nodes, max_nodes: int, mask, kpr
 def eagle3_lse_merge(o_part, lse_part, out_dtype=torch.float32, out: Optional[dict] = None,
                      stream=None) -> dict:
     """o_part [S, rows, Dh] fp32, lse_part [S, rows] fp32 -> dict(o [rows, Dh], lse [rows])."""
+    _shape(o_part, "o_part", None, None, None)
+    S, rows, Dh = o_part.shape
+    _shape(lse_part, "lse_part", S, rows)
     _dev(o_part, "o_part", torch.float32)
     _dev(lse_part, "lse_part", torch.float32)
-    S, rows, Dh = o_part.shape
+    _out_shapes(out, {"o": (rows, Dh), "lse": (rows,)})
     if out is None:
         out = {"o": torch.empty((rows, Dh), dtype=out_dtype, device=o_part.device),
                "lse": torch.empty((rows,), dtype=torch.float32, device=o_part.device)}
@@ -421,9 +493,25 @@ def eagle3_lse_merge(o_part, lse_part, out_dtype=torch.float32, out: Optional[di
     return out
 
 
+def _accept_inputs(cu_nodes, tokens, parents, mask, logits, max_depth: int, out: Optional[dict]):
+    _shape(logits, "logits", None, None)
+    T = logits.shape[0]
+    _shape(cu_nodes, "cu_nodes", None)
+    B = cu_nodes.numel() - 1
+    if tokens.numel() != T or parents.numel() != T:
+        raise ValueError(f"tokens and parents need one entry per logits row ({T})")
+    if mask is not None and (not isinstance(mask, torch.Tensor) or mask.dim() not in (1, 2) or mask.shape[0] != T):
+        raise ValueError(f"mask must be [T, W64] or [T] with T = {T} rows")
+    if max_depth < 0:
+        raise ValueError("max_depth must be >= 0")
+    _out_shapes(out, {"accept_len": (B,), "path": (B, max_depth + 1), "out_tokens": (B, max_depth + 1),
+                      "bonus": (B,)})
+
+
 def eagle3_accept(cu_nodes, tokens, parents, mask, logits, temperature: float, seed: int,
                   round: int, max_depth: int, workspace: Optional[torch.Tensor] = None,
                   out: Optional[dict] = None, stream=None) -> dict:
+    _accept_inputs(cu_nodes, tokens, parents, mask, logits, max_depth, out)
     _dev(cu_nodes, "cu_nodes", torch.int32)
     _dev(tokens, "tokens", torch.int32)
     _dev(parents, "parents", torch.int32)
@@ -454,6 +542,7 @@ def eagle3_accept_noalloc(cu_nodes, tokens, parents, mask, logits, temperature: 
                           round: int, max_depth: int, out: Optional[dict] = None, stream=None) -> dict:
     """eagle3_accept without a workspace (the library's fixed per-GPU scratch array); for
     callers that cannot allocate.  Pass `out` to allocate nothing here either."""
+    _accept_inputs(cu_nodes, tokens, parents, mask, logits, max_depth, out)
     _dev(cu_nodes, "cu_nodes", torch.int32)
     _dev(tokens, "tokens", torch.int32)
     _dev(parents, "parents", torch.int32)
@@ -484,6 +573,9 @@ def eagle3_accept_sampled(cu_nodes, tokens, parents, logits, draft_logits, draft
                           stream=None) -> dict:
     """Acceptance of sampled candidates: draft_logits [R, V] holds the drafter's logits, and
     draft_row[i] names the row of node i (-1 for a node without children)."""
+    _accept_inputs(cu_nodes, tokens, parents, None, logits, max_depth, out)
+    if draft_row.numel() != logits.shape[0]:
+        raise ValueError("draft_row needs one entry per logits row")
     _dev(cu_nodes, "cu_nodes", torch.int32)
     _dev(tokens, "tokens", torch.int32)
     _dev(parents, "parents", torch.int32)
@@ -537,6 +629,11 @@ def eagle3_commit_kv(cu_nodes, path, accept_len, k_tree, v_tree, dst_row, k_cach
                      dev_status: Optional[torch.Tensor] = None, stream=None) -> None:
     """Copy the accepted path's tree K/V rows (path [B, path_stride] from eagle3_accept) into
     the caches at rows dst_row[b] + i, in place."""
+    _shape(cu_nodes, "cu_nodes", None)
+    B = cu_nodes.numel() - 1
+    _shape(path, "path", B, None)
+    _shape(accept_len, "accept_len", B)
+    _shape(dst_row, "dst_row", B)
     for n, t in (("cu_nodes", cu_nodes), ("path", path), ("accept_len", accept_len),
                  ("dst_row", dst_row)):
         _dev(t, n, torch.int32)
@@ -565,6 +662,14 @@ def eagle3_drafter_catchup(drafter: Eagle3Drafter, tokens, pos, h_low, h_mid, h_
                            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Drafter keys/values of committed positions (rows) into the drafter prefix caches at
     dst_row, from the real target features; returns the fused features g [n, d] (fp32)."""
+    _shape(tokens, "tokens", None)
+    n_rows = tokens.numel()
+    for n, t in (("pos", pos), ("dst_row", dst_row)):
+        _shape(t, n, n_rows)
+    for n, t in (("h_low", h_low), ("h_mid", h_mid), ("h_high", h_high)):
+        _shape(t, n, n_rows, drafter.d)
+    if g_out is not None:
+        _shape(g_out, "g_out", n_rows, drafter.d)
     for n, t in (("tokens", tokens), ("pos", pos), ("dst_row", dst_row)):
         _dev(t, n, torch.int32)
     dt = h_low.dtype
@@ -596,11 +701,19 @@ def eagle3_causal_attention(q, k, v, scale: float, o: Optional[torch.Tensor] = N
                             lse: Optional[torch.Tensor] = None, stream=None):
     """Main causal attention of every position: q [L, Hq, Dh], k, v [L, Hkv, Dh] (bf16).
     Returns (o [L, Hq, Dh] fp32, lse [L, Hq] fp32)."""
+    _shape(q, "q", None, None, None)
+    L, Hq, Dh = q.shape
+    Hkv = k.shape[1] if isinstance(k, torch.Tensor) and k.dim() == 3 else -1
+    if Hkv <= 0 or Hq % Hkv:
+        raise ValueError("k must be [L, Hkv, Dh] with Hq a multiple of Hkv")
+    _shape(k, "k", L, Hkv, Dh)
+    _shape(v, "v", L, Hkv, Dh)
+    for n, t in (("o", o), ("lse", lse)):
+        if t is not None:
+            _shape(t, n, *((L, Hq, Dh) if n == "o" else (L, Hq)))
     dt = q.dtype
     for n, t in (("q", q), ("k", k), ("v", v)):
         _dev(t, n, dt)
-    L, Hq, Dh = q.shape
-    Hkv = k.shape[1]
     if o is None:
         o = torch.empty((L, Hq, Dh), dtype=torch.float32, device=q.device)
     if lse is None:
@@ -617,11 +730,19 @@ def eagle3_branch_attention(q, kb, vb, scale: float, o: Optional[torch.Tensor] =
                             lse: Optional[torch.Tensor] = None, stream=None):
     """Per-position branch attention: q [L, Hq, Dh], kb, vb [n_steps, L, Hkv, Dh].
     Returns (o [L, Hq, Dh] fp32, lse [L, Hq] fp32)."""
+    _shape(q, "q", None, None, None)
+    L, Hq, Dh = q.shape
+    _shape(kb, "kb", None, L, None, Dh)
+    n_steps, _, Hkv, _ = kb.shape
+    if Hkv <= 0 or Hq % Hkv:
+        raise ValueError("kb must be [n_steps, L, Hkv, Dh] with Hq a multiple of Hkv")
+    _shape(vb, "vb", n_steps, L, Hkv, Dh)
+    for n, t in (("o", o), ("lse", lse)):
+        if t is not None:
+            _shape(t, n, *((L, Hq, Dh) if n == "o" else (L, Hq)))
     dt = q.dtype
     for n, t in (("q", q), ("kb", kb), ("vb", vb)):
         _dev(t, n, dt)
-    L, Hq, Dh = q.shape
-    n_steps, _, Hkv, _ = kb.shape
     if o is None:
         o = torch.empty((L, Hq, Dh), dtype=torch.float32, device=q.device)
     if lse is None:
@@ -642,6 +763,10 @@ def eagle3_branch_attention(q, kb, vb, scale: float, o: Optional[torch.Tensor] =
 def eagle3_linear(x, w, out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                   stream=None) -> torch.Tensor:
     """Y = X W^T in fp32 through the drafter's GEMM kernels; x [M, K], w [N, K] (same dtype)."""
+    _shape(x, "x", None, None)
+    _shape(w, "w", None, x.shape[1])
+    if out is not None:
+        _shape(out, "out", x.shape[0], w.shape[0])
     _dev(w, "w")
     if not (isinstance(x, torch.Tensor) and x.is_cuda and x.dim() == 2 and x.stride(1) == 1):
         raise ValueError("x must be a 2-D device tensor with unit column stride")

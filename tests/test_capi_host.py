@@ -246,6 +246,76 @@ def test_binding_refuses_mismatched_caches():
         capi._cache_pair(torch.empty((10, 8, 256))[:, :, :128], torch.empty((10, 8, 128)), (8, 128))
 
 
+def test_binding_refuses_mismatched_shapes():
+    """The library sees raw pointers: every binding checks, on the host and before any device
+    check, that the tensors it passes have the shapes its size arguments imply (a smaller
+    tensor would be read or written out of bounds on the device).  CPU tensors suffice: the
+    shape check comes first."""
+    import torch
+    bf = torch.bfloat16
+    with pytest.raises(ValueError, match="w has shape"):
+        capi.eagle3_linear(torch.empty((4, 64), dtype=bf), torch.empty((8, 32), dtype=bf))
+    with pytest.raises(ValueError, match="out has shape"):
+        capi.eagle3_linear(torch.empty((4, 64), dtype=bf), torch.empty((8, 64), dtype=bf),
+                           out=torch.empty((4, 7)))
+    T, Hq, Hkv, Dh = 6, 8, 2, 64
+    q = torch.empty((T, Hq, Dh), dtype=bf)
+    kt = torch.empty((T, Hkv, Dh), dtype=bf)
+    cu = torch.tensor([0, T], dtype=torch.int32)
+    mask = torch.empty((T, 1), dtype=torch.uint64)
+    kp = torch.empty((40, Hkv, Dh), dtype=bf)
+    with pytest.raises(ValueError, match="k_tree has 5 rows"):
+        capi.eagle3_tree_attention(q, kt[:5], kt[:5], cu, T, mask, kp, kp, cu, 40, 0.125)
+    with pytest.raises(ValueError, match="differs"):
+        capi.eagle3_tree_attention(q, kt, kt[:, :, :32], cu, T, mask, kp, kp, cu, 40, 0.125)
+    with pytest.raises(ValueError, match="mask"):
+        capi.eagle3_tree_attention(q, kt, kt, cu, T, mask[:4], kp, kp, cu, 40, 0.125)
+    with pytest.raises(ValueError, match="kpre has shape"):
+        capi.eagle3_tree_attention(q, kt, kt, cu, T, mask, kp[:, :1], kp[:, :1], cu, 40, 0.125)
+    with pytest.raises(ValueError, match="multiple"):
+        capi.eagle3_tree_attention(q, torch.empty((T, 3, Dh), dtype=bf), torch.empty((T, 3, Dh), dtype=bf),
+                                   cu, T, mask, kp, kp, cu, 40, 0.125)
+    with pytest.raises(ValueError, match="lse_part has shape"):
+        capi.eagle3_lse_merge(torch.empty((3, 10, 64)), torch.empty((3, 9)))
+    logits = torch.empty((T, 100), dtype=bf)
+    tok = torch.empty((T,), dtype=torch.int32)
+    with pytest.raises(ValueError, match="one entry per logits row"):
+        capi.eagle3_accept(cu, tok[:5], tok, mask, logits, 1.0, 0, 0, 3)
+    with pytest.raises(ValueError, match="path has shape"):
+        capi.eagle3_accept(cu, tok, tok, mask, logits, 1.0, 0, 0, 3,
+                           out={"path": torch.empty((1, 3), dtype=torch.int32)})
+    with pytest.raises(ValueError, match="draft_row"):
+        capi.eagle3_accept_sampled(cu, tok, tok, logits, logits, tok[:2], 1.0, 0, 0, 3, 4)
+    with pytest.raises(ValueError, match="dst_row has shape"):
+        capi.eagle3_commit_kv(cu, torch.empty((1, 4), dtype=torch.int32), torch.empty((1,), dtype=torch.int32),
+                              kt, kt, torch.empty((2,), dtype=torch.int32), kp, kp)
+    L = 32
+    with pytest.raises(ValueError, match="v has shape"):
+        capi.eagle3_causal_attention(torch.empty((L, Hq, Dh), dtype=bf), torch.empty((L, Hkv, Dh), dtype=bf),
+                                     torch.empty((L - 1, Hkv, Dh), dtype=bf), 0.125)
+    with pytest.raises(ValueError, match="vb has shape"):
+        capi.eagle3_branch_attention(torch.empty((L, Hq, Dh), dtype=bf), torch.empty((3, L, Hkv, Dh), dtype=bf),
+                                     torch.empty((2, L, Hkv, Dh), dtype=bf), 0.125)
+    with pytest.raises(ValueError, match="parents has"):
+        capi.eagle3_build_tree_mask(cu, tok[:3], None, T, T=T)
+
+
+def test_make_drafter_checks_weight_shapes():
+    """make_drafter refuses weights whose shapes disagree with the layer the struct describes."""
+    import torch
+    d, Hq, Hkv, Dh, F, V = 64, 4, 2, 16, 96, 50
+    w = {"embed": (V, d), "w_fuse": (d, 3 * d), "g_embed": (d,), "g_feat": (d,), "g_mlp": (d,),
+         "g_final": (d,), "w_qkv": ((Hq + 2 * Hkv) * Dh, 2 * d), "w_o": (d, Hq * Dh),
+         "w_gate_up": (2 * F, d), "w_down": (d, F), "w_lm": (V, d)}
+    weights = {k: torch.empty(v) for k, v in w.items()}
+    weights["w_qkv"] = torch.empty(((Hq + 2 * Hkv) * Dh, d))   # half the input width
+    with pytest.raises(ValueError, match="w_qkv has shape"):
+        capi.make_drafter(weights, Hq, Hkv, Dh)
+    weights = {k: torch.empty(v) for k, v in w.items()}
+    with pytest.raises(ValueError, match="multiple"):
+        capi.make_drafter(weights, Hq, 3, Dh)
+
+
 def test_accept_noalloc_host_validation(lib):
     """eagle3_accept_noalloc rejects a winner list larger than its fixed scratch array (and
     bad arguments) on the host, before any device call."""
