@@ -108,6 +108,11 @@ ATTN_CASES = [
     # prefix lengths 0 and 8192 in one call: a lone root's output is its own value (large),
     # a long prefix's output is an average of 8192 values (small); per-row tolerance
     ("bf16_prefix_0_and_8192", torch.bfloat16, 32, 8, 128, [1, 61, 5], [0, 8192, 8192], 0),
+    # automatic splits where each (request, KV head) has a single row block: 80 rows per KV
+    # head in one 128-row block (the 70B-shaped drafter steps) and 40 rows in one 64-row
+    # block (the 8B-shaped ones), ragged prefixes down to less than one key tile
+    ("rows80_one_block_auto_splits", torch.bfloat16, 64, 8, 128, [10, 3, 10], [8192, 77, 1000], 0),
+    ("rows40_one_block_auto_splits", torch.bfloat16, 32, 8, 128, [10, 10, 1], [2048, 333, 40], 0),
 ]
 
 
