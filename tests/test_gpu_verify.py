@@ -113,6 +113,9 @@ ATTN_CASES = [
     # block (the 8B-shaped ones), ragged prefixes down to less than one key tile
     ("rows80_one_block_auto_splits", torch.bfloat16, 64, 8, 128, [10, 3, 10], [8192, 77, 1000], 0),
     ("rows40_one_block_auto_splits", torch.bfloat16, 32, 8, 128, [10, 10, 1], [2048, 333, 40], 0),
+    # head size 64 with a prefix in both bf16 workgroup shapes (96 and 48 rows per KV head)
+    ("dh64_rows96_prefix", torch.bfloat16, 16, 2, 64, [12, 5], [1000, 64], 0),
+    ("dh64_rows48_prefix", torch.bfloat16, 8, 2, 64, [12, 3], [500, 129], 0),
 ]
 
 
